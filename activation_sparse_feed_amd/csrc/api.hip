@@ -1,0 +1,148 @@
+// C ABI of the activation-sparse gated FFN (declared in include/sffn.h):
+// argument validation on the host, workspace carving and kernel launches.
+// Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include "../../include/sffn.h"
+#include "launch.h"
+
+namespace {
+
+using namespace sffn;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+size_t elt_bytes(int dtype) { return dtype == SFFN_BF16 ? 2 : 4; }
+
+// Shape checks shared by every call.
+int32_t check_shape(const sffn_shape* s) {
+  if (s == nullptr) return SFFN_ERR_ARG;
+  if (s->T < 0 || s->d_model <= 0 || s->d_ff <= 0 || s->cap < 0 || s->tile <= 0)
+    return SFFN_ERR_ARG;
+  if (s->dtype != SFFN_F32 && s->dtype != SFFN_BF16) return SFFN_ERR_ARG;
+  if (s->tile != 128) return SFFN_ERR_UNSUPPORTED;
+  if (s->d_ff % 128 != 0 || s->d_ff > 65535) return SFFN_ERR_UNSUPPORTED;
+  if (s->d_model % 8 != 0 || s->d_model < 8 || s->d_model > 8192) return SFFN_ERR_UNSUPPORTED;
+  if (s->cap > 128) return SFFN_ERR_UNSUPPORTED;
+  return SFFN_OK;
+}
+
+bool ptrs_ok(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+size_t dense_ws(const sffn_shape* s) {
+  return align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
+}
+
+size_t hybrid_ws(const sffn_shape* s) {
+  return route_workspace_bytes(s->T) + align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? SFFN_OK : SFFN_ERR_HIP; }
+
+// Guard band of the activity decision (see the TwELL epilogue).  bf16: the
+// 16x16x32 MFMA chain rounds once per instruction, K/32 roundings, plus the
+// bias add; float32: one FMA rounding per k.  Both with a factor 4 margin
+// over the unit roundoff 2^-24 (the bound on sum |x_k w_k| is ||x|| ||w||).
+GuardBand guard_band(const sffn_shape* s) {
+  const float u4 = 0x1p-22f;
+  if (s->dtype == SFFN_BF16) return GuardBand{u4 * (float)(s->d_model / 32 + 2), u4};
+  return GuardBand{u4 * (float)(s->d_model + 2), u4};
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                   uint16_t* count, uint16_t* idx, void* val, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({x, wg_t, count}) || (b_g && !aligned16(b_g))) return SFFN_ERR_ARG;
+  if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
+  return hip_status(launch_gate_twell(shape->dtype, x, wg_t, b_g, count, idx, val, shape->T,
+                                      shape->d_model, shape->d_ff, shape->cap, guard_band(shape),
+                                      (hipStream_t)stream));
+}
+
+int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t, const void* wd,
+                       const uint16_t* count, const uint16_t* idx, const void* val, void* y,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({x, wu_t, wd, count, y})) return SFFN_ERR_ARG;
+  if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
+  const int nt = shape->d_ff / 128;
+  const size_t need = sparse_workspace_bytes(shape->T, nt, shape->d_model);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || ws_bytes < need))
+    return SFFN_ERR_WORKSPACE;
+  return hip_status(launch_sparse_updown(shape->dtype, x, wu_t, wd, count, idx, val, y,
+                                         workspace, shape->T, shape->d_model, nt, shape->cap,
+                                         (hipStream_t)stream));
+}
+
+int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                     const void* wu_t, const void* wd, const uint16_t* count, int32_t* routed,
+                     int32_t* n_routed, void* workspace, size_t ws_bytes, void* y, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({x, wg_t, wu_t, wd, count, routed, n_routed, y}) || (b_g && !aligned16(b_g)))
+    return SFFN_ERR_ARG;
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < hybrid_ws(shape))
+    return SFFN_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = shape->T, K = shape->d_model, N = shape->d_ff;
+  hipError_t e = launch_route(count, T, N / 128, shape->cap, routed, n_routed, workspace, s);
+  if (e != hipSuccess) return SFFN_ERR_HIP;
+  void* h = (char*)workspace + route_workspace_bytes(T);
+  e = launch_dense_gateup(shape->dtype, x, wg_t, b_g, wu_t, h, T, routed, n_routed, K, N, s);
+  if (e != hipSuccess) return SFFN_ERR_HIP;
+  e = launch_down(shape->dtype, h, wd, y, T, routed, n_routed, N, K, s);
+  return hip_status(e);
+}
+
+int32_t dense_ffn_ref(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                      const void* wu_t, const void* wd, void* workspace, size_t ws_bytes, void* y,
+                      void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({x, wg_t, wu_t, wd, y}) || (b_g && !aligned16(b_g))) return SFFN_ERR_ARG;
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < dense_ws(shape))
+    return SFFN_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = shape->T, K = shape->d_model, N = shape->d_ff;
+  hipError_t e = launch_dense_gateup(shape->dtype, x, wg_t, b_g, wu_t, workspace, T, nullptr,
+                                     nullptr, K, N, s);
+  if (e != hipSuccess) return SFFN_ERR_HIP;
+  return hip_status(launch_down(shape->dtype, workspace, wd, y, T, nullptr, nullptr, N, K, s));
+}
+
+size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
+  if (check_shape(shape) != SFFN_OK) return 0;
+  switch (which) {
+    case SFFN_WS_HYBRID: return hybrid_ws(shape);
+    case SFFN_WS_DENSE: return dense_ws(shape);
+    case SFFN_WS_SPARSE: return sparse_workspace_bytes(shape->T, shape->d_ff / 128, shape->d_model);
+    default: return 0;
+  }
+}
+
+const char* sffn_strerror(int32_t status) {
+  switch (status) {
+    case SFFN_OK: return "success";
+    case SFFN_ERR_ARG: return "invalid argument (null or misaligned pointer, bad size)";
+    case SFFN_ERR_UNSUPPORTED: return "shape or parameter outside the supported range";
+    case SFFN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SFFN_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown sffn status";
+  }
+}
+
+}  // extern "C"

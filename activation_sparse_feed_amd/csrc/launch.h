@@ -1,0 +1,47 @@
+// Internal launchers of the sffn kernels (host side, C++ linkage).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sffn {
+
+// Guard band of the TwELL activity decision: an entry is re-evaluated exactly
+// when |z32| <= coef_xw * ||x_t|| * ||w_j|| + coef_b * |b_j|.
+struct GuardBand {
+  float coef_xw;
+  float coef_b;
+};
+
+hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const float* b_g,
+                             uint16_t* count, uint16_t* idx, void* val, int T, int K, int N,
+                             int cap, GuardBand gb, hipStream_t stream);
+
+// h[m, :] = ReLU(x[row(m)] wg_t^T + b) * (x[row(m)] wu_t^T) for m < rows, where
+// row(m) = rowmap[m] (rowmap != nullptr) and rows = *n_rows_dev (n_rows_dev !=
+// nullptr) else rows = M.
+hipError_t launch_dense_gateup(int dtype, const void* x, const void* wg_t, const float* b_g,
+                               const void* wu_t, void* h, int M, const int* rowmap,
+                               const int* n_rows_dev, int K, int N, hipStream_t stream);
+
+// y[row(m), :] = h[m, :] wd for m < rows (same row rules as above).
+hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
+                       const int* rowmap, const int* n_rows_dev, int K, int N,
+                       hipStream_t stream);
+
+// Number of column splits of the fused sparse kernel for this shape.
+int sparse_splits(int T, int n_tiles, int d_model);
+size_t sparse_workspace_bytes(int T, int n_tiles, int d_model);
+
+hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, const void* wd,
+                                const uint16_t* count, const uint16_t* idx, const void* val,
+                                void* y, void* ws, int T, int K, int n_tiles, int cap,
+                                hipStream_t stream);
+
+// Routing scan: flags, per-block counts, ascending compaction.
+size_t route_workspace_bytes(int T);
+hipError_t launch_route(const uint16_t* count, int T, int n_tiles, int cap, int32_t* routed,
+                        int32_t* n_routed, void* ws, hipStream_t stream);
+
+}  // namespace sffn

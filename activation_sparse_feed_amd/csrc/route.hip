@@ -1,0 +1,97 @@
+// Hybrid routing scan (pwwt.cn article, section 03: the rare high-activity
+// tokens that do not fit the compact format are diverted to a dense path).
+//
+// A row is routed when any of its TwELL tiles holds more active columns than
+// the capacity.  Two small kernels, no atomics, deterministic:
+//   route_flags    one thread per row: flag = OR_k (count[t, k] > cap);
+//                  per-256-row block counts
+//   route_compact  each block adds the counts of the blocks before it and
+//                  writes its flagged rows in ascending order; the last block
+//                  writes n_routed.
+#include "common.cuh"
+#include "launch.h"
+
+namespace sffn {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict__ count, int T,
+                                                      int nt, int cap, int* __restrict__ flags,
+                                                      int* __restrict__ block_count) {
+  const int t = blockIdx.x * kBlock + threadIdx.x;
+  int f = 0;
+  if (t < T) {
+    const uint16_t* row = count + (size_t)t * nt;
+    for (int k = 0; k < nt; ++k) f |= (int)row[k] > cap;
+    flags[t] = f;
+  }
+  const int n = __syncthreads_count(f);
+  if (threadIdx.x == 0) block_count[blockIdx.x] = n;
+}
+
+__global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ flags, int T,
+                                                        const int* __restrict__ block_count,
+                                                        int32_t* __restrict__ routed,
+                                                        int32_t* __restrict__ n_routed) {
+  __shared__ int wave_tot[kBlock / kWave];
+  __shared__ int prefix_s;
+  const int b = blockIdx.x;
+  // exclusive prefix over earlier blocks
+  int acc = 0;
+  for (int i = threadIdx.x; i < b; i += kBlock) acc += block_count[i];
+  // block reduction of acc
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  if (lane == 0) wave_tot[w] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int p = 0;
+    for (int i = 0; i < kBlock / kWave; ++i) p += wave_tot[i];
+    prefix_s = p;
+  }
+  __syncthreads();
+  const int prefix = prefix_s;
+  __syncthreads();
+  // in-block scan of the flags
+  const int t = b * kBlock + threadIdx.x;
+  const int f = (t < T) ? flags[t] : 0;
+  const uint64_t m = __ballot(f);
+  if (lane == 0) wave_tot[w] = __popcll(m);
+  __syncthreads();
+  int off = prefix;
+  for (int i = 0; i < w; ++i) off += wave_tot[i];
+  if (f) routed[off + lanes_below(m)] = t;
+  if (b == (int)gridDim.x - 1 && threadIdx.x == kBlock - 1) {
+    int tot = off;
+    for (int i = w; i < kBlock / kWave; ++i) tot += wave_tot[i];
+    *n_routed = tot;
+  }
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t route_workspace_bytes(int T) {
+  const int nb = (T + kBlock - 1) / kBlock;
+  return align256((size_t)T * 4) + align256((size_t)nb * 4);
+}
+
+hipError_t launch_route(const uint16_t* count, int T, int n_tiles, int cap, int32_t* routed,
+                        int32_t* n_routed, void* ws, hipStream_t stream) {
+  const int nb = (T + kBlock - 1) / kBlock;
+  int* flags = (int*)ws;
+  int* block_count = (int*)((char*)ws + align256((size_t)T * 4));
+  hipLaunchKernelGGL(route_flags, dim3(nb), dim3(kBlock), 0, stream, count, T, n_tiles, cap, flags,
+                     block_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_compact, dim3(nb), dim3(kBlock), 0, stream, flags, T, block_count,
+                     routed, n_routed);
+  return hipGetLastError();
+}
+
+}  // namespace sffn

@@ -1,0 +1,219 @@
+// Fused up(.)gate -> down over the TwELL nonzeros (pwwt.cn article, section
+// 02: one pass computes the up projection only for the packed nonzeros,
+// multiplies by the gate value and accumulates the down projection, so the
+// intermediate h never goes to memory).
+//
+// Work item = (token t, column split s): one wavefront walks the live TwELL
+// entries of tiles [s*nt/S, (s+1)*nt/S) of row t.  For each entry (j, h):
+//   u  = x_t . wu_t[j]      16-byte loads of the wu_t row, lane-local dot,
+//                           wave reduction
+//   y += (h * u) * wd[j]    16-byte loads of the wd row, float32 FMA into the
+//                           lane's slice of y_t held in registers
+// With S == 1 the wave writes y_t once, rounded to dtype.  With S > 1 (few
+// tokens, e.g. decode) each split writes a float32 partial; the last split to
+// finish a token (ticket counter) sums the partials in split order, writes
+// y_t and re-arms the ticket, so the result does not depend on timing.
+// Rows with any tile over capacity are skipped (the hybrid route owns them).
+#include "common.cuh"
+#include "launch.h"
+
+namespace sffn {
+
+namespace {
+
+struct SparseArgs {
+  const void* x;
+  const void* wu;
+  const void* wd;
+  const uint16_t* count;
+  const uint16_t* idx;
+  const void* val;
+  void* y;
+  int* tickets;    // [T], S > 1 only
+  float* partial;  // [S, T, K], S > 1 only
+  int T, K, nt, cap, S;
+};
+
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void sparse_updown(SparseArgs a) {
+  constexpr int E = Elt<T>::kPerChunk;
+  const int lane = lane_id();
+  const int item = uniform((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int t = item / a.S;
+  const int s = item - t * a.S;
+  if (t >= a.T) return;
+  const uint16_t* cnt_row = a.count + (size_t)t * a.nt;
+
+  // routed row?  (any tile over capacity)
+  bool over = false;
+  for (int k = lane; k < a.nt; k += kWave) over |= (int)cnt_row[k] > a.cap;
+  if (__ballot(over) != 0ull) return;
+
+  const int nch = a.K / E;  // 16-byte chunks per row
+  const T* xrow = (const T*)a.x + (size_t)t * a.K;
+  float xv[NCH][E];
+  float yv[NCH][E];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + kWave * c;
+    if (ch < nch) {
+      Elt<T>::unpack(ldg16(xrow + (size_t)ch * E), xv[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) xv[c][e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) yv[c][e] = 0.f;
+  }
+
+  const int k_lo = (int)(((long)s * a.nt) / a.S);
+  const int k_hi = (int)(((long)(s + 1) * a.nt) / a.S);
+  const T* wu = (const T*)a.wu;
+  const T* wd = (const T*)a.wd;
+  for (int k = k_lo; k < k_hi; ++k) {
+    const int n = min((int)cnt_row[k], a.cap);
+    const size_t base = ((size_t)t * a.nt + k) * a.cap;
+    for (int e = 0; e < n; ++e) {
+      const int j = uniform((int)a.idx[base + e]);
+      if (j >= a.nt * 128) continue;  // never true for a TwELL written by twell_pack
+      const float h = Elt<T>::load1(a.val, base + e);
+      const T* urow = wu + (size_t)j * a.K;
+      const T* drow = wd + (size_t)j * a.K;
+      u32x4_t ur[NCH], dr[NCH];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int ch = lane + kWave * c;
+        ur[c] = ch < nch ? ldg16(urow + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+        dr[c] = ch < nch ? ldg16(drow + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      float p = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        float uf[E];
+        Elt<T>::unpack(ur[c], uf);
+#pragma unroll
+        for (int q = 0; q < E; ++q) p = fmaf(xv[c][q], uf[q], p);
+      }
+      const float g = h * wave_sum(p);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        float df[E];
+        Elt<T>::unpack(dr[c], df);
+#pragma unroll
+        for (int q = 0; q < E; ++q) yv[c][q] = fmaf(g, df[q], yv[c][q]);
+      }
+    }
+  }
+
+  if (a.S == 1) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + kWave * c;
+      if (ch < nch)
+#pragma unroll
+        for (int q = 0; q < E; ++q) Elt<T>::store1(a.y, (size_t)t * a.K + (size_t)ch * E + q, yv[c][q]);
+    }
+    return;
+  }
+
+  // split partial, then the last split of this token reduces in split order
+  float* prow = a.partial + ((size_t)s * a.T + t) * a.K;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + kWave * c;
+    if (ch < nch) {
+#pragma unroll
+      for (int q = 0; q < E; q += 4)
+        *(float4*)(prow + (size_t)ch * E + q) = make_float4(yv[c][q], yv[c][q + 1], yv[c][q + 2], yv[c][q + 3]);
+    }
+  }
+  __threadfence();
+  int ticket = 0;
+  if (lane == 0) ticket = atomicAdd(a.tickets + t, 1);
+  ticket = __shfl(ticket, 0, kWave);
+  if (ticket != a.S - 1) return;
+  __threadfence();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int q = 0; q < E; ++q) yv[c][q] = 0.f;
+  for (int ss = 0; ss < a.S; ++ss) {
+    const float* pr = a.partial + ((size_t)ss * a.T + t) * a.K;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + kWave * c;
+      if (ch < nch) {
+#pragma unroll
+        for (int q = 0; q < E; q += 4) {
+          const float4 v = *(const float4*)(pr + (size_t)ch * E + q);
+          yv[c][q] += v.x; yv[c][q + 1] += v.y; yv[c][q + 2] += v.z; yv[c][q + 3] += v.w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + kWave * c;
+    if (ch < nch)
+#pragma unroll
+      for (int q = 0; q < E; ++q) Elt<T>::store1(a.y, (size_t)t * a.K + (size_t)ch * E + q, yv[c][q]);
+  }
+  if (lane == 0) a.tickets[t] = 0;
+}
+
+template <typename T>
+hipError_t launch_typed(const SparseArgs& a, int nch_per_lane, hipStream_t stream) {
+  const int items = a.T * a.S;
+  const dim3 grid((unsigned)((items + 3) / 4));
+  switch (nch_per_lane) {
+    case 1: hipLaunchKernelGGL((sparse_updown<T, 1>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((sparse_updown<T, 2>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((sparse_updown<T, 4>), grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((sparse_updown<T, 8>), grid, dim3(256), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((sparse_updown<T, 16>), grid, dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((sparse_updown<T, 32>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+int sparse_splits(int T, int n_tiles, int /*d_model*/) {
+  // enough wavefronts to cover the chip (~2048) when there are few tokens
+  if (T <= 0) return 1;
+  int s = (2048 + T - 1) / T;
+  if (s > n_tiles) s = n_tiles;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : s;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t sparse_workspace_bytes(int T, int n_tiles, int d_model) {
+  const int S = sparse_splits(T, n_tiles, d_model);
+  if (S <= 1) return 0;
+  return align256((size_t)T * 4) + (size_t)S * T * d_model * 4;
+}
+
+hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, const void* wd,
+                                const uint16_t* count, const uint16_t* idx, const void* val,
+                                void* y, void* ws, int T, int K, int n_tiles, int cap,
+                                hipStream_t stream) {
+  const int S = sparse_splits(T, n_tiles, K);
+  SparseArgs a{x, wu_t, wd, count, idx, val, y, nullptr, nullptr, T, K, n_tiles, cap, S};
+  if (S > 1) {
+    a.tickets = (int*)ws;
+    a.partial = (float*)((char*)ws + align256((size_t)T * 4));
+  }
+  if (dtype == 1) return launch_typed<uint16_t>(a, pow2_at_least((K / 8 + 63) / 64), stream);
+  return launch_typed<float>(a, pow2_at_least((K / 4 + 63) / 64), stream);
+}
+
+}  // namespace sffn

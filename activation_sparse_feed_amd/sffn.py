@@ -1,0 +1,194 @@
+"""Python binding of libsffn.so: argument marshalling only.
+
+Every function takes torch tensors that live on the GPU, checks their dtype,
+shape and contiguity, and passes raw device pointers plus the current HIP
+stream to the C entry point of the same name.  All arithmetic happens in the
+library's kernels; there is no fallback: if the library is missing, importing
+this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsffn.so")
+
+SFFN_OK, SFFN_ERR_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ERR_HIP = 0, -1, -2, -3, -4
+SFFN_F32, SFFN_BF16 = 0, 1
+WS_HYBRID, WS_DENSE, WS_SPARSE = 0, 1, 2
+TILE = 128
+
+EXPORTED = ("twell_pack", "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref",
+            "sffn_workspace_bytes", "sffn_strerror")
+
+
+class SffnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("cap", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m activation_sparse_feed_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    sp = ctypes.POINTER(Shape)
+    lib.twell_pack.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sparse_ffn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    for fn in ("twell_pack", "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref"):
+        getattr(lib, fn).restype = i32
+    lib.sffn_workspace_bytes.argtypes = [sp, i32]
+    lib.sffn_workspace_bytes.restype = sz
+    lib.sffn_strerror.argtypes = [i32]
+    lib.sffn_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = load_library()
+
+
+def strerror(status: int) -> str:
+    return _lib.sffn_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SFFN_OK:
+        raise SffnError(fn, status, strerror(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SFFN_BF16
+    if t.dtype == torch.float32:
+        return SFFN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_shape(T: int, d_model: int, d_ff: int, cap: int, dtype: int, tile: int = TILE) -> Shape:
+    return Shape(int(T), int(d_model), int(d_ff), int(tile), int(cap), int(dtype))
+
+
+def shape_of(x: torch.Tensor, w: torch.Tensor, cap: int) -> Shape:
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [T, d_model] and weights [d_ff, d_model]")
+    if x.dtype != w.dtype:
+        raise TypeError("x and the weights must share a dtype")
+    return make_shape(x.shape[0], x.shape[1], w.shape[0], cap, _dtype_code(x))
+
+
+def workspace_bytes(shape: Shape, which: int) -> int:
+    return int(_lib.sffn_workspace_bytes(ctypes.byref(shape), int(which)))
+
+
+def alloc_workspace(shape: Shape, which: int, device=None) -> torch.Tensor:
+    """Zero-filled device workspace for one call kind (the sparse kernel expects
+    zero on first use and leaves it zero)."""
+    n = workspace_bytes(shape, which)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device or "cuda")
+
+
+def alloc_twell(shape: Shape, device=None):
+    """count [T, n_tiles] u16, idx [T, n_tiles, cap] u16, val [T, n_tiles, cap] dtype."""
+    nt = shape.d_ff // shape.tile
+    dt = torch.bfloat16 if shape.dtype == SFFN_BF16 else torch.float32
+    dev = device or "cuda"
+    count = torch.empty((shape.T, nt), dtype=torch.uint16, device=dev)
+    idx = torch.empty((shape.T, nt, max(shape.cap, 1)), dtype=torch.uint16, device=dev)
+    val = torch.empty((shape.T, nt, max(shape.cap, 1)), dtype=dt, device=dev)
+    return count, idx, val
+
+
+def twell_pack(shape: Shape, x, wg_t, b_g, count, idx, val, stream=None) -> None:
+    _check("twell_pack", _lib.twell_pack(ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g),
+                                         _ptr(count), _ptr(idx), _ptr(val), _stream(stream)))
+
+
+def sparse_ffn_fwd(shape: Shape, x, wu_t, wd, count, idx, val, y, workspace=None,
+                   stream=None) -> None:
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("sparse_ffn_fwd", _lib.sparse_ffn_fwd(
+        ctypes.byref(shape), _ptr(x), _ptr(wu_t), _ptr(wd), _ptr(count), _ptr(idx), _ptr(val),
+        _ptr(y), _ptr(workspace), ws_n, _stream(stream)))
+
+
+def hybrid_route(shape: Shape, x, wg_t, b_g, wu_t, wd, count, routed, n_routed, workspace, y,
+                 stream=None) -> None:
+    ws_n = workspace.numel() * workspace.element_size()
+    _check("hybrid_route", _lib.hybrid_route(
+        ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd), _ptr(count),
+        _ptr(routed), _ptr(n_routed), _ptr(workspace), ws_n, _ptr(y), _stream(stream)))
+
+
+def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=None) -> None:
+    ws_n = workspace.numel() * workspace.element_size()
+    _check("dense_ffn_ref", _lib.dense_ffn_ref(
+        ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd),
+        _ptr(workspace), ws_n, _ptr(y), _stream(stream)))
+
+
+class SparseFFN:
+    """Buffers for repeated sparse forwards of one shape: TwELL arrays, routed
+    list, workspaces.  ``forward`` issues twell_pack, sparse_ffn_fwd and
+    hybrid_route on one stream with no host synchronisation."""
+
+    def __init__(self, T: int, d_model: int, d_ff: int, cap: int, dtype: torch.dtype,
+                 device="cuda"):
+        code = SFFN_BF16 if dtype == torch.bfloat16 else SFFN_F32
+        self.shape = make_shape(T, d_model, d_ff, cap, code)
+        self.dtype = dtype
+        self.count, self.idx, self.val = alloc_twell(self.shape, device)
+        self.routed = torch.empty(max(T, 1), dtype=torch.int32, device=device)
+        self.n_routed = torch.zeros(1, dtype=torch.int32, device=device)
+        self.ws_sparse = alloc_workspace(self.shape, WS_SPARSE, device)
+        self.ws_hybrid = alloc_workspace(self.shape, WS_HYBRID, device)
+        self.y = torch.empty((T, d_model), dtype=dtype, device=device)
+
+    def forward(self, x, wg_t, b_g, wu_t, wd, stream=None) -> torch.Tensor:
+        s = self.shape
+        twell_pack(s, x, wg_t, b_g, self.count, self.idx, self.val, stream)
+        sparse_ffn_fwd(s, x, wu_t, wd, self.count, self.idx, self.val, self.y, self.ws_sparse,
+                       stream)
+        hybrid_route(s, x, wg_t, b_g, wu_t, wd, self.count, self.routed, self.n_routed,
+                     self.ws_hybrid, self.y, stream)
+        return self.y
+
+
+class DenseFFN:
+    """Buffers for repeated dense reference forwards of one shape."""
+
+    def __init__(self, T: int, d_model: int, d_ff: int, dtype: torch.dtype, device="cuda"):
+        code = SFFN_BF16 if dtype == torch.bfloat16 else SFFN_F32
+        self.shape = make_shape(T, d_model, d_ff, 0, code)
+        self.ws = alloc_workspace(self.shape, WS_DENSE, device)
+        self.y = torch.empty((T, d_model), dtype=dtype, device=device)
+
+    def forward(self, x, wg_t, b_g, wu_t, wd, stream=None) -> torch.Tensor:
+        dense_ffn_ref(self.shape, x, wg_t, b_g, wu_t, wd, self.ws, self.y, stream)
+        return self.y

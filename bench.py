@@ -1,0 +1,207 @@
+"""Benchmark of the activation-sparse gated FFN forward on one MI355X.
+
+A step is one sparse forward of the whole hot path over one batch of
+synthetic tokens: twell_pack (gate GEMM + TwELL epilogue), sparse_ffn_fwd
+(fused up*gate -> down over the packed nonzeros) and hybrid_route (routing scan
++ dense fallback of the overflowing rows).  The same-GPU dense gated FFN
+(dense_ffn_ref) is timed beside it for the speed-up.  Inputs are resident in
+HBM before the timed region starts.
+
+Prints one JSON line (metric, value = sparse FFN tokens/s, roofline of the
+dominant kernel, CPU oracle baseline, per-kernel times, speed-up over dense).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="prefill_1pct")
+    p.add_argument("--beta", type=float, default=None, help="override the gate bias -beta")
+    p.add_argument("--cap", type=int, default=None, help="override the TwELL capacity")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=None,
+                   help="rows of the CPU oracle sample (default: whole batch, at most 4096)")
+    p.add_argument("--no-dense", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(inp, rows: int) -> dict:
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = inp.workload
+    sel = np.arange(min(rows, w.T))
+    x = inp.rows_f64("x", sel)
+    wg, wu, wd = inp.as_f64("wg_t"), inp.as_f64("wu_t"), inp.as_f64("wd")
+    t0 = time.perf_counter()
+    oracle.sparse_forward(x, wg, inp.b_g, wu, wd, w.tile, w.cap)
+    dt = time.perf_counter() - t0
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": len(sel) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(sel)} of {w.T} tokens of {w.name}, one float64 sparse forward "
+                      f"(gate with exact sign, TwELL pack, route, fused sum), {dt:.2f} s",
+            "cpu_model": cpu, "os_cpu_count": os.cpu_count()}
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the activation-"
+              "sparse FFN path is built and measured for a single MI355X.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from activation_sparse_feed_amd import sffn, workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if args.cap is not None:
+        w = w.replace(cap=args.cap)
+    inp = wl.generate(w, beta=args.beta)
+    beta = w.beta if args.beta is None else args.beta
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, wg, wu, wd = dev(inp.x), dev(inp.wg_t), dev(inp.wu_t), dev(inp.wd)
+    b = torch.from_numpy(inp.b_g).cuda()
+    ffn = sffn.SparseFFN(w.T, w.d_model, w.d_ff, w.cap, dt)
+    dense = sffn.DenseFFN(w.T, w.d_model, w.d_ff, dt)
+    s = ffn.shape
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        ffn.forward(x, wg, b, wu, wd)
+        if not args.no_dense:
+            dense.forward(x, wg, b, wu, wd)
+    torch.cuda.synchronize()
+
+    # ---- timed sparse forward, per-kernel events on the launch stream
+    K = args.steps
+    E = torch.cuda.Event
+    ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        sffn.twell_pack(s, x, wg, b, ffn.count, ffn.idx, ffn.val)
+        ev[i][1].record()
+        sffn.sparse_ffn_fwd(s, x, wu, wd, ffn.count, ffn.idx, ffn.val, ffn.y, ffn.ws_sparse)
+        ev[i][2].record()
+        sffn.hybrid_route(s, x, wg, b, wu, wd, ffn.count, ffn.routed, ffn.n_routed,
+                          ffn.ws_hybrid, ffn.y)
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    t_gate = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    t_sparse = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+    t_hybrid = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]))
+    t_events = float(np.mean([ev[i][0].elapsed_time(ev[i][3]) for i in range(K)]))
+
+    # ---- dense reference
+    t_dense = None
+    if not args.no_dense:
+        d0, d1 = E(enable_timing=True), E(enable_timing=True)
+        torch.cuda.synchronize()
+        d0.record()
+        for _ in range(K):
+            dense.forward(x, wg, b, wu, wd)
+        d1.record()
+        torch.cuda.synchronize()
+        t_dense = d0.elapsed_time(d1) / K
+
+    count = ffn.count.to(torch.int64)
+    nnz_live = int(torch.clamp(count, max=w.cap).sum().item()) if w.cap > 0 else 0
+    n_routed = int(ffn.n_routed.item())
+    nnz_total = int(count.sum().item())
+
+    T, d, n = w.T, w.d_model, w.d_ff
+    eb = 2 if w.dtype == "bf16" else 4
+    gate_flop = 2.0 * T * d * n
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    gate_tflops = gate_flop / (t_gate * 1e-3) / 1e12
+    # fused kernel: algorithmic bytes = x + y + live TwELL + distinct gathered rows
+    routed_mask = torch.zeros(T, dtype=torch.bool, device="cuda")
+    routed_mask[ffn.routed[:n_routed].long()] = True
+    live = (torch.arange(max(w.cap, 1), device="cuda")[None, None, :]
+            < torch.clamp(count, max=w.cap)[:, :, None]) & ~routed_mask[:, None, None]
+    uniq = int(torch.unique(ffn.idx.to(torch.int64)[live]).numel()) if w.cap > 0 else 0
+    sparse_bytes = 2.0 * T * d * eb + nnz_live * (2 + eb) + T * (n // 128) * 2 + uniq * 2.0 * d * eb
+    sparse_flop = 4.0 * d * int(live.sum().item())
+
+    out = {
+        "metric": "sparse gated-FFN tokens/s (1 GPU)",
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normals, gate bias -beta)",
+        "config": {"workload": w.name, "tokens": T, "d_model": d, "d_ff": n, "beta": beta,
+                   "tile": w.tile, "cap": w.cap, "rows": w.rows},
+        "roofline": {"kernel": "twell_pack (gate GEMM + TwELL epilogue)", "bound": "mfma",
+                     "achieved": gate_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": gate_tflops / peak, "traffic": None},
+        "kernels_ms": {"twell_pack": t_gate, "sparse_ffn_fwd": t_sparse,
+                       "hybrid_route": t_hybrid, "events_step": t_events,
+                       "dense_ffn_ref": t_dense},
+        "sparse_ffn_fwd": {"algorithmic_bytes": sparse_bytes, "gb_per_s": sparse_bytes / (t_sparse * 1e-3) / 1e9,
+                           "hbm_frac": sparse_bytes / (t_sparse * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "flop": sparse_flop, "tflop_per_s": sparse_flop / (t_sparse * 1e-3) / 1e12,
+                           "distinct_columns": uniq},
+        "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,
+        "speedup_vs_dense": (t_dense / ms_step) if t_dense else None,
+        "dense_tflops": (3 * gate_flop / (t_dense * 1e-3) / 1e12) if t_dense else None,
+        "activity": {"nnz_per_row": nnz_total / T, "density": nnz_total / (T * n),
+                     "routed_rows": n_routed},
+        "device": torch.cuda.get_device_name(0),
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows if args.cpu_rows is not None else min(T, 4096)
+        out["cpu_baseline"] = cpu_baseline(inp, rows)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

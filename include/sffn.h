@@ -1,0 +1,159 @@
+/*
+ * sffn.h -- C ABI of the activation-sparse gated FFN forward on AMD MI355X (gfx950).
+ *
+ * The method ("Sparser, Faster, Lighter Transformer Language Models", as
+ * described by the pwwt.cn article, sections 01-03, the kongchang.com article,
+ * sections "TwELL" and "custom CUDA kernels", and the neo-ai.one article):
+ *
+ *   gated FFN   y = (ReLU(x W_g + b_g) * (x W_u)) W_d           (pwwt.cn 01)
+ *   TwELL       the gate projection's epilogue writes the ReLU survivors of
+ *               each row, tile by tile over 1D column tiles, as small ELLPACK
+ *               lists (column index + value), with no separate conversion
+ *               kernel                                            (pwwt.cn 02)
+ *   fused       one kernel computes the up projection only on the packed
+ *               nonzeros, scales by the gate value and accumulates the down
+ *               projection, never storing h                       (pwwt.cn 02)
+ *   hybrid      rows whose nonzeros do not fit the compact format are routed
+ *               to a dense fallback on the matrix cores           (pwwt.cn 03)
+ *
+ * Conventions shared by every call:
+ *   - All buffer pointers are DEVICE pointers, 16-byte aligned.  Shapes and
+ *     scalars are passed by value or through the host struct sffn_shape.
+ *   - Every call is asynchronous on the given HIP stream (hipStream_t passed
+ *     as void*; NULL means the default stream).  The library never allocates,
+ *     frees or synchronises.  The caller owns all memory, workspace included.
+ *   - Layouts (row-major):
+ *       x, y                  [T, d_model]
+ *       wg_t, wu_t, wd        [d_ff, d_model]; row j holds the d_model weights
+ *                             of FFN neuron j (gate column j, up column j,
+ *                             down row j)
+ *       b_g                   [d_ff] float32 gate bias, may be NULL (zero)
+ *       count                 uint16 [T, n_tiles], n_tiles = d_ff / tile
+ *       idx                   uint16 [T, n_tiles, cap]: global column index j
+ *       val                   dtype  [T, n_tiles, cap]
+ *   - dtype (sffn_shape.dtype) applies to x, the weights, val, y and the
+ *     internal h of the dense paths: SFFN_F32 or SFFN_BF16.  Accumulation is
+ *     always float32; outputs are rounded to dtype with round-to-nearest-even.
+ *   - Preconditions (else SFFN_ERR_ARG or SFFN_ERR_UNSUPPORTED, detected on the
+ *     host before anything is launched, nothing written):
+ *       tile == 128; d_ff % 128 == 0; 128 <= d_ff <= 65535;
+ *       0 <= cap <= 128; d_model % 8 == 0; 8 <= d_model <= 8192;
+ *       0 <= T; T == 0 is a no-op returning SFFN_OK.
+ *     Inputs must be finite (no Inf/NaN).
+ *   - Errors: every call returns an sffn_status.  A failed launch returns
+ *     SFFN_ERR_HIP; device faults surface at the caller's next synchronisation.
+ */
+#ifndef SFFN_H
+#define SFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SFFN_OK = 0,
+  SFFN_ERR_ARG = -1,         /* null/misaligned pointer, negative or inconsistent size */
+  SFFN_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
+  SFFN_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than sffn_workspace_bytes */
+  SFFN_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} sffn_status;
+
+typedef enum { SFFN_F32 = 0, SFFN_BF16 = 1 } sffn_dtype;
+
+/* Which call a workspace query is for. */
+typedef enum { SFFN_WS_HYBRID = 0, SFFN_WS_DENSE = 1, SFFN_WS_SPARSE = 2 } sffn_ws_kind;
+
+typedef struct {
+  int32_t T;       /* tokens (rows of x and y) */
+  int32_t d_model; /* model width */
+  int32_t d_ff;    /* FFN width (number of gate/up/down neurons) */
+  int32_t tile;    /* TwELL column-tile width; must be 128 */
+  int32_t cap;     /* TwELL capacity: slots per (row, tile) */
+  int32_t dtype;   /* sffn_dtype */
+} sffn_shape;
+
+/*
+ * twell_pack -- gate projection with the TwELL epilogue (pwwt.cn article,
+ * section 02: the format is produced directly in the gate GEMM's epilogue).
+ *
+ *   z[t, j] = sum_k x[t, k] * wg_t[j, k] + b_g[j]        (float32 accumulation)
+ *   active  = z > 0 (strict), decided on the EXACT value of z: entries whose
+ *             float32 result lies within the accumulation error bound of zero
+ *             are re-evaluated exactly in the epilogue.
+ *   For each row t and tile k (columns 128k .. 128k+127):
+ *     count[t, k]   = number of active columns in the tile (uncapped, <= 128)
+ *     idx[t, k, s]  = s-th active column, ascending, global index j, for
+ *                     s < min(count, cap)
+ *     val[t, k, s]  = z at that column, rounded to dtype
+ *   Slots s >= min(count, cap) are left unwritten (unspecified).
+ *
+ * x: [T, d_model] dtype; wg_t: [d_ff, d_model] dtype; b_g: [d_ff] f32 or NULL;
+ * count/idx/val: outputs as laid out above.  No workspace.
+ */
+int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t,
+                   const float* b_g, uint16_t* count, uint16_t* idx, void* val,
+                   void* stream);
+
+/*
+ * sparse_ffn_fwd -- fused up(.)gate -> down over the TwELL nonzeros (pwwt.cn
+ * article, section 02).  For every row t with count[t, k] <= cap for all k:
+ *
+ *   y[t, :] = sum over k, s < count[t, k] of
+ *               val[t,k,s] * (x[t, :] . wu_t[idx[t,k,s], :]) * wd[idx[t,k,s], :]
+ *
+ * accumulated in float32 and written once, rounded to dtype.  Rows with any
+ * count above cap are not touched (hybrid_route writes them).
+ * workspace: at least sffn_workspace_bytes(shape, SFFN_WS_SPARSE) bytes of
+ * device memory that the caller zero-fills once before its first use with
+ * this library; calls leave it zero-filled where it must be.  May be NULL
+ * when that size is 0.  Calls that share a workspace must be stream-ordered.
+ */
+int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t,
+                       const void* wd, const uint16_t* count, const uint16_t* idx,
+                       const void* val, void* y, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * hybrid_route -- route overflowing rows to a dense fallback (pwwt.cn article,
+ * section 03: rare high-activity tokens go to a dense backup path on the
+ * matrix cores).
+ *
+ *   routed[0 .. n_routed) = ascending rows t with count[t, k] > cap for some k
+ *   *n_routed             = their number (written on the device; no host sync)
+ *   for each routed row:  y[t, :] = (ReLU(x_t W_g + b_g) * (x_t W_u)) W_d,
+ *                         gate recomputed from x, h rounded to dtype.
+ * Rows that are not routed are not touched.  routed: int32 [T] (entries past
+ * n_routed unspecified); n_routed: one int32.  workspace: at least
+ * sffn_workspace_bytes(shape, SFFN_WS_HYBRID) bytes (side buffer for the
+ * routed rows' h and the routing scan).
+ */
+int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
+                     const float* b_g, const void* wu_t, const void* wd,
+                     const uint16_t* count, int32_t* routed, int32_t* n_routed,
+                     void* workspace, size_t ws_bytes, void* y, void* stream);
+
+/*
+ * dense_ffn_ref -- the dense gated FFN used as the speed-up reference
+ * (pwwt.cn article, section 01 formula, computed densely on the matrix cores):
+ *   h = ReLU(x wg_t^T + b_g) * (x wu_t^T)  rounded to dtype, in workspace;
+ *   y = h wd, float32 accumulation, rounded to dtype.
+ * workspace: at least sffn_workspace_bytes(shape, SFFN_WS_DENSE) bytes.
+ */
+int32_t dense_ffn_ref(const sffn_shape* shape, const void* x, const void* wg_t,
+                      const float* b_g, const void* wu_t, const void* wd,
+                      void* workspace, size_t ws_bytes, void* y, void* stream);
+
+/* Workspace bytes needed by one call for this shape (0 if the shape is invalid). */
+size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which);
+
+/* Static, NUL-terminated description of a status code. */
+const char* sffn_strerror(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFFN_H */

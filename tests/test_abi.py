@@ -1,0 +1,113 @@
+"""The C ABI on the host: every symbol the header declares is exported, and
+argument errors are reported before anything is launched (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.abspath(os.path.join(os.path.dirname(__file__), ".."))
+HEADER = os.path.join(ROOT, "include", "sffn.h")
+
+
+@pytest.fixture(scope="module")
+def sffn():
+    from activation_sparse_feed_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    from activation_sparse_feed_amd import sffn as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("twell_pack", "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref",
+              "sffn_workspace_bytes", "sffn_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(sffn):
+    lib = ctypes.CDLL(sffn.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(sffn.EXPORTED)
+
+
+def _shape(sffn, **kw):
+    base = dict(T=64, d_model=256, d_ff=512, cap=8, dtype=sffn.SFFN_BF16)
+    base.update(kw)
+    s = sffn.make_shape(base["T"], base["d_model"], base["d_ff"], base["cap"], base["dtype"])
+    for k in ("tile",):
+        if k in kw:
+            setattr(s, k, kw[k])
+    return s
+
+
+P = ctypes.c_void_p(0x10000)        # aligned fake device pointer: never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _pack(sffn, s, x=P, w=P, b=None, c=P, i=P, v=P):
+    return sffn._lib.twell_pack(ctypes.byref(s) if s is not None else None, x, w, b, c, i, v, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tile=64), -2), (dict(d_ff=100), -2), (dict(d_ff=65536 + 128), -2),
+    (dict(cap=129), -2), (dict(cap=-1), -1), (dict(T=-1), -1), (dict(d_model=12), -2),
+    (dict(d_model=8200), -2), (dict(dtype=7), -1), (dict(d_model=0), -1),
+])
+def test_shape_errors(sffn, kw, status):
+    assert _pack(sffn, _shape(sffn, **kw)) == status
+
+
+def test_null_and_misaligned_pointers(sffn):
+    s = _shape(sffn)
+    assert _pack(sffn, None) == sffn.SFFN_ERR_ARG
+    assert _pack(sffn, s, x=None) == sffn.SFFN_ERR_ARG
+    assert _pack(sffn, s, w=MISALIGNED) == sffn.SFFN_ERR_ARG
+    assert _pack(sffn, s, b=MISALIGNED) == sffn.SFFN_ERR_ARG
+    assert _pack(sffn, s, c=None) == sffn.SFFN_ERR_ARG
+
+
+def test_zero_tokens_is_ok_without_buffers(sffn):
+    s = _shape(sffn, T=0)
+    assert _pack(sffn, s, x=None, w=None, c=None, i=None, v=None) == sffn.SFFN_OK
+    lib = sffn._lib
+    assert lib.dense_ffn_ref(ctypes.byref(s), None, None, None, None, None, None, 0, None, None) == 0
+
+
+def test_workspace_errors(sffn):
+    s = _shape(sffn)
+    lib = sffn._lib
+    need = sffn.workspace_bytes(s, sffn.WS_DENSE)
+    assert need >= 64 * 512 * 2
+    assert lib.dense_ffn_ref(ctypes.byref(s), P, P, None, P, P, P, need - 1, P, None) == -3
+    assert lib.dense_ffn_ref(ctypes.byref(s), P, P, None, P, P, None, need, P, None) == -3
+    need_h = sffn.workspace_bytes(s, sffn.WS_HYBRID)
+    assert need_h > 64 * 512 * 2
+    assert lib.hybrid_route(ctypes.byref(s), P, P, None, P, P, P, P, P, P, need_h - 1, P, None) == -3
+    # few tokens: the fused kernel splits columns and needs a partial buffer
+    sd = _shape(sffn, T=4)
+    need_s = sffn.workspace_bytes(sd, sffn.WS_SPARSE)
+    assert need_s > 0
+    assert lib.sparse_ffn_fwd(ctypes.byref(sd), P, P, P, P, P, P, P, None, 0, None) == -3
+    assert sffn.workspace_bytes(_shape(sffn, T=4096), sffn.WS_SPARSE) == 0
+
+
+def test_workspace_query_of_invalid_shape_is_zero(sffn):
+    assert sffn.workspace_bytes(_shape(sffn, tile=32), sffn.WS_DENSE) == 0
+    assert sffn.workspace_bytes(_shape(sffn), 9) == 0
+
+
+def test_strerror(sffn):
+    for code in (0, -1, -2, -3, -4, 5):
+        assert isinstance(sffn.strerror(code), str) and sffn.strerror(code)
+    assert sffn.strerror(-3) != sffn.strerror(-1)

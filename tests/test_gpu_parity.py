@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+TwELL counts, live indices, the routed-row set and n_routed are compared bit
+for bit; TwELL values within the storage rounding; y by relative Frobenius
+error (1e-5 float32, 5e-3 bf16 with float32 accumulation), over all compared
+rows and separately over routed and non-routed rows.  Full-size workloads run
+at their real shape on the GPU and are compared on a row sample that always
+includes routed rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_feed_amd import workloads as wl
+from helpers import (check_twell, check_y, device_inputs, oracle_rows, sample_rows, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sffn():
+    from activation_sparse_feed_amd import sffn
+    return sffn
+
+
+def run_sparse(inp: wl.Inputs, cap: int):
+    sffn = _sffn()
+    w = inp.workload
+    d = device_inputs(inp)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    ffn = sffn.SparseFFN(w.T, w.d_model, w.d_ff, cap, dt)
+    y = ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    torch.cuda.synchronize()
+    return ffn, y, d
+
+
+def compare(inp: wl.Inputs, cap: int, rows=None, ffn=None, y=None) -> dict:
+    w = inp.workload
+    if ffn is None:
+        ffn, y, _ = run_sparse(inp, cap)
+    T = w.T
+    n_r = int(ffn.n_routed.item())
+    routed_gpu = ffn.routed[:n_r].cpu().numpy().astype(np.int64)
+    count_all = ffn.count.cpu().numpy().astype(np.int64)
+    # the routed list is the ascending set of rows with a tile over capacity
+    # in the GPU's own counts (full-size consistency) ...
+    assert np.array_equal(routed_gpu, np.nonzero(count_all.max(1) > cap)[0])
+    if rows is None:
+        rows = np.arange(T)
+    ref = oracle_rows(inp, rows, w.tile, cap)
+    # ... and those counts match the oracle bit for bit on the compared rows
+    check_twell(w.dtype, ffn.count[rows], ffn.idx[rows], ffn.val[rows], ref, cap)
+    routed_ref = rows[ref["routed"]]
+    assert np.array_equal(np.intersect1d(routed_gpu, rows), routed_ref)
+    if len(rows) == T:
+        assert n_r == len(ref["routed"])
+    mask = np.zeros(len(rows), dtype=bool)
+    mask[ref["routed"]] = True
+    errs = check_y(w.dtype, to_f64(y[rows]), ref["y"], mask)
+    errs["n_routed"] = n_r
+    return errs
+
+
+# ------------------------------------------------------------------ workloads
+def test_tiny_f32_all_rows():
+    inp = wl.generate(wl.WORKLOADS["tiny_f32"])
+    e = compare(inp, 8)
+    assert e["n_routed"] == 0
+
+
+def test_bf16_ragged_tail_with_routing():
+    inp = wl.generate_custom(T=300, d_model=512, d_ff=1024, dtype="bf16", beta=1.9,
+                             seed_base=11, cap=4)
+    e = compare(inp, 4)
+    assert e["n_routed"] > 0
+
+
+def test_f32_ragged_tail_with_routing():
+    inp = wl.generate_custom(T=200, d_model=264, d_ff=384, dtype="f32", beta=1.7,
+                             seed_base=12, cap=3)
+    e = compare(inp, 3)
+    assert e["n_routed"] > 0
+
+
+def test_prefill_full_size_sampled():
+    w = wl.WORKLOADS["prefill_1pct"]
+    inp = wl.generate(w)
+    ffn, y, _ = run_sparse(inp, w.cap)
+    n_r = int(ffn.n_routed.item())
+    rows = sample_rows(w.T, 160, must=ffn.routed[:n_r].cpu().numpy(), seed=1)
+    compare(inp, w.cap, rows, ffn, y)
+
+
+def test_hybrid_mix_full_size_sampled():
+    w = wl.WORKLOADS["hybrid_mix"]
+    inp = wl.generate(w)
+    ffn, y, _ = run_sparse(inp, w.cap)
+    n_r = int(ffn.n_routed.item())
+    heavy = np.nonzero(inp.scales > 1)[0]
+    routed = ffn.routed[:n_r].cpu().numpy()
+    assert set(heavy.tolist()) <= set(routed.tolist())
+    assert 60 <= n_r <= 260
+    rows = sample_rows(w.T, 96, must=np.concatenate([heavy, routed[:40]]), seed=2)
+    e = compare(inp, w.cap, rows, ffn, y)
+    assert "routed" in e and "not_routed" in e
+
+
+def test_decode_all_rows():
+    inp = wl.generate(wl.WORKLOADS["decode_1pct"])
+    compare(inp, 8)
+
+
+def test_large_lognormal_full_size_sampled():
+    w = wl.WORKLOADS["large_lognormal"]
+    inp = wl.generate(w)
+    ffn, y, _ = run_sparse(inp, w.cap)
+    n_r = int(ffn.n_routed.item())
+    assert 0.08 * w.T < n_r < 0.3 * w.T
+    routed = ffn.routed[:n_r].cpu().numpy()
+    rows = sample_rows(w.T, 40, must=routed[::max(1, n_r // 12)], seed=3)
+    compare(inp, w.cap, rows, ffn, y)
+
+
+# ------------------------------------------------------------- dense reference
+@pytest.mark.parametrize("name,T", [("tiny_f32", None), ("prefill_1pct", 512),
+                                    ("decode_1pct", None)])
+def test_dense_reference(name, T):
+    sffn = _sffn()
+    w = wl.WORKLOADS[name]
+    if T is not None:
+        w = w.replace(T=T)
+    inp = wl.generate(w)
+    d = device_inputs(inp)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dense = sffn.DenseFFN(w.T, w.d_model, w.d_ff, dt)
+    y = to_f64(dense.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"]))
+    rows = np.arange(w.T)
+    ref = oracle_rows(inp, rows, w.tile, w.cap)
+    check_y(w.dtype, y, ref["y_dense"], np.zeros(w.T, dtype=bool))
+
+
+# ---------------------------------------------------------------- edge cases
+def _small(beta, dtype="bf16", T=64, seed=21):
+    return wl.generate_custom(T=T, d_model=256, d_ff=512, dtype=dtype, beta=beta, seed_base=seed)
+
+
+def test_single_token():
+    compare(_small(1.5, T=1), 8)
+
+
+def test_capacity_zero_routes_every_active_row():
+    e = compare(_small(2.0), 0)
+    assert e["n_routed"] > 0
+
+
+def test_capacity_full_tile_routes_nothing():
+    e = compare(_small(0.0), 128)
+    assert e["n_routed"] == 0
+
+
+def test_huge_bias_gives_exact_zeros():
+    inp = _small(1e4)
+    ffn, y, _ = run_sparse(inp, 8)
+    assert int(ffn.count.to(torch.int32).sum().item()) == 0
+    assert int(ffn.n_routed.item()) == 0
+    assert torch.count_nonzero(y).item() == 0
+
+
+def test_positive_bias_routes_every_row():
+    inp = _small(-50.0, T=40)
+    e = compare(inp, 8)
+    assert e["n_routed"] == 40
+
+
+def test_zero_tokens_is_a_noop():
+    sffn = _sffn()
+    s = sffn.make_shape(0, 256, 512, 8, sffn.SFFN_BF16)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((512, 256), dtype=torch.bfloat16, device="cuda")
+    c, i, v = sffn.alloc_twell(sffn.make_shape(1, 256, 512, 8, sffn.SFFN_BF16))
+    sffn.twell_pack(s, x, w, None, c, i, v)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_sign_near_zero(dtype):
+    """Entries whose float32 sum is 0 or of the wrong sign are decided on the
+    exact value (both the float64 stage and the exact fixed-point stage)."""
+    T, K, N = 5, 64, 256
+    inp = wl.generate_custom(T=T, d_model=K, d_ff=N, dtype=dtype, beta=2.0, seed_base=31)
+    x = inp.as_f64("x")
+    wg = inp.as_f64("wg_t")
+    b = inp.b_g.copy()
+    # row 0: z = 2^-59 (needs the exact stage), 2^-59 negative, exact zero,
+    # 2^-40 (decided by the float64 stage)
+    x[0, :] = 0.0
+    x[0, :3] = [1.0, 2.0 ** -30, 2.0 ** -30]
+    wg[:4, :] = 0.0
+    wg[0, :3] = [1.0, 2.0 ** -30, 2.0 ** -30]
+    wg[1, :3] = [1.0, -2.0 ** -30, -2.0 ** -30]
+    wg[2, 0] = 1.0
+    wg[3, :2] = [1.0, 2.0 ** -10]
+    b[:4] = -1.0
+    # row 1: same cancellations with a large lane spread
+    x[1, :] = 0.0
+    x[1, 0], x[1, 40] = 1.0, 2.0 ** -30
+    wg[4, :] = 0.0
+    wg[4, 0], wg[4, 40] = 1.0, 2.0 ** -31
+    b[4] = -1.0
+    store = (lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))) if dtype == "bf16" \
+        else (lambda a: a.astype(np.float32))
+    inp.x, inp.wg_t, inp.b_g = store(x), store(wg), b.astype(np.float32)
+    assert np.array_equal(inp.as_f64("x"), x) and np.array_equal(inp.as_f64("wg_t"), wg)
+    ffn, y, _ = run_sparse(inp, 8)
+    ref = oracle_rows(inp, np.arange(T), 128, 8)
+    assert ref["z"][0, 0] == 2.0 ** -59 and ref["z"][0, 2] == 0.0 and ref["z"][1, 4] > 0
+    assert ref["z"][0, 3] > 0
+    compare(inp, 8, None, ffn, y)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = wl.WORKLOADS["prefill_1pct"].replace(T=1024)
+    inp = wl.generate(w)
+    ffn, y1, d = run_sparse(inp, w.cap)
+    c1, i1, v1 = ffn.count.clone(), ffn.idx.clone(), ffn.val.clone()
+    y1 = y1.clone()
+    y2 = ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    torch.cuda.synchronize()
+    assert torch.equal(c1, ffn.count)
+    live = torch.arange(w.cap, device="cuda")[None, None, :] < torch.clamp(
+        c1.to(torch.int32), max=w.cap)[:, :, None]
+    assert torch.equal(torch.where(live, i1.to(torch.int32), -1),
+                       torch.where(live, ffn.idx.to(torch.int32), -1))
+    assert torch.equal(torch.where(live, v1, 0), torch.where(live, ffn.val, 0))
+    assert torch.equal(y1, y2)
+
+
+def test_decode_split_reduction_repeats():
+    """The split-partial reduction (few tokens) re-arms its tickets: repeated
+    calls give identical results."""
+    inp = wl.generate(wl.WORKLOADS["decode_1pct"])
+    ffn, y1, d = run_sparse(inp, 8)
+    y1 = y1.clone()
+    for _ in range(3):
+        y2 = ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
