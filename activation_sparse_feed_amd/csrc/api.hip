@@ -3,7 +3,7 @@
 // Nothing here allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
-#include "../../include/sffn.h"
+#include "sffn.h"
 #include "launch.h"
 
 namespace {
@@ -37,6 +37,15 @@ size_t dense_ws(const sffn_shape* s) {
   return align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
 }
 
+size_t pack_ws(const sffn_shape* s) {
+  return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4);
+}
+
+// The buffer-load GEMM addresses an activation matrix with 32-bit offsets.
+bool act_bytes_too_large(const sffn_shape* s) {
+  return (uint64_t)s->T * (uint64_t)s->d_model * elt_bytes(s->dtype) >= (1ull << 31);
+}
+
 size_t hybrid_ws(const sffn_shape* s) {
   return route_workspace_bytes(s->T) + align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
 }
@@ -57,16 +66,36 @@ GuardBand guard_band(const sffn_shape* s) {
 
 extern "C" {
 
+int32_t twell_weight_norms(const sffn_shape* shape, const void* wg_t, float* wg_norms,
+                           void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (!ptrs_ok({wg_t, wg_norms})) return SFFN_ERR_ARG;
+  return hip_status(launch_row_norms(shape->dtype, wg_t, shape->d_ff, wg_norms, nullptr, 0,
+                                     nullptr, shape->d_model, (hipStream_t)stream));
+}
+
 int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
-                   uint16_t* count, uint16_t* idx, void* val, void* stream) {
+                   const float* wg_norms, uint16_t* count, uint16_t* idx, void* val,
+                   void* workspace, size_t ws_bytes, void* stream) {
   int32_t st = check_shape(shape);
   if (st != SFFN_OK) return st;
   if (shape->T == 0) return SFFN_OK;
-  if (!ptrs_ok({x, wg_t, count}) || (b_g && !aligned16(b_g))) return SFFN_ERR_ARG;
+  if (!ptrs_ok({x, wg_t, count}) || (b_g && !aligned16(b_g)) || (wg_norms && !aligned16(wg_norms)))
+    return SFFN_ERR_ARG;
   if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
-  return hip_status(launch_gate_twell(shape->dtype, x, wg_t, b_g, count, idx, val, shape->T,
-                                      shape->d_model, shape->d_ff, shape->cap, guard_band(shape),
-                                      (hipStream_t)stream));
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < pack_ws(shape))
+    return SFFN_ERR_WORKSPACE;
+  if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  float* xn = (float*)workspace;
+  float* wn = (float*)((char*)workspace + align256((size_t)shape->T * 4));
+  hipError_t e = launch_row_norms(shape->dtype, x, shape->T, xn, wg_t, wg_norms ? 0 : shape->d_ff,
+                                  wn, shape->d_model, s);
+  if (e != hipSuccess) return SFFN_ERR_HIP;
+  return hip_status(launch_gate_twell(shape->dtype, x, wg_t, b_g, xn, wg_norms ? wg_norms : wn,
+                                      count, idx, val, shape->T, shape->d_model, shape->d_ff,
+                                      shape->cap, guard_band(shape), s));
 }
 
 int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t, const void* wd,
@@ -96,6 +125,7 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t, c
     return SFFN_ERR_ARG;
   if (workspace == nullptr || !aligned16(workspace) || ws_bytes < hybrid_ws(shape))
     return SFFN_ERR_WORKSPACE;
+  if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int T = shape->T, K = shape->d_model, N = shape->d_ff;
   hipError_t e = launch_route(count, T, N / 128, shape->cap, routed, n_routed, workspace, s);
@@ -130,6 +160,7 @@ size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
     case SFFN_WS_HYBRID: return hybrid_ws(shape);
     case SFFN_WS_DENSE: return dense_ws(shape);
     case SFFN_WS_SPARSE: return sparse_workspace_bytes(shape->T, shape->d_ff / 128, shape->d_model);
+    case SFFN_WS_PACK: return pack_ws(shape);
     default: return 0;
   }
 }

@@ -76,6 +76,34 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// DPP move of a float (all rows and banks enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes, returned uniformly: butterfly within each 16-lane
+// row (quad_perm [1,0,3,2], [2,3,0,1], row_ror 4, row_ror 8), then the four
+// row sums read from lanes 0, 16, 32, 48.  Fixed order: deterministic.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Dot of two packed bfloat16 pairs accumulated in float32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 template <typename T>
 __device__ __forceinline__ T uniform(T v) {
   return (T)__builtin_amdgcn_readfirstlane((int)v);

@@ -1,0 +1,279 @@
+// Second-generation bf16 GEMM main loop for gfx950 (K-contiguous A and B).
+//
+//   workgroup tile 256 (M) x 128 (N = NB * BNW), 4 waves as 2 x 2, each wave
+//   128 x (NB x BNW/2); v_mfma_f32_16x16x32_bf16, float32 accumulators.
+//   K step 64, three LDS stages of 48 KB filled by buffer loads straight into
+//   LDS (16 bytes per lane, no VGPR staging).  Each 128-byte LDS row holds its
+//   eight 16-byte chunks XOR-swizzled by (row & 7): a load instruction writes
+//   64 consecutive chunks, so lane l fetches global chunk (l & 7) ^ (l >> 3) of
+//   its row; fragment reads of 8 consecutive rows then hit 8 distinct bank
+//   groups.  Rows past the valid range read as zero through the buffer range
+//   check.  One barrier per K step: stage kt is consumed while stages kt+1 and
+//   kt+2 are in flight.
+//
+// NORMS: the waves also accumulate sum of squares of the A rows (waves with
+// wn == 0) and B rows (waves with wm == 0) from the bf16 fragments they feed to
+// the MFMA (packed dot2), for the guard band of the TwELL epilogue.
+#pragma once
+
+#include "common.cuh"
+
+namespace sffn {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Workgroup barrier for the LDS pipeline: waits for this wave's LDS
+// instructions, then s_barrier.  Unlike __syncthreads() it does not drain the
+// vector-memory counter, so buffer loads into later LDS stages stay in flight;
+// the caller waits for its own stage with s_waitcnt vmcnt first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Byte offset of an LDS pointer (LDS addresses are 32-bit).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Tile of a linear workgroup id.  Workgroups are dispatched round-robin over
+// the 8 XCDs (id % 8); each XCD is given a contiguous run of tile indices, and
+// tile indices walk groups of 4 M-tiles with N fastest inside a group, so the
+// workgroups resident on one XCD share A and B tiles in its L2.  Any mapping
+// is correct; this one only affects cache reuse.
+__device__ __forceinline__ void tile_of(int bid, int mt, int nt, int* m, int* n) {
+  const int total = mt * nt;
+  const int xcd = bid & 7, j = bid >> 3;
+  const int per = total >> 3, extra = total & 7;
+  const int t = xcd * per + min(xcd, extra) + j;  // contiguous run per XCD
+  constexpr int GM = 4;
+  const int group = t / (GM * nt);
+  const int gm = min(GM, mt - group * GM);
+  const int r = t - group * GM * nt;
+  *m = group * GM + r % gm;
+  *n = r / gm;
+}
+
+// WAVES_N: waves along N (2: 2 x 2 waves of 128 rows x BNW/2 columns; 1: 4 x 1
+// waves of 64 rows x BNW columns, so that every row of a B matrix's tile lives
+// in one wave).
+template <int NB, int BNW, bool NORMS, int BK_ = 32, int WAVES_N = 2>
+struct Gemm2 {
+  static constexpr int BM = 256, BK = BK_, STAGES = 3;
+  static constexpr int BN = NB * BNW;
+  static constexpr int ROWB = BK * 2;                  // bytes per LDS row
+  static constexpr int CPR = BK / 8;                   // 16-byte chunks per row
+  static constexpr int ROWS = BM + BN;                 // LDS rows per stage
+  static constexpr int STAGE_BYTES = ROWS * ROWB;
+  static constexpr int RPB = 64 / CPR;                 // rows per 1 KB load block
+  static constexpr int BLOCKS = ROWS / RPB;            // 1 KB load blocks per stage
+  static constexpr int LOADS = BLOCKS / 4;             // load instructions per wave per stage
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(!NORMS || WAVES_N == 2, "norm split assumes 2 x 2 waves");
+  static constexpr int WAVES_M = 4 / WAVES_N;
+  static constexpr int WM = BM / WAVES_M, WN = BNW / WAVES_N;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
+  static_assert(BN == 128, "workgroup N tile");
+  static_assert(BLOCKS % 4 == 0, "load blocks per wave");
+
+  // Physical 16-byte slot of logical chunk q in row r: 8 consecutive rows
+  // read at one logical chunk land in 8 distinct 16-byte bank groups.
+  static __device__ __forceinline__ int slot(int r, int q) {
+    return BK == 64 ? (q ^ (r & 7)) : (q ^ ((r >> 1) & 3));
+  }
+
+  f32x4_t acc[NB][FM][FN];
+  float sqa[FM];
+  float sqb[NB][FN];
+  uint32_t voff[LOADS];     // per-lane byte offset of its chunk within the source matrix
+  __amdgpu_buffer_rsrc_t ra;
+  __amdgpu_buffer_rsrc_t rb[NB];
+
+  // A: [*, K] bf16 rows; rows m0 .. m0+255 (gathered through rowmap when
+  // given); rows >= m_valid read as zero.  B[b]: [N, K] bf16; rows n0 ..
+  __device__ __forceinline__ void init(const uint16_t* A, size_t a_rows_total, const int* rowmap,
+                                       int m0, int m_valid, const uint16_t* const* B, int n0,
+                                       int N, int K) {
+    const int lane = lane_id();
+    const int w = uniform((int)(threadIdx.x >> 6));
+    const uint32_t ld = (uint32_t)K * 2u;
+    const uint16_t* abase = rowmap ? A : A + (size_t)m0 * K;
+    const size_t a_rows = rowmap ? a_rows_total : (size_t)min(m_valid - m0, BM);
+    ra = make_rsrc(abase, (uint32_t)(a_rows * ld));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) rb[b] = make_rsrc(B[b] + (size_t)n0 * K, (uint32_t)(BNW * ld));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = w * LOADS + i;
+      const int row = blk * RPB + lane / CPR;
+      const int q = slot(row, lane % CPR);  // slot is an involution: physical -> logical
+      if (blk * RPB < BM) {
+        const int m = m0 + row;
+        uint32_t off = 0x80000000u;  // beyond any buffer: reads as zero
+        if (m < m_valid) off = (uint32_t)((rowmap ? (uint32_t)rowmap[m] : (uint32_t)row) * ld);
+        voff[i] = off + (uint32_t)q * 16u;
+      } else {
+        const int rb_ = row - BM;
+        voff[i] = (uint32_t)(rb_ % BNW) * ld + (uint32_t)q * 16u;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[b][fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sqa[fm] = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) sqb[b][fn] = 0.f;
+    (void)N;
+  }
+
+  __device__ __forceinline__ void issue(uint8_t* stage, int k0) {
+    const int w = uniform((int)(threadIdx.x >> 6));
+    const int soff = k0 * 2;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int blk = w * LOADS + i;  // wave-uniform
+      lds_void_t* dst = (lds_void_t*)(stage + blk * 1024);
+      if (blk * RPB < BM) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[i], soff, 0, 0);
+      } else if (NB == 1 || (blk * RPB - BM) < BNW) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], dst, 16, voff[i], soff, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[NB - 1], dst, 16, voff[i], soff, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void compute(const uint8_t* stage) {
+    const int lane = lane_id();
+    const int w = uniform((int)(threadIdx.x >> 6));
+    const int wm = w % WAVES_M, wn = w / WAVES_M;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      // rows of every fragment start at a multiple of 16, so the swizzle only
+      // depends on the lane's row within the fragment
+      const int cq = slot(lane & 15, ks * 4 + (lane >> 4)) * 16;
+      bf16x8_t af[FM], bfr[NB][FN];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int r = BM + b * BNW + wn * WN + fn * 16 + (lane & 15);
+          bfr[b][fn] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+        }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = wm * WM + fm * 16 + (lane & 15);
+        af[fm] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[b][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr[b][fn],
+                                                                    acc[b][fm][fn], 0, 0, 0);
+      if (NORMS) {
+        // the two waves that load the same A rows (same wm) share their norm
+        // work by fragment halves, and likewise for B rows (same wn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          if ((fm * 2) / FM == wn) {
+            const u32x4_t v = __builtin_bit_cast(u32x4_t, af[fm]);
+            sqa[fm] = dot2_bf16(v.x, v.x, dot2_bf16(v.y, v.y, dot2_bf16(v.z, v.z, dot2_bf16(v.w, v.w, sqa[fm]))));
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            if (((b * FN + fn) * 2) / (NB * FN) == wm) {
+              const u32x4_t v = __builtin_bit_cast(u32x4_t, bfr[b][fn]);
+              sqb[b][fn] = dot2_bf16(v.x, v.x, dot2_bf16(v.y, v.y, dot2_bf16(v.z, v.z, dot2_bf16(v.w, v.w, sqb[b][fn]))));
+            }
+          }
+      }
+    }
+  }
+
+  // Full K loop; K must be a multiple of 64.  lds must hold LDS_BYTES.
+  __device__ __forceinline__ void run(uint8_t* lds, int K) {
+    const int nk = K / BK;
+    issue(lds, 0);
+    if (nk > 1) issue(lds + STAGE_BYTES, BK);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<LOADS>());
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      }
+      lds_barrier();
+      if (kt + 2 < nk) issue(lds + ((kt + 2) % STAGES) * STAGE_BYTES, (kt + 2) * BK);
+      compute(lds + (kt % STAGES) * STAGE_BYTES);
+    }
+    __syncthreads();
+  }
+
+  // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= N only.
+  template <int N>
+  static constexpr int vmcnt_imm() {
+    return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  }
+
+  // Guard-band norms: sqrt of the row sums of squares, A rows to rn_a[256]
+  // and B rows to rn_b[NB * BNW] (LDS).
+  __device__ __forceinline__ void write_norms(float* rn_a, float* rn_b) {
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    const int wm = w % WAVES_M, wn = w / WAVES_M;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      float s = sqa[fm];
+      s += __shfl_xor(s, 16, kWave);
+      s += __shfl_xor(s, 32, kWave);
+      if ((fm * 2) / FM == wn && lane < 16) rn_a[wm * WM + fm * 16 + lane] = sqrtf(s);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        float s = sqb[b][fn];
+        s += __shfl_xor(s, 16, kWave);
+        s += __shfl_xor(s, 32, kWave);
+        if (((b * FN + fn) * 2) / (NB * FN) == wm && lane < 16)
+          rn_b[b * BNW + wn * WN + fn * 16 + lane] = sqrtf(s);
+      }
+  }
+
+  // f(b, row, col, value) over the accumulators (row in 0..255, col in 0..BNW-1).
+  template <typename F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    const int wm = w % WAVES_M, wn = w / WAVES_M;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = wm * WM + fm * 16 + 4 * (lane >> 4) + r;
+            const int col = wn * WN + fn * 16 + (lane & 15);
+            f(b, row, col, acc[b][fm][fn][r]);
+          }
+  }
+};
+
+}  // namespace sffn

@@ -15,8 +15,13 @@ struct GuardBand {
 };
 
 hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const float* b_g,
-                             uint16_t* count, uint16_t* idx, void* val, int T, int K, int N,
-                             int cap, GuardBand gb, hipStream_t stream);
+                             const float* xnorm, const float* wnorm, uint16_t* count,
+                             uint16_t* idx, void* val, int T, int K, int N, int cap,
+                             GuardBand gb, hipStream_t stream);
+
+// Row norms of a [rows_a, K] and a [rows_b, K] matrix in one launch.
+hipError_t launch_row_norms(int dtype, const void* a, int rows_a, float* out_a, const void* b,
+                            int rows_b, float* out_b, int K, hipStream_t stream);
 
 // h[m, :] = ReLU(x[row(m)] wg_t^T + b) * (x[row(m)] wu_t^T) for m < rows, where
 // row(m) = rowmap[m] (rowmap != nullptr) and rows = *n_rows_dev (n_rows_dev !=

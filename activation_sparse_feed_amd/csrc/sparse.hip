@@ -161,6 +161,142 @@ __global__ __launch_bounds__(256) void sparse_updown(SparseArgs a) {
   if (lane == 0) a.tickets[t] = 0;
 }
 
+// Many tokens (prefill): one token per wave, WAVES tokens per workgroup.  The
+// waves of a workgroup walk the column tiles in windows of kWinTiles tiles and
+// meet at a barrier after each window, so the workgroups resident on one XCD
+// sweep the weight rows in near lockstep and the rows they share are served
+// from that XCD's L2 rather than from the last-level cache or HBM.  Per
+// window, a wave first lists its live entries (lane-parallel, in LDS), then
+// processes them two at a time so that four row loads are in flight:
+//   u = x_t . wu_t[j] with packed bf16 dot2, uniform DPP reduction;
+//   y_t += (h * u) * wd[j] in float32 registers.
+constexpr int kWinTiles = 4;
+
+template <int NCH, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
+  constexpr int E = 8;  // bf16 per 16-byte chunk
+  constexpr int LIST = kWinTiles * 128;  // upper bound of live entries per window (cap <= 128)
+  __shared__ uint32_t list_j[WAVES][kWinTiles * 32];
+  __shared__ float list_h[WAVES][kWinTiles * 32];
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  const int t = uniform((int)(blockIdx.x * WAVES + w));
+  const int nch = a.K / E;
+  bool active = t < a.T;
+  const uint16_t* cnt_row = a.count + (size_t)(active ? t : 0) * a.nt;
+  if (active) {
+    bool over = false;
+    for (int k = lane; k < a.nt; k += kWave) over |= (int)cnt_row[k] > a.cap;
+    active = __ballot(over) == 0ull;
+  }
+  u32x4_t xr[NCH];
+  float yv[NCH][E];
+  const uint16_t* xrow = (const uint16_t*)a.x + (size_t)(active ? t : 0) * a.K;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + kWave * c;
+    xr[c] = (active && ch < nch) ? ldg16(xrow + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < E; ++e) yv[c][e] = 0.f;
+  }
+  const uint16_t* wu = (const uint16_t*)a.wu;
+  const uint16_t* wd = (const uint16_t*)a.wd;
+  const int cap = a.cap;
+  const int per_win = kWinTiles * cap;  // slots examined per window (<= LIST)
+  (void)LIST;
+  for (int k0 = 0; k0 < a.nt; k0 += kWinTiles) {
+    if (active) {
+      // lane-parallel listing of the window's live entries (ascending column)
+      int n = 0;
+      for (int base = 0; base < per_win; base += kWave) {
+        const int slot = base + lane;
+        const int k = k0 + slot / (cap > 0 ? cap : 1);
+        const int ss = cap > 0 ? slot % cap : 0;
+        bool live = false;
+        uint32_t j = 0;
+        float h = 0.f;
+        if (cap > 0 && slot < per_win && k < a.nt) {
+          const int c = min((int)cnt_row[k], cap);
+          if (ss < c) {
+            const size_t off = ((size_t)t * a.nt + k) * cap + ss;
+            j = a.idx[off];
+            h = bf16_to_f32(((const uint16_t*)a.val)[off]);
+            live = j < (uint32_t)(a.nt * 128);
+          }
+        }
+        const uint64_t m = __ballot(live);
+        if (live) {
+          const int pos = n + lanes_below(m);
+          if (pos < kWinTiles * 32) { list_j[w][pos] = j; list_h[w][pos] = h; }
+        }
+        n += __popcll(m);
+      }
+      n = min(n, kWinTiles * 32);
+      __builtin_amdgcn_wave_barrier();
+      // software pipeline: the wu row of entry i+1 is in flight while entry
+      // i is reduced and its wd row streams in
+      u32x4_t ur[NCH], dr[NCH];
+      if (n > 0) {
+        const uint16_t* u0 = wu + (size_t)uniform((int)list_j[w][0]) * a.K;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const int ch = lane + kWave * c;
+          ur[c] = ch < nch ? ldg16(u0 + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+      for (int i = 0; i < n; ++i) {
+        const int j = uniform((int)list_j[w][i]);
+        const float h = list_h[w][i];
+        const uint16_t* dptr = wd + (size_t)j * a.K;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const int ch = lane + kWave * c;
+          dr[c] = ch < nch ? ldg16(dptr + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          p = dot2_bf16(xr[c].x, ur[c].x, p);
+          p = dot2_bf16(xr[c].y, ur[c].y, p);
+          p = dot2_bf16(xr[c].z, ur[c].z, p);
+          p = dot2_bf16(xr[c].w, ur[c].w, p);
+        }
+        if (i + 1 < n) {
+          const uint16_t* un = wu + (size_t)uniform((int)list_j[w][i + 1]) * a.K;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const int ch = lane + kWave * c;
+            ur[c] = ch < nch ? ldg16(un + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+          }
+        }
+        const float g = h * wave_sum_uniform(p);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          float f[E];
+          Elt<uint16_t>::unpack(dr[c], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) yv[c][e] = fmaf(g, f[e], yv[c][e]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + kWave * c;
+    if (ch < nch) {
+      u32x4_t o;
+      o.x = (uint32_t)f32_to_bf16(yv[c][0]) | ((uint32_t)f32_to_bf16(yv[c][1]) << 16);
+      o.y = (uint32_t)f32_to_bf16(yv[c][2]) | ((uint32_t)f32_to_bf16(yv[c][3]) << 16);
+      o.z = (uint32_t)f32_to_bf16(yv[c][4]) | ((uint32_t)f32_to_bf16(yv[c][5]) << 16);
+      o.w = (uint32_t)f32_to_bf16(yv[c][6]) | ((uint32_t)f32_to_bf16(yv[c][7]) << 16);
+      *(u32x4_t*)((uint16_t*)a.y + (size_t)t * a.K + (size_t)ch * E) = o;
+    }
+  }
+}
+
 template <typename T>
 hipError_t launch_typed(const SparseArgs& a, int nch_per_lane, hipStream_t stream) {
   const int items = a.T * a.S;
@@ -172,6 +308,17 @@ hipError_t launch_typed(const SparseArgs& a, int nch_per_lane, hipStream_t strea
     case 8: hipLaunchKernelGGL((sparse_updown<T, 8>), grid, dim3(256), 0, stream, a); break;
     case 16: hipLaunchKernelGGL((sparse_updown<T, 16>), grid, dim3(256), 0, stream, a); break;
     case 32: hipLaunchKernelGGL((sparse_updown<T, 32>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_window(const SparseArgs& a, int nch, hipStream_t stream) {
+  switch (nch) {
+    case 1: hipLaunchKernelGGL((sparse_updown_win<1, 16>), dim3((a.T + 15) / 16), dim3(1024), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((sparse_updown_win<2, 16>), dim3((a.T + 15) / 16), dim3(1024), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((sparse_updown_win<4, 16>), dim3((a.T + 15) / 16), dim3(1024), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((sparse_updown_win<8, 8>), dim3((a.T + 7) / 8), dim3(512), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -212,7 +359,11 @@ hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, cons
     a.tickets = (int*)ws;
     a.partial = (float*)((char*)ws + align256((size_t)T * 4));
   }
-  if (dtype == 1) return launch_typed<uint16_t>(a, pow2_at_least((K / 8 + 63) / 64), stream);
+  if (dtype == 1) {
+    const int nch = pow2_at_least((K / 8 + 63) / 64);
+    if (S == 1 && cap <= 32 && nch <= 8) return launch_window(a, nch, stream);
+    return launch_typed<uint16_t>(a, nch, stream);
+  }
   return launch_typed<float>(a, pow2_at_least((K / 4 + 63) / 64), stream);
 }
 

@@ -1,12 +1,14 @@
 // Gate projection with the TwELL epilogue.
 //
-// One workgroup computes a 128-token x 128-column tile of z = x wg_t^T + b_g,
-// i.e. exactly one TwELL column tile for 128 rows, so every (row, tile) list
-// is built inside one workgroup with no atomics and no second kernel (the
-// format is produced in the GEMM epilogue: pwwt.cn article, section 02; 1D
-// column tiles: same section, and the neo-ai.one article on TwELL).
+// One workgroup computes a tile of 128 or 256 tokens x 128 columns of
+// z = x wg_t^T + b_g, i.e. exactly one TwELL column tile for those rows, so
+// every (row, tile) list is built inside one workgroup with no atomics and no
+// second kernel (the format is produced in the GEMM epilogue: pwwt.cn article,
+// section 02; 1D column tiles: same section, and the neo-ai.one article on
+// TwELL).  The row norms of the guard band come from a small norms pass.
 //
-// Epilogue, per row (one wavefront per row, two columns per lane):
+// Epilogue of the 128-row kernels, per row (one wavefront per row, two
+// columns per lane):
 //   1. guard band: entries with |z32| <= coef_xw ||x_t|| ||w_j|| + coef_b |b_j|
 //      are re-evaluated exactly (exact.cuh), so activity is the sign of the
 //      exact z;
@@ -17,6 +19,7 @@
 #include "common.cuh"
 #include "exact.cuh"
 #include "gemm_core.cuh"
+#include "gemm_v2.cuh"
 #include "launch.h"
 
 namespace sffn {
@@ -33,83 +36,143 @@ struct GateArgs {
   uint16_t* count;
   uint16_t* idx;
   void* val;
+  const float* xnorm;  // ||x_t||, [T]
+  const float* wnorm;  // ||wg_t[j]||, [N]
   int T, K, N, cap;
   GuardBand gb;
 };
 
+// Copy the row norms of a tile into LDS (rows past T read as 0).
+__device__ __forceinline__ void load_tile_norms(const GateArgs& a, int m0, int bm, int n0,
+                                                float* rn_a, float* rn_b) {
+  for (int i = threadIdx.x; i < bm; i += blockDim.x) rn_a[i] = (m0 + i < a.T) ? a.xnorm[m0 + i] : 0.f;
+  for (int i = threadIdx.x; i < kTile; i += blockDim.x) rn_b[i] = a.wnorm[n0 + i];
+}
+
 // Rows [r0, r0 + nrows) of the tile are staged in zs (row stride zld, float32
-// or bfloat16 bits); the four waves take every fourth row.
+// or bfloat16 bits); the four waves take every fourth row.  Rows whose
+// entries are all outside the guard band are emitted at once; rows with an
+// entry inside it are listed in `defer` (LDS, 1 + nrows ints) and emitted in a
+// second pass after their flagged entries were re-evaluated exactly, so the
+// slow path runs on a few rows spread over all waves instead of stalling the
+// row walk.
 __device__ __forceinline__ float zget(const float* zs, int i) { return zs[i]; }
 __device__ __forceinline__ float zget(const uint16_t* zs, int i) { return bf16_to_f32(zs[i]); }
 
+struct RowCtx {
+  int nt, kt, m0, n0, r0;
+  float b0, b1, nw0, nw1, band_scale;
+};
+
+// Activity of the two entries of this lane in row rr, and the guard-band flags.
+template <typename ZT>
+__device__ __forceinline__ void row_state(const GateArgs& a, const RowCtx& c, const ZT* zs,
+                                          int zld, const float* rn_a, int rr, float& z0, float& z1,
+                                          uint64_t& f0, uint64_t& f1) {
+  const int lane = lane_id();
+  z0 = zget(zs, rr * zld + lane);
+  z1 = zget(zs, rr * zld + 64 + lane);
+  const float nx = rn_a[c.r0 + rr];
+  const float d0 = c.band_scale * (a.gb.coef_xw * nx * c.nw0 + a.gb.coef_b * fabsf(c.b0));
+  const float d1 = c.band_scale * (a.gb.coef_xw * nx * c.nw1 + a.gb.coef_b * fabsf(c.b1));
+  f0 = __ballot(!(fabsf(z0) > d0));
+  f1 = __ballot(!(fabsf(z1) > d1));
+}
+
+// Compaction of one row: ascending active columns into the first cap slots.
+template <typename T>
+__device__ __forceinline__ void emit_row(const GateArgs& a, const RowCtx& c, int t, bool act0,
+                                         bool act1, float z0, float z1) {
+  const int lane = lane_id();
+  const uint64_t m0m = __ballot(act0);
+  const uint64_t m1m = __ballot(act1);
+  const int c0 = __popcll(m0m);
+  const size_t base = ((size_t)t * c.nt + c.kt) * a.cap;
+  if (act0) {
+    const int s = lanes_below(m0m);
+    if (s < a.cap) {
+      a.idx[base + s] = (uint16_t)(c.n0 + lane);
+      Elt<T>::store1(a.val, base + s, z0);
+    }
+  }
+  if (act1) {
+    const int s = c0 + lanes_below(m1m);
+    if (s < a.cap) {
+      a.idx[base + s] = (uint16_t)(c.n0 + 64 + lane);
+      Elt<T>::store1(a.val, base + s, z1);
+    }
+  }
+  if (lane == 0) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)(c0 + __popcll(m1m));
+}
+
 template <typename T, typename ZT>
 __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, float band_scale,
-                           const float* rn_a, const float* rn_b, int r0, int m0, int n0) {
+                           const float* rn_a, const float* rn_b, int r0, int m0, int n0,
+                           int* defer, uint32_t* exact_lds) {
   const int lane = lane_id();
-  const int w = threadIdx.x >> 6;
-  const int nt = a.N / kTile;
-  const int kt = n0 / kTile;
-  const float b0 = a.b ? a.b[n0 + lane] : 0.f;
-  const float b1 = a.b ? a.b[n0 + 64 + lane] : 0.f;
-  const float nw0 = rn_b[lane], nw1 = rn_b[64 + lane];
+  const int w = uniform((int)(threadIdx.x >> 6));
+  RowCtx c;
+  c.nt = a.N / kTile;
+  c.kt = n0 / kTile;
+  c.m0 = m0;
+  c.n0 = n0;
+  c.r0 = r0;
+  c.b0 = a.b ? a.b[n0 + lane] : 0.f;
+  c.b1 = a.b ? a.b[n0 + 64 + lane] : 0.f;
+  c.nw0 = rn_b[lane];
+  c.nw1 = rn_b[64 + lane];
+  c.band_scale = band_scale;
+  if (threadIdx.x == 0) defer[0] = 0;
+  __syncthreads();
+  for (int rr = w; rr < nrows; rr += 4) {
+    const int t = m0 + r0 + rr;
+    if (t >= a.T) break;
+    float z0, z1;
+    uint64_t f0, f1;
+    row_state(a, c, zs, zld, rn_a, rr, z0, z1, f0, f1);
+    if (f0 | f1) {
+      if (lane == 0) defer[1 + atomicAdd(&defer[0], 1)] = rr;
+      continue;
+    }
+    emit_row<T>(a, c, t, z0 > 0.f, z1 > 0.f, z0, z1);
+  }
+  __syncthreads();
+  const int nd = defer[0];
   const T* x = (const T*)a.x;
   const T* wg = (const T*)a.wg;
-  for (int rr = w; rr < nrows; rr += 4) {
-    const int r = r0 + rr;
-    const int t = m0 + r;
-    if (t >= a.T) break;
-    float z0 = zget(zs, rr * zld + lane);
-    float z1 = zget(zs, rr * zld + 64 + lane);
-    const float nx = rn_a[r];
-    const float d0 = band_scale * (a.gb.coef_xw * nx * nw0 + a.gb.coef_b * fabsf(b0));
-    const float d1 = band_scale * (a.gb.coef_xw * nx * nw1 + a.gb.coef_b * fabsf(b1));
+  for (int i = w; i < nd; i += 4) {
+    const int rr = uniform(defer[1 + i]);
+    const int t = m0 + r0 + rr;
+    float z0, z1;
+    uint64_t f0, f1;
+    row_state(a, c, zs, zld, rn_a, rr, z0, z1, f0, f1);
     bool act0 = z0 > 0.f, act1 = z1 > 0.f;
-    uint64_t f0 = __ballot(!(fabsf(z0) > d0));
-    uint64_t f1 = __ballot(!(fabsf(z1) > d1));
     while (f0 | f1) {
-      int c;
-      if (f0) { c = __builtin_ctzll(f0); f0 &= f0 - 1; }
-      else    { c = 64 + __builtin_ctzll(f1); f1 &= f1 - 1; }
-      const float bc = a.b ? a.b[n0 + c] : 0.f;
-      const ExactResult e = exact_gate_value<T>(x + (size_t)t * a.K, wg + (size_t)(n0 + c) * a.K,
-                                                bc, a.K);
-      if (c < 64) {
-        if (lane == c) { act0 = e.sign > 0; z0 = (float)e.value; }
+      int col;
+      if (f0) { col = __builtin_ctzll(f0); f0 &= f0 - 1; }
+      else    { col = 64 + __builtin_ctzll(f1); f1 &= f1 - 1; }
+      const float bc = a.b ? a.b[n0 + col] : 0.f;
+      const ExactResult e = exact_gate_value<T>(x + (size_t)t * a.K,
+                                                wg + (size_t)(n0 + col) * a.K, bc, a.K,
+                                                exact_lds + w * kExactLdsWords);
+      if (col < 64) {
+        if (lane == col) { act0 = e.sign > 0; z0 = (float)e.value; }
       } else {
-        if (lane == c - 64) { act1 = e.sign > 0; z1 = (float)e.value; }
+        if (lane == col - 64) { act1 = e.sign > 0; z1 = (float)e.value; }
       }
     }
-    const uint64_t m0m = __ballot(act0);
-    const uint64_t m1m = __ballot(act1);
-    const int c0 = __popcll(m0m);
-    const size_t base = ((size_t)t * nt + kt) * a.cap;
-    if (act0) {
-      const int s = lanes_below(m0m);
-      if (s < a.cap) {
-        a.idx[base + s] = (uint16_t)(n0 + lane);
-        Elt<T>::store1(a.val, base + s, z0);
-      }
-    }
-    if (act1) {
-      const int s = c0 + lanes_below(m1m);
-      if (s < a.cap) {
-        a.idx[base + s] = (uint16_t)(n0 + 64 + lane);
-        Elt<T>::store1(a.val, base + s, z1);
-      }
-    }
-    if (lane == 0) a.count[(size_t)t * nt + kt] = (uint16_t)(c0 + __popcll(m1m));
+    emit_row<T>(a, c, t, act0, act1, z0, z1);
   }
 }
 
-// bf16: the whole 128 x 128 z tile (bias added) is staged in LDS as bfloat16,
-// which is the value TwELL stores anyway; the guard band is widened by 2^-7
-// to cover that rounding.  The accumulators are dead after staging, which
-// keeps the exact re-evaluation from competing with them for registers.
+// bf16, d_model % 8 == 0: 128 x 128 tiles on the register-staged main loop.
+// The whole z tile (bias added) is staged in LDS as bfloat16, the value TwELL
+// stores anyway; the guard band is widened by 2^-7 to cover that rounding.
 constexpr int kZld16 = kTile + 8;
 
 __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
-  using G = MfmaGemm<1, kTile, true>;
-  static_assert(G::LDS_BYTES >= (size_t)(128 * kZld16 * 2 + 256 * 4), "epilogue staging fits");
+  using G = MfmaGemm<1, kTile, false>;
+  static_assert(G::LDS_BYTES >= (size_t)36864 + 4 * kExactLdsWords * 4, "epilogue staging fits");
   __shared__ __attribute__((aligned(16))) uint16_t lds[G::LDS_BYTES / 2];
   const int nt = a.N / kTile;
   const int m0 = (blockIdx.x / nt) * G::BM;
@@ -118,23 +181,160 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
   const uint16_t* B[1] = {(const uint16_t*)a.wg};
   g.init((const uint16_t*)a.x, a.K, nullptr, m0, a.T, B, a.K, n0, a.N);
   g.run(lds, a.K);
-  // stage-buffer space is free now: z tile (bf16), then the row norms
   uint16_t* zs = lds;
   float* rn_a = (float*)(lds + 128 * kZld16);
   float* rn_b = rn_a + 128;
-  g.write_norms(rn_a, rn_b);
+  load_tile_norms(a, m0, 128, n0, rn_a, rn_b);
   g.for_each([&](int, int row, int col, float v) {
     const float bb = a.b ? a.b[n0 + col] : 0.f;
     zs[row * kZld16 + col] = f32_to_bf16(v + bb);
   });
   __syncthreads();
-  twell_rows<uint16_t>(a, zs, kZld16, 128, 1.0f + 0x1p-7f, rn_a, rn_b, 0, m0, n0);
+  twell_rows<uint16_t>(a, zs, kZld16, 128, 1.0f + 0x1p-7f, rn_a, rn_b, 0, m0, n0,
+                       (int*)(rn_b + 128), (uint32_t*)((uint8_t*)lds + 36864));
+}
+
+// bf16, d_model % 32 == 0: 256 x 128 tiles on the buffer-load main loop, TwELL
+// built straight from the MFMA accumulators.
+//
+// The four waves each hold 64 rows x all 128 columns of the tile: rows
+// 64 wm + 16 fm + 4 g + r and columns 16 fn + i, for lane 16 g + i and
+// accumulator (fm, fn, r).  For a fixed (fm, r), one ballot per fn gives, in
+// its 16-bit segment g, the activity of columns 16 fn .. 16 fn + 15 of row
+// 16 fm + 4 g + r.  A column's slot is the number of active columns before it
+// in its row: the popcounts of the row's segments of lower fn plus the active
+// lanes below it in its own segment; the row's count is the sum over fn.  All
+// of it stays inside the wave.
+//
+// Guard band: each entry is first tested against a bound for its whole row
+// (largest column norm and bias of the tile); only entries inside it get the
+// per-entry band, and only those inside that are re-evaluated exactly.
+using GateGemm = Gemm2<1, kTile, false, 32, 1>;
+
+struct AccEpi {
+  int m0, n0, nt, kt, wm, lane, gi, li;
+  float cw, cb;
+  float bias[GateGemm::FN], nw[GateGemm::FN];
+  const float* rn_a;
+  uint32_t* exact_lds;  // this wave's exact-stage area
+};
+
+// One accumulator row group (fm, r): 4 rows of the wave, all 128 columns.
+// Template indices keep every accumulator access static (no spill of the
+// accumulator array to scratch).
+template <int FM, int R>
+__device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, const AccEpi& c) {
+  constexpr int FN = GateGemm::FN;
+  const int row = c.wm * GateGemm::WM + FM * 16 + 4 * c.gi + R;
+  const int t = c.m0 + row;
+  const bool valid = t < a.T;
+  const float nx = c.rn_a[row];
+  const float dmax = c.cw * nx + c.cb;
+  float v[FN];
+  bool act[FN];
+  bool fl = false;
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    v[fn] = g.acc[0][FM][fn][R] + c.bias[fn];
+    act[fn] = v[fn] > 0.f;
+    fl |= valid && !(fabsf(v[fn]) > dmax);
+  }
+  if (__ballot(fl)) {
+    // rare: per-entry band, exact re-evaluation inside it
+    for (int fn = 0; fn < FN; ++fn) {
+      const float d = a.gb.coef_xw * nx * c.nw[fn] + a.gb.coef_b * fabsf(c.bias[fn]);
+      uint64_t fb = __ballot(valid && !(fabsf(v[fn]) > d));
+      while (fb) {
+        const int L = __builtin_ctzll(fb);
+        fb &= fb - 1;
+        const int lrow = c.wm * GateGemm::WM + FM * 16 + 4 * (L >> 4) + R;
+        const int lcol = fn * 16 + (L & 15);
+        const float bl = a.b ? a.b[c.n0 + lcol] : 0.f;
+        const ExactResult e = exact_gate_value<uint16_t>(
+            (const uint16_t*)a.x + (size_t)(c.m0 + lrow) * a.K,
+            (const uint16_t*)a.wg + (size_t)(c.n0 + lcol) * a.K, bl, a.K, c.exact_lds);
+        if (c.lane == L) {
+          act[fn] = e.sign > 0;
+          v[fn] = (float)e.value;
+        }
+      }
+    }
+  }
+  const size_t base = ((size_t)t * c.nt + c.kt) * a.cap;
+  int running = 0;
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const uint64_t m = __ballot(act[fn]);
+    const uint32_t seg = (uint32_t)(m >> (16 * c.gi)) & 0xffffu;
+    const int slot = running + __builtin_popcount(seg & ((1u << c.li) - 1u));
+    if (act[fn] && valid && slot < a.cap) {
+      a.idx[base + slot] = (uint16_t)(c.n0 + fn * 16 + c.li);
+      ((uint16_t*)a.val)[base + slot] = f32_to_bf16(v[fn]);
+    }
+    running += __builtin_popcount(seg);
+  }
+  if (c.li == 0 && valid) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)running;
+}
+
+template <int FM, int R>
+struct EpiLoop {
+  __device__ static __forceinline__ void run(const GateArgs& a, GateGemm& g, const AccEpi& c) {
+    epi_group<FM, R>(a, g, c);
+    if constexpr (R + 1 < 4) EpiLoop<FM, R + 1>::run(a, g, c);
+    else if constexpr (FM + 1 < GateGemm::FM) EpiLoop<FM + 1, 0>::run(a, g, c);
+  }
+};
+
+__global__ __launch_bounds__(256, 2) void gate_twell_bf16_v2(GateArgs a) {
+  using G = GateGemm;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
+  const int nt = a.N / kTile;
+  int mi, ni;
+  tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, nt, &mi, &ni);
+  AccEpi c;
+  c.m0 = mi * G::BM;
+  c.n0 = ni * kTile;
+  c.nt = nt;
+  c.kt = ni;
+  G g;
+  const uint16_t* B[1] = {(const uint16_t*)a.wg};
+  g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, c.m0, a.T, B, c.n0, a.N, a.K);
+  g.run(lds, a.K);
+
+  float* rn_a = (float*)lds;  // [256]
+  float* rn_b = rn_a + 256;   // [128]
+  static_assert(G::LDS_BYTES >= 2048 + 4 * kExactLdsWords * 4, "epilogue LDS fits");
+  load_tile_norms(a, c.m0, 256, c.n0, rn_a, rn_b);
+  __syncthreads();
+  c.rn_a = rn_a;
+  c.lane = lane_id();
+  c.wm = uniform((int)(threadIdx.x >> 6));
+  c.exact_lds = (uint32_t*)(lds + 2048) + c.wm * kExactLdsWords;
+  c.gi = c.lane >> 4;
+  c.li = c.lane & 15;
+  c.cw = 0.f;
+  c.cb = 0.f;
+#pragma unroll
+  for (int fn = 0; fn < G::FN; ++fn) {
+    const int col = fn * 16 + c.li;
+    c.bias[fn] = a.b ? a.b[c.n0 + col] : 0.f;
+    c.nw[fn] = rn_b[col];
+    c.cw = fmaxf(c.cw, a.gb.coef_xw * c.nw[fn]);
+    c.cb = fmaxf(c.cb, a.gb.coef_b * fabsf(c.bias[fn]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    c.cw = fmaxf(c.cw, __shfl_xor(c.cw, o, kWave));
+    c.cb = fmaxf(c.cb, __shfl_xor(c.cb, o, kWave));
+  }
+  EpiLoop<0, 0>::run(a, g, c);
 }
 
 __global__ __launch_bounds__(256) void gate_twell_f32(GateArgs a) {
-  using G = ValuGemm<1, kTile, false, true>;
-  constexpr size_t kZBytes = (64 * kZld + 256) * 4;
-  constexpr size_t kBytes = G::LDS_BYTES > kZBytes ? G::LDS_BYTES : kZBytes;
+  using G = ValuGemm<1, kTile, false, false>;
+  constexpr size_t kZBytes = 35840;  // >= (64 * kZld + 256 + 65) * 4, 256-aligned
+  static_assert(kZBytes >= (64 * kZld + 256 + 65) * 4, "staging");
+  constexpr size_t kBytes = (G::LDS_BYTES > kZBytes ? G::LDS_BYTES : kZBytes) + 4 * kExactLdsWords * 4;
   __shared__ __attribute__((aligned(16))) float lds[kBytes / 4];
   const int nt = a.N / kTile;
   const int m0 = (blockIdx.x / nt) * G::BM;
@@ -145,7 +345,7 @@ __global__ __launch_bounds__(256) void gate_twell_f32(GateArgs a) {
   float* zs = lds;
   float* rn_a = zs + 64 * kZld;
   float* rn_b = rn_a + 128;
-  g.write_norms(rn_a, rn_b);
+  load_tile_norms(a, m0, 128, n0, rn_a, rn_b);
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
     g.for_each([&](int, int row, int col, float v) {
@@ -155,23 +355,28 @@ __global__ __launch_bounds__(256) void gate_twell_f32(GateArgs a) {
       }
     });
     __syncthreads();
-    twell_rows<float>(a, zs, kZld, 64, 1.0f, rn_a, rn_b, half * 64, m0, n0);
+    twell_rows<float>(a, zs, kZld, 64, 1.0f, rn_a, rn_b, half * 64, m0, n0,
+                      (int*)(rn_b + 128), (uint32_t*)((uint8_t*)lds + kBytes - 4 * kExactLdsWords * 4));
   }
 }
 
 }  // namespace
 
 hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const float* b_g,
-                             uint16_t* count, uint16_t* idx, void* val, int T, int K, int N,
-                             int cap, GuardBand gb, hipStream_t stream) {
-  GateArgs a{x, wg_t, b_g, count, idx, val, T, K, N, cap, gb};
-  const int mt = (T + 127) / 128;
+                             const float* xnorm, const float* wnorm, uint16_t* count,
+                             uint16_t* idx, void* val, int T, int K, int N, int cap,
+                             GuardBand gb, hipStream_t stream) {
+  GateArgs a{x, wg_t, b_g, count, idx, val, xnorm, wnorm, T, K, N, cap, gb};
   const int nt = N / kTile;
-  const dim3 grid((unsigned)(mt * nt));
-  if (dtype == 1) {
-    hipLaunchKernelGGL(gate_twell_bf16, grid, dim3(256), 0, stream, a);
+  if (dtype == 1 && K % 32 == 0) {
+    const dim3 g2((unsigned)(((T + 255) / 256) * nt));
+    hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(256), 0, stream, a);
+  } else if (dtype == 1) {
+    hipLaunchKernelGGL(gate_twell_bf16, dim3((unsigned)(((T + 127) / 128) * nt)), dim3(256), 0,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL(gate_twell_f32, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(gate_twell_f32, dim3((unsigned)(((T + 127) / 128) * nt)), dim3(256), 0,
+                       stream, a);
   }
   return hipGetLastError();
 }

@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libsffn.so")
 
 SFFN_OK, SFFN_ERR_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ERR_HIP = 0, -1, -2, -3, -4
 SFFN_F32, SFFN_BF16 = 0, 1
-WS_HYBRID, WS_DENSE, WS_SPARSE = 0, 1, 2
+WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK = 0, 1, 2, 3
 TILE = 128
 
-EXPORTED = ("twell_pack", "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref",
-            "sffn_workspace_bytes", "sffn_strerror")
+EXPORTED = ("twell_weight_norms", "twell_pack", "sparse_ffn_fwd", "hybrid_route",
+            "dense_ffn_ref", "sffn_workspace_bytes", "sffn_strerror")
 
 
 class SffnError(RuntimeError):
@@ -43,11 +43,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
     sp = ctypes.POINTER(Shape)
-    lib.twell_pack.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+    lib.twell_weight_norms.argtypes = [sp, vp, vp, vp]
+    lib.twell_pack.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sparse_ffn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
-    for fn in ("twell_pack", "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref"):
+    for fn in ("twell_weight_norms", "twell_pack", "sparse_ffn_fwd", "hybrid_route",
+               "dense_ffn_ref"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
     lib.sffn_workspace_bytes.restype = sz
@@ -125,9 +127,17 @@ def alloc_twell(shape: Shape, device=None):
     return count, idx, val
 
 
-def twell_pack(shape: Shape, x, wg_t, b_g, count, idx, val, stream=None) -> None:
+def twell_weight_norms(shape: Shape, wg_t, wg_norms, stream=None) -> None:
+    _check("twell_weight_norms", _lib.twell_weight_norms(ctypes.byref(shape), _ptr(wg_t),
+                                                         _ptr(wg_norms), _stream(stream)))
+
+
+def twell_pack(shape: Shape, x, wg_t, b_g, count, idx, val, workspace, wg_norms=None,
+               stream=None) -> None:
+    ws_n = workspace.numel() * workspace.element_size()
     _check("twell_pack", _lib.twell_pack(ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g),
-                                         _ptr(count), _ptr(idx), _ptr(val), _stream(stream)))
+                                         _ptr(wg_norms), _ptr(count), _ptr(idx), _ptr(val),
+                                         _ptr(workspace), ws_n, _stream(stream)))
 
 
 def sparse_ffn_fwd(shape: Shape, x, wu_t, wd, count, idx, val, y, workspace=None,
@@ -156,7 +166,9 @@ def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=Non
 class SparseFFN:
     """Buffers for repeated sparse forwards of one shape: TwELL arrays, routed
     list, workspaces.  ``forward`` issues twell_pack, sparse_ffn_fwd and
-    hybrid_route on one stream with no host synchronisation."""
+    hybrid_route on one stream with no host synchronisation.  ``wg_norms``
+    (from ``weight_norms``) may be passed to skip recomputing the gate-weight
+    row norms on every call."""
 
     def __init__(self, T: int, d_model: int, d_ff: int, cap: int, dtype: torch.dtype,
                  device="cuda"):
@@ -167,12 +179,18 @@ class SparseFFN:
         self.routed = torch.empty(max(T, 1), dtype=torch.int32, device=device)
         self.n_routed = torch.zeros(1, dtype=torch.int32, device=device)
         self.ws_sparse = alloc_workspace(self.shape, WS_SPARSE, device)
+        self.ws_pack = alloc_workspace(self.shape, WS_PACK, device)
         self.ws_hybrid = alloc_workspace(self.shape, WS_HYBRID, device)
         self.y = torch.empty((T, d_model), dtype=dtype, device=device)
 
-    def forward(self, x, wg_t, b_g, wu_t, wd, stream=None) -> torch.Tensor:
+    def weight_norms(self, wg_t, stream=None) -> torch.Tensor:
+        n = torch.empty(self.shape.d_ff, dtype=torch.float32, device=wg_t.device)
+        twell_weight_norms(self.shape, wg_t, n, stream)
+        return n
+
+    def forward(self, x, wg_t, b_g, wu_t, wd, wg_norms=None, stream=None) -> torch.Tensor:
         s = self.shape
-        twell_pack(s, x, wg_t, b_g, self.count, self.idx, self.val, stream)
+        twell_pack(s, x, wg_t, b_g, self.count, self.idx, self.val, self.ws_pack, wg_norms, stream)
         sparse_ffn_fwd(s, x, wu_t, wd, self.count, self.idx, self.val, self.y, self.ws_sparse,
                        stream)
         hybrid_route(s, x, wg_t, b_g, wu_t, wd, self.count, self.routed, self.n_routed,

@@ -38,7 +38,8 @@
  *     host before anything is launched, nothing written):
  *       tile == 128; d_ff % 128 == 0; 128 <= d_ff <= 65535;
  *       0 <= cap <= 128; d_model % 8 == 0; 8 <= d_model <= 8192;
- *       0 <= T; T == 0 is a no-op returning SFFN_OK.
+ *       0 <= T; T == 0 is a no-op returning SFFN_OK;
+ *       T * d_model * sizeof(dtype) < 2^31 (twell_pack, hybrid_route).
  *     Inputs must be finite (no Inf/NaN).
  *   - Errors: every call returns an sffn_status.  A failed launch returns
  *     SFFN_ERR_HIP; device faults surface at the caller's next synchronisation.
@@ -64,7 +65,12 @@ typedef enum {
 typedef enum { SFFN_F32 = 0, SFFN_BF16 = 1 } sffn_dtype;
 
 /* Which call a workspace query is for. */
-typedef enum { SFFN_WS_HYBRID = 0, SFFN_WS_DENSE = 1, SFFN_WS_SPARSE = 2 } sffn_ws_kind;
+typedef enum {
+  SFFN_WS_HYBRID = 0,
+  SFFN_WS_DENSE = 1,
+  SFFN_WS_SPARSE = 2,
+  SFFN_WS_PACK = 3
+} sffn_ws_kind;
 
 typedef struct {
   int32_t T;       /* tokens (rows of x and y) */
@@ -76,13 +82,23 @@ typedef struct {
 } sffn_shape;
 
 /*
+ * twell_weight_norms -- Euclidean norm of every row of wg_t (float32 [d_ff]),
+ * an input of twell_pack's exact-sign guard band.  The gate weights do not
+ * change between calls, so a caller can compute these once per weight matrix
+ * and pass them to every twell_pack call.  No workspace.
+ */
+int32_t twell_weight_norms(const sffn_shape* shape, const void* wg_t, float* wg_norms,
+                           void* stream);
+
+/*
  * twell_pack -- gate projection with the TwELL epilogue (pwwt.cn article,
  * section 02: the format is produced directly in the gate GEMM's epilogue).
  *
  *   z[t, j] = sum_k x[t, k] * wg_t[j, k] + b_g[j]        (float32 accumulation)
  *   active  = z > 0 (strict), decided on the EXACT value of z: entries whose
- *             float32 result lies within the accumulation error bound of zero
- *             are re-evaluated exactly in the epilogue.
+ *             float32 result lies within a rigorous bound of the accumulation
+ *             error around zero (proportional to ||x_t|| ||wg_t[j]||) are
+ *             re-evaluated exactly in the epilogue.
  *   For each row t and tile k (columns 128k .. 128k+127):
  *     count[t, k]   = number of active columns in the tile (uncapped, <= 128)
  *     idx[t, k, s]  = s-th active column, ascending, global index j, for
@@ -91,11 +107,14 @@ typedef struct {
  *   Slots s >= min(count, cap) are left unwritten (unspecified).
  *
  * x: [T, d_model] dtype; wg_t: [d_ff, d_model] dtype; b_g: [d_ff] f32 or NULL;
- * count/idx/val: outputs as laid out above.  No workspace.
+ * wg_norms: the output of twell_weight_norms for this wg_t, or NULL (then they
+ * are computed inside the call); count/idx/val: outputs as laid out above.
+ * workspace: at least sffn_workspace_bytes(shape, SFFN_WS_PACK) bytes (row
+ * norms of x, and of wg_t when wg_norms is NULL).
  */
 int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t,
-                   const float* b_g, uint16_t* count, uint16_t* idx, void* val,
-                   void* stream);
+                   const float* b_g, const float* wg_norms, uint16_t* count, uint16_t* idx,
+                   void* val, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * sparse_ffn_fwd -- fused up(.)gate -> down over the TwELL nonzeros (pwwt.cn

@@ -55,8 +55,12 @@ P = ctypes.c_void_p(0x10000)        # aligned fake device pointer: never derefer
 MISALIGNED = ctypes.c_void_p(0x10008)
 
 
-def _pack(sffn, s, x=P, w=P, b=None, c=P, i=P, v=P):
-    return sffn._lib.twell_pack(ctypes.byref(s) if s is not None else None, x, w, b, c, i, v, None)
+WS = ctypes.c_void_p(0x20000)
+
+
+def _pack(sffn, s, x=P, w=P, b=None, c=P, i=P, v=P, n=None, ws=WS, ws_n=1 << 30):
+    return sffn._lib.twell_pack(ctypes.byref(s) if s is not None else None, x, w, b, n, c, i, v,
+                                ws, ws_n, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -75,11 +79,13 @@ def test_null_and_misaligned_pointers(sffn):
     assert _pack(sffn, s, w=MISALIGNED) == sffn.SFFN_ERR_ARG
     assert _pack(sffn, s, b=MISALIGNED) == sffn.SFFN_ERR_ARG
     assert _pack(sffn, s, c=None) == sffn.SFFN_ERR_ARG
+    assert _pack(sffn, s, n=MISALIGNED) == sffn.SFFN_ERR_ARG
+    assert sffn._lib.twell_weight_norms(ctypes.byref(s), P, None, None) == sffn.SFFN_ERR_ARG
 
 
 def test_zero_tokens_is_ok_without_buffers(sffn):
     s = _shape(sffn, T=0)
-    assert _pack(sffn, s, x=None, w=None, c=None, i=None, v=None) == sffn.SFFN_OK
+    assert _pack(sffn, s, x=None, w=None, c=None, i=None, v=None, ws=None, ws_n=0) == sffn.SFFN_OK
     lib = sffn._lib
     assert lib.dense_ffn_ref(ctypes.byref(s), None, None, None, None, None, None, 0, None, None) == 0
 
@@ -87,6 +93,13 @@ def test_zero_tokens_is_ok_without_buffers(sffn):
 def test_workspace_errors(sffn):
     s = _shape(sffn)
     lib = sffn._lib
+    need_p = sffn.workspace_bytes(s, sffn.WS_PACK)
+    assert need_p >= (64 + 512) * 4
+    assert _pack(sffn, s, ws_n=need_p - 1) == -3
+    assert _pack(sffn, s, ws=None) == -3
+    # activations too large for 32-bit buffer offsets
+    big = _shape(sffn, T=1 << 17, d_model=8192)
+    assert _pack(sffn, big) == -2
     need = sffn.workspace_bytes(s, sffn.WS_DENSE)
     assert need >= 64 * 512 * 2
     assert lib.dense_ffn_ref(ctypes.byref(s), P, P, None, P, P, P, need - 1, P, None) == -3

@@ -180,8 +180,27 @@ def test_zero_tokens_is_a_noop():
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((512, 256), dtype=torch.bfloat16, device="cuda")
     c, i, v = sffn.alloc_twell(sffn.make_shape(1, 256, 512, 8, sffn.SFFN_BF16))
-    sffn.twell_pack(s, x, w, None, c, i, v)
+    ws = sffn.alloc_workspace(sffn.make_shape(1, 256, 512, 8, sffn.SFFN_BF16), sffn.WS_PACK)
+    sffn.twell_pack(s, x, w, None, c, i, v, ws)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["prefill_1pct", "tiny_f32"])
+def test_precomputed_weight_norms_give_identical_twell(name):
+    w = wl.WORKLOADS[name]
+    if w.T > 512:
+        w = w.replace(T=512)
+    inp = wl.generate(w)
+    ffn, y1, d = run_sparse(inp, w.cap)
+    c1, i1 = ffn.count.clone(), ffn.idx.clone()
+    y1 = y1.clone()
+    norms = ffn.weight_norms(d["wg_t"])
+    y2 = ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], norms)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), ffn.count.view(torch.int16))
+    assert torch.equal(y1, y2)
+    ref = np.linalg.norm(inp.as_f64("wg_t"), axis=1)
+    assert np.allclose(norms.cpu().numpy(), ref, rtol=1e-4)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
