@@ -206,6 +206,89 @@ struct Gemm2 {
     }
   }
 
+  // ---- fragment-pipelined K loop (BK == 32): the MFMAs of step kt run on
+  // fragments read during step kt-1, while the fragments of step kt+1 are read
+  // from LDS and the buffer loads of step kt+2 are in flight.
+  struct Frags {
+    bf16x8_t a[FM];
+    bf16x8_t b[NB][FN];
+  };
+
+  __device__ __forceinline__ void load_frags(Frags& f, const uint8_t* stage) const {
+    const int lane = lane_id();
+    const int w = uniform((int)(threadIdx.x >> 6));
+    const int wm = w % WAVES_M, wn = w / WAVES_M;
+    const int cq = slot(lane & 15, lane >> 4) * 16;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int r = BM + b * BNW + wn * WN + fn * 16 + (lane & 15);
+        f.b[b][fn] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+      }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = wm * WM + fm * 16 + (lane & 15);
+      f.a[fm] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+    }
+  }
+
+  __device__ __forceinline__ void mma(const Frags& f) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[b][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[fm], f.b[b][fn],
+                                                                  acc[b][fm][fn], 0, 0, 0);
+  }
+
+  __device__ __forceinline__ void pipe_step(uint8_t* lds, int kt, int nk, Frags& cur, Frags& nxt) {
+    if (kt + 1 < nk) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // stage kt+1 landed (this wave's part)
+      lds_barrier();                               // ... and every wave's
+      if (kt + 2 < nk) issue(lds + ((kt + 2) % STAGES) * STAGE_BYTES, (kt + 2) * BK);
+      load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
+    }
+    mma(cur);
+  }
+
+  __device__ __forceinline__ void pipe_full(uint8_t* lds, int kt, Frags& cur, Frags& nxt) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    lds_barrier();
+    issue(lds + ((kt + 2) % STAGES) * STAGE_BYTES, (kt + 2) * BK);
+    load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
+    mma(cur);
+  }
+
+  __device__ __forceinline__ void run_pipe(uint8_t* lds, int K) {
+    static_assert(BK == 32, "pipelined loop reads one 32-wide K slice per step");
+    const int nk = K / BK;
+    issue(lds, 0);
+    if (nk > 1) issue(lds + STAGE_BYTES, BK);
+    if (nk > 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LOADS>());
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    }
+    lds_barrier();
+    Frags f0, f1;
+    load_frags(f0, lds);
+    int kt = 0;
+    // steady state: no conditions, so the fragment reads of step kt+1 overlap
+    // the MFMAs of step kt without a conservative wait at a merge point
+    for (; kt + 3 < nk; kt += 2) {
+      pipe_full(lds, kt, f0, f1);
+      pipe_full(lds, kt + 1, f1, f0);
+    }
+    for (; kt < nk; kt += 2) {
+      pipe_step(lds, kt, nk, f0, f1);
+      if (kt + 1 < nk) pipe_step(lds, kt + 1, nk, f1, f0);
+    }
+    __syncthreads();
+  }
+
   // Full K loop; K must be a multiple of 64.  lds must hold LDS_BYTES.
   __device__ __forceinline__ void run(uint8_t* lds, int K) {
     const int nk = K / BK;

@@ -170,9 +170,12 @@ __global__ __launch_bounds__(256) void sparse_updown(SparseArgs a) {
 // processes them two at a time so that four row loads are in flight:
 //   u = x_t . wu_t[j] with packed bf16 dot2, uniform DPP reduction;
 //   y_t += (h * u) * wd[j] in float32 registers.
-constexpr int kWinTiles = 4;
+#ifndef SFFN_WIN_TILES
+#define SFFN_WIN_TILES 4
+#endif
+constexpr int kWinTiles = SFFN_WIN_TILES;
 
-template <int NCH, int WAVES>
+template <int NCH, int WAVES, bool FULL>
 __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
   constexpr int E = 8;  // bf16 per 16-byte chunk
   constexpr int LIST = kWinTiles * 128;  // upper bound of live entries per window (cap <= 128)
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int ch = lane + kWave * c;
-    xr[c] = (active && ch < nch) ? ldg16(xrow + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+    xr[c] = (active && (FULL || ch < nch)) ? ldg16(xrow + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < E; ++e) yv[c][e] = 0.f;
   }
@@ -233,54 +236,81 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
       }
       n = min(n, kWinTiles * 32);
       __builtin_amdgcn_wave_barrier();
-      // software pipeline: the wu row of entry i+1 is in flight while entry
-      // i is reduced and its wd row streams in
-      u32x4_t ur[NCH], dr[NCH];
-      if (n > 0) {
-        const uint16_t* u0 = wu + (size_t)uniform((int)list_j[w][0]) * a.K;
+      // Entries go in pairs: the down projection of a pair is one packed
+      // dot2 per output element, y += (wd_j0, wd_j1) . (g0, g1), with g split
+      // into a bf16 high part and a bf16 remainder (two dot2) so that the
+      // pair costs as much as one float32 FMA pass while keeping about 16
+      // significant bits of g.  The wu row of the next entry is in flight
+      // while the current one is reduced.
+      u32x4_t ur[NCH], dr0[NCH], dr1[NCH];
+      auto load_row = [&](u32x4_t* dst, const uint16_t* row) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
           const int ch = lane + kWave * c;
-          ur[c] = ch < nch ? ldg16(u0 + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+          dst[c] = (FULL || ch < nch) ? ldg16(row + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
         }
-      }
-      for (int i = 0; i < n; ++i) {
-        const int j = uniform((int)list_j[w][i]);
-        const float h = list_h[w][i];
-        const uint16_t* dptr = wd + (size_t)j * a.K;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          const int ch = lane + kWave * c;
-          dr[c] = ch < nch ? ldg16(dptr + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
-        }
+      };
+      auto dot_x = [&](const u32x4_t* r) {
         float p = 0.f;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          p = dot2_bf16(xr[c].x, ur[c].x, p);
-          p = dot2_bf16(xr[c].y, ur[c].y, p);
-          p = dot2_bf16(xr[c].z, ur[c].z, p);
-          p = dot2_bf16(xr[c].w, ur[c].w, p);
+          p = dot2_bf16(xr[c].x, r[c].x, p);
+          p = dot2_bf16(xr[c].y, r[c].y, p);
+          p = dot2_bf16(xr[c].z, r[c].z, p);
+          p = dot2_bf16(xr[c].w, r[c].w, p);
         }
-        if (i + 1 < n) {
-          const uint16_t* un = wu + (size_t)uniform((int)list_j[w][i + 1]) * a.K;
+        return p;
+      };
+      auto row_j = [&](int i) { return wu + (size_t)uniform((int)list_j[w][i]) * a.K; };
+      auto drow_j = [&](int i) { return wd + (size_t)uniform((int)list_j[w][i]) * a.K; };
+      if (n > 0) load_row(ur, row_j(0));
+      int i = 0;
+      for (; i + 1 < n; i += 2) {
+        const float h0 = list_h[w][i], h1 = list_h[w][i + 1];
+        load_row(dr0, drow_j(i));
+        const float p0 = dot_x(ur);
+        load_row(ur, row_j(i + 1));
+        const float g0 = h0 * wave_sum_uniform(p0);
+        load_row(dr1, drow_j(i + 1));
+        const float p1 = dot_x(ur);
+        if (i + 2 < n) load_row(ur, row_j(i + 2));
+        const float g1 = h1 * wave_sum_uniform(p1);
+        const uint32_t gh0 = f32_to_bf16(g0), gh1 = f32_to_bf16(g1);
+        const uint32_t gl0 = f32_to_bf16(g0 - bf16_to_f32((uint16_t)gh0));
+        const uint32_t gl1 = f32_to_bf16(g1 - bf16_to_f32((uint16_t)gh1));
+        const uint32_t gh = gh0 | (gh1 << 16), gl = gl0 | (gl1 << 16);
 #pragma unroll
-          for (int c = 0; c < NCH; ++c) {
-            const int ch = lane + kWave * c;
-            ur[c] = ch < nch ? ldg16(un + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int c = 0; c < NCH; ++c) {
+          const uint32_t a4[4] = {dr0[c].x, dr0[c].y, dr0[c].z, dr0[c].w};
+          const uint32_t b4[4] = {dr1[c].x, dr1[c].y, dr1[c].z, dr1[c].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = __builtin_amdgcn_perm(b4[q], a4[q], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(b4[q], a4[q], 0x07060302u);
+            yv[c][2 * q] = dot2_bf16(lo, gl, dot2_bf16(lo, gh, yv[c][2 * q]));
+            yv[c][2 * q + 1] = dot2_bf16(hi, gl, dot2_bf16(hi, gh, yv[c][2 * q + 1]));
           }
         }
-        const float g = h * wave_sum_uniform(p);
+      }
+      if (i < n) {  // odd count: last entry alone, float32 FMA
+        const float h = list_h[w][i];
+        load_row(dr0, drow_j(i));
+        const float g = h * wave_sum_uniform(dot_x(ur));
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
           float f[E];
-          Elt<uint16_t>::unpack(dr[c], f);
+          Elt<uint16_t>::unpack(dr0[c], f);
 #pragma unroll
           for (int e = 0; e < E; ++e) yv[c][e] = fmaf(g, f[e], yv[c][e]);
         }
       }
       __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
+#ifndef SFFN_WIN_SYNC_EVERY
+#define SFFN_WIN_SYNC_EVERY 1
+#endif
+    if (SFFN_WIN_SYNC_EVERY > 0 && ((k0 / kWinTiles + 1) % (SFFN_WIN_SYNC_EVERY > 0 ? SFFN_WIN_SYNC_EVERY : 1)) == 0)
+      __syncthreads();
   }
   if (!active) return;
 #pragma unroll
@@ -313,12 +343,22 @@ hipError_t launch_typed(const SparseArgs& a, int nch_per_lane, hipStream_t strea
   return hipGetLastError();
 }
 
+template <int NCH, int WAVES>
+void launch_win(const SparseArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.T + WAVES - 1) / WAVES)), block(WAVES * 64);
+  if (a.K == NCH * 64 * 8) hipLaunchKernelGGL((sparse_updown_win<NCH, WAVES, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((sparse_updown_win<NCH, WAVES, false>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_window(const SparseArgs& a, int nch, hipStream_t stream) {
   switch (nch) {
-    case 1: hipLaunchKernelGGL((sparse_updown_win<1, 16>), dim3((a.T + 15) / 16), dim3(1024), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((sparse_updown_win<2, 16>), dim3((a.T + 15) / 16), dim3(1024), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((sparse_updown_win<4, 16>), dim3((a.T + 15) / 16), dim3(1024), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((sparse_updown_win<8, 8>), dim3((a.T + 7) / 8), dim3(512), 0, stream, a); break;
+    case 1: launch_win<1, 16>(a, stream); break;
+    case 2: launch_win<2, 16>(a, stream); break;
+#ifndef SFFN_WIN_WAVES4
+#define SFFN_WIN_WAVES4 16
+#endif
+    case 4: launch_win<4, SFFN_WIN_WAVES4>(a, stream); break;
+    case 8: launch_win<8, 8>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void gate_twell_bf16_v2(GateArgs a) {
   G g;
   const uint16_t* B[1] = {(const uint16_t*)a.wg};
   g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, c.m0, a.T, B, c.n0, a.N, a.K);
-  g.run(lds, a.K);
+  g.run_pipe(lds, a.K);
 
   float* rn_a = (float*)lds;  // [256]
   float* rn_b = rn_a + 256;   // [128]
