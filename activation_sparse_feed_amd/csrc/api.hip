@@ -41,9 +41,11 @@ size_t pack_ws(const sffn_shape* s) {
   return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4);
 }
 
-// The buffer-load GEMM addresses an activation matrix with 32-bit offsets.
+// The buffer-load GEMMs address an activation matrix, and the down weight,
+// with 32-bit byte offsets.
 bool act_bytes_too_large(const sffn_shape* s) {
-  return (uint64_t)s->T * (uint64_t)s->d_model * elt_bytes(s->dtype) >= (1ull << 31);
+  return (uint64_t)s->T * (uint64_t)s->d_model * elt_bytes(s->dtype) >= (1ull << 31) ||
+         (uint64_t)s->d_ff * (uint64_t)s->d_model * elt_bytes(s->dtype) >= (1ull << 31);
 }
 
 size_t hybrid_ws(const sffn_shape* s) {
@@ -146,6 +148,7 @@ int32_t dense_ffn_ref(const sffn_shape* shape, const void* x, const void* wg_t, 
   if (!ptrs_ok({x, wg_t, wu_t, wd, y}) || (b_g && !aligned16(b_g))) return SFFN_ERR_ARG;
   if (workspace == nullptr || !aligned16(workspace) || ws_bytes < dense_ws(shape))
     return SFFN_ERR_WORKSPACE;
+  if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int T = shape->T, K = shape->d_model, N = shape->d_ff;
   hipError_t e = launch_dense_gateup(shape->dtype, x, wg_t, b_g, wu_t, workspace, T, nullptr,

@@ -60,9 +60,15 @@ __device__ __forceinline__ void tile_of(int bid, int mt, int nt, int* m, int* n)
 // WAVES_N: waves along N (2: 2 x 2 waves of 128 rows x BNW/2 columns; 1: 4 x 1
 // waves of 64 rows x BNW columns, so that every row of a B matrix's tile lives
 // in one wave).
-template <int NB, int BNW, bool NORMS, int BK_ = 32, int WAVES_N = 2>
+// B_KN: the single B matrix is [K, N] (N-contiguous, e.g. the down projection
+// weight).  Its K step is staged as BK rows of BNW columns (256 bytes), with
+// 16-byte chunks XOR-swizzled by 2 * (k & 7); MFMA B fragments are read with
+// the gfx950 transposing LDS read, which hands each lane four consecutive k of
+// one column per 8-byte read.
+template <int NB, int BNW, bool NORMS, int BK_ = 32, int WAVES_N = 2, bool B_KN = false,
+          int BM_ = 256, int STAGES_ = 3>
 struct Gemm2 {
-  static constexpr int BM = 256, BK = BK_, STAGES = 3;
+  static constexpr int BM = BM_, BK = BK_, STAGES = STAGES_;
   static constexpr int BN = NB * BNW;
   static constexpr int ROWB = BK * 2;                  // bytes per LDS row
   static constexpr int CPR = BK / 8;                   // 16-byte chunks per row
@@ -73,11 +79,15 @@ struct Gemm2 {
   static constexpr int LOADS = BLOCKS / 4;             // load instructions per wave per stage
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(!NORMS || WAVES_N == 2, "norm split assumes 2 x 2 waves");
+  static_assert(!B_KN || (NB == 1 && BNW == 128 && BK == 32 && !NORMS), "K-major B layout");
+  static constexpr int KN_ROWB = BNW * 2;   // bytes per staged k row of a [K, N] B
+  static __device__ __forceinline__ int kn_slot(int k, int q) { return q ^ (2 * (k & 7)); }
   static constexpr int WAVES_M = 4 / WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BNW / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
   static_assert(BN == 128, "workgroup N tile");
+  static_assert(BM == 256 || BM == 128, "workgroup M tile");
   static_assert(BLOCKS % 4 == 0, "load blocks per wave");
 
   // Physical 16-byte slot of logical chunk q in row r: 8 consecutive rows
@@ -92,6 +102,7 @@ struct Gemm2 {
   uint32_t voff[LOADS];     // per-lane byte offset of its chunk within the source matrix
   __amdgpu_buffer_rsrc_t ra;
   __amdgpu_buffer_rsrc_t rb[NB];
+  int b_ld;  // B_KN: bytes per row of B
 
   // A: [*, K] bf16 rows; rows m0 .. m0+255 (gathered through rowmap when
   // given); rows >= m_valid read as zero.  B[b]: [N, K] bf16; rows n0 ..
@@ -104,8 +115,13 @@ struct Gemm2 {
     const uint16_t* abase = rowmap ? A : A + (size_t)m0 * K;
     const size_t a_rows = rowmap ? a_rows_total : (size_t)min(m_valid - m0, BM);
     ra = make_rsrc(abase, (uint32_t)(a_rows * ld));
+    if (B_KN) {
+      b_ld = N * 2;
+      rb[0] = make_rsrc(B[0] + n0, (uint32_t)((size_t)K * N * 2 - (size_t)n0 * 2));
+    } else {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) rb[b] = make_rsrc(B[b] + (size_t)n0 * K, (uint32_t)(BNW * ld));
+      for (int b = 0; b < NB; ++b) rb[b] = make_rsrc(B[b] + (size_t)n0 * K, (uint32_t)(BNW * ld));
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int blk = w * LOADS + i;
@@ -116,9 +132,15 @@ struct Gemm2 {
         uint32_t off = 0x80000000u;  // beyond any buffer: reads as zero
         if (m < m_valid) off = (uint32_t)((rowmap ? (uint32_t)rowmap[m] : (uint32_t)row) * ld);
         voff[i] = off + (uint32_t)q * 16u;
-      } else {
+      } else if (!B_KN) {
         const int rb_ = row - BM;
         voff[i] = (uint32_t)(rb_ % BNW) * ld + (uint32_t)q * 16u;
+      } else {
+        // B block blk - BM/RPB covers k rows 4 b .. 4 b + 3 of 256 bytes
+        const int bb = blk - BM / RPB;
+        const int kk = 4 * bb + (lane >> 4);
+        const int qq = kn_slot(kk, lane & 15);
+        voff[i] = (uint32_t)kk * (uint32_t)b_ld + (uint32_t)qq * 16u;
       }
     }
 #pragma unroll
@@ -145,6 +167,8 @@ struct Gemm2 {
       lds_void_t* dst = (lds_void_t*)(stage + blk * 1024);
       if (blk * RPB < BM) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[i], soff, 0, 0);
+      } else if (B_KN) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], dst, 16, voff[i], k0 * b_ld, 0, 0);
       } else if (NB == 1 || (blk * RPB - BM) < BNW) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], dst, 16, voff[i], soff, 0, 0);
       } else {
@@ -219,13 +243,35 @@ struct Gemm2 {
     const int w = uniform((int)(threadIdx.x >> 6));
     const int wm = w % WAVES_M, wn = w / WAVES_M;
     const int cq = slot(lane & 15, lane >> 4) * 16;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
+    if (B_KN) {
+      const uint8_t* bst = stage + BM * ROWB;
+      const int g = lane >> 4, i = lane & 15;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int r = BM + b * BNW + wn * WN + fn * 16 + (lane & 15);
-        f.b[b][fn] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+        const int nl = wn * WN + fn * 16 + 4 * (i & 3);
+        const int k1 = 8 * g + (i >> 2), k2 = k1 + 4;
+        const uint8_t* p1 = bst + k1 * KN_ROWB + kn_slot(k1, nl >> 3) * 16 + (nl & 7) * 2;
+        const uint8_t* p2 = bst + k2 * KN_ROWB + kn_slot(k2, nl >> 3) * 16 + (nl & 7) * 2;
+        typedef short s16x4_t __attribute__((ext_vector_type(4)));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(lds_void_t*)p1);
+        const s16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(lds_void_t*)p2);
+        const u32x4_t u = {(uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16),
+                           (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16),
+                           (uint32_t)(uint16_t)v2[0] | ((uint32_t)(uint16_t)v2[1] << 16),
+                           (uint32_t)(uint16_t)v2[2] | ((uint32_t)(uint16_t)v2[3] << 16)};
+        f.b[0][fn] = __builtin_bit_cast(bf16x8_t, u);
       }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int r = BM + b * BNW + wn * WN + fn * 16 + (lane & 15);
+          f.b[b][fn] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+        }
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int r = wm * WM + fm * 16 + (lane & 15);
@@ -244,47 +290,45 @@ struct Gemm2 {
                                                                   acc[b][fm][fn], 0, 0, 0);
   }
 
+  // Step kt: stage kt+1 must have landed (loads of stages kt+2 .. kt+S-2 may
+  // still be in flight), then the loads of stage kt+S-1 are issued into the
+  // buffer of stage kt-1, whose fragments were read during step kt-2.
+  template <bool STEADY>
   __device__ __forceinline__ void pipe_step(uint8_t* lds, int kt, int nk, Frags& cur, Frags& nxt) {
-    if (kt + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());  // stage kt+1 landed (this wave's part)
-      lds_barrier();                               // ... and every wave's
-      if (kt + 2 < nk) issue(lds + ((kt + 2) % STAGES) * STAGE_BYTES, (kt + 2) * BK);
+    if (STEADY || kt + 1 < nk) {
+      if (STEADY) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<(STAGES - 3) * LOADS>());
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      }
+      lds_barrier();
+      if (STEADY || kt + STAGES - 1 < nk)
+        issue(lds + ((kt + STAGES - 1) % STAGES) * STAGE_BYTES, (kt + STAGES - 1) * BK);
       load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
     }
     mma(cur);
   }
 
-  __device__ __forceinline__ void pipe_full(uint8_t* lds, int kt, Frags& cur, Frags& nxt) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-    lds_barrier();
-    issue(lds + ((kt + 2) % STAGES) * STAGE_BYTES, (kt + 2) * BK);
-    load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
-    mma(cur);
-  }
-
   __device__ __forceinline__ void run_pipe(uint8_t* lds, int K) {
     static_assert(BK == 32, "pipelined loop reads one 32-wide K slice per step");
+    static_assert(STAGES >= 3, "stages");
     const int nk = K / BK;
-    issue(lds, 0);
-    if (nk > 1) issue(lds + STAGE_BYTES, BK);
-    if (nk > 1) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LOADS>());
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-    }
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(lds + s * STAGE_BYTES, s * BK);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
     lds_barrier();
     Frags f0, f1;
     load_frags(f0, lds);
     int kt = 0;
-    // steady state: no conditions, so the fragment reads of step kt+1 overlap
-    // the MFMAs of step kt without a conservative wait at a merge point
-    for (; kt + 3 < nk; kt += 2) {
-      pipe_full(lds, kt, f0, f1);
-      pipe_full(lds, kt + 1, f1, f0);
+    // steady state (every stage it refers to exists): no conditions, so the
+    // fragment reads of step kt+1 overlap the MFMAs of step kt
+    for (; kt + STAGES < nk; kt += 2) {  // step kt+1 issues stage kt+STAGES
+      pipe_step<true>(lds, kt, nk, f0, f1);
+      pipe_step<true>(lds, kt + 1, nk, f1, f0);
     }
     for (; kt < nk; kt += 2) {
-      pipe_step(lds, kt, nk, f0, f1);
-      if (kt + 1 < nk) pipe_step(lds, kt + 1, nk, f1, f0);
+      pipe_step<false>(lds, kt, nk, f0, f1);
+      if (kt + 1 < nk) pipe_step<false>(lds, kt + 1, nk, f1, f0);
     }
     __syncthreads();
   }

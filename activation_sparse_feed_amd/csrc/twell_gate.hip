@@ -209,7 +209,13 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 // Guard band: each entry is first tested against a bound for its whole row
 // (largest column norm and bias of the tile); only entries inside it get the
 // per-entry band, and only those inside that are re-evaluated exactly.
-using GateGemm = Gemm2<1, kTile, false, 32, 1>;
+#ifndef SFFN_GATE_BM
+#define SFFN_GATE_BM 128
+#endif
+#ifndef SFFN_GATE_STAGES
+#define SFFN_GATE_STAGES 5
+#endif
+using GateGemm = Gemm2<1, kTile, false, 32, 1, false, SFFN_GATE_BM, SFFN_GATE_STAGES>;
 
 struct AccEpi {
   int m0, n0, nt, kt, wm, lane, gi, li;
@@ -285,7 +291,10 @@ struct EpiLoop {
   }
 };
 
-__global__ __launch_bounds__(256, 2) void gate_twell_bf16_v2(GateArgs a) {
+#ifndef SFFN_GATE_OCC
+#define SFFN_GATE_OCC 2
+#endif
+__global__ __launch_bounds__(256, SFFN_GATE_OCC) void gate_twell_bf16_v2(GateArgs a) {
   using G = GateGemm;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   const int nt = a.N / kTile;
@@ -301,10 +310,10 @@ __global__ __launch_bounds__(256, 2) void gate_twell_bf16_v2(GateArgs a) {
   g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, c.m0, a.T, B, c.n0, a.N, a.K);
   g.run_pipe(lds, a.K);
 
-  float* rn_a = (float*)lds;  // [256]
+  float* rn_a = (float*)lds;  // [BM]
   float* rn_b = rn_a + 256;   // [128]
   static_assert(G::LDS_BYTES >= 2048 + 4 * kExactLdsWords * 4, "epilogue LDS fits");
-  load_tile_norms(a, c.m0, 256, c.n0, rn_a, rn_b);
+  load_tile_norms(a, c.m0, G::BM, c.n0, rn_a, rn_b);
   __syncthreads();
   c.rn_a = rn_a;
   c.lane = lane_id();
@@ -369,7 +378,7 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
   GateArgs a{x, wg_t, b_g, count, idx, val, xnorm, wnorm, T, K, N, cap, gb};
   const int nt = N / kTile;
   if (dtype == 1 && K % 32 == 0) {
-    const dim3 g2((unsigned)(((T + 255) / 256) * nt));
+    const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) * nt));
     hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(256), 0, stream, a);
   } else if (dtype == 1) {
     hipLaunchKernelGGL(gate_twell_bf16, dim3((unsigned)(((T + 127) / 128) * nt)), dim3(256), 0,

@@ -39,7 +39,8 @@
  *       tile == 128; d_ff % 128 == 0; 128 <= d_ff <= 65535;
  *       0 <= cap <= 128; d_model % 8 == 0; 8 <= d_model <= 8192;
  *       0 <= T; T == 0 is a no-op returning SFFN_OK;
- *       T * d_model * sizeof(dtype) < 2^31 (twell_pack, hybrid_route).
+ *       T * d_model * sizeof(dtype) < 2^31 and d_ff * d_model * sizeof(dtype)
+ *       < 2^31 (twell_pack, hybrid_route, dense_ffn_ref).
  *     Inputs must be finite (no Inf/NaN).
  *   - Errors: every call returns an sffn_status.  A failed launch returns
  *     SFFN_ERR_HIP; device faults surface at the caller's next synchronisation.
