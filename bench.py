@@ -40,7 +40,44 @@ def parse_args():
     p.add_argument("--cpu-rows", type=int, default=None,
                    help="rows of the CPU oracle sample (default: whole batch, at most 4096)")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run device copies of MIB MiB (reference for the HBM byte "
+                        "counters of a profiling run) and exit")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_twell_pack_prefill_1pct.md")
+GATE_SOURCES = ("activation_sparse_feed_amd/csrc/twell_gate.hip",
+                "activation_sparse_feed_amd/csrc/gemm_v2.cuh",
+                "activation_sparse_feed_amd/csrc/exact.cuh",
+                "activation_sparse_feed_amd/csrc/common.cuh")
+
+
+def gate_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GATE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per twell_pack launch from the stored counter summary (its
+    'key: value' lines), or None when the counters were taken on another
+    workload or on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(": ", 1) for line in f.read().splitlines()
+                      if line.count(": ") == 1 and " " not in line.split(": ", 1)[0])
+    except OSError:
+        return None
+    if kv.get("workload") != workload or kv.get("source_digest") != gate_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(inp, rows: int) -> dict:
@@ -83,6 +120,16 @@ def main() -> int:
     import numpy as np
     import torch
     from activation_sparse_feed_amd import sffn, workloads as wl
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": max(1, args.steps)}))
+        return 0
 
     w = wl.WORKLOADS[args.workload]
     if args.cap is not None:
@@ -183,7 +230,8 @@ def main() -> int:
                    "tile": w.tile, "cap": w.cap, "rows": w.rows},
         "roofline": {"kernel": "twell_pack (gate GEMM + TwELL epilogue)", "bound": "mfma",
                      "achieved": gate_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gate_tflops / peak, "traffic": None},
+                     "frac": gate_tflops / peak, "traffic": measured_traffic(w.name),
+                     "traffic_unit": "bytes per launch (HBM, counter-derived)"},
         "kernels_ms": {"twell_pack": t_gate, "sparse_ffn_fwd": t_sparse,
                        "hybrid_route": t_hybrid, "events_step": t_events,
                        "dense_ffn_ref": t_dense},
