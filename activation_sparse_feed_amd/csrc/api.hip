@@ -38,7 +38,8 @@ size_t dense_ws(const sffn_shape* s) {
 }
 
 size_t pack_ws(const sffn_shape* s) {
-  return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4);
+  return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4) +
+         gate_workspace_bytes(s->dtype, s->T, s->d_model, s->d_ff);
 }
 
 // The buffer-load GEMMs address an activation matrix, and the down weight,
@@ -92,12 +93,14 @@ int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t, con
   hipStream_t s = (hipStream_t)stream;
   float* xn = (float*)workspace;
   float* wn = (float*)((char*)workspace + align256((size_t)shape->T * 4));
-  hipError_t e = launch_row_norms(shape->dtype, x, shape->T, xn, wg_t, wg_norms ? 0 : shape->d_ff,
-                                  wn, shape->d_model, s);
+  void* gws = (char*)wn + align256((size_t)shape->d_ff * 4);
+  const int rows_x = gate_needs_xnorm(shape->dtype, shape->T, shape->d_model) ? shape->T : 0;
+  const int rows_w = wg_norms ? 0 : shape->d_ff;
+  hipError_t e = launch_row_norms(shape->dtype, x, rows_x, xn, wg_t, rows_w, wn, shape->d_model, s);
   if (e != hipSuccess) return SFFN_ERR_HIP;
   return hip_status(launch_gate_twell(shape->dtype, x, wg_t, b_g, xn, wg_norms ? wg_norms : wn,
                                       count, idx, val, shape->T, shape->d_model, shape->d_ff,
-                                      shape->cap, guard_band(shape), s));
+                                      shape->cap, guard_band(shape), gws, s));
 }
 
 int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t, const void* wd,
@@ -109,7 +112,7 @@ int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t,
   if (!ptrs_ok({x, wu_t, wd, count, y})) return SFFN_ERR_ARG;
   if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
   const int nt = shape->d_ff / 128;
-  const size_t need = sparse_workspace_bytes(shape->T, nt, shape->d_model);
+  const size_t need = sparse_workspace_bytes(shape->dtype, shape->T, nt, shape->d_model, shape->cap);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || ws_bytes < need))
     return SFFN_ERR_WORKSPACE;
   return hip_status(launch_sparse_updown(shape->dtype, x, wu_t, wd, count, idx, val, y,
@@ -162,7 +165,9 @@ size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
   switch (which) {
     case SFFN_WS_HYBRID: return hybrid_ws(shape);
     case SFFN_WS_DENSE: return dense_ws(shape);
-    case SFFN_WS_SPARSE: return sparse_workspace_bytes(shape->T, shape->d_ff / 128, shape->d_model);
+    case SFFN_WS_SPARSE:
+      return sparse_workspace_bytes(shape->dtype, shape->T, shape->d_ff / 128, shape->d_model,
+                                    shape->cap);
     case SFFN_WS_PACK: return pack_ws(shape);
     default: return 0;
   }

@@ -14,10 +14,16 @@ struct GuardBand {
   float coef_b;
 };
 
+// Gate GEMM + TwELL epilogue.  gate_ws: gate_workspace_bytes() bytes (tickets
+// of the few-token split kernel, zero on first use and left zero, then its
+// partial tiles); xnorm is not read when gate_needs_xnorm() is false (that
+// kernel computes the norms of x in its main loop).
+size_t gate_workspace_bytes(int dtype, int T, int K, int N);
+bool gate_needs_xnorm(int dtype, int T, int K);
 hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const float* b_g,
                              const float* xnorm, const float* wnorm, uint16_t* count,
                              uint16_t* idx, void* val, int T, int K, int N, int cap,
-                             GuardBand gb, hipStream_t stream);
+                             GuardBand gb, void* gate_ws, hipStream_t stream);
 
 // Row norms of a [rows_a, K] and a [rows_b, K] matrix in one launch.
 hipError_t launch_row_norms(int dtype, const void* a, int rows_a, float* out_a, const void* b,
@@ -37,7 +43,7 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
 
 // Number of column splits of the fused sparse kernel for this shape.
 int sparse_splits(int T, int n_tiles, int d_model);
-size_t sparse_workspace_bytes(int T, int n_tiles, int d_model);
+size_t sparse_workspace_bytes(int dtype, int T, int n_tiles, int d_model, int cap);
 
 hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, const void* wd,
                                 const uint16_t* count, const uint16_t* idx, const void* val,

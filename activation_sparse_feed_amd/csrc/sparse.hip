@@ -327,6 +327,231 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
   }
 }
 
+// Few tokens (bf16): two passes, so that every pass has thousands of
+// independent row loads in flight instead of one token's chain per wave.
+//
+// Pass 1 (sparse_up_pass): for each live entry (t, k, s) of a non-routed row,
+//   a[t, k, s] = val * (x_t . wu_t[j])   in float32, into the workspace.
+// One wavefront per (token, group of G = 64 / cap tiles): lane l examines
+// slot l % cap of tile k0 + l / cap, so one ballot lists the group's live
+// entries; x_t stays in registers (16-byte chunks) and the entries' wu_t rows
+// are read two at a time with packed bf16 dot2, reduced with DPP.
+//
+// Pass 2 (sparse_down_pass): y[t, c0 .. c0 + 512) = sum over the token's live
+// entries of a * wd[j, c0 .. c0 + 512).  Workgroup = (token, 512-column
+// chunk), its four waves take every fourth tile group; each lane owns 8
+// output columns (one 16-byte load per entry row), the four partial chunks are
+// summed in LDS in wave order and written once, rounded.  Rows with every
+// count 0 get y = 0; routed rows are left alone.  No atomics: deterministic.
+struct TwoPassArgs {
+  const uint16_t* x;
+  const uint16_t* wu;
+  const uint16_t* wd;
+  const uint16_t* count;
+  const uint16_t* idx;
+  const uint16_t* val;
+  uint16_t* y;
+  float* acts;  // [T, nt, cap]
+  int T, K, nt, cap;
+};
+
+__device__ __forceinline__ bool row_routed(const uint16_t* cnt_row, int nt, int cap) {
+  bool over = false;
+  for (int k = lane_id(); k < nt; k += kWave) over |= (int)cnt_row[k] > cap;
+  return __ballot(over) != 0ull;
+}
+
+template <int NCH>
+__global__ __launch_bounds__(256) void sparse_up_pass(TwoPassArgs a, int groups) {
+  constexpr int E = 8;
+  const int lane = lane_id();
+  const int item = uniform((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int t = item / groups;
+  const int gi = item - t * groups;
+  if (t >= a.T) return;
+  const uint16_t* cnt_row = a.count + (size_t)t * a.nt;
+  if (row_routed(cnt_row, a.nt, a.cap)) return;
+  const int cap = a.cap;
+  const int G = cap >= kWave ? 1 : kWave / cap;
+  const int k_first = gi * G;
+  const int nch = a.K / E;
+  const uint16_t* xrow = a.x + (size_t)t * a.K;
+  u32x4_t xr[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + kWave * c;
+    xr[c] = ch < nch ? ldg16(xrow + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  auto load_row = [&](u32x4_t* dst, int j) {
+    const uint16_t* row = a.wu + (size_t)j * a.K;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + kWave * c;
+      dst[c] = ch < nch ? ldg16(row + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto dot_x = [&](const u32x4_t* r) {
+    float p = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      p = dot2_bf16(xr[c].x, r[c].x, p);
+      p = dot2_bf16(xr[c].y, r[c].y, p);
+      p = dot2_bf16(xr[c].z, r[c].z, p);
+      p = dot2_bf16(xr[c].w, r[c].w, p);
+    }
+    return p;
+  };
+  const int slots = G * cap;  // slots of this group (G == 1 when cap >= 64)
+  for (int base = 0; base < slots; base += kWave) {
+    const int q = base + lane;
+    const int k = k_first + q / cap;
+    const int ss = q - (q / cap) * cap;
+    bool live = false;
+    int j = 0;
+    float h = 0.f;
+    size_t off = 0;
+    if (q < slots && k < a.nt && ss < min((int)cnt_row[k], cap)) {
+      off = ((size_t)t * a.nt + k) * cap + ss;
+      j = a.idx[off];
+      h = bf16_to_f32(a.val[off]);
+      live = j < a.nt * 128;
+    }
+    uint64_t m = __ballot(live);
+    u32x4_t r0[NCH], r1[NCH];
+    int e0 = -1;
+    if (m) {
+      e0 = __builtin_ctzll(m);
+      m &= m - 1;
+      load_row(r0, __builtin_amdgcn_readlane(j, e0));
+    }
+    while (e0 >= 0) {
+      int e1 = -1;
+      if (m) {
+        e1 = __builtin_ctzll(m);
+        m &= m - 1;
+        load_row(r1, __builtin_amdgcn_readlane(j, e1));
+      }
+      const float p0 = wave_sum_uniform(dot_x(r0));
+      if (lane == e0) a.acts[off] = h * p0;
+      if (e1 < 0) break;
+      e0 = -1;
+      if (m) {
+        e0 = __builtin_ctzll(m);
+        m &= m - 1;
+        load_row(r0, __builtin_amdgcn_readlane(j, e0));
+      }
+      const float p1 = wave_sum_uniform(dot_x(r1));
+      if (lane == e1) a.acts[off] = h * p1;
+    }
+  }
+}
+
+constexpr int kDownCols = 512;  // output columns per workgroup of pass 2
+#ifndef SFFN_DOWN_INFLIGHT
+#define SFFN_DOWN_INFLIGHT 8
+#endif
+constexpr int kDownInflight = SFFN_DOWN_INFLIGHT;  // wd row loads in flight per wave
+
+__global__ __launch_bounds__(256) void sparse_down_pass(TwoPassArgs a, int groups, int chunks) {
+  __shared__ f32x4_t red[3][2][64];
+  const int lane = lane_id();
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int t = (int)blockIdx.x / chunks;
+  const int cc = (int)blockIdx.x - t * chunks;
+  const uint16_t* cnt_row = a.count + (size_t)t * a.nt;
+  if (row_routed(cnt_row, a.nt, a.cap)) return;  // uniform over the workgroup
+  const int cap = a.cap;
+  const int col = cc * kDownCols + 8 * lane;
+  const bool cok = col < a.K;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = 0.f;
+  const int G = cap >= kWave ? 1 : (cap > 0 ? kWave / cap : 1);
+  const int slots = G * cap;
+  for (int gi = w; gi < groups && cap > 0; gi += 4) {
+    const int k_first = gi * G;
+    for (int base = 0; base < slots; base += kWave) {
+      const int q = base + lane;
+      const int k = k_first + q / cap;
+      const int ss = q - (q / cap) * cap;
+      bool live = false;
+      int j = 0;
+      float g = 0.f;
+      if (q < slots && k < a.nt && ss < min((int)cnt_row[k], cap)) {
+        const size_t off = ((size_t)t * a.nt + k) * cap + ss;
+        j = a.idx[off];
+        g = a.acts[off];
+        live = j < a.nt * 128;
+      }
+      uint64_t m = __ballot(live);
+      // kDownInflight rows in flight
+      while (m) {
+        int es[kDownInflight];
+        u32x4_t d[kDownInflight];
+#pragma unroll
+        for (int u = 0; u < kDownInflight; ++u) {
+          es[u] = -1;
+          if (m) {
+            es[u] = __builtin_ctzll(m);
+            m &= m - 1;
+            const int jj = __builtin_amdgcn_readlane(j, es[u]);
+            d[u] = cok ? ldg16(a.wd + (size_t)jj * a.K + col) : u32x4_t{0u, 0u, 0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kDownInflight; ++u) {
+          if (es[u] < 0) break;
+          const float gg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g), es[u]));
+          float f[8];
+          Elt<uint16_t>::unpack(d[u], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = fmaf(gg, f[e], y[e]);
+        }
+      }
+    }
+  }
+  if (w > 0) {
+    red[w - 1][0][lane] = f32x4_t{y[0], y[1], y[2], y[3]};
+    red[w - 1][1][lane] = f32x4_t{y[4], y[5], y[6], y[7]};
+  }
+  __syncthreads();
+  if (w != 0 || !cok) return;
+#pragma unroll
+  for (int v = 0; v < 3; ++v) {
+    const f32x4_t lo = red[v][0][lane], hi = red[v][1][lane];
+    y[0] += lo.x; y[1] += lo.y; y[2] += lo.z; y[3] += lo.w;
+    y[4] += hi.x; y[5] += hi.y; y[6] += hi.z; y[7] += hi.w;
+  }
+  u32x4_t o;
+  o.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(y[4]) | ((uint32_t)f32_to_bf16(y[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(y[6]) | ((uint32_t)f32_to_bf16(y[7]) << 16);
+  *(u32x4_t*)(a.y + (size_t)t * a.K + col) = o;
+}
+
+hipError_t launch_two_pass(const SparseArgs& s, float* acts, hipStream_t stream) {
+  TwoPassArgs a{(const uint16_t*)s.x, (const uint16_t*)s.wu, (const uint16_t*)s.wd, s.count,
+                s.idx, (const uint16_t*)s.val, (uint16_t*)s.y, acts, s.T, s.K, s.nt, s.cap};
+  const int G = s.cap >= kWave ? 1 : (s.cap > 0 ? kWave / s.cap : 1);
+  const int groups = (s.nt + G - 1) / G;
+  if (s.cap > 0) {
+    const dim3 grid((unsigned)((s.T * groups + 3) / 4));
+    const int nch = (s.K / 8 + 63) / 64;
+    if (nch <= 1) hipLaunchKernelGGL(sparse_up_pass<1>, grid, dim3(256), 0, stream, a, groups);
+    else if (nch <= 2) hipLaunchKernelGGL(sparse_up_pass<2>, grid, dim3(256), 0, stream, a, groups);
+    else if (nch <= 4) hipLaunchKernelGGL(sparse_up_pass<4>, grid, dim3(256), 0, stream, a, groups);
+    else if (nch <= 8) hipLaunchKernelGGL(sparse_up_pass<8>, grid, dim3(256), 0, stream, a, groups);
+    else hipLaunchKernelGGL(sparse_up_pass<16>, grid, dim3(256), 0, stream, a, groups);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int chunks = (s.K + kDownCols - 1) / kDownCols;
+  hipLaunchKernelGGL(sparse_down_pass, dim3((unsigned)(s.T * chunks)), dim3(256), 0, stream, a,
+                     groups, chunks);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_typed(const SparseArgs& a, int nch_per_lane, hipStream_t stream) {
   const int items = a.T * a.S;
@@ -372,6 +597,12 @@ int pow2_at_least(int v) {
 
 }  // namespace
 
+#ifndef SFFN_TWO_PASS_MAX_T
+#define SFFN_TWO_PASS_MAX_T 256
+#endif
+// bf16 with few tokens takes the two-pass kernels.
+static bool use_two_pass(int dtype, int T) { return dtype == 1 && T <= SFFN_TWO_PASS_MAX_T; }
+
 int sparse_splits(int T, int n_tiles, int /*d_model*/) {
   // enough wavefronts to cover the chip (~2048) when there are few tokens
   if (T <= 0) return 1;
@@ -383,7 +614,8 @@ int sparse_splits(int T, int n_tiles, int /*d_model*/) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t sparse_workspace_bytes(int T, int n_tiles, int d_model) {
+size_t sparse_workspace_bytes(int dtype, int T, int n_tiles, int d_model, int cap) {
+  if (use_two_pass(dtype, T)) return align256((size_t)T * n_tiles * (size_t)cap * 4);
   const int S = sparse_splits(T, n_tiles, d_model);
   if (S <= 1) return 0;
   return align256((size_t)T * 4) + (size_t)S * T * d_model * 4;
@@ -393,6 +625,10 @@ hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, cons
                                 const uint16_t* count, const uint16_t* idx, const void* val,
                                 void* y, void* ws, int T, int K, int n_tiles, int cap,
                                 hipStream_t stream) {
+  if (use_two_pass(dtype, T)) {
+    SparseArgs a{x, wu_t, wd, count, idx, val, y, nullptr, nullptr, T, K, n_tiles, cap, 1};
+    return launch_two_pass(a, (float*)ws, stream);
+  }
   const int S = sparse_splits(T, n_tiles, K);
   SparseArgs a{x, wu_t, wd, count, idx, val, y, nullptr, nullptr, T, K, n_tiles, cap, S};
   if (S > 1) {

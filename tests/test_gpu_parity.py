@@ -141,6 +141,19 @@ def test_dense_reference(name, T):
     check_y(w.dtype, y, ref["y_dense"], np.zeros(w.T, dtype=bool))
 
 
+# ------------------------------------------------------- few-token kernels
+@pytest.mark.parametrize("T,K,N,beta,cap", [
+    (48, 1056, 1024, 1.6, 8),   # split-K gate with 4 row fragments, K tail in a 512-column chunk
+    (64, 2048, 2048, 2.0, 8),   # split-K gate, several splits per tile
+    (17, 4096, 1408, 2.3, 8),   # ragged row fragment, long K
+    (100, 264, 640, 1.5, 4),    # two-pass sparse kernels with K % 32 != 0, routing
+    (256, 512, 1024, 1.9, 8),   # largest token count of the two-pass kernels
+])
+def test_few_token_paths(T, K, N, beta, cap):
+    inp = wl.generate_custom(T=T, d_model=K, d_ff=N, dtype="bf16", beta=beta, seed_base=41)
+    compare(inp, cap)
+
+
 # ---------------------------------------------------------------- edge cases
 def _small(beta, dtype="bf16", T=64, seed=21):
     return wl.generate_custom(T=T, d_model=256, d_ff=512, dtype=dtype, beta=beta, seed_base=seed)
