@@ -103,14 +103,15 @@ struct ExactResult {
 // elements (K a multiple of the 16-byte chunk width).  Every lane of the wave
 // must call it with the same arguments and gets the same result.  lds_acc:
 // kExactLdsWords words of LDS owned by this wave (used by stage 2 only).
-template <typename T>
+// U: 16-byte chunks per lane whose loads are issued together (more U, fewer
+// round trips to memory, more registers).
+template <typename T, int U = 2>
 __device__ ExactResult exact_gate_value(const T* __restrict__ xrow, const T* __restrict__ wrow,
                                         float b, int K, uint32_t* lds_acc) {
   constexpr int E = Elt<T>::kPerChunk;
   const int lane = lane_id();
   const int nch = K / E;
   double s = 0.0, a = 0.0;
-  constexpr int U = 2;  // chunks per lane whose loads are issued together
   for (int base = 0; base < nch; base += kWave * U) {
     u32x4_t xc[U], wc[U];
 #pragma unroll

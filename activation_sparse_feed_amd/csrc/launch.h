@@ -14,10 +14,10 @@ struct GuardBand {
   float coef_b;
 };
 
-// Gate GEMM + TwELL epilogue.  gate_ws: gate_workspace_bytes() bytes (tickets
-// of the few-token split kernel, zero on first use and left zero, then its
-// partial tiles); xnorm is not read when gate_needs_xnorm() is false (that
-// kernel computes the norms of x in its main loop).
+// Gate GEMM + TwELL epilogue.  gate_ws: gate_workspace_bytes() bytes (partial
+// tiles of the few-token split-K kernels); xnorm is not read when
+// gate_needs_xnorm() is false (those kernels compute the norms of x from the
+// operands they load).
 size_t gate_workspace_bytes(int dtype, int T, int K, int N);
 bool gate_needs_xnorm(int dtype, int T, int K);
 hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const float* b_g,

@@ -105,7 +105,7 @@ __device__ __forceinline__ void emit_row(const GateArgs& a, const RowCtx& c, int
   if (lane == 0) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)(c0 + __popcll(m1m));
 }
 
-template <typename T, typename ZT>
+template <typename T, typename ZT, int EXACT_U = 2>
 __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, float band_scale,
                            const float* rn_a, const float* rn_b, int r0, int m0, int n0,
                            int* defer, uint32_t* exact_lds) {
@@ -152,7 +152,7 @@ __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, 
       if (f0) { col = __builtin_ctzll(f0); f0 &= f0 - 1; }
       else    { col = 64 + __builtin_ctzll(f1); f1 &= f1 - 1; }
       const float bc = a.b ? a.b[n0 + col] : 0.f;
-      const ExactResult e = exact_gate_value<T>(x + (size_t)t * a.K,
+      const ExactResult e = exact_gate_value<T, EXACT_U>(x + (size_t)t * a.K,
                                                 wg + (size_t)(n0 + col) * a.K, bc, a.K,
                                                 exact_lds + w * kExactLdsWords);
       if (col < 64) {
@@ -370,25 +370,33 @@ __global__ __launch_bounds__(256) void gate_twell_f32(GateArgs a) {
 }
 
 // Few tokens (T <= 64, e.g. decode): the gate GEMM is a stream of wg_t, and
-// a grid of one workgroup per column tile would leave most CUs idle.
-// Workgroup = (column tile kt, K split s) of S splits; its four waves take
-// consecutive quarters of the split's K range, so the 128 rows of wg_t of one
-// tile are read by 4S waves with no overlap.  MFMA operands are loaded from
-// global memory straight into registers (a 16-row x 64-byte fragment per
-// load; the next K step reads the other half of the same cache lines), one
-// step ahead of the MFMAs; x rows past T are zero.  The waves also accumulate
-// the sums of squares of the x values they load, which over the 4S waves of a
-// tile cover every element of the T rows once: the row norms of the guard band
-// come out of the main loop.
+// a grid of one workgroup per column tile would leave most CUs idle.  Two
+// kernels:
 //
-// Reduction: the four waves' tiles are summed in LDS, (w0 + w2) + (w1 + w3);
-// the workgroup writes that partial (fragment order) and its row sums of
-// squares to the workspace and takes a ticket; the last workgroup of the tile
-// sums the S partials in split order, adds the bias, stages z in LDS and
-// builds the TwELL lists with the row walk of the fp32 kernel (guard band,
-// exact re-evaluation), then re-arms the ticket.  The sums do not depend on
-// which workgroup finishes last, so the output is deterministic.
+// gate_skinny_partial: workgroup = (column tile kt, K split s) of S splits;
+// its four waves take consecutive quarters of the split's K range (at most
+// kSkinnySteps MFMA K steps each), so the 128 rows of wg_t of one tile are
+// read by 4S waves with no overlap.  Each wave issues the loads of all its
+// steps at once, straight from global memory into MFMA operand registers (a
+// 16-row x 64-byte fragment per load; consecutive steps read the two halves of
+// the same cache lines), then runs the MFMAs; x rows past T repeat row 0 and are never emitted.  The
+// waves also accumulate the sums of squares of the x values they load, which
+// over the 4S waves of a tile cover every element of the T rows once, so the
+// row norms of the guard band come out of this pass.  The four waves' tiles
+// are summed in LDS, (w0 + w2) + (w1 + w3), and the workgroup writes that
+// partial (fragment order) and its row sums of squares to the workspace.
+//
+// gate_skinny_epilogue: one workgroup per (tile, 16-row fragment) sums the S
+// partials in split order, adds the bias, stages z in LDS and builds the TwELL
+// lists with the row walk of the fp32 kernel (guard band, exact
+// re-evaluation with all of a row's loads in flight at once).  The kernel
+// boundary orders the partial writes before their reads, so no fence or
+// counter is needed, and the sums are in a fixed order: deterministic.
 constexpr int kSkinnyFN = kTile / 16;
+#ifndef SFFN_SKINNY_STEPS
+#define SFFN_SKINNY_STEPS 4
+#endif
+constexpr int kSkinnySteps = SFFN_SKINNY_STEPS;  // max K steps of 32 per wave
 
 template <int MF>
 struct Skinny {
@@ -397,17 +405,14 @@ struct Skinny {
   // floats per partial: NFRAG fragments of 64 lanes x 4, then ROWS sums of squares
   static constexpr int PART = NFRAG * 256 + ROWS;
   static constexpr int RED_BYTES = 2 * NFRAG * 64 * 16 + 4 * ROWS * 4;
-  static constexpr int EPI_BYTES = (ROWS * kZld + ROWS + kTile + ROWS + 1) * 4 + 4 * kExactLdsWords * 4;
-  static constexpr int LDS_BYTES = RED_BYTES > EPI_BYTES ? RED_BYTES : EPI_BYTES;
 };
 
 template <int MF>
-__global__ __launch_bounds__(256) void gate_twell_skinny(GateArgs a, float* partial,
-                                                         int* tickets, int S) {
+__global__ __launch_bounds__(256) void gate_skinny_partial(GateArgs a, float* partial, int S) {
   using SK = Skinny<MF>;
   constexpr int FN = kSkinnyFN;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[SK::LDS_BYTES];
-  __shared__ int last_flag;
+  constexpr int ST = kSkinnySteps;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[SK::RED_BYTES];
   const int lane = lane_id();
   const int w = uniform((int)(threadIdx.x >> 6));
   const int kt = (int)blockIdx.x / S;
@@ -416,22 +421,27 @@ __global__ __launch_bounds__(256) void gate_twell_skinny(GateArgs a, float* part
   const int nk = a.K / 32;
   const int sp = s * 4 + w, nsp = S * 4;
   const int k_lo = (int)(((long)sp * nk) / nsp);
-  const int k_hi = (int)(((long)(sp + 1) * nk) / nsp);
+  const int nst = (int)(((long)(sp + 1) * nk) / nsp) - k_lo;  // <= ST (host guarantees)
   const int r = lane & 15, g = lane >> 4;
 
-  const uint16_t* bp[FN];
-  const uint16_t* ap[MF];
-  bool aok[MF];
+  const uint16_t* bp = (const uint16_t*)a.wg + (size_t)(n0 + r) * a.K + (size_t)k_lo * 32 + 8 * g;
+  const size_t bstride = (size_t)16 * a.K;  // next fragment: 16 rows down
+  u32x4_t bf[ST][FN], af[ST][MF];
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn)
-    bp[fn] = (const uint16_t*)a.wg + (size_t)(n0 + 16 * fn + r) * a.K + 8 * g;
+  for (int i = 0; i < ST; ++i) {
+    if (i < nst) {
 #pragma unroll
-  for (int fm = 0; fm < MF; ++fm) {
-    const int row = 16 * fm + r;
-    aok[fm] = row < a.T;
-    ap[fm] = (const uint16_t*)a.x + (size_t)(aok[fm] ? row : 0) * a.K + 8 * g;
+      for (int fn = 0; fn < FN; ++fn) bf[i][fn] = ldg16(bp + fn * bstride + i * 32);
+#pragma unroll
+      for (int fm = 0; fm < MF; ++fm) {
+        // rows past T read row 0: MFMA output rows depend only on their own A
+        // row, and those rows are never emitted
+        const int row = 16 * fm + r;
+        af[i][fm] = ldg16((const uint16_t*)a.x + (size_t)(row < a.T ? row : 0) * a.K +
+                          (size_t)(k_lo + i) * 32 + 8 * g);
+      }
+    }
   }
-
   f32x4_t acc[MF][FN];
   float sq[MF];
 #pragma unroll
@@ -440,42 +450,19 @@ __global__ __launch_bounds__(256) void gate_twell_skinny(GateArgs a, float* part
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  struct Fr {
-    u32x4_t a[MF];
-    u32x4_t b[FN];
-  };
-  auto load = [&](Fr& f, int kk) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) f.b[fn] = ldg16(bp[fn] + (size_t)kk * 32);
+  for (int i = 0; i < ST; ++i) {
+    if (i < nst) {
 #pragma unroll
-    for (int fm = 0; fm < MF; ++fm) {
-      const u32x4_t v = ldg16(ap[fm] + (size_t)kk * 32);
-      f.a[fm] = aok[fm] ? v : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto mma = [&](const Fr& f) {
+      for (int fm = 0; fm < MF; ++fm) {
 #pragma unroll
-    for (int fm = 0; fm < MF; ++fm) {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, f.a[fm]), __builtin_bit_cast(bf16x8_t, f.b[fn]),
-            acc[fm][fn], 0, 0, 0);
-      const u32x4_t v = f.a[fm];
-      sq[fm] = dot2_bf16(v.x, v.x, dot2_bf16(v.y, v.y, dot2_bf16(v.z, v.z, dot2_bf16(v.w, v.w, sq[fm]))));
-    }
-  };
-  if (k_lo < k_hi) {
-    Fr f0, f1;
-    load(f0, k_lo);
-    int kk = k_lo;
-    while (true) {
-      if (kk + 1 < k_hi) load(f1, kk + 1);
-      mma(f0);
-      if (++kk >= k_hi) break;
-      if (kk + 1 < k_hi) load(f0, kk + 1);
-      mma(f1);
-      if (++kk >= k_hi) break;
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, af[i][fm]), __builtin_bit_cast(bf16x8_t, bf[i][fn]),
+              acc[fm][fn], 0, 0, 0);
+        const u32x4_t v = af[i][fm];
+        sq[fm] = dot2_bf16(v.x, v.x, dot2_bf16(v.y, v.y, dot2_bf16(v.z, v.z, dot2_bf16(v.w, v.w, sq[fm]))));
+      }
     }
   }
   // row sums of squares: lanes r, r+16, r+32, r+48 hold row 16 fm + r
@@ -486,8 +473,8 @@ __global__ __launch_bounds__(256) void gate_twell_skinny(GateArgs a, float* part
   }
 
   // ---- workgroup reduction in LDS: (w0 + w2) + (w1 + w3)
-  f32x4_t* red = (f32x4_t*)lds;                                   // [2][NFRAG][64]
-  float* redsq = (float*)(lds + 2 * SK::NFRAG * 64 * 16);         // [4][ROWS]
+  f32x4_t* red = (f32x4_t*)lds;                            // [2][NFRAG][64]
+  float* redsq = (float*)(lds + 2 * SK::NFRAG * 64 * 16);  // [4][ROWS]
   if (g == 0) {
 #pragma unroll
     for (int fm = 0; fm < MF; ++fm) redsq[w * SK::ROWS + 16 * fm + r] = sq[fm];
@@ -513,65 +500,90 @@ __global__ __launch_bounds__(256) void gate_twell_skinny(GateArgs a, float* part
       for (int fn = 0; fn < FN; ++fn) red[(fm * FN + fn) * 64 + lane] = acc[fm][fn];
   }
   __syncthreads();
+  if (w != 0) return;
   float* mine = partial + ((size_t)kt * S + s) * SK::PART;
-  if (w == 0) {
-#pragma unroll
-    for (int fm = 0; fm < MF; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const f32x4_t v = acc[fm][fn] + red[(fm * FN + fn) * 64 + lane];
-        *(f32x4_t*)(mine + (size_t)((fm * FN + fn) * 64 + lane) * 4) = v;
-      }
-    for (int i = lane; i < SK::ROWS; i += kWave)
-      mine[SK::NFRAG * 256 + i] =
-          (redsq[i] + redsq[2 * SK::ROWS + i]) + (redsq[SK::ROWS + i] + redsq[3 * SK::ROWS + i]);
-    __threadfence();
-    if (lane == 0) last_flag = atomicAdd(tickets + kt, 1) == S - 1;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-
-  // ---- last workgroup of the tile: z = sum of the S partials + bias
-  float* zs = (float*)lds;                    // [ROWS][kZld]
-  float* rn_a = zs + SK::ROWS * kZld;         // [ROWS]
-  float* rn_b = rn_a + SK::ROWS;              // [128]
-  int* defer = (int*)(rn_b + kTile);          // [1 + ROWS]
-  uint32_t* exact_lds = (uint32_t*)(lds + SK::LDS_BYTES - 4 * kExactLdsWords * 4);
-  const float* part0 = partial + (size_t)kt * S * SK::PART;
-  // wave w sums fragments fn = 2w, 2w + 1 of every fm
 #pragma unroll
   for (int fm = 0; fm < MF; ++fm)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int fn = 2 * w + q;
-      f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int ss = 0; ss < S; ++ss)
-        v += *(const f32x4_t*)(part0 + (size_t)ss * SK::PART + (size_t)((fm * FN + fn) * 64 + lane) * 4);
-      const int col = 16 * fn + r;
-      const float bb = a.b ? a.b[n0 + col] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) zs[(16 * fm + 4 * g + i) * kZld + col] = v[i] + bb;
+    for (int fn = 0; fn < FN; ++fn) {
+      const f32x4_t v = acc[fm][fn] + red[(fm * FN + fn) * 64 + lane];
+      *(f32x4_t*)(mine + (size_t)((fm * FN + fn) * 64 + lane) * 4) = v;
     }
-  for (int i = threadIdx.x; i < SK::ROWS; i += blockDim.x) {
-    float t = 0.f;
-    for (int ss = 0; ss < S; ++ss) t += part0[(size_t)ss * SK::PART + SK::NFRAG * 256 + i];
-    rn_a[i] = sqrtf(t);
-  }
-  for (int i = threadIdx.x; i < kTile; i += blockDim.x) rn_b[i] = a.wnorm[n0 + i];
-  if (threadIdx.x == 0) tickets[kt] = 0;
-  __syncthreads();
-  twell_rows<uint16_t>(a, (const float*)zs, kZld, SK::ROWS, 1.0f, rn_a, rn_b, 0, 0, n0, defer,
-                       exact_lds);
+  for (int i = lane; i < SK::ROWS; i += kWave)
+    mine[SK::NFRAG * 256 + i] =
+        (redsq[i] + redsq[2 * SK::ROWS + i]) + (redsq[SK::ROWS + i] + redsq[3 * SK::ROWS + i]);
 }
 
-// Splits of the few-token gate kernel: about 512 workgroups, at least two K
-// steps per wave.
+template <int MF>
+__global__ __launch_bounds__(256) void gate_skinny_epilogue(GateArgs a, const float* partial,
+                                                            int S) {
+  using SK = Skinny<MF>;
+  constexpr int FN = kSkinnyFN;
+  constexpr int EPI_BYTES = (16 * kZld + SK::ROWS + kTile + 17) * 4 + 4 * kExactLdsWords * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[EPI_BYTES];
+  const int kt = (int)blockIdx.x / MF;
+  const int fm = (int)blockIdx.x - kt * MF;  // this workgroup's 16 rows: 16 fm ..
+  const int n0 = kt * kTile;
+  if (16 * fm >= a.T) return;
+  float* zs = (float*)lds;           // [16][kZld]
+  float* rn_a = zs + 16 * kZld;      // [ROWS], entries 16 fm .. 16 fm + 15 used
+  float* rn_b = rn_a + SK::ROWS;     // [128]
+  int* defer = (int*)(rn_b + kTile); // [1 + 16]
+  uint32_t* exact_lds = (uint32_t*)(lds + EPI_BYTES - 4 * kExactLdsWords * 4);
+  const float* part0 = partial + (size_t)kt * S * SK::PART + (size_t)fm * FN * 256;
+  // the FN fragments of row fragment fm are 2 float4 per thread; thread tid
+  // sums entries tid and tid + 256 of the S partials in split order, eight
+  // splits' loads in flight at a time
+  f32x4_t v[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    f32x4_t ld[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          ld[u][m] = *(const f32x4_t*)(part0 + (size_t)(s0 + u) * SK::PART +
+                                       (size_t)(threadIdx.x + 256 * m) * 4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) v[m] += ld[u][m];
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int p = threadIdx.x + 256 * m;  // fn * 64 + fragment lane
+    const int fl = p & 63, fn = p >> 6;
+    const int col = 16 * fn + (fl & 15);
+    const float bb = a.b ? a.b[n0 + col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zs[(4 * (fl >> 4) + i) * kZld + col] = v[m][i] + bb;
+  }
+  if (threadIdx.x < 16) {
+    float t = 0.f;
+    for (int ss = 0; ss < S; ++ss)
+      t += partial[((size_t)kt * S + ss) * SK::PART + SK::NFRAG * 256 + 16 * fm + threadIdx.x];
+    rn_a[16 * fm + threadIdx.x] = sqrtf(t);
+  }
+  for (int i = threadIdx.x; i < kTile; i += blockDim.x) rn_b[i] = a.wnorm[n0 + i];
+  __syncthreads();
+  twell_rows<uint16_t, float, 8>(a, (const float*)zs, kZld, 16, 1.0f, rn_a, rn_b, 16 * fm, 0, n0,
+                                 defer, exact_lds);
+}
+
+// Splits of the few-token gate: at least enough that no wave has more than
+// kSkinnySteps K steps, and about SFFN_SKINNY_WGS workgroups when the K
+// range allows it (one step per wave at most that many splits).
+#ifndef SFFN_SKINNY_WGS
+#define SFFN_SKINNY_WGS 512
+#endif
 int skinny_splits(int K, int N) {
   const int nt = N / kTile;
   const int nk = K / 32;
-  int S = (512 + nt - 1) / nt;
-  S = min(S, max(1, nk / 8));
+  const int s_min = (nk + 4 * kSkinnySteps - 1) / (4 * kSkinnySteps);
+  const int s_max = max(1, nk / 4);
+  int S = max(SFFN_SKINNY_WGS / nt, s_min);
+  S = min(S, max(s_max, s_min));
   return max(S, 1);
 }
 
@@ -584,7 +596,7 @@ size_t gate_workspace_bytes(int dtype, int T, int K, int N) {
   const int nt = N / kTile;
   const int S = skinny_splits(K, N);
   const size_t part = T <= 32 ? Skinny<2>::PART : Skinny<4>::PART;
-  return (((size_t)nt * 4 + 255) & ~(size_t)255) + (size_t)nt * S * part * 4;
+  return (size_t)nt * S * part * 4;
 }
 
 bool gate_needs_xnorm(int dtype, int T, int K) { return !use_skinny(dtype, T, K); }
@@ -596,20 +608,19 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
   GateArgs a{x, wg_t, b_g, count, idx, val, xnorm, wnorm, T, K, N, cap, gb};
   const int nt = N / kTile;
   if (use_skinny(dtype, T, K)) {
-    // Guard band for this summation order: at most ceil(nk / 4S) MFMA steps
-    // in a wave, two adds across the waves, S partials and the bias, each
-    // with the same 4u margin as the one-pass kernels.
+    // Guard band for this summation order: at most kSkinnySteps MFMA steps in
+    // a wave, two adds across the waves, S partials and the bias, each with
+    // the same 4u margin as the one-pass kernels.
     const int S = skinny_splits(K, N);
-    const int nk = K / 32;
-    const int steps = (nk + 4 * S - 1) / (4 * S);
-    a.gb.coef_xw = 0x1p-22f * (float)(steps + S + 4);
-    int* tickets = (int*)gate_ws;
-    float* partial = (float*)((char*)gate_ws + (((size_t)nt * 4 + 255) & ~(size_t)255));
-    const dim3 grid((unsigned)(nt * S));
-    if (T <= 32)
-      hipLaunchKernelGGL(gate_twell_skinny<2>, grid, dim3(256), 0, stream, a, partial, tickets, S);
-    else
-      hipLaunchKernelGGL(gate_twell_skinny<4>, grid, dim3(256), 0, stream, a, partial, tickets, S);
+    a.gb.coef_xw = 0x1p-22f * (float)(kSkinnySteps + S + 4);
+    float* partial = (float*)gate_ws;
+    if (T <= 32) {
+      hipLaunchKernelGGL(gate_skinny_partial<2>, dim3((unsigned)(nt * S)), dim3(256), 0, stream, a, partial, S);
+      hipLaunchKernelGGL(gate_skinny_epilogue<2>, dim3((unsigned)(nt * 2)), dim3(256), 0, stream, a, partial, S);
+    } else {
+      hipLaunchKernelGGL(gate_skinny_partial<4>, dim3((unsigned)(nt * S)), dim3(256), 0, stream, a, partial, S);
+      hipLaunchKernelGGL(gate_skinny_epilogue<4>, dim3((unsigned)(nt * 4)), dim3(256), 0, stream, a, partial, S);
+    }
   } else if (dtype == 1 && K % 32 == 0) {
     const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) * nt));
     hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(256), 0, stream, a);

@@ -112,10 +112,8 @@ int32_t twell_weight_norms(const sffn_shape* shape, const void* wg_t, float* wg_
  * are computed inside the call); count/idx/val: outputs as laid out above.
  * workspace: at least sffn_workspace_bytes(shape, SFFN_WS_PACK) bytes (row
  * norms of x, and of wg_t when wg_norms is NULL; for few tokens, also the
- * partial tiles and ticket counters of the split-K gate kernel).  The caller
- * zero-fills it once before its first use with this library; calls leave it
- * zero-filled where it must be.  Calls that share a workspace must be
- * stream-ordered.
+ * partial tiles of the split-K gate kernels).  No initial contents needed.
+ * Calls that share a workspace must be stream-ordered.
  */
 int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t,
                    const float* b_g, const float* wg_norms, uint16_t* count, uint16_t* idx,
