@@ -26,12 +26,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+#ifndef SFFN_GEMM_INTERLEAVE
+#define SFFN_GEMM_INTERLEAVE 0
+#endif
+
 // Workgroup barrier for the LDS pipeline: waits for this wave's LDS
 // instructions, then s_barrier.  Unlike __syncthreads() it does not drain the
 // vector-memory counter, so buffer loads into later LDS stages stay in flight;
 // the caller waits for its own stage with s_waitcnt vmcnt first.
+// Written with builtins (not inline asm) so that the compiler's own wait
+// insertion sees the lgkmcnt(0) and does not add a second wait before the
+// next MFMAs.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
 }
 
 // Byte offset of an LDS pointer (LDS addresses are 32-bit).
@@ -230,19 +238,20 @@ struct Gemm2 {
     }
   }
 
-  // ---- fragment-pipelined K loop (BK == 32): the MFMAs of step kt run on
-  // fragments read during step kt-1, while the fragments of step kt+1 are read
-  // from LDS and the buffer loads of step kt+2 are in flight.
+  // ---- fragment-pipelined K loop: the MFMAs of step kt run on fragments
+  // read during step kt-1, while the fragments of step kt+1 are read from LDS
+  // and the buffer loads of later stages are in flight.  A step is one LDS
+  // stage of BK columns (KS = BK / 32 MFMA K slices).
+  static constexpr int KS = BK / 32;
   struct Frags {
-    bf16x8_t a[FM];
-    bf16x8_t b[NB][FN];
+    bf16x8_t a[KS][FM];
+    bf16x8_t b[KS][NB][FN];
   };
 
   __device__ __forceinline__ void load_frags(Frags& f, const uint8_t* stage) const {
     const int lane = lane_id();
     const int w = uniform((int)(threadIdx.x >> 6));
     const int wm = w % WAVES_M, wn = w / WAVES_M;
-    const int cq = slot(lane & 15, lane >> 4) * 16;
     if (B_KN) {
       const uint8_t* bst = stage + BM * ROWB;
       const int g = lane >> 4, i = lane & 15;
@@ -261,38 +270,52 @@ struct Gemm2 {
                            (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16),
                            (uint32_t)(uint16_t)v2[0] | ((uint32_t)(uint16_t)v2[1] << 16),
                            (uint32_t)(uint16_t)v2[2] | ((uint32_t)(uint16_t)v2[3] << 16)};
-        f.b[0][fn] = __builtin_bit_cast(bf16x8_t, u);
+        f.b[0][0][fn] = __builtin_bit_cast(bf16x8_t, u);
       }
     } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cq = slot(lane & 15, ks * 4 + (lane >> 4)) * 16;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int r = BM + b * BNW + wn * WN + fn * 16 + (lane & 15);
-          f.b[b][fn] = *(const bf16x8_t*)(stage + r * ROWB + cq);
-        }
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int r = BM + b * BNW + wn * WN + fn * 16 + (lane & 15);
+            f.b[ks][b][fn] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+          }
+      }
     }
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int r = wm * WM + fm * 16 + (lane & 15);
-      f.a[fm] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cq = slot(lane & 15, ks * 4 + (lane >> 4)) * 16;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = wm * WM + fm * 16 + (lane & 15);
+        f.a[ks][fm] = *(const bf16x8_t*)(stage + r * ROWB + cq);
+      }
     }
   }
 
   __device__ __forceinline__ void mma(const Frags& f) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[b][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[fm], f.b[b][fn],
-                                                                  acc[b][fm][fn], 0, 0, 0);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[b][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                f.a[ks][fm], f.b[ks][b][fn], acc[b][fm][fn], 0, 0, 0);
   }
 
   // Step kt: stage kt+1 must have landed (loads of stages kt+2 .. kt+S-2 may
   // still be in flight), then the loads of stage kt+S-1 are issued into the
   // buffer of stage kt-1, whose fragments were read during step kt-2.
+  // The scheduling barriers keep the compiler from moving the MFMAs of one
+  // step next to the fragment reads that feed them (which would make every
+  // MFMA wait for an LDS read): the reads of step kt+1 are all issued before
+  // the MFMAs of step kt.
   template <bool STEADY>
   __device__ __forceinline__ void pipe_step(uint8_t* lds, int kt, int nk, Frags& cur, Frags& nxt) {
     if (STEADY || kt + 1 < nk) {
@@ -306,11 +329,33 @@ struct Gemm2 {
         issue(lds + ((kt + STAGES - 1) % STAGES) * STAGE_BYTES, (kt + STAGES - 1) * BK);
       load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
     }
+#if SFFN_GEMM_INTERLEAVE
     mma(cur);
+    if (STEADY) {
+      // one MFMA after each buffer load and each fragment read, so that the
+      // matrix core is fed while the memory instructions issue
+      constexpr int NM = KS * FM * NB * FN, ND = KS * (NB * FN * (B_KN ? 2 : 1) + FM);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - LOADS - ND, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#else
+    __builtin_amdgcn_sched_barrier(0);
+    mma(cur);
+    __builtin_amdgcn_sched_barrier(0);
+#endif
   }
 
   __device__ __forceinline__ void run_pipe(uint8_t* lds, int K) {
-    static_assert(BK == 32, "pipelined loop reads one 32-wide K slice per step");
     static_assert(STAGES >= 3, "stages");
     const int nk = K / BK;
     for (int s = 0; s < STAGES - 1; ++s)

@@ -215,7 +215,10 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 #ifndef SFFN_GATE_STAGES
 #define SFFN_GATE_STAGES 5
 #endif
-using GateGemm = Gemm2<1, kTile, false, 32, 1, false, SFFN_GATE_BM, SFFN_GATE_STAGES>;
+#ifndef SFFN_GATE_BK
+#define SFFN_GATE_BK 32
+#endif
+using GateGemm = Gemm2<1, kTile, false, SFFN_GATE_BK, 1, false, SFFN_GATE_BM, SFFN_GATE_STAGES>;
 
 struct AccEpi {
   int m0, n0, nt, kt, wm, lane, gi, li;
@@ -621,7 +624,7 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
       hipLaunchKernelGGL(gate_skinny_partial<4>, dim3((unsigned)(nt * S)), dim3(256), 0, stream, a, partial, S);
       hipLaunchKernelGGL(gate_skinny_epilogue<4>, dim3((unsigned)(nt * 4)), dim3(256), 0, stream, a, partial, S);
     }
-  } else if (dtype == 1 && K % 32 == 0) {
+  } else if (dtype == 1 && K % GateGemm::BK == 0) {
     const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) * nt));
     hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(256), 0, stream, a);
   } else if (dtype == 1) {
