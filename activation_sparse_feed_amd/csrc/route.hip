@@ -3,7 +3,7 @@
 //
 // A row is routed when any of its TwELL tiles holds more active columns than
 // the capacity.  Two small kernels, no atomics, deterministic:
-//   route_flags    one thread per row: flag = OR_k (count[t, k] > cap);
+//   route_flags    per row (lanes over the tiles): flag = OR_k (count[t, k] > cap);
 //                  per-256-row block counts
 //   route_compact  each block adds the counts of the blocks before it and
 //                  writes its flagged rows in ascending order; the last block
@@ -20,15 +20,37 @@ constexpr int kBlock = 256;
 __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict__ count, int T,
                                                       int nt, int cap, int* __restrict__ flags,
                                                       int* __restrict__ block_count) {
-  const int t = blockIdx.x * kBlock + threadIdx.x;
-  int f = 0;
-  if (t < T) {
-    const uint16_t* row = count + (size_t)t * nt;
-    for (int k = 0; k < nt; ++k) f |= (int)row[k] > cap;
-    flags[t] = f;
+  // wave w takes rows w, w + 4, ... of the block; for each row the lanes read
+  // the tiles' counts side by side (coalesced), sixteen rows' loads in flight
+  __shared__ int wave_n[kBlock / kWave];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int b0 = blockIdx.x * kBlock;
+  constexpr int R = 16;
+  int n = 0;
+  for (int u0 = 0; u0 < kBlock / 4 && b0 + u0 * 4 < T; u0 += R) {
+    bool over[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int t = b0 + (u0 + u) * 4 + w;
+      over[u] = false;
+      if (t < T)
+        for (int k = lane; k < nt; k += kWave) over[u] |= (int)count[(size_t)t * nt + k] > cap;
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int t = b0 + (u0 + u) * 4 + w;
+      const int f = __ballot(over[u]) != 0ull;
+      if (t < T && lane == 0) flags[t] = f;
+      n += f;
+    }
   }
-  const int n = __syncthreads_count(f);
-  if (threadIdx.x == 0) block_count[blockIdx.x] = n;
+  if (lane == 0) wave_n[w] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int i = 0; i < kBlock / kWave; ++i) tot += wave_n[i];
+    block_count[blockIdx.x] = tot;
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ flags, int T,

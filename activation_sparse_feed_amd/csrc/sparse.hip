@@ -329,20 +329,26 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
 
 // Few tokens (bf16): two passes, so that every pass has thousands of
 // independent row loads in flight instead of one token's chain per wave.
+// Both passes take a group of consecutive TwELL tiles per wavefront with one
+// lane per slot (lane l: slot l % cap of tile k0 + l / cap), and load every
+// slot's count, index and value speculatively in one round trip (slots past
+// the count are in bounds and ignored), so a wave waits for memory twice: once
+// for the slot metadata, once per batch of weight rows.
 //
-// Pass 1 (sparse_up_pass): for each live entry (t, k, s) of a non-routed row,
+// Pass 1 (sparse_up_pass): for each live entry (t, k, s),
 //   a[t, k, s] = val * (x_t . wu_t[j])   in float32, into the workspace.
-// One wavefront per (token, group of G = 64 / cap tiles): lane l examines
-// slot l % cap of tile k0 + l / cap, so one ballot lists the group's live
-// entries; x_t stays in registers (16-byte chunks) and the entries' wu_t rows
-// are read two at a time with packed bf16 dot2, reduced with DPP.
+// x_t stays in registers (16-byte chunks); up to kUpBatch wu_t rows are read
+// at once, then reduced with packed bf16 dot2 and DPP.  Entries of routed rows
+// are computed too (they are rare and pass 2 ignores them), which saves the
+// row scan.
 //
 // Pass 2 (sparse_down_pass): y[t, c0 .. c0 + 512) = sum over the token's live
 // entries of a * wd[j, c0 .. c0 + 512).  Workgroup = (token, 512-column
-// chunk), its four waves take every fourth tile group; each lane owns 8
-// output columns (one 16-byte load per entry row), the four partial chunks are
-// summed in LDS in wave order and written once, rounded.  Rows with every
-// count 0 get y = 0; routed rows are left alone.  No atomics: deterministic.
+// chunk), its kDownWaves waves take every kDownWaves-th tile group; each lane
+// owns 8 output columns (one 16-byte load per entry row, kDownInflight rows in
+// flight), the partial chunks are summed in LDS in wave order and written
+// once, rounded.  Rows with every count 0 get y = 0; routed rows are left
+// alone.  No atomics: deterministic.
 struct TwoPassArgs {
   const uint16_t* x;
   const uint16_t* wu;
@@ -355,10 +361,40 @@ struct TwoPassArgs {
   int T, K, nt, cap;
 };
 
-__device__ __forceinline__ bool row_routed(const uint16_t* cnt_row, int nt, int cap) {
-  bool over = false;
-  for (int k = lane_id(); k < nt; k += kWave) over |= (int)cnt_row[k] > cap;
-  return __ballot(over) != 0ull;
+#ifndef SFFN_UP_SLOTS
+#define SFFN_UP_SLOTS 16
+#endif
+#ifndef SFFN_UP_BATCH
+#define SFFN_UP_BATCH 4
+#endif
+constexpr int kUpSlots = SFFN_UP_SLOTS;  // slots per wave in pass 1 (<= 64)
+constexpr int kUpBatch = SFFN_UP_BATCH;  // wu_t rows in flight per wave
+
+// Tiles per group for a given number of lanes: whole tiles, at least one.
+__host__ __device__ inline int tiles_per_group(int lanes, int cap) {
+  return cap >= lanes ? 1 : lanes / cap;
+}
+
+// One lane per slot of tiles [k_first, k_first + G): live flag, column, slot offset.
+struct SlotMeta {
+  bool live;
+  int j;
+  size_t off;
+};
+
+__device__ __forceinline__ SlotMeta slot_meta(const TwoPassArgs& a, int t, int k_first, int G,
+                                              int q) {
+  SlotMeta m{false, 0, 0};
+  const int cap = a.cap;
+  const int k = k_first + q / cap;
+  const int ss = q - (q / cap) * cap;
+  if (q < G * cap && k < a.nt) {
+    m.off = ((size_t)t * a.nt + k) * cap + ss;
+    const int c = a.count[(size_t)t * a.nt + k];
+    m.j = a.idx[m.off];
+    m.live = ss < min(c, cap) && m.j < a.nt * 128;
+  }
+  return m;
 }
 
 template <int NCH>
@@ -369,11 +405,8 @@ __global__ __launch_bounds__(256) void sparse_up_pass(TwoPassArgs a, int groups)
   const int t = item / groups;
   const int gi = item - t * groups;
   if (t >= a.T) return;
-  const uint16_t* cnt_row = a.count + (size_t)t * a.nt;
-  if (row_routed(cnt_row, a.nt, a.cap)) return;
   const int cap = a.cap;
-  const int G = cap >= kWave ? 1 : kWave / cap;
-  const int k_first = gi * G;
+  const int G = tiles_per_group(kUpSlots, cap);
   const int nch = a.K / E;
   const uint16_t* xrow = a.x + (size_t)t * a.K;
   u32x4_t xr[NCH];
@@ -382,109 +415,80 @@ __global__ __launch_bounds__(256) void sparse_up_pass(TwoPassArgs a, int groups)
     const int ch = lane + kWave * c;
     xr[c] = ch < nch ? ldg16(xrow + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
   }
-  auto load_row = [&](u32x4_t* dst, int j) {
-    const uint16_t* row = a.wu + (size_t)j * a.K;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int ch = lane + kWave * c;
-      dst[c] = ch < nch ? ldg16(row + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto dot_x = [&](const u32x4_t* r) {
-    float p = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      p = dot2_bf16(xr[c].x, r[c].x, p);
-      p = dot2_bf16(xr[c].y, r[c].y, p);
-      p = dot2_bf16(xr[c].z, r[c].z, p);
-      p = dot2_bf16(xr[c].w, r[c].w, p);
-    }
-    return p;
-  };
-  const int slots = G * cap;  // slots of this group (G == 1 when cap >= 64)
-  for (int base = 0; base < slots; base += kWave) {
+  for (int base = 0; base < G * cap; base += kUpSlots) {
     const int q = base + lane;
-    const int k = k_first + q / cap;
-    const int ss = q - (q / cap) * cap;
-    bool live = false;
-    int j = 0;
-    float h = 0.f;
-    size_t off = 0;
-    if (q < slots && k < a.nt && ss < min((int)cnt_row[k], cap)) {
-      off = ((size_t)t * a.nt + k) * cap + ss;
-      j = a.idx[off];
-      h = bf16_to_f32(a.val[off]);
-      live = j < a.nt * 128;
-    }
-    uint64_t m = __ballot(live);
-    u32x4_t r0[NCH], r1[NCH];
-    int e0 = -1;
-    if (m) {
-      e0 = __builtin_ctzll(m);
-      m &= m - 1;
-      load_row(r0, __builtin_amdgcn_readlane(j, e0));
-    }
-    while (e0 >= 0) {
-      int e1 = -1;
-      if (m) {
-        e1 = __builtin_ctzll(m);
-        m &= m - 1;
-        load_row(r1, __builtin_amdgcn_readlane(j, e1));
+    const SlotMeta sm = lane < kUpSlots ? slot_meta(a, t, gi * G, G, q) : SlotMeta{false, 0, 0};
+    const float h = sm.live ? bf16_to_f32(a.val[sm.off]) : 0.f;
+    uint64_t m = __ballot(sm.live);
+    while (m) {
+      int es[kUpBatch];
+      u32x4_t r[kUpBatch][NCH];
+#pragma unroll
+      for (int u = 0; u < kUpBatch; ++u) {
+        es[u] = -1;
+        if (m) {
+          es[u] = __builtin_ctzll(m);
+          m &= m - 1;
+          const uint16_t* row = a.wu + (size_t)__builtin_amdgcn_readlane(sm.j, es[u]) * a.K;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const int ch = lane + kWave * c;
+            r[u][c] = ch < nch ? ldg16(row + (size_t)ch * E) : u32x4_t{0u, 0u, 0u, 0u};
+          }
+        }
       }
-      const float p0 = wave_sum_uniform(dot_x(r0));
-      if (lane == e0) a.acts[off] = h * p0;
-      if (e1 < 0) break;
-      e0 = -1;
-      if (m) {
-        e0 = __builtin_ctzll(m);
-        m &= m - 1;
-        load_row(r0, __builtin_amdgcn_readlane(j, e0));
+#pragma unroll
+      for (int u = 0; u < kUpBatch; ++u) {
+        if (es[u] < 0) break;
+        float p = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          p = dot2_bf16(xr[c].x, r[u][c].x, p);
+          p = dot2_bf16(xr[c].y, r[u][c].y, p);
+          p = dot2_bf16(xr[c].z, r[u][c].z, p);
+          p = dot2_bf16(xr[c].w, r[u][c].w, p);
+        }
+        p = wave_sum_uniform(p);
+        if (lane == es[u]) a.acts[sm.off] = h * p;
       }
-      const float p1 = wave_sum_uniform(dot_x(r1));
-      if (lane == e1) a.acts[off] = h * p1;
     }
   }
 }
 
 constexpr int kDownCols = 512;  // output columns per workgroup of pass 2
+constexpr int kDownWaves = 8;   // waves per workgroup of pass 2
 #ifndef SFFN_DOWN_INFLIGHT
 #define SFFN_DOWN_INFLIGHT 8
 #endif
 constexpr int kDownInflight = SFFN_DOWN_INFLIGHT;  // wd row loads in flight per wave
 
-__global__ __launch_bounds__(256) void sparse_down_pass(TwoPassArgs a, int groups, int chunks) {
-  __shared__ f32x4_t red[3][2][64];
+__global__ __launch_bounds__(kDownWaves * 64) void sparse_down_pass(TwoPassArgs a, int groups,
+                                                                    int chunks) {
+  __shared__ f32x4_t red[kDownWaves - 1][2][64];
+  __shared__ int routed_flag;
   const int lane = lane_id();
   const int w = uniform((int)(threadIdx.x >> 6));
   const int t = (int)blockIdx.x / chunks;
   const int cc = (int)blockIdx.x - t * chunks;
-  const uint16_t* cnt_row = a.count + (size_t)t * a.nt;
-  if (row_routed(cnt_row, a.nt, a.cap)) return;  // uniform over the workgroup
   const int cap = a.cap;
+  // routed row?  (wave 0 scans the counts while the others start their slots)
+  if (w == 0) {
+    bool over = false;
+    for (int k = lane; k < a.nt; k += kWave) over |= (int)a.count[(size_t)t * a.nt + k] > cap;
+    const bool any = __ballot(over) != 0ull;
+    if (lane == 0) routed_flag = any;
+  }
   const int col = cc * kDownCols + 8 * lane;
   const bool cok = col < a.K;
   float y[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) y[e] = 0.f;
-  const int G = cap >= kWave ? 1 : (cap > 0 ? kWave / cap : 1);
-  const int slots = G * cap;
-  for (int gi = w; gi < groups && cap > 0; gi += 4) {
-    const int k_first = gi * G;
-    for (int base = 0; base < slots; base += kWave) {
-      const int q = base + lane;
-      const int k = k_first + q / cap;
-      const int ss = q - (q / cap) * cap;
-      bool live = false;
-      int j = 0;
-      float g = 0.f;
-      if (q < slots && k < a.nt && ss < min((int)cnt_row[k], cap)) {
-        const size_t off = ((size_t)t * a.nt + k) * cap + ss;
-        j = a.idx[off];
-        g = a.acts[off];
-        live = j < a.nt * 128;
-      }
-      uint64_t m = __ballot(live);
-      // kDownInflight rows in flight
+  const int G = cap > 0 ? tiles_per_group(kWave, cap) : 1;
+  for (int gi = w; gi < groups && cap > 0; gi += kDownWaves) {
+    for (int base = 0; base < G * cap; base += kWave) {
+      const SlotMeta sm = slot_meta(a, t, gi * G, G, base + lane);
+      const float g = sm.live ? a.acts[sm.off] : 0.f;
+      uint64_t m = __ballot(sm.live);
       while (m) {
         int es[kDownInflight];
         u32x4_t d[kDownInflight];
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(256) void sparse_down_pass(TwoPassArgs a, int group
           if (m) {
             es[u] = __builtin_ctzll(m);
             m &= m - 1;
-            const int jj = __builtin_amdgcn_readlane(j, es[u]);
+            const int jj = __builtin_amdgcn_readlane(sm.j, es[u]);
             d[u] = cok ? ldg16(a.wd + (size_t)jj * a.K + col) : u32x4_t{0u, 0u, 0u, 0u};
           }
         }
@@ -515,9 +519,9 @@ __global__ __launch_bounds__(256) void sparse_down_pass(TwoPassArgs a, int group
     red[w - 1][1][lane] = f32x4_t{y[4], y[5], y[6], y[7]};
   }
   __syncthreads();
-  if (w != 0 || !cok) return;
+  if (w != 0 || !cok || routed_flag) return;
 #pragma unroll
-  for (int v = 0; v < 3; ++v) {
+  for (int v = 0; v < kDownWaves - 1; ++v) {
     const f32x4_t lo = red[v][0][lane], hi = red[v][1][lane];
     y[0] += lo.x; y[1] += lo.y; y[2] += lo.z; y[3] += lo.w;
     y[4] += hi.x; y[5] += hi.y; y[6] += hi.z; y[7] += hi.w;
@@ -533,9 +537,9 @@ __global__ __launch_bounds__(256) void sparse_down_pass(TwoPassArgs a, int group
 hipError_t launch_two_pass(const SparseArgs& s, float* acts, hipStream_t stream) {
   TwoPassArgs a{(const uint16_t*)s.x, (const uint16_t*)s.wu, (const uint16_t*)s.wd, s.count,
                 s.idx, (const uint16_t*)s.val, (uint16_t*)s.y, acts, s.T, s.K, s.nt, s.cap};
-  const int G = s.cap >= kWave ? 1 : (s.cap > 0 ? kWave / s.cap : 1);
-  const int groups = (s.nt + G - 1) / G;
   if (s.cap > 0) {
+    const int G = tiles_per_group(kUpSlots, s.cap);
+    const int groups = (s.nt + G - 1) / G;
     const dim3 grid((unsigned)((s.T * groups + 3) / 4));
     const int nch = (s.K / 8 + 63) / 64;
     if (nch <= 1) hipLaunchKernelGGL(sparse_up_pass<1>, grid, dim3(256), 0, stream, a, groups);
@@ -546,9 +550,11 @@ hipError_t launch_two_pass(const SparseArgs& s, float* acts, hipStream_t stream)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int G = s.cap > 0 ? tiles_per_group(kWave, s.cap) : 1;
+  const int groups = (s.nt + G - 1) / G;
   const int chunks = (s.K + kDownCols - 1) / kDownCols;
-  hipLaunchKernelGGL(sparse_down_pass, dim3((unsigned)(s.T * chunks)), dim3(256), 0, stream, a,
-                     groups, chunks);
+  hipLaunchKernelGGL(sparse_down_pass, dim3((unsigned)(s.T * chunks)), dim3(kDownWaves * 64), 0,
+                     stream, a, groups, chunks);
   return hipGetLastError();
 }
 

@@ -146,6 +146,7 @@ def test_dense_reference(name, T):
     (48, 1056, 1024, 1.6, 8),   # split-K gate with 4 row fragments, K tail in a 512-column chunk
     (64, 2048, 2048, 2.0, 8),   # split-K gate, several splits per tile
     (17, 4096, 1408, 2.3, 8),   # ragged row fragment, long K
+    (5, 2048, 8192, 2.0, 8),    # one workgroup per column tile, ragged rows
     (100, 264, 640, 1.5, 4),    # two-pass sparse kernels with K % 32 != 0, routing
     (256, 512, 1024, 1.9, 8),   # largest token count of the two-pass kernels
 ])
