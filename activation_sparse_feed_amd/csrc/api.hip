@@ -49,8 +49,14 @@ bool act_bytes_too_large(const sffn_shape* s) {
          (uint64_t)s->d_ff * (uint64_t)s->d_model * elt_bytes(s->dtype) >= (1ull << 31);
 }
 
+bool routed_fast_path(const sffn_shape* s) {
+  return s->dtype == SFFN_BF16 && s->d_model % 32 == 0;
+}
+
 size_t hybrid_ws(const sffn_shape* s) {
-  return route_workspace_bytes(s->T) + align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
+  size_t n = route_workspace_bytes(s->T) + align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
+  if (routed_fast_path(s)) n += align256(routed_partial_bytes(s->T, s->d_model));
+  return n;
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? SFFN_OK : SFFN_ERR_HIP; }
@@ -136,6 +142,11 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t, c
   hipError_t e = launch_route(count, T, N / 128, shape->cap, routed, n_routed, workspace, s);
   if (e != hipSuccess) return SFFN_ERR_HIP;
   void* h = (char*)workspace + route_workspace_bytes(T);
+  if (routed_fast_path(shape)) {
+    float* partial = (float*)((char*)h + align256((size_t)T * N * elt_bytes(shape->dtype)));
+    return hip_status(launch_routed_ffn(x, wg_t, b_g, wu_t, wd, h, y, partial, T, routed,
+                                        n_routed, K, N, s));
+  }
   e = launch_dense_gateup(shape->dtype, x, wg_t, b_g, wu_t, h, T, routed, n_routed, K, N, s);
   if (e != hipSuccess) return SFFN_ERR_HIP;
   e = launch_down(shape->dtype, h, wd, y, T, routed, n_routed, N, K, s);

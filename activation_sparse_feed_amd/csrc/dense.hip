@@ -202,6 +202,134 @@ __global__ __launch_bounds__(256, 2) void down_bf16_v2(DenseArgs a) {
   });
 }
 
+// ------------------------------------------- routed rows (hybrid fallback)
+// The number of routed rows is only known on the device, so these kernels run
+// a fixed grid of workgroups that loop over the tiles (and K splits) of the
+// actual row count; tile i -> row tile i % mt, column tile i / mt, so the
+// active tiles are spread over all XCDs by the round-robin dispatch.  128-row tiles and a deeper LDS
+// pipeline than the full-size kernels: with few tiles there are few
+// workgroups per CU to hide memory latency with.
+#ifndef SFFN_ROUTED_STAGES
+#define SFFN_ROUTED_STAGES 5
+#endif
+constexpr int kRoutedGrid = 512;     // workgroups of the routed kernels
+constexpr int kRoutedMaxSplit = 8;   // K splits of the routed down GEMM
+
+// gate+up of the routed rows for one Gemm2 configuration: tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ... of the mt x nt tiles.
+template <typename G>
+__device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, uint8_t* lds) {
+  const int mt = (mv + G::BM - 1) / G::BM, nt = a.N / 64;
+  const int lane = lane_id();
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int wm = w % G::WAVES_M, wn = w / G::WAVES_M;
+  uint16_t* h = (uint16_t*)a.out;
+  const uint16_t* B[2] = {(const uint16_t*)a.b0, (const uint16_t*)a.b1};
+  G g;
+  for (int tile = (int)blockIdx.x; tile < mt * nt; tile += (int)gridDim.x) {
+    const int m0 = (tile % mt) * G::BM, n0 = (tile / mt) * 64;
+    g.init((const uint16_t*)a.a, (size_t)a.M, a.rowmap, m0, mv, B, n0, a.N, a.K);
+    g.run_pipe(lds, a.K);
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn) {
+      const int col = n0 + wn * G::WN + fn * 16 + (lane & 15);
+      const float bb = a.bias ? a.bias[col] : 0.f;
+#pragma unroll
+      for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * G::WM + fm * 16 + 4 * (lane >> 4) + r;
+          if (m < mv) {
+            const float z = g.acc[0][fm][fn][r] + bb;
+            h[(size_t)m * a.N + col] = f32_to_bf16(z > 0.f ? z * g.acc[1][fm][fn][r] : 0.f);
+          }
+        }
+    }
+  }
+}
+
+// Few routed rows: 128-row tiles with a deeper pipeline (few workgroups per CU
+// to hide memory latency with); many: the 256-row tiles of the full-size
+// kernel.
+constexpr int kRoutedBigRows = 1024;
+using RoutedSmall = Gemm2<2, 64, false, 32, 2, false, 128, SFFN_ROUTED_STAGES>;
+using RoutedBig = Gemm2<2, 64, false, 32, 2>;
+
+__global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
+  constexpr size_t kLds = RoutedSmall::LDS_BYTES > RoutedBig::LDS_BYTES ? RoutedSmall::LDS_BYTES
+                                                                        : RoutedBig::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  const int mv = uniform(rows_valid(a));  // scalar: the tile loop and buffer descriptors stay uniform
+  if (mv > kRoutedBigRows) gateup_routed_tiles<RoutedBig>(a, mv, lds);
+  else gateup_routed_tiles<RoutedSmall>(a, mv, lds);
+}
+
+// K splits of the routed down GEMM for mt x nt output tiles: enough work items
+// for the grid, at most kRoutedMaxSplit, at least 8 K steps per split.
+__host__ __device__ inline int routed_down_splits(int mt, int nt, int K) {
+  int s = kRoutedGrid / max(1, mt * nt);
+  s = min(s, kRoutedMaxSplit);
+  s = min(s, max(1, K / 256));
+  return max(s, 1);
+}
+
+// y rows of the routed list: with one split, written directly (rounded);
+// with S > 1, float32 partials [S][mt * 128][N] that down_routed_reduce sums.
+__global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partial) {
+  using G = Gemm2<1, 128, false, 32, 2, true, 128, SFFN_ROUTED_STAGES>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
+  const int mv = uniform(rows_valid(a));
+  const int mt = (mv + G::BM - 1) / G::BM, nt = (a.N + 127) / 128;
+  const int S = routed_down_splits(mt, nt, a.K);
+  const int nks = a.K / 32;
+  uint16_t* y = (uint16_t*)a.out;
+  for (int item = (int)blockIdx.x; item < mt * nt * S; item += (int)gridDim.x) {
+    const int mi = item % mt, rest = item / mt;
+    const int ni = rest % nt, si = rest / nt;
+    const int m0 = mi * G::BM, n0 = ni * 128;
+    const int k_lo = (int)(((long)si * nks) / S) * 32;
+    const int k_hi = (int)(((long)(si + 1) * nks) / S) * 32;
+    G g;
+    const uint16_t* B[1] = {(const uint16_t*)a.b0 + (size_t)k_lo * a.N};
+    g.init((const uint16_t*)a.a + k_lo, (size_t)a.M, nullptr, m0, mv, B, n0, a.N, k_hi - k_lo,
+           a.K, k_lo);
+    g.run_pipe(lds, k_hi - k_lo);
+    if (S == 1) {
+      g.for_each([&](int, int row, int col, float v) {
+        const int m = m0 + row, n = n0 + col;
+        if (m < mv && n < a.N) y[(size_t)a.rowmap[m] * a.N + n] = f32_to_bf16(v);
+      });
+    } else {
+      float* part = partial + ((size_t)si * mt * G::BM) * a.N;
+      g.for_each([&](int, int row, int col, float v) {
+        const int m = m0 + row, n = n0 + col;
+        if (m < mv && n < a.N) part[(size_t)m * a.N + n] = v;
+      });
+    }
+  }
+}
+
+// y[rowmap[m], n] = sum over splits of the partials, in split order.
+__global__ __launch_bounds__(256) void down_routed_reduce(DenseArgs a, const float* partial) {
+  const int mv = uniform(rows_valid(a));
+  const int mt = (mv + 127) / 128, nt = (a.N + 127) / 128;
+  const int S = routed_down_splits(mt, nt, a.K);
+  if (S == 1) return;
+  const size_t per = (size_t)mt * 128 * a.N;  // floats per split
+  const size_t n4 = (size_t)mv * a.N / 4;     // N % 8 == 0
+  uint16_t* y = (uint16_t*)a.out;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    f32x4_t v = *(const f32x4_t*)(partial + 4 * i);
+    for (int s = 1; s < S; ++s) v += *(const f32x4_t*)(partial + s * per + 4 * i);
+    const size_t e = 4 * i;
+    const int m = (int)(e / a.N), n = (int)(e - (size_t)m * a.N);
+    uint16_t* dst = y + (size_t)a.rowmap[m] * a.N + n;
+    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *(uint2*)dst = make_uint2(lo, hi);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dense_gateup(int dtype, const void* x, const void* wg_t, const float* b_g,
@@ -231,6 +359,38 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
   const dim3 grid((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
   if (dtype == 1) hipLaunchKernelGGL(down_bf16, grid, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(down_f32, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sffn
+
+namespace sffn {
+
+size_t routed_partial_bytes(int T, int N) {
+  // whenever S > 1 (see routed_down_splits): S * mt <= kRoutedGrid / nt, and
+  // S * mt <= kRoutedMaxSplit * ceil(T / 128)
+  const int nt = (N + 127) / 128;
+  const int tiles = min(kRoutedGrid / nt, kRoutedMaxSplit * ((T + 127) / 128));
+  return (size_t)tiles * 128 * (size_t)N * 4;
+}
+
+hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
+                             const void* wd, void* h, void* y, float* partial, int T,
+                             const int* routed, const int* n_routed, int d_model, int d_ff,
+                             hipStream_t stream) {
+  // h [rows, d_ff] = gate+up of the routed rows of x
+  DenseArgs g{x, wg_t, wu_t, b_g, h, routed, n_routed, T, d_model, d_ff};
+  const int tiles_max = ((T + 127) / 128) * (d_ff / 64);
+  hipLaunchKernelGGL(gateup_routed, dim3((unsigned)min(tiles_max, kRoutedGrid)), dim3(256), 0,
+                     stream, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // y rows = h wd
+  DenseArgs d{h, wd, nullptr, nullptr, y, routed, n_routed, T, d_ff, d_model};
+  hipLaunchKernelGGL(down_routed, dim3(kRoutedGrid), dim3(256), 0, stream, d, partial);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(down_routed_reduce, dim3(256), dim3(256), 0, stream, d, (const float*)partial);
   return hipGetLastError();
 }
 

@@ -114,21 +114,25 @@ struct Gemm2 {
 
   // A: [*, K] bf16 rows; rows m0 .. m0+255 (gathered through rowmap when
   // given); rows >= m_valid read as zero.  B[b]: [N, K] bf16; rows n0 ..
+  // K is the length of the K loop.  lda (0: K) is the row stride in elements
+  // of A and of a K-contiguous B; a_skip is the number of elements of each A
+  // row before A (a split of a longer K range starts inside the rows).
   __device__ __forceinline__ void init(const uint16_t* A, size_t a_rows_total, const int* rowmap,
                                        int m0, int m_valid, const uint16_t* const* B, int n0,
-                                       int N, int K) {
+                                       int N, int K, int lda = 0, int a_skip = 0) {
     const int lane = lane_id();
     const int w = uniform((int)(threadIdx.x >> 6));
-    const uint32_t ld = (uint32_t)K * 2u;
-    const uint16_t* abase = rowmap ? A : A + (size_t)m0 * K;
+    const int ldk = lda > 0 ? lda : K;
+    const uint32_t ld = (uint32_t)ldk * 2u;
+    const uint16_t* abase = rowmap ? A : A + (size_t)m0 * ldk;
     const size_t a_rows = rowmap ? a_rows_total : (size_t)min(m_valid - m0, BM);
-    ra = make_rsrc(abase, (uint32_t)(a_rows * ld));
+    ra = make_rsrc(abase, (uint32_t)(a_rows * ld - (size_t)a_skip * 2));
     if (B_KN) {
       b_ld = N * 2;
       rb[0] = make_rsrc(B[0] + n0, (uint32_t)((size_t)K * N * 2 - (size_t)n0 * 2));
     } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) rb[b] = make_rsrc(B[b] + (size_t)n0 * K, (uint32_t)(BNW * ld));
+      for (int b = 0; b < NB; ++b) rb[b] = make_rsrc(B[b] + (size_t)n0 * ldk, (uint32_t)(BNW * ld));
     }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -166,9 +170,36 @@ struct Gemm2 {
     (void)N;
   }
 
+  // Every load block of a wave comes from the same matrix (chosen once per
+  // wave, a uniform branch around whole loops: no per-load descriptor select).
+  static constexpr bool WAVE_ALIGNED =
+      !B_KN && (BM / RPB) % LOADS == 0 && (BNW / RPB) % LOADS == 0;
+
   __device__ __forceinline__ void issue(uint8_t* stage, int k0) {
     const int w = uniform((int)(threadIdx.x >> 6));
     const int soff = k0 * 2;
+    if constexpr (WAVE_ALIGNED) {
+      const int blk0 = w * LOADS;
+      lds_void_t* dst0 = (lds_void_t*)(stage + blk0 * 1024);
+      if (blk0 * RPB < BM) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)((uint8_t*)dst0 + i * 1024), 16,
+                                                   voff[i], soff, 0, 0);
+      } else if (NB == 1 || (blk0 * RPB - BM) < BNW) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void_t*)((uint8_t*)dst0 + i * 1024),
+                                                   16, voff[i], soff, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[NB - 1],
+                                                   (lds_void_t*)((uint8_t*)dst0 + i * 1024), 16,
+                                                   voff[i], soff, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int blk = w * LOADS + i;  // wave-uniform

@@ -41,6 +41,16 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
                        const int* rowmap, const int* n_rows_dev, int K, int N,
                        hipStream_t stream);
 
+// Dense FFN of the routed rows (hybrid fallback), row count on the device:
+// h [T, d_ff] (first n_routed rows used) and partial (routed_partial_bytes)
+// are workspace; y rows routed[m] are written.  bf16, d_model and d_ff
+// multiples of 32.
+size_t routed_partial_bytes(int T, int d_model);
+hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
+                             const void* wd, void* h, void* y, float* partial, int T,
+                             const int* routed, const int* n_routed, int d_model, int d_ff,
+                             hipStream_t stream);
+
 // Number of column splits of the fused sparse kernel for this shape.
 int sparse_splits(int T, int n_tiles, int d_model);
 size_t sparse_workspace_bytes(int dtype, int T, int n_tiles, int d_model, int cap);

@@ -3,11 +3,10 @@
 //
 // A row is routed when any of its TwELL tiles holds more active columns than
 // the capacity.  Two small kernels, no atomics, deterministic:
-//   route_flags    per row (lanes over the tiles): flag = OR_k (count[t, k] > cap);
-//                  per-256-row block counts
-//   route_compact  each block adds the counts of the blocks before it and
-//                  writes its flagged rows in ascending order; the last block
-//                  writes n_routed.
+//   route_flags    per row (lanes over the tiles): flag = OR_k (count[t, k] > cap)
+//   route_compact  each 256-row block counts the flags before it, then writes
+//                  its flagged rows in ascending order; the last block writes
+//                  n_routed.
 #include "common.cuh"
 #include "launch.h"
 
@@ -17,56 +16,43 @@ namespace {
 
 constexpr int kBlock = 256;
 
+constexpr int kFlagRows = 64;  // rows per workgroup of route_flags (16 per wave)
+
 __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict__ count, int T,
-                                                      int nt, int cap, int* __restrict__ flags,
-                                                      int* __restrict__ block_count) {
-  // wave w takes rows w, w + 4, ... of the block; for each row the lanes read
-  // the tiles' counts side by side (coalesced), sixteen rows' loads in flight
-  __shared__ int wave_n[kBlock / kWave];
+                                                      int nt, int cap, int* __restrict__ flags) {
+  // wave w takes rows w, w + 4, ... of the workgroup's 64; for each row the
+  // lanes read the tiles' counts side by side (coalesced), all sixteen rows'
+  // loads in flight together
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  const int b0 = blockIdx.x * kBlock;
-  constexpr int R = 16;
-  int n = 0;
-  for (int u0 = 0; u0 < kBlock / 4 && b0 + u0 * 4 < T; u0 += R) {
-    bool over[R];
+  constexpr int R = kFlagRows / 4;
+  bool over[R];
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int t = b0 + (u0 + u) * 4 + w;
-      over[u] = false;
-      if (t < T)
-        for (int k = lane; k < nt; k += kWave) over[u] |= (int)count[(size_t)t * nt + k] > cap;
-    }
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int t = b0 + (u0 + u) * 4 + w;
-      const int f = __ballot(over[u]) != 0ull;
-      if (t < T && lane == 0) flags[t] = f;
-      n += f;
-    }
+  for (int u = 0; u < R; ++u) {
+    const int t = blockIdx.x * kFlagRows + u * 4 + w;
+    over[u] = false;
+    if (t < T)
+      for (int k = lane; k < nt; k += kWave) over[u] |= (int)count[(size_t)t * nt + k] > cap;
   }
-  if (lane == 0) wave_n[w] = n;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int i = 0; i < kBlock / kWave; ++i) tot += wave_n[i];
-    block_count[blockIdx.x] = tot;
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    const int t = blockIdx.x * kFlagRows + u * 4 + w;
+    const int f = __ballot(over[u]) != 0ull;
+    if (t < T && lane == 0) flags[t] = f;
   }
 }
 
 __global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ flags, int T,
-                                                        const int* __restrict__ block_count,
                                                         int32_t* __restrict__ routed,
                                                         int32_t* __restrict__ n_routed) {
   __shared__ int wave_tot[kBlock / kWave];
   __shared__ int prefix_s;
   const int b = blockIdx.x;
-  // exclusive prefix over earlier blocks
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  // flagged rows before this block (every block counts them itself)
   int acc = 0;
-  for (int i = threadIdx.x; i < b; i += kBlock) acc += block_count[i];
-  // block reduction of acc
+  for (int i = threadIdx.x; i < b * kBlock; i += kBlock) acc += flags[i];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-  const int lane = lane_id(), w = threadIdx.x >> 6;
   if (lane == 0) wave_tot[w] = acc;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -97,22 +83,17 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
-size_t route_workspace_bytes(int T) {
-  const int nb = (T + kBlock - 1) / kBlock;
-  return align256((size_t)T * 4) + align256((size_t)nb * 4);
-}
+size_t route_workspace_bytes(int T) { return align256((size_t)T * 4); }
 
 hipError_t launch_route(const uint16_t* count, int T, int n_tiles, int cap, int32_t* routed,
                         int32_t* n_routed, void* ws, hipStream_t stream) {
-  const int nb = (T + kBlock - 1) / kBlock;
   int* flags = (int*)ws;
-  int* block_count = (int*)((char*)ws + align256((size_t)T * 4));
-  hipLaunchKernelGGL(route_flags, dim3(nb), dim3(kBlock), 0, stream, count, T, n_tiles, cap, flags,
-                     block_count);
+  hipLaunchKernelGGL(route_flags, dim3((unsigned)((T + kFlagRows - 1) / kFlagRows)), dim3(kBlock),
+                     0, stream, count, T, n_tiles, cap, flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_compact, dim3(nb), dim3(kBlock), 0, stream, flags, T, block_count,
-                     routed, n_routed);
+  hipLaunchKernelGGL(route_compact, dim3((unsigned)((T + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                     stream, flags, T, routed, n_routed);
   return hipGetLastError();
 }
 

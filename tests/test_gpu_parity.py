@@ -188,6 +188,12 @@ def test_positive_bias_routes_every_row():
     assert e["n_routed"] == 40
 
 
+def test_many_routed_rows_use_the_large_tile_fallback():
+    inp = _small(-50.0, T=1200)
+    e = compare(inp, 8)
+    assert e["n_routed"] == 1200
+
+
 def test_zero_tokens_is_a_noop():
     sffn = _sffn()
     s = sffn.make_shape(0, 256, 512, 8, sffn.SFFN_BF16)
