@@ -219,6 +219,9 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 #define SFFN_GATE_BK 32
 #endif
 using GateGemm = Gemm2<1, kTile, false, SFFN_GATE_BK, 1, false, SFFN_GATE_BM, SFFN_GATE_STAGES>;
+#ifndef SFFN_EPI_EXACT_U
+#define SFFN_EPI_EXACT_U 4  // exact re-evaluation: 16-byte chunks per lane loaded together
+#endif
 
 struct AccEpi {
   int m0, n0, nt, kt, wm, lane, gi, li;
@@ -259,7 +262,7 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, const 
         const int lrow = c.wm * GateGemm::WM + FM * 16 + 4 * (L >> 4) + R;
         const int lcol = fn * 16 + (L & 15);
         const float bl = a.b ? a.b[c.n0 + lcol] : 0.f;
-        const ExactResult e = exact_gate_value<uint16_t>(
+        const ExactResult e = exact_gate_value<uint16_t, SFFN_EPI_EXACT_U>(
             (const uint16_t*)a.x + (size_t)(c.m0 + lrow) * a.K,
             (const uint16_t*)a.wg + (size_t)(c.n0 + lcol) * a.K, bl, a.K, c.exact_lds);
         if (c.lane == L) {
