@@ -34,7 +34,10 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
 }
 
 size_t dense_ws(const sffn_shape* s) {
-  return align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
+  size_t n = align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
+  if (dense_skinny_ok(s->dtype, s->T, s->d_model, s->d_ff))
+    n += align256(dense_skinny_partial_bytes(s->d_model, s->d_ff));
+  return n;
 }
 
 size_t pack_ws(const sffn_shape* s) {
@@ -165,6 +168,10 @@ int32_t dense_ffn_ref(const sffn_shape* shape, const void* x, const void* wg_t, 
   if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int T = shape->T, K = shape->d_model, N = shape->d_ff;
+  if (dense_skinny_ok(shape->dtype, T, K, N)) {
+    float* partial = (float*)((char*)workspace + align256((size_t)T * N * elt_bytes(shape->dtype)));
+    return hip_status(launch_dense_skinny(x, wg_t, b_g, wu_t, wd, workspace, partial, y, T, K, N, s));
+  }
   hipError_t e = launch_dense_gateup(shape->dtype, x, wg_t, b_g, wu_t, workspace, T, nullptr,
                                      nullptr, K, N, s);
   if (e != hipSuccess) return SFFN_ERR_HIP;

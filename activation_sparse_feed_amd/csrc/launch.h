@@ -51,6 +51,15 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
                              const int* routed, const int* n_routed, int d_model, int d_ff,
                              hipStream_t stream);
 
+// Dense gated FFN for few tokens (split-K weight streams): bf16, M <= 32,
+// d_model and d_ff multiples of 128.  h [M, d_ff] and partial
+// (dense_skinny_partial_bytes) are workspace.
+bool dense_skinny_ok(int dtype, int M, int d_model, int d_ff);
+size_t dense_skinny_partial_bytes(int d_model, int d_ff);
+hipError_t launch_dense_skinny(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
+                               const void* wd, void* h, float* partial, void* y, int M,
+                               int d_model, int d_ff, hipStream_t stream);
+
 // Number of column splits of the fused sparse kernel for this shape.
 int sparse_splits(int T, int n_tiles, int d_model);
 size_t sparse_workspace_bytes(int dtype, int T, int n_tiles, int d_model, int cap);

@@ -141,6 +141,21 @@ def test_dense_reference(name, T):
     check_y(w.dtype, y, ref["y_dense"], np.zeros(w.T, dtype=bool))
 
 
+@pytest.mark.parametrize("T,K,N", [(1, 256, 512), (7, 384, 1280), (32, 1024, 4096)])
+def test_dense_reference_few_tokens(T, K, N):
+    """Split-K dense kernels (few tokens), ragged row fragments included."""
+    sffn = _sffn()
+    inp = wl.generate_custom(T=T, d_model=K, d_ff=N, dtype="bf16", beta=1.0, seed_base=51)
+    d = device_inputs(inp)
+    dense = sffn.DenseFFN(T, K, N, torch.bfloat16)
+    y1 = dense.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"]).clone()
+    y2 = dense.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ref = oracle_rows(inp, np.arange(T), 128, 8)
+    check_y("bf16", to_f64(y1), ref["y_dense"], np.zeros(T, dtype=bool))
+
+
 # ------------------------------------------------------- few-token kernels
 @pytest.mark.parametrize("T,K,N,beta,cap", [
     (48, 1056, 1024, 1.6, 8),   # split-K gate with 4 row fragments, K tail in a 512-column chunk
