@@ -74,9 +74,9 @@ __device__ __forceinline__ void tile_of(int bid, int mt, int nt, int* m, int* n)
 // the gfx950 transposing LDS read, which hands each lane four consecutive k of
 // one column per 8-byte read.
 template <int NB, int BNW, bool NORMS, int BK_ = 32, int WAVES_N = 2, bool B_KN = false,
-          int BM_ = 256, int STAGES_ = 3>
+          int BM_ = 256, int STAGES_ = 3, int NWAVES_ = 4>
 struct Gemm2 {
-  static constexpr int BM = BM_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BK = BK_, STAGES = STAGES_, NWAVES = NWAVES_;
   static constexpr int BN = NB * BNW;
   static constexpr int ROWB = BK * 2;                  // bytes per LDS row
   static constexpr int CPR = BK / 8;                   // 16-byte chunks per row
@@ -84,19 +84,20 @@ struct Gemm2 {
   static constexpr int STAGE_BYTES = ROWS * ROWB;
   static constexpr int RPB = 64 / CPR;                 // rows per 1 KB load block
   static constexpr int BLOCKS = ROWS / RPB;            // 1 KB load blocks per stage
-  static constexpr int LOADS = BLOCKS / 4;             // load instructions per wave per stage
+  static constexpr int LOADS = BLOCKS / NWAVES;        // load instructions per wave per stage
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(!NORMS || WAVES_N == 2, "norm split assumes 2 x 2 waves");
   static_assert(!B_KN || (NB == 1 && BNW == 128 && BK == 32 && !NORMS), "K-major B layout");
   static constexpr int KN_ROWB = BNW * 2;   // bytes per staged k row of a [K, N] B
   static __device__ __forceinline__ int kn_slot(int k, int q) { return q ^ (2 * (k & 7)); }
-  static constexpr int WAVES_M = 4 / WAVES_N;
+  static constexpr int WAVES_M = NWAVES / WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BNW / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
   static_assert(BN == 128, "workgroup N tile");
   static_assert(BM == 256 || BM == 128, "workgroup M tile");
-  static_assert(BLOCKS % 4 == 0, "load blocks per wave");
+  static_assert(BLOCKS % NWAVES == 0, "load blocks per wave");
+  static_assert(!NORMS || NWAVES == 4, "norm split assumes 4 waves");
 
   // Physical 16-byte slot of logical chunk q in row r: 8 consecutive rows
   // read at one logical chunk land in 8 distinct 16-byte bank groups.

@@ -194,11 +194,13 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
                        (int*)(rn_b + 128), (uint32_t*)((uint8_t*)lds + 36864));
 }
 
-// bf16, d_model % 32 == 0: 256 x 128 tiles on the buffer-load main loop, TwELL
-// built straight from the MFMA accumulators.
+// bf16, d_model % 32 == 0: 256 x 128 tiles on the buffer-load main loop (eight
+// waves, two per SIMD, one workgroup per CU: one A tile of 256 rows feeds the
+// whole TwELL tile, a quarter less L2-to-LDS traffic than two 128-row
+// workgroups), TwELL built straight from the MFMA accumulators.
 //
-// The four waves each hold 64 rows x all 128 columns of the tile: rows
-// 64 wm + 16 fm + 4 g + r and columns 16 fn + i, for lane 16 g + i and
+// Each wave holds WM rows x all 128 columns of the tile: rows
+// WM wm + 16 fm + 4 g + r and columns 16 fn + i, for lane 16 g + i and
 // accumulator (fm, fn, r).  For a fixed (fm, r), one ballot per fn gives, in
 // its 16-bit segment g, the activity of columns 16 fn .. 16 fn + 15 of row
 // 16 fm + 4 g + r.  A column's slot is the number of active columns before it
@@ -210,15 +212,19 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 // (largest column norm and bias of the tile); only entries inside it get the
 // per-entry band, and only those inside that are re-evaluated exactly.
 #ifndef SFFN_GATE_BM
-#define SFFN_GATE_BM 128
+#define SFFN_GATE_BM 256
 #endif
 #ifndef SFFN_GATE_STAGES
-#define SFFN_GATE_STAGES 5
+#define SFFN_GATE_STAGES 4
 #endif
 #ifndef SFFN_GATE_BK
 #define SFFN_GATE_BK 32
 #endif
-using GateGemm = Gemm2<1, kTile, false, SFFN_GATE_BK, 1, false, SFFN_GATE_BM, SFFN_GATE_STAGES>;
+#ifndef SFFN_GATE_WAVES
+#define SFFN_GATE_WAVES 8
+#endif
+using GateGemm = Gemm2<1, kTile, false, SFFN_GATE_BK, 1, false, SFFN_GATE_BM, SFFN_GATE_STAGES,
+                       SFFN_GATE_WAVES>;
 #ifndef SFFN_EPI_EXACT_U
 #define SFFN_EPI_EXACT_U 4  // exact re-evaluation: 16-byte chunks per lane loaded together
 #endif
@@ -298,9 +304,9 @@ struct EpiLoop {
 };
 
 #ifndef SFFN_GATE_OCC
-#define SFFN_GATE_OCC 2
+#define SFFN_GATE_OCC 1
 #endif
-__global__ __launch_bounds__(256, SFFN_GATE_OCC) void gate_twell_bf16_v2(GateArgs a) {
+__global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twell_bf16_v2(GateArgs a) {
   using G = GateGemm;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   const int nt = a.N / kTile;
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(256, SFFN_GATE_OCC) void gate_twell_bf16_v2(GateArg
 
   float* rn_a = (float*)lds;  // [BM]
   float* rn_b = rn_a + 256;   // [128]
-  static_assert(G::LDS_BYTES >= 2048 + 4 * kExactLdsWords * 4, "epilogue LDS fits");
+  static_assert(G::LDS_BYTES >= 2048 + G::NWAVES * kExactLdsWords * 4, "epilogue LDS fits");
   load_tile_norms(a, c.m0, G::BM, c.n0, rn_a, rn_b);
   __syncthreads();
   c.rn_a = rn_a;
@@ -629,7 +635,7 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
     }
   } else if (dtype == 1 && K % GateGemm::BK == 0) {
     const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) * nt));
-    hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(64 * GateGemm::NWAVES), 0, stream, a);
   } else if (dtype == 1) {
     hipLaunchKernelGGL(gate_twell_bf16, dim3((unsigned)(((T + 127) / 128) * nt)), dim3(256), 0,
                        stream, a);
