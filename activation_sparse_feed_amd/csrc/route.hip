@@ -3,10 +3,12 @@
 //
 // A row is routed when any of its TwELL tiles holds more active columns than
 // the capacity.  Two small kernels, no atomics, deterministic:
-//   route_flags    per row (lanes over the tiles): flag = OR_k (count[t, k] > cap)
-//   route_compact  each 256-row block counts the flags before it, then writes
-//                  its flagged rows in ascending order; the last block writes
-//                  n_routed.
+//   route_flags    per row (lanes over the tiles): flag = OR_k (count[t, k] > cap),
+//                  and the number of flagged rows of each 64-row group
+//   route_compact  each 256-row block adds the group counts before it, then
+//                  writes its flagged rows in ascending order; the last block
+//                  writes n_routed.
+// With at most 256 rows, one workgroup does both (route_small).
 #include "common.cuh"
 #include "launch.h"
 
@@ -19,7 +21,8 @@ constexpr int kBlock = 256;
 constexpr int kFlagRows = 64;  // rows per workgroup of route_flags (16 per wave)
 
 __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict__ count, int T,
-                                                      int nt, int cap, int* __restrict__ flags) {
+                                                      int nt, int cap, int* __restrict__ flags,
+                                                      int* __restrict__ group_count) {
   // wave w takes rows w, w + 4, ... of the workgroup's 64; for each row the
   // lanes read the tiles' counts side by side (coalesced), all sixteen rows'
   // loads in flight together
@@ -33,24 +36,32 @@ __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict
     if (t < T)
       for (int k = lane; k < nt; k += kWave) over[u] |= (int)count[(size_t)t * nt + k] > cap;
   }
+  __shared__ int wave_n[kBlock / kWave];
+  int n = 0;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const int t = blockIdx.x * kFlagRows + u * 4 + w;
     const int f = __ballot(over[u]) != 0ull;
     if (t < T && lane == 0) flags[t] = f;
+    n += f;
   }
+  if (lane == 0) wave_n[w] = n;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    group_count[blockIdx.x] = (wave_n[0] + wave_n[1]) + (wave_n[2] + wave_n[3]);
 }
 
 __global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ flags, int T,
+                                                        const int* __restrict__ group_count,
                                                         int32_t* __restrict__ routed,
                                                         int32_t* __restrict__ n_routed) {
   __shared__ int wave_tot[kBlock / kWave];
   __shared__ int prefix_s;
   const int b = blockIdx.x;
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  // flagged rows before this block (every block counts them itself)
+  // flagged rows before this block: the counts of the 64-row groups before it
   int acc = 0;
-  for (int i = threadIdx.x; i < b * kBlock; i += kBlock) acc += flags[i];
+  for (int i = threadIdx.x; i < b * (kBlock / kFlagRows); i += kBlock) acc += group_count[i];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
   if (lane == 0) wave_tot[w] = acc;
@@ -79,21 +90,71 @@ __global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ 
   }
 }
 
+// T <= 256: one workgroup does both steps (one launch instead of two).
+__global__ __launch_bounds__(kBlock) void route_small(const uint16_t* __restrict__ count, int T,
+                                                      int nt, int cap, int32_t* __restrict__ routed,
+                                                      int32_t* __restrict__ n_routed) {
+  __shared__ int flag_s[kBlock];
+  __shared__ int wave_tot[kBlock / kWave];
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  constexpr int R = 16;
+  for (int u0 = 0; u0 < kBlock / 4 && u0 * 4 < T; u0 += R) {
+    bool over[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int t = (u0 + u) * 4 + w;
+      over[u] = false;
+      if (t < T)
+        for (int k = lane; k < nt; k += kWave) over[u] |= (int)count[(size_t)t * nt + k] > cap;
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int t = (u0 + u) * 4 + w;
+      const int f = __ballot(over[u]) != 0ull;
+      if (t < T && lane == 0) flag_s[t] = f;
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int f = t < T ? flag_s[t] : 0;
+  const uint64_t m = __ballot(f);
+  if (lane == 0) wave_tot[w] = __popcll(m);
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += wave_tot[i];
+  if (f) routed[off + lanes_below(m)] = t;
+  if (threadIdx.x == kBlock - 1) {
+    int tot = off;
+    for (int i = w; i < kBlock / kWave; ++i) tot += wave_tot[i];
+    *n_routed = tot;
+  }
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
-size_t route_workspace_bytes(int T) { return align256((size_t)T * 4); }
+size_t route_workspace_bytes(int T) {
+  const int groups = (T + kFlagRows - 1) / kFlagRows;
+  return align256((size_t)T * 4) + align256((size_t)groups * 4);
+}
 
 hipError_t launch_route(const uint16_t* count, int T, int n_tiles, int cap, int32_t* routed,
                         int32_t* n_routed, void* ws, hipStream_t stream) {
+  if (T <= kBlock) {
+    hipLaunchKernelGGL(route_small, dim3(1), dim3(kBlock), 0, stream, count, T, n_tiles, cap,
+                       routed, n_routed);
+    return hipGetLastError();
+  }
+  const int groups = (T + kFlagRows - 1) / kFlagRows;
   int* flags = (int*)ws;
-  hipLaunchKernelGGL(route_flags, dim3((unsigned)((T + kFlagRows - 1) / kFlagRows)), dim3(kBlock),
-                     0, stream, count, T, n_tiles, cap, flags);
+  int* group_count = (int*)((char*)ws + align256((size_t)T * 4));
+  hipLaunchKernelGGL(route_flags, dim3((unsigned)groups), dim3(kBlock), 0, stream, count, T,
+                     n_tiles, cap, flags, group_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_compact, dim3((unsigned)((T + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                     stream, flags, T, routed, n_routed);
+                     stream, flags, T, group_count, routed, n_routed);
   return hipGetLastError();
 }
 
