@@ -192,7 +192,8 @@ constexpr int kDnFrags = kSkMF * kDnFN;
 constexpr int kDnPart = kDnFrags * 256;
 constexpr int kDnRowB = 256;                   // bytes per staged k row (128 columns)
 constexpr int kDnStepB = 32 * kDnRowB;         // 8 KB per K step
-__device__ __forceinline__ int dn_slot(int k, int q) { return q ^ (2 * (k & 7)); }
+// chunk swizzle of a staged row: no bank conflicts for the transposing reads
+__device__ __forceinline__ int dn_slot(int k, int q) { return q ^ (2 * ((k & 3) | ((k >> 1) & 4))); }
 
 __global__ __launch_bounds__(256) void skinny_down_partial(SkArgs a) {
   constexpr int MF = kSkMF, FN = kDnFN;

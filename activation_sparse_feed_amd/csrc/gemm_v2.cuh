@@ -70,7 +70,7 @@ __device__ __forceinline__ void tile_of(int bid, int mt, int nt, int* m, int* n)
 // in one wave).
 // B_KN: the single B matrix is [K, N] (N-contiguous, e.g. the down projection
 // weight).  Its K step is staged as BK rows of BNW columns (256 bytes), with
-// 16-byte chunks XOR-swizzled by 2 * (k & 7); MFMA B fragments are read with
+// 16-byte chunks XOR-swizzled by row (kn_slot); MFMA B fragments are read with
 // the gfx950 transposing LDS read, which hands each lane four consecutive k of
 // one column per 8-byte read.
 template <int NB, int BNW, bool NORMS, int BK_ = 32, int WAVES_N = 2, bool B_KN = false,
@@ -89,7 +89,12 @@ struct Gemm2 {
   static_assert(!NORMS || WAVES_N == 2, "norm split assumes 2 x 2 waves");
   static_assert(!B_KN || (NB == 1 && BNW == 128 && BK == 32 && !NORMS), "K-major B layout");
   static constexpr int KN_ROWB = BNW * 2;   // bytes per staged k row of a [K, N] B
-  static __device__ __forceinline__ int kn_slot(int k, int q) { return q ^ (2 * (k & 7)); }
+  // 16-byte chunk q of staged k row k sits at chunk q ^ 2 c(k), c(k) = bits 0, 1 and 3 of k:
+  // the rows one transposing read touches at a time (k = 8 g + 0..3, g = 0, 1,
+  // or those + 4) land in 16 distinct chunks, so no two lanes share a bank.
+  static __device__ __forceinline__ int kn_slot(int k, int q) {
+    return q ^ (2 * ((k & 3) | ((k >> 1) & 4)));
+  }
   static constexpr int WAVES_M = NWAVES / WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BNW / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
