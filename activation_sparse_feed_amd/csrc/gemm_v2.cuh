@@ -1,15 +1,16 @@
 // Second-generation bf16 GEMM main loop for gfx950 (K-contiguous A and B).
 //
-//   workgroup tile 256 (M) x 128 (N = NB * BNW), 4 waves as 2 x 2, each wave
-//   128 x (NB x BNW/2); v_mfma_f32_16x16x32_bf16, float32 accumulators.
-//   K step 64, three LDS stages of 48 KB filled by buffer loads straight into
-//   LDS (16 bytes per lane, no VGPR staging).  Each 128-byte LDS row holds its
-//   eight 16-byte chunks XOR-swizzled by (row & 7): a load instruction writes
-//   64 consecutive chunks, so lane l fetches global chunk (l & 7) ^ (l >> 3) of
-//   its row; fragment reads of 8 consecutive rows then hit 8 distinct bank
-//   groups.  Rows past the valid range read as zero through the buffer range
-//   check.  One barrier per K step: stage kt is consumed while stages kt+1 and
-//   kt+2 are in flight.
+//   workgroup tile BM (128 or 256) x BN (NB B matrices of BNW columns; 128, or
+//   256 for one B), NWAVES waves as WAVES_M x WAVES_N, each wave WM x WN per B
+//   matrix; v_mfma_f32_16x16x32_bf16, float32 accumulators.
+//   K step BK (32 or 64), STAGES LDS stages filled by buffer loads straight into
+//   LDS (16 bytes per lane, no VGPR staging).  Each LDS row of BK bf16 holds its
+//   16-byte chunks XOR-swizzled by row (slot): a load instruction writes 64
+//   consecutive chunks, so lane l fetches the global chunk that lands in its
+//   slot; fragment reads of consecutive rows then hit distinct bank groups.
+//   Rows past the valid range read as zero through the buffer range check.
+//   One barrier per K step: stage kt is consumed while the later stages are in
+//   flight.
 //
 // NORMS: the waves also accumulate sum of squares of the A rows (waves with
 // wn == 0) and B rows (waves with wm == 0) from the bf16 fragments they feed to
@@ -95,11 +96,11 @@ struct Gemm2 {
   static __device__ __forceinline__ int kn_slot(int k, int q) {
     return q ^ (2 * ((k & 3) | ((k >> 1) & 4)));
   }
-  static constexpr int WAVES_M = NWAVES / WAVES_N;
+  static constexpr int WAVES_M = NWAVES / WAVES_N, WAVE_COLS = WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BNW / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
-  static_assert(BN == 128, "workgroup N tile");
+  static_assert(BN == 128 || (BN == 256 && NB == 1 && !B_KN), "workgroup N tile");
   static_assert(BM == 256 || BM == 128, "workgroup M tile");
   static_assert(BLOCKS % NWAVES == 0, "load blocks per wave");
   static_assert(!NORMS || NWAVES == 4, "norm split assumes 4 waves");
@@ -117,6 +118,7 @@ struct Gemm2 {
   __amdgpu_buffer_rsrc_t ra;
   __amdgpu_buffer_rsrc_t rb[NB];
   int b_ld;  // B_KN: bytes per row of B
+  __amdgpu_buffer_rsrc_t rw;  // WAVE_ALIGNED: the matrix this wave's load blocks come from
 
   // A: [*, K] bf16 rows; rows m0 .. m0+255 (gathered through rowmap when
   // given); rows >= m_valid read as zero.  B[b]: [N, K] bf16; rows n0 ..
@@ -138,7 +140,11 @@ struct Gemm2 {
       rb[0] = make_rsrc(B[0] + n0, (uint32_t)((size_t)K * N * 2 - (size_t)n0 * 2));
     } else {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) rb[b] = make_rsrc(B[b] + (size_t)n0 * ldk, (uint32_t)(BNW * ld));
+      for (int b = 0; b < NB; ++b) {
+        // a 256-wide tile may hang over the end of B by 128 rows: those read as zero
+        const int rows = BNW > 128 ? min(BNW, N - n0) : BNW;
+        rb[b] = make_rsrc(B[b] + (size_t)n0 * ldk, (uint32_t)(rows * ld));
+      }
     }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -161,6 +167,10 @@ struct Gemm2 {
         voff[i] = (uint32_t)kk * (uint32_t)b_ld + (uint32_t)qq * 16u;
       }
     }
+    if constexpr (WAVE_ALIGNED) {
+      const int blk0 = w * LOADS;
+      rw = blk0 * RPB < BM ? ra : ((NB == 1 || (blk0 * RPB - BM) < BNW) ? rb[0] : rb[NB - 1]);
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -173,7 +183,6 @@ struct Gemm2 {
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) sqb[b][fn] = 0.f;
-    (void)N;
   }
 
   // Every load block of a wave comes from the same matrix (chosen once per
@@ -185,25 +194,13 @@ struct Gemm2 {
     const int w = uniform((int)(threadIdx.x >> 6));
     const int soff = k0 * 2;
     if constexpr (WAVE_ALIGNED) {
-      const int blk0 = w * LOADS;
-      lds_void_t* dst0 = (lds_void_t*)(stage + blk0 * 1024);
-      if (blk0 * RPB < BM) {
+      // the wave's descriptor was chosen once in init: no branch here, so the
+      // loads can be scheduled among the MFMAs of the step
+      lds_void_t* dst0 = (lds_void_t*)(stage + w * LOADS * 1024);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)((uint8_t*)dst0 + i * 1024), 16,
-                                                   voff[i], soff, 0, 0);
-      } else if (NB == 1 || (blk0 * RPB - BM) < BNW) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[0], (lds_void_t*)((uint8_t*)dst0 + i * 1024),
-                                                   16, voff[i], soff, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[NB - 1],
-                                                   (lds_void_t*)((uint8_t*)dst0 + i * 1024), 16,
-                                                   voff[i], soff, 0, 0);
-      }
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)((uint8_t*)dst0 + i * 1024), 16,
+                                                 voff[i], soff, 0, 0);
       return;
     }
 #pragma unroll

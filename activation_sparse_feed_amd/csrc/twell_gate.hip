@@ -194,23 +194,32 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
                        (int*)(rn_b + 128), (uint32_t*)((uint8_t*)lds + 36864));
 }
 
-// bf16, d_model % 32 == 0: 256 x 128 tiles on the buffer-load main loop (eight
-// waves, two per SIMD, one workgroup per CU: one A tile of 256 rows feeds the
+// bf16, d_model % 32 == 0: 256-row tiles on the buffer-load main loop, TwELL
+// built straight from the MFMA accumulators.  Default: 256 x 128 tiles, eight
+// waves, two per SIMD, one workgroup per CU (one A tile of 256 rows feeds the
 // whole TwELL tile, a quarter less L2-to-LDS traffic than two 128-row
-// workgroups), TwELL built straight from the MFMA accumulators.
+// workgroups); each wave holds 32 rows x the 128 columns of the TwELL tile.
+// The same code also builds 256 x 256 tiles of four waves as 2 x 2, each
+// holding 128 rows x one TwELL tile (SFFN_GATE_BN=256 SFFN_GATE_WN=2
+// SFFN_GATE_WAVES=4): fewer LDS reads per MFMA, but with one wave per SIMD the
+// buffer loads stall the MFMA stream, so it is slower at 4096 tokens and
+// about even at 16384.
 //
-// Each wave holds WM rows x all 128 columns of the tile: rows
-// WM wm + 16 fm + 4 g + r and columns 16 fn + i, for lane 16 g + i and
-// accumulator (fm, fn, r).  For a fixed (fm, r), one ballot per fn gives, in
-// its 16-bit segment g, the activity of columns 16 fn .. 16 fn + 15 of row
+// A wave holds rows WM wm + 16 fm + 4 g + r and columns WN wn + 16 fn + i of
+// the workgroup tile, for lane 16 g + i and accumulator (fm, fn, r).  For a
+// fixed (fm, r), one ballot per fn gives, in its 16-bit segment g, the
+// activity of columns 16 fn .. 16 fn + 15 of the wave's TwELL tile in row
 // 16 fm + 4 g + r.  A column's slot is the number of active columns before it
 // in its row: the popcounts of the row's segments of lower fn plus the active
 // lanes below it in its own segment; the row's count is the sum over fn.  All
 // of it stays inside the wave.
 //
 // Guard band: each entry is first tested against a bound for its whole row
-// (largest column norm and bias of the tile); only entries inside it get the
-// per-entry band, and only those inside that are re-evaluated exactly.
+// (largest column norm and bias of the wave's tile); only entries inside it
+// get the per-entry band, and only those inside that are re-evaluated exactly.
+#ifndef SFFN_GATE_BN
+#define SFFN_GATE_BN 128
+#endif
 #ifndef SFFN_GATE_BM
 #define SFFN_GATE_BM 256
 #endif
@@ -223,23 +232,30 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 #ifndef SFFN_GATE_WAVES
 #define SFFN_GATE_WAVES 8
 #endif
-using GateGemm = Gemm2<1, kTile, false, SFFN_GATE_BK, 1, false, SFFN_GATE_BM, SFFN_GATE_STAGES,
-                       SFFN_GATE_WAVES>;
+#ifndef SFFN_GATE_WN
+#define SFFN_GATE_WN 1
+#endif
+#ifndef SFFN_GATE_OCC
+#define SFFN_GATE_OCC 1
+#endif
+using GateGemm = Gemm2<1, SFFN_GATE_BN, false, SFFN_GATE_BK, SFFN_GATE_WN, false, SFFN_GATE_BM,
+                       SFFN_GATE_STAGES, SFFN_GATE_WAVES>;
+static_assert(GateGemm::WN == kTile, "each wave holds one TwELL column tile");
 #ifndef SFFN_EPI_EXACT_U
 #define SFFN_EPI_EXACT_U 4  // exact re-evaluation: 16-byte chunks per lane loaded together
 #endif
 
 struct AccEpi {
-  int m0, n0, nt, kt, wm, lane, gi, li;
+  int m0, n0, nt, kt, wm, lane, gi, li;  // n0: first column of the wave's TwELL tile
   float cw, cb;
   float bias[GateGemm::FN], nw[GateGemm::FN];
   const float* rn_a;
   uint32_t* exact_lds;  // this wave's exact-stage area
 };
 
-// One accumulator row group (fm, r): 4 rows of the wave, all 128 columns.
-// Template indices keep every accumulator access static (no spill of the
-// accumulator array to scratch).
+// One accumulator row group (fm, r): 4 rows of the wave, all 128 columns of
+// its TwELL tile.  Template indices keep every accumulator access static (no
+// spill of the accumulator array to scratch).
 template <int FM, int R>
 __device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, const AccEpi& c) {
   constexpr int FN = GateGemm::FN;
@@ -303,34 +319,41 @@ struct EpiLoop {
   }
 };
 
-#ifndef SFFN_GATE_OCC
-#define SFFN_GATE_OCC 1
-#endif
 __global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twell_bf16_v2(GateArgs a) {
   using G = GateGemm;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   const int nt = a.N / kTile;
   int mi, ni;
-  tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, nt, &mi, &ni);
-  AccEpi c;
-  c.m0 = mi * G::BM;
-  c.n0 = ni * kTile;
-  c.nt = nt;
-  c.kt = ni;
+  tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, (a.N + G::BN - 1) / G::BN, &mi, &ni);
+  const int m0 = mi * G::BM, n0 = ni * G::BN;
   G g;
   const uint16_t* B[1] = {(const uint16_t*)a.wg};
-  g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, c.m0, a.T, B, c.n0, a.N, a.K);
+  g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, m0, a.T, B, n0, a.N, a.K);
   g.run_pipe(lds, a.K);
 
-  float* rn_a = (float*)lds;  // [BM]
-  float* rn_b = rn_a + 256;   // [128]
-  static_assert(G::LDS_BYTES >= 2048 + G::NWAVES * kExactLdsWords * 4, "epilogue LDS fits");
-  load_tile_norms(a, c.m0, G::BM, c.n0, rn_a, rn_b);
+  // epilogue LDS (the pipeline stages are free after run_pipe's barrier):
+  // row norms, column norms, one exact-stage area per wave
+  float* rn_a = (float*)lds;     // [BM]
+  float* rn_b = rn_a + G::BM;    // [BN]
+  constexpr int kExactOff = (G::BM + G::BN) * 4;
+  static_assert(G::LDS_BYTES >= kExactOff + G::NWAVES * kExactLdsWords * 4, "epilogue LDS fits");
+  for (int i = threadIdx.x; i < G::BM; i += blockDim.x)
+    rn_a[i] = (m0 + i < a.T) ? a.xnorm[m0 + i] : 0.f;
+  for (int i = threadIdx.x; i < G::BN; i += blockDim.x)
+    rn_b[i] = (n0 + i < a.N) ? a.wnorm[n0 + i] : 0.f;
   __syncthreads();
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int wn = w / G::WAVES_M;
+  AccEpi c;
+  c.m0 = m0;
+  c.n0 = n0 + wn * G::WN;
+  if (c.n0 >= a.N) return;  // the half of a 256-wide tile past the last column
+  c.nt = nt;
+  c.kt = c.n0 / kTile;
   c.rn_a = rn_a;
   c.lane = lane_id();
-  c.wm = uniform((int)(threadIdx.x >> 6));
-  c.exact_lds = (uint32_t*)(lds + 2048) + c.wm * kExactLdsWords;
+  c.wm = w % G::WAVES_M;
+  c.exact_lds = (uint32_t*)(lds + kExactOff) + w * kExactLdsWords;
   c.gi = c.lane >> 4;
   c.li = c.lane & 15;
   c.cw = 0.f;
@@ -339,7 +362,7 @@ __global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twel
   for (int fn = 0; fn < G::FN; ++fn) {
     const int col = fn * 16 + c.li;
     c.bias[fn] = a.b ? a.b[c.n0 + col] : 0.f;
-    c.nw[fn] = rn_b[col];
+    c.nw[fn] = rn_b[wn * G::WN + col];
     c.cw = fmaxf(c.cw, a.gb.coef_xw * c.nw[fn]);
     c.cb = fmaxf(c.cb, a.gb.coef_b * fabsf(c.bias[fn]));
   }
@@ -634,7 +657,8 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
       hipLaunchKernelGGL(gate_skinny_epilogue<4>, dim3((unsigned)(nt * 4)), dim3(256), 0, stream, a, partial, S);
     }
   } else if (dtype == 1 && K % GateGemm::BK == 0) {
-    const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) * nt));
+    const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
+                             ((N + GateGemm::BN - 1) / GateGemm::BN)));
     hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(64 * GateGemm::NWAVES), 0, stream, a);
   } else if (dtype == 1) {
     hipLaunchKernelGGL(gate_twell_bf16, dim3((unsigned)(((T + 127) / 128) * nt)), dim3(256), 0,
