@@ -105,10 +105,11 @@ __device__ __forceinline__ void emit_row(const GateArgs& a, const RowCtx& c, int
   if (lane == 0) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)(c0 + __popcll(m1m));
 }
 
+// bias_lds (optional): the tile's 128 bias values already staged in LDS.
 template <typename T, typename ZT, int EXACT_U = 2>
 __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, float band_scale,
                            const float* rn_a, const float* rn_b, int r0, int m0, int n0,
-                           int* defer, uint32_t* exact_lds) {
+                           int* defer, uint32_t* exact_lds, const float* bias_lds = nullptr) {
   const int lane = lane_id();
   const int w = uniform((int)(threadIdx.x >> 6));
   RowCtx c;
@@ -117,8 +118,13 @@ __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, 
   c.m0 = m0;
   c.n0 = n0;
   c.r0 = r0;
-  c.b0 = a.b ? a.b[n0 + lane] : 0.f;
-  c.b1 = a.b ? a.b[n0 + 64 + lane] : 0.f;
+  if (bias_lds) {
+    c.b0 = bias_lds[lane];
+    c.b1 = bias_lds[64 + lane];
+  } else {
+    c.b0 = a.b ? a.b[n0 + lane] : 0.f;
+    c.b1 = a.b ? a.b[n0 + 64 + lane] : 0.f;
+  }
   c.nw0 = rn_b[lane];
   c.nw1 = rn_b[64 + lane];
   c.band_scale = band_scale;
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(256) void gate_skinny_epilogue(GateArgs a, const fl
                                                             int S) {
   using SK = Skinny<MF>;
   constexpr int FN = kSkinnyFN;
-  constexpr int EPI_BYTES = (16 * kZld + SK::ROWS + kTile + 17) * 4 + 4 * kExactLdsWords * 4;
+  constexpr int EPI_BYTES = (16 * kZld + SK::ROWS + 2 * kTile + 17) * 4 + 4 * kExactLdsWords * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[EPI_BYTES];
   const int kt = (int)blockIdx.x / MF;
   const int fm = (int)blockIdx.x - kt * MF;  // this workgroup's 16 rows: 16 fm ..
@@ -563,47 +569,64 @@ __global__ __launch_bounds__(256) void gate_skinny_epilogue(GateArgs a, const fl
   float* zs = (float*)lds;           // [16][kZld]
   float* rn_a = zs + 16 * kZld;      // [ROWS], entries 16 fm .. 16 fm + 15 used
   float* rn_b = rn_a + SK::ROWS;     // [128]
-  int* defer = (int*)(rn_b + kTile); // [1 + 16]
+  float* bias_s = rn_b + kTile;      // [128]
+  int* defer = (int*)(bias_s + kTile); // [1 + 16]
   uint32_t* exact_lds = (uint32_t*)(lds + EPI_BYTES - 4 * kExactLdsWords * 4);
   const float* part0 = partial + (size_t)kt * S * SK::PART + (size_t)fm * FN * 256;
-  // the FN fragments of row fragment fm are 2 float4 per thread; thread tid
-  // sums entries tid and tid + 256 of the S partials in split order, eight
-  // splits' loads in flight at a time
+  // Every load of the workgroup is issued before the first is used (one
+  // memory round trip for the first eight splits): the bias and column norms,
+  // the partial row sums of squares (threads 0..15) and the partial z.  Split
+  // indices past S are clamped and their terms masked, so the code is straight.
+  // The FN fragments of row fragment fm are 2 float4 per thread; thread tid
+  // sums entries tid and tid + 256 of the S partials in split order.
+  const int col0 = 16 * ((int)threadIdx.x >> 6) + ((int)threadIdx.x & 15);  // entry tid; entry tid + 256 is col0 + 64
+  float bb[2] = {0.f, 0.f};
+  if (a.b) {
+    bb[0] = a.b[n0 + col0];
+    bb[1] = a.b[n0 + col0 + 64];
+  }
+  const float wn = a.wnorm[n0 + ((int)threadIdx.x & (kTile - 1))];
+  const bool sq_thread = threadIdx.x < 16;
+  const float* sq0 = partial + (size_t)kt * S * SK::PART + SK::NFRAG * 256 + 16 * fm + (threadIdx.x & 15);
   f32x4_t v[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  float t = 0.f;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {
     f32x4_t ld[8][2];
+    float q[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < S)
+    for (int u = 0; u < 8; ++u) {
+      const int su = min(s0 + u, S - 1);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-          ld[u][m] = *(const f32x4_t*)(part0 + (size_t)(s0 + u) * SK::PART +
-                                       (size_t)(threadIdx.x + 256 * m) * 4);
+      for (int m = 0; m < 2; ++m)
+        ld[u][m] = *(const f32x4_t*)(part0 + (size_t)su * SK::PART + (size_t)(threadIdx.x + 256 * m) * 4);
+      q[u] = sq0[(size_t)su * SK::PART];
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < S)
+    for (int u = 0; u < 8; ++u) {
+      const bool in = s0 + u < S;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) v[m] += ld[u][m];
+      for (int m = 0; m < 2; ++m) v[m] += in ? ld[u][m] : zero4;
+      t += in ? q[u] : 0.f;  // sums of squares: the masked terms are +0
+    }
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int p = threadIdx.x + 256 * m;  // fn * 64 + fragment lane
-    const int fl = p & 63, fn = p >> 6;
-    const int col = 16 * fn + (fl & 15);
-    const float bb = a.b ? a.b[n0 + col] : 0.f;
+    const int fl = p & 63;
+    const int col = col0 + 64 * m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) zs[(4 * (fl >> 4) + i) * kZld + col] = v[m][i] + bb;
+    for (int i = 0; i < 4; ++i) zs[(4 * (fl >> 4) + i) * kZld + col] = v[m][i] + bb[m];
   }
-  if (threadIdx.x < 16) {
-    float t = 0.f;
-    for (int ss = 0; ss < S; ++ss)
-      t += partial[((size_t)kt * S + ss) * SK::PART + SK::NFRAG * 256 + 16 * fm + threadIdx.x];
-    rn_a[16 * fm + threadIdx.x] = sqrtf(t);
+  if (sq_thread) rn_a[16 * fm + threadIdx.x] = sqrtf(t);
+  if (threadIdx.x < kTile) rn_b[threadIdx.x] = wn;
+  if (((threadIdx.x >> 4) & 3) == 0) {  // one thread per column of 0..63
+    bias_s[col0] = bb[0];
+    bias_s[col0 + 64] = bb[1];
   }
-  for (int i = threadIdx.x; i < kTile; i += blockDim.x) rn_b[i] = a.wnorm[n0 + i];
   __syncthreads();
   twell_rows<uint16_t, float, 8>(a, (const float*)zs, kZld, 16, 1.0f, rn_a, rn_b, 16 * fm, 0, n0,
-                                 defer, exact_lds);
+                                 defer, exact_lds, bias_s);
 }
 
 // Splits of the few-token gate: at least enough that no wave has more than
