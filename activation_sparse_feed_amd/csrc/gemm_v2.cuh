@@ -27,9 +27,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-#ifndef SFFN_GEMM_INTERLEAVE
-#define SFFN_GEMM_INTERLEAVE 0
-#endif
 
 // Workgroup barrier for the LDS pipeline: waits for this wave's LDS
 // instructions, then s_barrier.  Unlike __syncthreads() it does not drain the
@@ -101,7 +98,7 @@ struct Gemm2 {
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
   static_assert(BN == 128 || (BN == 256 && NB == 1 && !B_KN), "workgroup N tile");
-  static_assert(BM == 256 || BM == 128, "workgroup M tile");
+  static_assert(BM == 256 || BM == 128 || BM == 64 || BM == 32, "workgroup M tile");
   static_assert(BLOCKS % NWAVES == 0, "load blocks per wave");
   static_assert(!NORMS || NWAVES == 4, "norm split assumes 4 waves");
 
@@ -350,7 +347,20 @@ struct Gemm2 {
   // step next to the fragment reads that feed them (which would make every
   // MFMA wait for an LDS read): the reads of step kt+1 are all issued before
   // the MFMAs of step kt.
-  template <bool STEADY>
+  // Sums of squares of the A rows from the fragments of a step (lane l: row
+  // l & 15 of fragment fm, one quarter of the step's K range), for the waves
+  // that call it.
+  __device__ __forceinline__ void sq_a(const Frags& f) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const u32x4_t v = __builtin_bit_cast(u32x4_t, f.a[ks][fm]);
+        sqa[fm] = dot2_bf16(v.x, v.x, dot2_bf16(v.y, v.y, dot2_bf16(v.z, v.z, dot2_bf16(v.w, v.w, sqa[fm]))));
+      }
+  }
+
+  template <bool STEADY, bool SQA = false>
   __device__ __forceinline__ void pipe_step(uint8_t* lds, int kt, int nk, Frags& cur, Frags& nxt) {
     if (STEADY || kt + 1 < nk) {
       if (STEADY) {
@@ -363,32 +373,15 @@ struct Gemm2 {
         issue(lds + ((kt + STAGES - 1) % STAGES) * STAGE_BYTES, (kt + STAGES - 1) * BK);
       load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
     }
-#if SFFN_GEMM_INTERLEAVE
-    mma(cur);
-    if (STEADY) {
-      // one MFMA after each buffer load and each fragment read, so that the
-      // matrix core is fed while the memory instructions issue
-      constexpr int NM = KS * FM * NB * FN, ND = KS * (NB * FN * (B_KN ? 2 : 1) + FM);
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < ND; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - LOADS - ND, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#else
     __builtin_amdgcn_sched_barrier(0);
     mma(cur);
+    if (SQA && uniform((int)(threadIdx.x >> 6)) / WAVES_M == 0) sq_a(cur);
     __builtin_amdgcn_sched_barrier(0);
-#endif
   }
 
+  // SQA: the waves with wn == 0 also accumulate the sums of squares of the A
+  // rows (sqa, per lane as in sq_a).
+  template <bool SQA = false>
   __device__ __forceinline__ void run_pipe(uint8_t* lds, int K) {
     static_assert(STAGES >= 3, "stages");
     const int nk = K / BK;
@@ -402,12 +395,12 @@ struct Gemm2 {
     // steady state (every stage it refers to exists): no conditions, so the
     // fragment reads of step kt+1 overlap the MFMAs of step kt
     for (; kt + STAGES < nk; kt += 2) {  // step kt+1 issues stage kt+STAGES
-      pipe_step<true>(lds, kt, nk, f0, f1);
-      pipe_step<true>(lds, kt + 1, nk, f1, f0);
+      pipe_step<true, SQA>(lds, kt, nk, f0, f1);
+      pipe_step<true, SQA>(lds, kt + 1, nk, f1, f0);
     }
     for (; kt < nk; kt += 2) {
-      pipe_step<false>(lds, kt, nk, f0, f1);
-      if (kt + 1 < nk) pipe_step<false>(lds, kt + 1, nk, f1, f0);
+      pipe_step<false, SQA>(lds, kt, nk, f0, f1);
+      if (kt + 1 < nk) pipe_step<false, SQA>(lds, kt + 1, nk, f1, f0);
     }
     __syncthreads();
   }

@@ -555,6 +555,55 @@ __global__ __launch_bounds__(256) void gate_skinny_partial(GateArgs a, float* pa
         (redsq[i] + redsq[2 * SK::ROWS + i]) + (redsq[SK::ROWS + i] + redsq[3 * SK::ROWS + i]);
 }
 
+// gate_skinny_stream (d_model % 64 == 0): the same partials from a workgroup
+// that streams its tile's wg_t rows over its split's K range through an LDS
+// ring (the buffer-load pipeline with an A tile of the 16 MF token rows; every
+// load instruction fetches 1 KB of whole cache lines).  The four waves take 32
+// columns each, so their tiles are disjoint: no reduction across waves, and
+// one workgroup per (tile, split) with S chosen so that the grid fits the chip
+// at once.  Wave 0 also sums the squares of the x values it feeds to the MFMA.
+#ifndef SFFN_STREAM_STAGES
+#define SFFN_STREAM_STAGES 4
+#endif
+template <int MF>
+using StreamGemm = Gemm2<1, kTile, false, 64, 4, false, 16 * MF, SFFN_STREAM_STAGES, 4>;
+
+template <int MF>
+__global__ __launch_bounds__(256) void gate_skinny_stream(GateArgs a, float* partial, int S) {
+  using SK = Skinny<MF>;
+  using G = StreamGemm<MF>;
+  static_assert(G::FM == MF && G::FN == 2, "wave tile: all token rows, 32 columns");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
+  const int kt = (int)blockIdx.x / S;
+  const int s = (int)blockIdx.x - kt * S;
+  const int nc = a.K / 64;  // 64-wide K chunks
+  const int c_lo = (int)(((long)s * nc) / S), c_hi = (int)(((long)(s + 1) * nc) / S);
+  const int k_lo = c_lo * 64;
+  G g;
+  const uint16_t* B[1] = {(const uint16_t*)a.wg + k_lo};
+  g.init((const uint16_t*)a.x + k_lo, (size_t)a.T, nullptr, 0, a.T, B, kt * kTile, a.N,
+         (c_hi - c_lo) * 64, a.K, k_lo);
+  g.template run_pipe<true>(lds, (c_hi - c_lo) * 64);
+  const int lane = lane_id();
+  const int w = uniform((int)(threadIdx.x >> 6));
+  float* mine = partial + ((size_t)kt * S + s) * SK::PART;
+  // fragment (fm, fn) of wave w is fragment (fm, 2 w + fn) of the tile
+#pragma unroll
+  for (int fm = 0; fm < MF; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+      *(f32x4_t*)(mine + (size_t)((fm * kSkinnyFN + 2 * w + fn) * 64 + lane) * 4) = g.acc[0][fm][fn];
+  if (w == 0) {
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm) {
+      float q = g.sqa[fm];
+      q += __shfl_xor(q, 16, kWave);
+      q += __shfl_xor(q, 32, kWave);
+      if (lane < 16) mine[SK::NFRAG * 256 + 16 * fm + lane] = q;
+    }
+  }
+}
+
 template <int MF>
 __global__ __launch_bounds__(256) void gate_skinny_epilogue(GateArgs a, const float* partial,
                                                             int S) {
@@ -646,13 +695,26 @@ int skinny_splits(int K, int N) {
 }
 
 bool use_skinny(int dtype, int T, int K) { return dtype == 1 && T <= 64 && K % 32 == 0; }
+bool use_stream(int K) { return K % 64 == 0; }
+
+// Splits of the streaming kernel: as many as two workgroups per CU allow
+// (SFFN_STREAM_WGS in all), at most one per 64-wide K chunk.
+#ifndef SFFN_STREAM_WGS
+#define SFFN_STREAM_WGS 512
+#endif
+int stream_splits(int K, int N) {
+  const int nt = N / kTile;
+  return max(1, min(SFFN_STREAM_WGS / nt, K / 64));
+}
+
+int few_token_splits(int K, int N) { return use_stream(K) ? stream_splits(K, N) : skinny_splits(K, N); }
 
 }  // namespace
 
 size_t gate_workspace_bytes(int dtype, int T, int K, int N) {
   if (!use_skinny(dtype, T, K)) return 0;
   const int nt = N / kTile;
-  const int S = skinny_splits(K, N);
+  const int S = few_token_splits(K, N);
   const size_t part = T <= 32 ? Skinny<2>::PART : Skinny<4>::PART;
   return (size_t)nt * S * part * 4;
 }
@@ -666,18 +728,25 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
   GateArgs a{x, wg_t, b_g, count, idx, val, xnorm, wnorm, T, K, N, cap, gb};
   const int nt = N / kTile;
   if (use_skinny(dtype, T, K)) {
-    // Guard band for this summation order: at most kSkinnySteps MFMA steps in
-    // a wave, two adds across the waves, S partials and the bias, each with
-    // the same 4u margin as the one-pass kernels.
-    const int S = skinny_splits(K, N);
-    a.gb.coef_xw = 0x1p-22f * (float)(kSkinnySteps + S + 4);
+    // Guard band for this summation order: the MFMA steps of a split (at most
+    // kSkinnySteps per wave and two adds across the waves for the partial
+    // kernel; the whole split, ceil(nc / S) 64-wide chunks, for the streaming
+    // kernel), S partials and the bias, each with the same 4u margin as the
+    // one-pass kernels.
+    const bool strm = use_stream(K);
+    const int S = few_token_splits(K, N);
+    const int steps = strm ? 2 * ((K / 64 + S - 1) / S) : kSkinnySteps + 2;
+    a.gb.coef_xw = 0x1p-22f * (float)(steps + S + 2);
     float* partial = (float*)gate_ws;
+    const dim3 gp((unsigned)(nt * S)), blk(256);
     if (T <= 32) {
-      hipLaunchKernelGGL(gate_skinny_partial<2>, dim3((unsigned)(nt * S)), dim3(256), 0, stream, a, partial, S);
-      hipLaunchKernelGGL(gate_skinny_epilogue<2>, dim3((unsigned)(nt * 2)), dim3(256), 0, stream, a, partial, S);
+      if (strm) hipLaunchKernelGGL(gate_skinny_stream<2>, gp, blk, 0, stream, a, partial, S);
+      else hipLaunchKernelGGL(gate_skinny_partial<2>, gp, blk, 0, stream, a, partial, S);
+      hipLaunchKernelGGL(gate_skinny_epilogue<2>, dim3((unsigned)(nt * 2)), blk, 0, stream, a, partial, S);
     } else {
-      hipLaunchKernelGGL(gate_skinny_partial<4>, dim3((unsigned)(nt * S)), dim3(256), 0, stream, a, partial, S);
-      hipLaunchKernelGGL(gate_skinny_epilogue<4>, dim3((unsigned)(nt * 4)), dim3(256), 0, stream, a, partial, S);
+      if (strm) hipLaunchKernelGGL(gate_skinny_stream<4>, gp, blk, 0, stream, a, partial, S);
+      else hipLaunchKernelGGL(gate_skinny_partial<4>, gp, blk, 0, stream, a, partial, S);
+      hipLaunchKernelGGL(gate_skinny_epilogue<4>, dim3((unsigned)(nt * 4)), blk, 0, stream, a, partial, S);
     }
   } else if (dtype == 1 && K % GateGemm::BK == 0) {
     const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
