@@ -561,7 +561,7 @@ __global__ __launch_bounds__(256) void gate_skinny_partial(GateArgs a, float* pa
 // load instruction fetches 1 KB of whole cache lines).  The four waves take 32
 // columns each, so their tiles are disjoint: no reduction across waves, and
 // one workgroup per (tile, split) with S chosen so that the grid fits the chip
-// at once.  Wave 0 also sums the squares of the x values it feeds to the MFMA.
+// at once (about one workgroup per CU).  Wave 0 also sums the squares of the x values it feeds to the MFMA.
 #ifndef SFFN_STREAM_STAGES
 #define SFFN_STREAM_STAGES 4
 #endif
@@ -697,10 +697,11 @@ int skinny_splits(int K, int N) {
 bool use_skinny(int dtype, int T, int K) { return dtype == 1 && T <= 64 && K % 32 == 0; }
 bool use_stream(int K) { return K % 64 == 0; }
 
-// Splits of the streaming kernel: as many as two workgroups per CU allow
-// (SFFN_STREAM_WGS in all), at most one per 64-wide K chunk.
+// Splits of the streaming kernel: about one workgroup per CU (SFFN_STREAM_WGS
+// in all; fewer, longer streams also leave fewer partials to sum), at most one
+// per 64-wide K chunk.
 #ifndef SFFN_STREAM_WGS
-#define SFFN_STREAM_WGS 512
+#define SFFN_STREAM_WGS 256
 #endif
 int stream_splits(int K, int N) {
   const int nt = N / kTile;
