@@ -5,6 +5,7 @@
 
 #include "sffn.h"
 #include "launch.h"
+#include "route.cuh"
 
 namespace {
 
@@ -142,13 +143,18 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t, c
   if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int T = shape->T, K = shape->d_model, N = shape->d_ff;
-  hipError_t e = launch_route(count, T, N / 128, shape->cap, routed, n_routed, workspace, s);
-  if (e != hipSuccess) return SFFN_ERR_HIP;
   void* h = (char*)workspace + route_workspace_bytes(T);
+  const bool fused_route = routed_fast_path(shape) && T <= kRouteBlock;
+  hipError_t e = hipSuccess;
+  if (!fused_route) {
+    e = launch_route(count, T, N / 128, shape->cap, routed, n_routed, workspace, s);
+    if (e != hipSuccess) return SFFN_ERR_HIP;
+  }
   if (routed_fast_path(shape)) {
     float* partial = (float*)((char*)h + align256((size_t)T * N * elt_bytes(shape->dtype)));
     return hip_status(launch_routed_ffn(x, wg_t, b_g, wu_t, wd, h, y, partial, T, routed,
-                                        n_routed, K, N, s));
+                                        n_routed, fused_route ? count : nullptr, N / 128,
+                                        shape->cap, K, N, s));
   }
   e = launch_dense_gateup(shape->dtype, x, wg_t, b_g, wu_t, h, T, routed, n_routed, K, N, s);
   if (e != hipSuccess) return SFFN_ERR_HIP;

@@ -14,6 +14,7 @@
 #include "gemm_core.cuh"
 #include "gemm_v2.cuh"
 #include "launch.h"
+#include "route.cuh"
 
 namespace sffn {
 
@@ -28,6 +29,14 @@ struct DenseArgs {
   const int* rowmap;
   const int* n_rows_dev;
   int M, K, N;
+  // routed gate+up only: when route_count is set, each workgroup finds the
+  // routed rows of the M <= 256 rows itself from the TwELL counts (no row map
+  // or device count is read) and workgroup 0 writes them to routed_out and
+  // n_routed_out for the down kernels.
+  const uint16_t* route_count = nullptr;
+  int route_nt = 0, route_cap = 0;
+  int32_t* routed_out = nullptr;
+  int32_t* n_routed_out = nullptr;
 };
 
 __device__ __forceinline__ int rows_valid(const DenseArgs& a) {
@@ -254,14 +263,35 @@ __device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, 
 constexpr int kRoutedBigRows = 1024;
 using RoutedSmall = Gemm2<2, 64, false, 32, 2, false, 128, SFFN_ROUTED_STAGES>;
 using RoutedBig = Gemm2<2, 64, false, 32, 2>;
+// With the fused route (at most kRouteBlock rows): one stage less, so that the
+// row list fits beside the ring and two workgroups still share a CU.
+using RoutedFused = Gemm2<2, 64, false, 32, 2, false, 128, SFFN_ROUTED_STAGES - 1>;
 
+template <bool FUSED>
 __global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
-  constexpr size_t kLds = RoutedSmall::LDS_BYTES > RoutedBig::LDS_BYTES ? RoutedSmall::LDS_BYTES
-                                                                        : RoutedBig::LDS_BYTES;
+  constexpr size_t kLds = FUSED ? RoutedFused::LDS_BYTES
+                          : RoutedSmall::LDS_BYTES > RoutedBig::LDS_BYTES ? RoutedSmall::LDS_BYTES
+                                                                          : RoutedBig::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
-  const int mv = uniform(rows_valid(a));  // scalar: the tile loop and buffer descriptors stay uniform
-  if (mv > kRoutedBigRows) gateup_routed_tiles<RoutedBig>(a, mv, lds);
-  else gateup_routed_tiles<RoutedSmall>(a, mv, lds);
+  if constexpr (FUSED) {
+    static_assert(kLds >= kRouteBlock * 4, "route flags fit the pipeline LDS");
+    static_assert(kRouteBlock <= kRoutedBigRows, "few rows");
+    __shared__ int rows_s[kRouteBlock];
+    __shared__ int wave_tot[kRouteBlock / kWave];
+    // the route scan (flags in the pipeline LDS, which is free until the tiles start)
+    const int mv = uniform(route_rows_lds(a.route_count, a.M, a.route_nt, a.route_cap, (int*)lds,
+                                          rows_s, wave_tot));
+    if (blockIdx.x == 0) {
+      if ((int)threadIdx.x < mv) a.routed_out[threadIdx.x] = rows_s[threadIdx.x];
+      if (threadIdx.x == 0) *a.n_routed_out = mv;
+    }
+    a.rowmap = rows_s;
+    gateup_routed_tiles<RoutedFused>(a, mv, lds);
+  } else {
+    const int mv = uniform(rows_valid(a));  // scalar: the tile loop and buffer descriptors stay uniform
+    if (mv > kRoutedBigRows) gateup_routed_tiles<RoutedBig>(a, mv, lds);
+    else gateup_routed_tiles<RoutedSmall>(a, mv, lds);
+  }
 }
 
 // K splits of the routed down GEMM for mt x nt output tiles: enough work items
@@ -376,13 +406,25 @@ size_t routed_partial_bytes(int T, int N) {
 
 hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
                              const void* wd, void* h, void* y, float* partial, int T,
-                             const int* routed, const int* n_routed, int d_model, int d_ff,
+                             int32_t* routed, int32_t* n_routed, const uint16_t* route_count,
+                             int route_nt, int route_cap, int d_model, int d_ff,
                              hipStream_t stream) {
   // h [rows, d_ff] = gate+up of the routed rows of x
   DenseArgs g{x, wg_t, wu_t, b_g, h, routed, n_routed, T, d_model, d_ff};
+  if (route_count) {
+    g.route_count = route_count;
+    g.route_nt = route_nt;
+    g.route_cap = route_cap;
+    g.routed_out = routed;
+    g.n_routed_out = n_routed;
+  }
   const int tiles_max = ((T + 127) / 128) * (d_ff / 64);
-  hipLaunchKernelGGL(gateup_routed, dim3((unsigned)min(tiles_max, kRoutedGrid)), dim3(256), 0,
-                     stream, g);
+  if (route_count)
+    hipLaunchKernelGGL(gateup_routed<true>, dim3((unsigned)min(tiles_max, kRoutedGrid)), dim3(256),
+                       0, stream, g);
+  else
+    hipLaunchKernelGGL(gateup_routed<false>, dim3((unsigned)min(tiles_max, kRoutedGrid)), dim3(256),
+                       0, stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // y rows = h wd

@@ -44,11 +44,14 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
 // Dense FFN of the routed rows (hybrid fallback), row count on the device:
 // h [T, d_ff] (first n_routed rows used) and partial (routed_partial_bytes)
 // are workspace; y rows routed[m] are written.  bf16, d_model and d_ff
-// multiples of 32.
+// multiples of 32.  With route_count (T <= kRouteBlock), the routed rows are
+// found from the TwELL counts inside the gate+up kernel, which also writes
+// routed and n_routed; otherwise they are read from routed and n_routed.
 size_t routed_partial_bytes(int T, int d_model);
 hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
                              const void* wd, void* h, void* y, float* partial, int T,
-                             const int* routed, const int* n_routed, int d_model, int d_ff,
+                             int32_t* routed, int32_t* n_routed, const uint16_t* route_count,
+                             int route_nt, int route_cap, int d_model, int d_ff,
                              hipStream_t stream);
 
 // Dense gated FFN for few tokens (split-K weight streams): bf16, M <= 32,

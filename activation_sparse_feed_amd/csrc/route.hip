@@ -8,9 +8,10 @@
 //   route_compact  each 256-row block adds the group counts before it, then
 //                  writes its flagged rows in ascending order; the last block
 //                  writes n_routed.
-// With at most 256 rows, one workgroup does both (route_small).
+// With at most 256 rows, one workgroup does both (route_small, route.cuh).
 #include "common.cuh"
 #include "launch.h"
+#include "route.cuh"
 
 namespace sffn {
 
@@ -94,40 +95,10 @@ __global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ 
 __global__ __launch_bounds__(kBlock) void route_small(const uint16_t* __restrict__ count, int T,
                                                       int nt, int cap, int32_t* __restrict__ routed,
                                                       int32_t* __restrict__ n_routed) {
-  __shared__ int flag_s[kBlock];
-  __shared__ int wave_tot[kBlock / kWave];
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  constexpr int R = 16;
-  for (int u0 = 0; u0 < kBlock / 4 && u0 * 4 < T; u0 += R) {
-    bool over[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int t = (u0 + u) * 4 + w;
-      over[u] = false;
-      if (t < T)
-        for (int k = lane; k < nt; k += kWave) over[u] |= (int)count[(size_t)t * nt + k] > cap;
-    }
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int t = (u0 + u) * 4 + w;
-      const int f = __ballot(over[u]) != 0ull;
-      if (t < T && lane == 0) flag_s[t] = f;
-    }
-  }
-  __syncthreads();
-  const int t = threadIdx.x;
-  const int f = t < T ? flag_s[t] : 0;
-  const uint64_t m = __ballot(f);
-  if (lane == 0) wave_tot[w] = __popcll(m);
-  __syncthreads();
-  int off = 0;
-  for (int i = 0; i < w; ++i) off += wave_tot[i];
-  if (f) routed[off + lanes_below(m)] = t;
-  if (threadIdx.x == kBlock - 1) {
-    int tot = off;
-    for (int i = w; i < kBlock / kWave; ++i) tot += wave_tot[i];
-    *n_routed = tot;
-  }
+  __shared__ int flag_s[kRouteBlock], rows_s[kRouteBlock], wave_tot[kRouteBlock / kWave];
+  const int n = route_rows_lds(count, T, nt, cap, flag_s, rows_s, wave_tot);
+  if ((int)threadIdx.x < n) routed[threadIdx.x] = rows_s[threadIdx.x];
+  if (threadIdx.x == 0) *n_routed = n;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }

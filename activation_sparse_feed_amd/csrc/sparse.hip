@@ -418,7 +418,9 @@ __global__ __launch_bounds__(256) void sparse_up_pass(TwoPassArgs a, int groups)
   for (int base = 0; base < G * cap; base += kUpSlots) {
     const int q = base + lane;
     const SlotMeta sm = lane < kUpSlots ? slot_meta(a, t, gi * G, G, q) : SlotMeta{false, 0, 0};
-    const float h = sm.live ? bf16_to_f32(a.val[sm.off]) : 0.f;
+    // value loaded with the slot's count and index (one round trip), used if live
+    const float hv = bf16_to_f32(a.val[sm.off]);
+    const float h = sm.live ? hv : 0.f;
     uint64_t m = __ballot(sm.live);
     while (m) {
       int es[kUpBatch];
@@ -487,7 +489,10 @@ __global__ __launch_bounds__(kDownWaves * 64) void sparse_down_pass(TwoPassArgs 
   for (int gi = w; gi < groups && cap > 0; gi += kDownWaves) {
     for (int base = 0; base < G * cap; base += kWave) {
       const SlotMeta sm = slot_meta(a, t, gi * G, G, base + lane);
-      const float g = sm.live ? a.acts[sm.off] : 0.f;
+      // activation loaded with the slot's count and index (one round trip);
+      // slots that are not live hold stale workspace values and are masked
+      const float gv = a.acts[sm.off];
+      const float g = sm.live ? gv : 0.f;
       uint64_t m = __ballot(sm.live);
       while (m) {
         int es[kDownInflight];

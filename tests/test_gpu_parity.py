@@ -164,10 +164,14 @@ def test_dense_reference_few_tokens(T, K, N):
     (5, 2048, 8192, 2.0, 8),    # one workgroup per column tile, ragged rows
     (100, 264, 640, 1.5, 4),    # two-pass sparse kernels with K % 32 != 0, routing
     (256, 512, 1024, 1.9, 8),   # largest token count of the two-pass kernels
+    (256, 512, 1024, 1.2, 8),   # many routed rows, route scan inside the routed gate+up kernel
+    (257, 512, 1024, 1.2, 8),   # one row more: separate route kernels
 ])
 def test_few_token_paths(T, K, N, beta, cap):
     inp = wl.generate_custom(T=T, d_model=K, d_ff=N, dtype="bf16", beta=beta, seed_base=41)
-    compare(inp, cap)
+    e = compare(inp, cap)
+    if beta < 1.5:
+        assert e["n_routed"] > 10
 
 
 # ---------------------------------------------------------------- edge cases
