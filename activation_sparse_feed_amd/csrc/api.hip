@@ -59,7 +59,7 @@ bool routed_fast_path(const sffn_shape* s) {
 
 size_t hybrid_ws(const sffn_shape* s) {
   size_t n = route_workspace_bytes(s->T) + align256((size_t)s->T * s->d_ff * elt_bytes(s->dtype));
-  if (routed_fast_path(s)) n += align256(routed_partial_bytes(s->T, s->d_model));
+  if (routed_fast_path(s)) n += align256(routed_partial_bytes(s->T, s->d_model, s->d_ff));
   return n;
 }
 

@@ -10,6 +10,8 @@
 // Both take an optional row map (gather of x rows / scatter of y rows) and an
 // optional device-side row count, so the hybrid route runs them on the routed
 // rows without a host synchronisation.
+#include <algorithm>
+
 #include "common.cuh"
 #include "gemm_core.cuh"
 #include "gemm_v2.cuh"
@@ -294,13 +296,29 @@ __global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
   }
 }
 
-// K splits of the routed down GEMM for mt x nt output tiles: enough work items
-// for the grid, at most kRoutedMaxSplit, at least 8 K steps per split.
+// K splits of the routed down GEMM for mt x nt output tiles: the fewest splits
+// whose work items fill at least 90% of the grid's last round (few tiles: enough
+// items for the grid; just over a round: two or more shorter rounds instead of
+// a nearly empty one), else the best filling; at most kRoutedMaxSplit, at least
+// 8 K steps per split, and at most three rounds of items (which bounds the
+// partials at 3 * kRoutedGrid tiles of 128 x 128 floats).
 __host__ __device__ inline int routed_down_splits(int mt, int nt, int K) {
-  int s = kRoutedGrid / max(1, mt * nt);
-  s = min(s, kRoutedMaxSplit);
-  s = min(s, max(1, K / 256));
-  return max(s, 1);
+  const int tiles = max(1, mt * nt);
+  const int s_max = max(1, min(kRoutedMaxSplit, K / 256));
+  int best = 1;
+  int best_num = 0, best_den = 1;  // best filling as a fraction
+  for (int s = 1; s <= s_max; ++s) {
+    const int items = tiles * s;
+    if (s > 1 && items > 3 * kRoutedGrid) break;
+    const int slots = ((items + kRoutedGrid - 1) / kRoutedGrid) * kRoutedGrid;
+    if (10 * items >= 9 * slots) return s;
+    if ((long)items * best_den > (long)best_num * slots) {
+      best = s;
+      best_num = items;
+      best_den = slots;
+    }
+  }
+  return best;
 }
 
 // y rows of the routed list: with one split, written directly (rounded);
@@ -396,12 +414,16 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
 
 namespace sffn {
 
-size_t routed_partial_bytes(int T, int N) {
-  // whenever S > 1 (see routed_down_splits): S * mt <= kRoutedGrid / nt, and
-  // S * mt <= kRoutedMaxSplit * ceil(T / 128)
+size_t routed_partial_bytes(int T, int N, int K) {
+  // the largest S * mt of routed_down_splits over every possible row count
+  // (S > 1 only: one split writes y directly)
   const int nt = (N + 127) / 128;
-  const int tiles = min(kRoutedGrid / nt, kRoutedMaxSplit * ((T + 127) / 128));
-  return (size_t)tiles * 128 * (size_t)N * 4;
+  size_t rows = 0;
+  for (int mt = 1; mt <= (T + 127) / 128; ++mt) {
+    const int S = routed_down_splits(mt, nt, K);
+    if (S > 1) rows = std::max(rows, (size_t)S * mt * 128);
+  }
+  return rows * (size_t)N * 4;
 }
 
 hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,

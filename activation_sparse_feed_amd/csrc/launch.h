@@ -47,7 +47,7 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
 // multiples of 32.  With route_count (T <= kRouteBlock), the routed rows are
 // found from the TwELL counts inside the gate+up kernel, which also writes
 // routed and n_routed; otherwise they are read from routed and n_routed.
-size_t routed_partial_bytes(int T, int d_model);
+size_t routed_partial_bytes(int T, int d_model, int d_ff);
 hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
                              const void* wd, void* h, void* y, float* partial, int T,
                              int32_t* routed, int32_t* n_routed, const uint16_t* route_count,

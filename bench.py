@@ -40,6 +40,9 @@ def parse_args():
     p.add_argument("--cpu-rows", type=int, default=None,
                    help="rows of the CPU oracle sample (default: whole batch, at most 4096)")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--cold-steps", type=int, default=10,
+                   help="steps of the cold pass (a 512 MiB read between steps evicts the "
+                        "Infinity Cache); 0 skips it")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device copies of MIB MiB (reference for the HBM byte "
                         "counters of a profiling run) and exit")
@@ -80,6 +83,23 @@ def measured_traffic(workload: str):
         return None
 
 
+def gpu_clocks():
+    """Current GPU clocks as reported by rocm-smi (None if it is unavailable)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if exe is None:
+        return None
+    try:
+        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        card = next(iter(d.values()))
+        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()
+                or "fclk" in k.lower()}
+    except Exception:  # noqa: BLE001 - the clocks are context, never a reason to fail
+        return None
+
+
 def cpu_baseline(inp, rows: int) -> dict:
     import numpy as np
     import oracle
@@ -101,6 +121,10 @@ def cpu_baseline(inp, rows: int) -> dict:
         dt = time.perf_counter() - t0
         if dt >= 10.0 or passes >= 30:
             break
+    # the oracle's dense FFN on the same rows (fp64 BLAS), for context
+    t1 = time.perf_counter()
+    oracle.ffn_dense(x, wg, inp.b_g, wu, wd)
+    t_dense = time.perf_counter() - t1
     cpu = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -113,7 +137,8 @@ def cpu_baseline(inp, rows: int) -> dict:
     return {"value": passes * len(sel) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(sel)} of {w.T} tokens of {w.name}, {passes} float64 sparse forwards "
                       f"(gate with exact sign, TwELL pack, route, fused sum), {dt:.2f} s",
-            "cpu_model": cpu, "os_cpu_count": os.cpu_count()}
+            "cpu_model": cpu, "os_cpu_count": os.cpu_count(),
+            "oracle_dense_tokens_per_s": len(sel) / t_dense}
 
 
 def main() -> int:
@@ -187,6 +212,44 @@ def main() -> int:
     t_sparse = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
     t_hybrid = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]))
     t_events = float(np.mean([ev[i][0].elapsed_time(ev[i][3]) for i in range(K)]))
+    step_ev = np.array([ev[i][0].elapsed_time(ev[i][3]) for i in range(K)])
+
+    # ---- cold pass: the same three calls after reading a 512 MiB buffer, which
+    # evicts the 256 MB Infinity Cache with clean lines (a write would leave
+    # dirty lines whose write-back lands inside the timed calls), so the weights
+    # come from HBM; the dense reference is timed the same way
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+        sink = torch.zeros((), dtype=torch.int64, device="cuda")
+        nc = args.cold_steps
+        cev = [[E(enable_timing=True) for _ in range(4)] for _ in range(nc)]
+        for i in range(nc):
+            sink += flush.sum()
+            cev[i][0].record()
+            sffn.twell_pack(s, x, wg, b, ffn.count, ffn.idx, ffn.val, ffn.ws_pack, wg_norms)
+            cev[i][1].record()
+            sffn.sparse_ffn_fwd(s, x, wu, wd, ffn.count, ffn.idx, ffn.val, ffn.y, ffn.ws_sparse)
+            cev[i][2].record()
+            sffn.hybrid_route(s, x, wg, b, wu, wd, ffn.count, ffn.routed, ffn.n_routed,
+                              ffn.ws_hybrid, ffn.y)
+            cev[i][3].record()
+        dev_ = [[E(enable_timing=True) for _ in range(2)] for _ in range(nc)]
+        if not args.no_dense:
+            for i in range(nc):
+                sink += flush.sum()
+                dev_[i][0].record()
+                dense.forward(x, wg, b, wu, wd)
+                dev_[i][1].record()
+        torch.cuda.synchronize()
+        del flush
+        cm = lambda a, z: float(np.median([cev[i][a].elapsed_time(cev[i][z]) for i in range(nc)]))
+        cold = {"steps": nc, "twell_pack_ms": cm(0, 1), "sparse_ffn_fwd_ms": cm(1, 2),
+                "hybrid_route_ms": cm(2, 3), "step_ms": cm(0, 3)}
+        if not args.no_dense:
+            cold["dense_ffn_ref_ms"] = float(np.median([dev_[i][0].elapsed_time(dev_[i][1])
+                                                        for i in range(nc)]))
+            cold["speedup_vs_dense"] = cold["dense_ffn_ref_ms"] / cold["step_ms"]
 
     # ---- dense reference
     t_dense = None
@@ -199,6 +262,24 @@ def main() -> int:
         d1.record()
         torch.cuda.synchronize()
         t_dense = d0.elapsed_time(d1) / K
+
+    # ---- sanity line: the same dense FFN from torch's own GEMMs (hipBLASLt)
+    t_torch = None
+    if not args.no_dense and w.dtype == "bf16":
+        def torch_ffn():
+            z = torch.nn.functional.linear(x, wg) + b.to(dt)
+            u = torch.nn.functional.linear(x, wu)
+            return torch.mm(torch.relu(z) * u, wd)
+        for _ in range(3):
+            torch_ffn()
+        t0_, t1_ = E(enable_timing=True), E(enable_timing=True)
+        torch.cuda.synchronize()
+        t0_.record()
+        for _ in range(K):
+            torch_ffn()
+        t1_.record()
+        torch.cuda.synchronize()
+        t_torch = t0_.elapsed_time(t1_) / K
 
     count = ffn.count.to(torch.int64)
     nnz_live = int(torch.clamp(count, max=w.cap).sum().item()) if w.cap > 0 else 0
@@ -245,12 +326,18 @@ def main() -> int:
                            "hbm_frac": sparse_bytes / (t_sparse * 1e-3) / 1e9 / PEAK_HBM_GBS,
                            "flop": sparse_flop, "tflop_per_s": sparse_flop / (t_sparse * 1e-3) / 1e12,
                            "distinct_columns": uniq},
+        "step_ms_percentiles": {"p10": float(np.percentile(step_ev, 10)),
+                                "p50": float(np.median(step_ev)),
+                                "p90": float(np.percentile(step_ev, 90))},
+        "cold": cold,
+        "torch_dense_ms": t_torch,
         "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,
         "speedup_vs_dense": (t_dense / ms_step) if t_dense else None,
         "dense_tflops": (3 * gate_flop / (t_dense * 1e-3) / 1e12) if t_dense else None,
         "activity": {"nnz_per_row": nnz_total / T, "density": nnz_total / (T * n),
                      "routed_rows": n_routed},
         "device": torch.cuda.get_device_name(0),
+        "clocks": gpu_clocks(),
         "host": platform.node(),
     }
     if not args.no_cpu_baseline:
