@@ -150,7 +150,9 @@ int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t,
  * Rows that are not routed are not touched.  routed: int32 [T] (entries past
  * n_routed unspecified); n_routed: one int32.  workspace: at least
  * sffn_workspace_bytes(shape, SFFN_WS_HYBRID) bytes (side buffer for the
- * routed rows' h and the routing scan).
+ * routed rows' h, the split-K partials of their down projection and the
+ * routing scan).  No initial contents needed.  Calls that share a workspace
+ * must be stream-ordered.
  */
 int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
                      const float* b_g, const void* wu_t, const void* wd,
