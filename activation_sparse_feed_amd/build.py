@@ -16,8 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsffn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "twell_gate.hip", "dense.hip", "dense_skinny.hip", "sparse.hip", "route.hip",
-           "norms.hip"]
+SOURCES = ["api.hip", "twell_gate.hip", "convert.hip", "dense.hip", "dense_skinny.hip", "sparse.hip",
+           "route.hip", "norms.hip"]
 ARCH = os.environ.get("SFFN_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instructions are kept out of the generated code.

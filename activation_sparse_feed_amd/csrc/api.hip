@@ -63,6 +63,10 @@ size_t hybrid_ws(const sffn_shape* s) {
   return n;
 }
 
+size_t convert_ws(const sffn_shape* s) {
+  return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4);
+}
+
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? SFFN_OK : SFFN_ERR_HIP; }
 
 // Guard band of the activity decision (see the TwELL epilogue).  bf16: the
@@ -184,6 +188,84 @@ int32_t dense_ffn_ref(const sffn_shape* shape, const void* x, const void* wg_t, 
   return hip_status(launch_down(shape->dtype, workspace, wd, y, T, nullptr, nullptr, N, K, s));
 }
 
+int32_t gate_preact(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                    float* z, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({x, wg_t, z}) || (b_g && !aligned16(b_g))) return SFFN_ERR_ARG;
+  if (!preact_supported(shape->dtype, shape->d_model) || act_bytes_too_large(shape))
+    return SFFN_ERR_UNSUPPORTED;
+  return hip_status(launch_gate_preact(x, wg_t, b_g, z, shape->T, shape->d_model, shape->d_ff,
+                                       (hipStream_t)stream));
+}
+
+namespace {
+
+// Row norms for the converters' guard band: x always, wg_t unless given.
+int32_t convert_norms(const sffn_shape* s, const void* x, const void* wg_t, const float* wg_norms,
+                      void* workspace, float** xn, const float** wn, hipStream_t stream) {
+  *xn = (float*)workspace;
+  float* wbuf = (float*)((char*)workspace + align256((size_t)s->T * 4));
+  *wn = wg_norms ? wg_norms : wbuf;
+  return hip_status(launch_row_norms(s->dtype, x, s->T, *xn, wg_t, wg_norms ? 0 : s->d_ff, wbuf,
+                                     s->d_model, stream));
+}
+
+int32_t check_convert(const sffn_shape* s, const float* z, const void* x, const void* wg_t,
+                      const float* b_g, const float* wg_norms, void* workspace, size_t ws_bytes) {
+  if (!ptrs_ok({z, x, wg_t}) || (b_g && !aligned16(b_g)) || (wg_norms && !aligned16(wg_norms)))
+    return SFFN_ERR_ARG;
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < convert_ws(s))
+    return SFFN_ERR_WORKSPACE;
+  if (!preact_supported(s->dtype, s->d_model) || act_bytes_too_large(s))
+    return SFFN_ERR_UNSUPPORTED;
+  return SFFN_OK;
+}
+
+}  // namespace
+
+int32_t twell_from_preact(const sffn_shape* shape, const float* z, const void* x,
+                          const void* wg_t, const float* b_g, const float* wg_norms,
+                          uint16_t* count, uint16_t* idx, void* val, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({count}) || (shape->cap > 0 && !ptrs_ok({idx, val}))) return SFFN_ERR_ARG;
+  st = check_convert(shape, z, x, wg_t, b_g, wg_norms, workspace, ws_bytes);
+  if (st != SFFN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* xn;
+  const float* wn;
+  st = convert_norms(shape, x, wg_t, wg_norms, workspace, &xn, &wn, s);
+  if (st != SFFN_OK) return st;
+  return hip_status(launch_twell_convert(z, x, wg_t, b_g, xn, wn, count, idx, val, shape->T,
+                                         shape->d_model, shape->d_ff, shape->cap,
+                                         guard_band(shape), s));
+}
+
+int32_t ell_from_preact(const sffn_shape* shape, int32_t width, const float* z, const void* x,
+                        const void* wg_t, const float* b_g, const float* wg_norms,
+                        uint16_t* ell_count, uint16_t* ell_idx, void* ell_val, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (width < 0 || width > shape->d_ff) return SFFN_ERR_ARG;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({ell_count}) || (width > 0 && !ptrs_ok({ell_idx, ell_val}))) return SFFN_ERR_ARG;
+  st = check_convert(shape, z, x, wg_t, b_g, wg_norms, workspace, ws_bytes);
+  if (st != SFFN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* xn;
+  const float* wn;
+  st = convert_norms(shape, x, wg_t, wg_norms, workspace, &xn, &wn, s);
+  if (st != SFFN_OK) return st;
+  return hip_status(launch_ell_convert(z, x, wg_t, b_g, xn, wn, width, ell_count, ell_idx,
+                                       ell_val, shape->T, shape->d_model, shape->d_ff,
+                                       guard_band(shape), s));
+}
+
 size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
   if (check_shape(shape) != SFFN_OK) return 0;
   switch (which) {
@@ -193,6 +275,7 @@ size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
       return sparse_workspace_bytes(shape->dtype, shape->T, shape->d_ff / 128, shape->d_model,
                                     shape->cap);
     case SFFN_WS_PACK: return pack_ws(shape);
+    case SFFN_WS_CONVERT: return convert_ws(shape);
     default: return 0;
   }
 }

@@ -25,6 +25,22 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
                              uint16_t* idx, void* val, int T, int K, int N, int cap,
                              GuardBand gb, void* gate_ws, hipStream_t stream);
 
+// Separate-conversion baseline (bf16, K a multiple of 32): the gate GEMM
+// storing the float32 pre-activation z [T, N] (bias added), and converters
+// from z to TwELL and to a row-wise ELLPACK of the given width (ecount [T],
+// eidx / eval [T, width]).  Same activity decision as launch_gate_twell.
+bool preact_supported(int dtype, int K);
+hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g, float* z, int T,
+                              int K, int N, hipStream_t stream);
+hipError_t launch_twell_convert(const float* z, const void* x, const void* wg_t, const float* b_g,
+                                const float* xnorm, const float* wnorm, uint16_t* count,
+                                uint16_t* idx, void* val, int T, int K, int N, int cap,
+                                GuardBand gb, hipStream_t stream);
+hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, const float* b_g,
+                              const float* xnorm, const float* wnorm, int width,
+                              uint16_t* ecount, uint16_t* eidx, void* eval, int T, int K, int N,
+                              GuardBand gb, hipStream_t stream);
+
 // Row norms of a [rows_a, K] and a [rows_b, K] matrix in one launch.
 hipError_t launch_row_norms(int dtype, const void* a, int rows_a, float* out_a, const void* b,
                             int rows_b, float* out_b, int K, hipStream_t stream);

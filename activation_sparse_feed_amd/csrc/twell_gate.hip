@@ -21,155 +21,11 @@
 #include "gemm_core.cuh"
 #include "gemm_v2.cuh"
 #include "launch.h"
+#include "twell_emit.cuh"
 
 namespace sffn {
 
 namespace {
-
-constexpr int kTile = 128;
-constexpr int kZld = kTile + 4;  // LDS row stride of the staged z half-tile (floats)
-
-struct GateArgs {
-  const void* x;
-  const void* wg;
-  const float* b;
-  uint16_t* count;
-  uint16_t* idx;
-  void* val;
-  const float* xnorm;  // ||x_t||, [T]
-  const float* wnorm;  // ||wg_t[j]||, [N]
-  int T, K, N, cap;
-  GuardBand gb;
-};
-
-// Copy the row norms of a tile into LDS (rows past T read as 0).
-__device__ __forceinline__ void load_tile_norms(const GateArgs& a, int m0, int bm, int n0,
-                                                float* rn_a, float* rn_b) {
-  for (int i = threadIdx.x; i < bm; i += blockDim.x) rn_a[i] = (m0 + i < a.T) ? a.xnorm[m0 + i] : 0.f;
-  for (int i = threadIdx.x; i < kTile; i += blockDim.x) rn_b[i] = a.wnorm[n0 + i];
-}
-
-// Rows [r0, r0 + nrows) of the tile are staged in zs (row stride zld, float32
-// or bfloat16 bits); the four waves take every fourth row.  Rows whose
-// entries are all outside the guard band are emitted at once; rows with an
-// entry inside it are listed in `defer` (LDS, 1 + nrows ints) and emitted in a
-// second pass after their flagged entries were re-evaluated exactly, so the
-// slow path runs on a few rows spread over all waves instead of stalling the
-// row walk.
-__device__ __forceinline__ float zget(const float* zs, int i) { return zs[i]; }
-__device__ __forceinline__ float zget(const uint16_t* zs, int i) { return bf16_to_f32(zs[i]); }
-
-struct RowCtx {
-  int nt, kt, m0, n0, r0;
-  float b0, b1, nw0, nw1, band_scale;
-};
-
-// Activity of the two entries of this lane in row rr, and the guard-band flags.
-template <typename ZT>
-__device__ __forceinline__ void row_state(const GateArgs& a, const RowCtx& c, const ZT* zs,
-                                          int zld, const float* rn_a, int rr, float& z0, float& z1,
-                                          uint64_t& f0, uint64_t& f1) {
-  const int lane = lane_id();
-  z0 = zget(zs, rr * zld + lane);
-  z1 = zget(zs, rr * zld + 64 + lane);
-  const float nx = rn_a[c.r0 + rr];
-  const float d0 = c.band_scale * (a.gb.coef_xw * nx * c.nw0 + a.gb.coef_b * fabsf(c.b0));
-  const float d1 = c.band_scale * (a.gb.coef_xw * nx * c.nw1 + a.gb.coef_b * fabsf(c.b1));
-  f0 = __ballot(!(fabsf(z0) > d0));
-  f1 = __ballot(!(fabsf(z1) > d1));
-}
-
-// Compaction of one row: ascending active columns into the first cap slots.
-template <typename T>
-__device__ __forceinline__ void emit_row(const GateArgs& a, const RowCtx& c, int t, bool act0,
-                                         bool act1, float z0, float z1) {
-  const int lane = lane_id();
-  const uint64_t m0m = __ballot(act0);
-  const uint64_t m1m = __ballot(act1);
-  const int c0 = __popcll(m0m);
-  const size_t base = ((size_t)t * c.nt + c.kt) * a.cap;
-  if (act0) {
-    const int s = lanes_below(m0m);
-    if (s < a.cap) {
-      a.idx[base + s] = (uint16_t)(c.n0 + lane);
-      Elt<T>::store1(a.val, base + s, z0);
-    }
-  }
-  if (act1) {
-    const int s = c0 + lanes_below(m1m);
-    if (s < a.cap) {
-      a.idx[base + s] = (uint16_t)(c.n0 + 64 + lane);
-      Elt<T>::store1(a.val, base + s, z1);
-    }
-  }
-  if (lane == 0) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)(c0 + __popcll(m1m));
-}
-
-// bias_lds (optional): the tile's 128 bias values already staged in LDS.
-template <typename T, typename ZT, int EXACT_U = 2>
-__device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, float band_scale,
-                           const float* rn_a, const float* rn_b, int r0, int m0, int n0,
-                           int* defer, uint32_t* exact_lds, const float* bias_lds = nullptr) {
-  const int lane = lane_id();
-  const int w = uniform((int)(threadIdx.x >> 6));
-  RowCtx c;
-  c.nt = a.N / kTile;
-  c.kt = n0 / kTile;
-  c.m0 = m0;
-  c.n0 = n0;
-  c.r0 = r0;
-  if (bias_lds) {
-    c.b0 = bias_lds[lane];
-    c.b1 = bias_lds[64 + lane];
-  } else {
-    c.b0 = a.b ? a.b[n0 + lane] : 0.f;
-    c.b1 = a.b ? a.b[n0 + 64 + lane] : 0.f;
-  }
-  c.nw0 = rn_b[lane];
-  c.nw1 = rn_b[64 + lane];
-  c.band_scale = band_scale;
-  if (threadIdx.x == 0) defer[0] = 0;
-  __syncthreads();
-  for (int rr = w; rr < nrows; rr += 4) {
-    const int t = m0 + r0 + rr;
-    if (t >= a.T) break;
-    float z0, z1;
-    uint64_t f0, f1;
-    row_state(a, c, zs, zld, rn_a, rr, z0, z1, f0, f1);
-    if (f0 | f1) {
-      if (lane == 0) defer[1 + atomicAdd(&defer[0], 1)] = rr;
-      continue;
-    }
-    emit_row<T>(a, c, t, z0 > 0.f, z1 > 0.f, z0, z1);
-  }
-  __syncthreads();
-  const int nd = defer[0];
-  const T* x = (const T*)a.x;
-  const T* wg = (const T*)a.wg;
-  for (int i = w; i < nd; i += 4) {
-    const int rr = uniform(defer[1 + i]);
-    const int t = m0 + r0 + rr;
-    float z0, z1;
-    uint64_t f0, f1;
-    row_state(a, c, zs, zld, rn_a, rr, z0, z1, f0, f1);
-    bool act0 = z0 > 0.f, act1 = z1 > 0.f;
-    while (f0 | f1) {
-      int col;
-      if (f0) { col = __builtin_ctzll(f0); f0 &= f0 - 1; }
-      else    { col = 64 + __builtin_ctzll(f1); f1 &= f1 - 1; }
-      const float bc = a.b ? a.b[n0 + col] : 0.f;
-      const ExactResult e = exact_gate_value<T, EXACT_U>(x + (size_t)t * a.K,
-                                                wg + (size_t)(n0 + col) * a.K, bc, a.K,
-                                                exact_lds + w * kExactLdsWords);
-      if (col < 64) {
-        if (lane == col) { act0 = e.sign > 0; z0 = (float)e.value; }
-      } else {
-        if (lane == col - 64) { act1 = e.sign > 0; z1 = (float)e.value; }
-      }
-    }
-    emit_row<T>(a, c, t, act0, act1, z0, z1);
-  }
-}
 
 // bf16, d_model % 8 == 0: 128 x 128 tiles on the register-staged main loop.
 // The whole z tile (bias added) is staged in LDS as bfloat16, the value TwELL
@@ -223,30 +79,6 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 // Guard band: each entry is first tested against a bound for its whole row
 // (largest column norm and bias of the wave's tile); only entries inside it
 // get the per-entry band, and only those inside that are re-evaluated exactly.
-#ifndef SFFN_GATE_BN
-#define SFFN_GATE_BN 128
-#endif
-#ifndef SFFN_GATE_BM
-#define SFFN_GATE_BM 256
-#endif
-#ifndef SFFN_GATE_STAGES
-#define SFFN_GATE_STAGES 4
-#endif
-#ifndef SFFN_GATE_BK
-#define SFFN_GATE_BK 32
-#endif
-#ifndef SFFN_GATE_WAVES
-#define SFFN_GATE_WAVES 8
-#endif
-#ifndef SFFN_GATE_WN
-#define SFFN_GATE_WN 1
-#endif
-#ifndef SFFN_GATE_OCC
-#define SFFN_GATE_OCC 1
-#endif
-using GateGemm = Gemm2<1, SFFN_GATE_BN, false, SFFN_GATE_BK, SFFN_GATE_WN, false, SFFN_GATE_BM,
-                       SFFN_GATE_STAGES, SFFN_GATE_WAVES>;
-static_assert(GateGemm::WN == kTile, "each wave holds one TwELL column tile");
 #ifndef SFFN_EPI_EXACT_U
 #define SFFN_EPI_EXACT_U 4  // exact re-evaluation: 16-byte chunks per lane loaded together
 #endif
@@ -762,5 +594,6 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
   }
   return hipGetLastError();
 }
+
 
 }  // namespace sffn

@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libsffn.so")
 
 SFFN_OK, SFFN_ERR_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ERR_HIP = 0, -1, -2, -3, -4
 SFFN_F32, SFFN_BF16 = 0, 1
-WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK = 0, 1, 2, 3
+WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK, WS_CONVERT = 0, 1, 2, 3, 4
 TILE = 128
 
 EXPORTED = ("twell_weight_norms", "twell_pack", "sparse_ffn_fwd", "hybrid_route",
-            "dense_ffn_ref", "sffn_workspace_bytes", "sffn_strerror")
+            "dense_ffn_ref", "gate_preact", "twell_from_preact", "ell_from_preact",
+            "sffn_workspace_bytes", "sffn_strerror")
 
 
 class SffnError(RuntimeError):
@@ -48,8 +49,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_ffn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.gate_preact.argtypes = [sp, vp, vp, vp, vp, vp]
+    lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("twell_weight_norms", "twell_pack", "sparse_ffn_fwd", "hybrid_route",
-               "dense_ffn_ref"):
+               "dense_ffn_ref", "gate_preact", "twell_from_preact", "ell_from_preact"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
     lib.sffn_workspace_bytes.restype = sz
@@ -161,6 +165,38 @@ def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=Non
     _check("dense_ffn_ref", _lib.dense_ffn_ref(
         ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd),
         _ptr(workspace), ws_n, _ptr(y), _stream(stream)))
+
+
+def gate_preact(shape: Shape, x, wg_t, b_g, z, stream=None) -> None:
+    if z.dtype != torch.float32 or tuple(z.shape) != (shape.T, shape.d_ff):
+        raise ValueError("z must be float32 [T, d_ff]")
+    _check("gate_preact", _lib.gate_preact(ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g),
+                                           _ptr(z), _stream(stream)))
+
+
+def twell_from_preact(shape: Shape, z, x, wg_t, b_g, count, idx, val, workspace, wg_norms=None,
+                      stream=None) -> None:
+    ws_n = workspace.numel() * workspace.element_size()
+    _check("twell_from_preact", _lib.twell_from_preact(
+        ctypes.byref(shape), _ptr(z), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wg_norms), _ptr(count),
+        _ptr(idx), _ptr(val), _ptr(workspace), ws_n, _stream(stream)))
+
+
+def alloc_ell(shape: Shape, width: int, device=None):
+    """Row-wise ELLPACK buffers: count [T] u16, idx [T, width] u16, val [T, width] bf16."""
+    dev = device or "cuda"
+    count = torch.empty(shape.T, dtype=torch.uint16, device=dev)
+    idx = torch.empty((shape.T, max(width, 1)), dtype=torch.uint16, device=dev)
+    val = torch.empty((shape.T, max(width, 1)), dtype=torch.bfloat16, device=dev)
+    return count, idx, val
+
+
+def ell_from_preact(shape: Shape, width: int, z, x, wg_t, b_g, count, idx, val, workspace,
+                    wg_norms=None, stream=None) -> None:
+    ws_n = workspace.numel() * workspace.element_size()
+    _check("ell_from_preact", _lib.ell_from_preact(
+        ctypes.byref(shape), int(width), _ptr(z), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wg_norms),
+        _ptr(count), _ptr(idx), _ptr(val), _ptr(workspace), ws_n, _stream(stream)))
 
 
 class SparseFFN:

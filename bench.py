@@ -40,6 +40,9 @@ def parse_args():
     p.add_argument("--cpu-rows", type=int, default=None,
                    help="rows of the CPU oracle sample (default: whole batch, at most 4096)")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-conversion", action="store_true",
+                   help="skip the separate-conversion baseline (gate GEMM storing z, then "
+                        "standalone TwELL and row-ELLPACK conversions)")
     p.add_argument("--cold-steps", type=int, default=10,
                    help="steps of the cold pass (a 512 MiB read between steps evicts the "
                         "Infinity Cache); 0 skips it")
@@ -51,6 +54,7 @@ def parse_args():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_twell_pack_prefill_1pct.md")
 GATE_SOURCES = ("activation_sparse_feed_amd/csrc/twell_gate.hip",
+                "activation_sparse_feed_amd/csrc/twell_emit.cuh",
                 "activation_sparse_feed_amd/csrc/gemm_v2.cuh",
                 "activation_sparse_feed_amd/csrc/exact.cuh",
                 "activation_sparse_feed_amd/csrc/common.cuh")
@@ -139,6 +143,15 @@ def cpu_baseline(inp, rows: int) -> dict:
                       f"(gate with exact sign, TwELL pack, route, fused sum), {dt:.2f} s",
             "cpu_model": cpu, "os_cpu_count": os.cpu_count(),
             "oracle_dense_tokens_per_s": len(sel) / t_dense}
+
+
+def d_model_ok(d_model: int) -> bool:
+    """The separate-conversion calls need d_model % 32 == 0."""
+    return d_model % 32 == 0
+
+
+def nnz_live_of(count, cap: int) -> int:
+    return int(count.clamp(max=cap).sum().item()) if cap > 0 else 0
 
 
 def main() -> int:
@@ -304,6 +317,76 @@ def main() -> int:
         torch.cuda.synchronize()
         t_torch = t0_.elapsed_time(t1_) / K
 
+    # ---- separate-conversion baseline: the gate GEMM stores the float32
+    # pre-activation z, then standalone kernels build TwELL and a classic
+    # row-wise ELLPACK padded to the longest row (not part of the step above)
+    conversion = None
+    # (measured where twell_pack runs the same GEMM, more than 64 tokens)
+    if not args.no_conversion and w.dtype == "bf16" and d_model_ok(w.d_model) and w.T > 64:
+        eb_ = 2
+        z = torch.empty((w.T, w.d_ff), dtype=torch.float32, device="cuda")
+        ws_c = sffn.alloc_workspace(s, sffn.WS_CONVERT)
+        tw = sffn.alloc_twell(s)
+        width = int(ffn.count.to(torch.int64).sum(1).max().item())
+        ell = sffn.alloc_ell(s, width)
+        def conv_pass():
+            sffn.gate_preact(s, x, wg, b, z)
+            sffn.twell_from_preact(s, z, x, wg, b, *tw, ws_c, wg_norms)
+        for _ in range(2):
+            conv_pass()
+            sffn.ell_from_preact(s, width, z, x, wg, b, *ell, ws_c, wg_norms)
+        torch.cuda.synchronize()
+        # K passes back to back (as the step above), then per-call events
+        c0, c1 = E(enable_timing=True), E(enable_timing=True)
+        c0.record()
+        for _ in range(K):
+            conv_pass()
+        c1.record()
+        torch.cuda.synchronize()
+        t_two_pass = c0.elapsed_time(c1) / K
+        cv = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for i in range(K):
+            cv[i][0].record()
+            sffn.gate_preact(s, x, wg, b, z)
+            cv[i][1].record()
+            sffn.twell_from_preact(s, z, x, wg, b, *tw, ws_c, wg_norms)
+            cv[i][2].record()
+            sffn.ell_from_preact(s, width, z, x, wg, b, *ell, ws_c, wg_norms)
+            cv[i][3].record()
+        # the fused call timed the same way, right after
+        f0, f1 = E(enable_timing=True), E(enable_timing=True)
+        f0.record()
+        for _ in range(K):
+            sffn.twell_pack(s, x, wg, b, ffn.count, ffn.idx, ffn.val, ffn.ws_pack, wg_norms)
+        f1.record()
+        torch.cuda.synchronize()
+        t_fused = f0.elapsed_time(f1) / K
+        cmean = lambda a, e: float(np.mean([cv[i][a].elapsed_time(cv[i][e]) for i in range(K)]))
+        t_pre, t_conv, t_ell = cmean(0, 1), cmean(1, 2), cmean(2, 3)
+        cnt = ffn.count.to(torch.int64)
+        live_c = torch.arange(max(w.cap, 1), device="cuda")[None, None, :] < torch.clamp(cnt, max=w.cap)[:, :, None]
+        same = bool(torch.equal(tw[0], ffn.count)) and bool(torch.equal(
+            torch.where(live_c, tw[1].to(torch.int64), -1), torch.where(live_c, ffn.idx.to(torch.int64), -1)))
+        nnz_all = int(cnt.sum().item())
+        nt_ = w.d_ff // w.tile
+        z_bytes = 4.0 * w.T * w.d_ff
+        conversion = {
+            "fused_twell_pack_ms": t_fused,
+            "two_pass_ms": t_two_pass,
+            "two_pass_over_fused": t_two_pass / t_fused,
+            "gate_preact_ms": t_pre, "twell_from_preact_ms": t_conv, "ell_from_preact_ms": t_ell,
+            "z_bytes": z_bytes,
+            "twell_from_preact_gb_per_s": (z_bytes + w.T * nt_ * 2 + nnz_live_of(cnt, w.cap) * (2 + eb_)) / (t_conv * 1e-3) / 1e9,
+            "ell_from_preact_gb_per_s": (z_bytes + w.T * 2 + nnz_all * (2 + eb_)) / (t_ell * 1e-3) / 1e9,
+            "twell_matches_fused": same,
+            "ell_width": width,
+            "storage_bytes": {"live_entries": nnz_all * (2 + eb_),
+                              "twell": w.T * nt_ * 2 + w.T * nt_ * w.cap * (2 + eb_),
+                              "row_ellpack_padded_to_longest_row": w.T * 2 + w.T * width * (2 + eb_),
+                              "dense_h": w.T * w.d_ff * eb_},
+        }
+        del z, tw, ell, ws_c
+
     count = ffn.count.to(torch.int64)
     nnz_live = int(torch.clamp(count, max=w.cap).sum().item()) if w.cap > 0 else 0
     n_routed = int(ffn.n_routed.item())
@@ -366,6 +449,7 @@ def main() -> int:
                                 "p90": float(np.percentile(step_ev, 90))},
         "cold": cold,
         "torch_dense_ms": t_torch,
+        "separate_conversion": conversion,
         "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,
         "speedup_vs_dense": (t_dense / ms_step) if t_dense else None,
         "dense_tflops": (3 * gate_flop / (t_dense * 1e-3) / 1e12) if t_dense else None,

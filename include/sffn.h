@@ -70,7 +70,8 @@ typedef enum {
   SFFN_WS_HYBRID = 0,
   SFFN_WS_DENSE = 1,
   SFFN_WS_SPARSE = 2,
-  SFFN_WS_PACK = 3
+  SFFN_WS_PACK = 3,
+  SFFN_WS_CONVERT = 4
 } sffn_ws_kind;
 
 typedef struct {
@@ -169,6 +170,56 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
 int32_t dense_ffn_ref(const sffn_shape* shape, const void* x, const void* wg_t,
                       const float* b_g, const void* wu_t, const void* wd,
                       void* workspace, size_t ws_bytes, void* y, void* stream);
+
+/*
+ * Separate-conversion baseline.  The pwwt.cn article (sections 01 and 02)
+ * argues that writing the whole gate activation and converting it to a sparse
+ * format afterwards costs an extra launch, a global-memory write and read and
+ * a synchronisation, and that the classic row-wise ELLPACK (one list per row,
+ * padded to a common width; kongchang.com article, "ELLPACK" passage) fits
+ * tiled GEMMs poorly.  These three calls build that design so both claims can
+ * be measured against twell_pack.  They are not on the fused forward path.
+ * bf16 only, d_model % 32 == 0 (else SFFN_ERR_UNSUPPORTED), plus the size
+ * limits of twell_pack.
+ *
+ * gate_preact -- z[t, j] = sum_k x[t, k] * wg_t[j, k] + b_g[j], float32,
+ * row-major [T, d_ff] (T * d_ff * 4 bytes, caller-owned).  The accumulation is
+ * twell_pack's own for T > 64 (for fewer tokens twell_pack splits the sum
+ * over K; the float32 values may then differ in the last bits, the activity
+ * decision does not).  No workspace.
+ */
+int32_t gate_preact(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                    float* z, void* stream);
+
+/*
+ * twell_from_preact -- TwELL from a z written by gate_preact for the same x,
+ * wg_t and b_g: count/idx/val exactly as twell_pack defines them (activity on
+ * the exact value of z, through the same guard band and exact re-evaluation).
+ * wg_norms as for twell_pack (or NULL).  workspace: at least
+ * sffn_workspace_bytes(shape, SFFN_WS_CONVERT) bytes (row norms), no initial
+ * contents; calls sharing it must be stream-ordered.
+ */
+int32_t twell_from_preact(const sffn_shape* shape, const float* z, const void* x,
+                          const void* wg_t, const float* b_g, const float* wg_norms,
+                          uint16_t* count, uint16_t* idx, void* val, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * ell_from_preact -- classic row-wise ELLPACK of ReLU(z), z from gate_preact:
+ *   ell_count[t]     = active columns of row t (uncapped; uint16 [T])
+ *   ell_idx[t, s]    = s-th active column of the row, ascending, for
+ *                      s < min(ell_count[t], width)  (uint16 [T, width])
+ *   ell_val[t, s]    = z at that column, rounded to bf16 (bf16 [T, width])
+ * Slots past min(ell_count[t], width) are left unwritten.  The classic format
+ * pads every row to the longest one: width = max_t ell_count[t] keeps every
+ * entry.  0 <= width <= d_ff (else SFFN_ERR_ARG); ell_idx and ell_val may be
+ * NULL when width == 0.  shape->cap is not used.  Activity, wg_norms and
+ * workspace as for twell_from_preact.
+ */
+int32_t ell_from_preact(const sffn_shape* shape, int32_t width, const float* z, const void* x,
+                        const void* wg_t, const float* b_g, const float* wg_norms,
+                        uint16_t* ell_count, uint16_t* ell_idx, void* ell_val, void* workspace,
+                        size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by one call for this shape (0 if the shape is invalid). */
 size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which);

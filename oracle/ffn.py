@@ -139,6 +139,45 @@ def twell_unpack(count, idx, val, d_ff: int) -> np.ndarray:
     return h
 
 
+def ell_pack(z, width: int):
+    """Classic row-wise ELLPACK of the ReLU output: one list per row over all
+    columns, padded to a common width (the "traditional ELLPACK" that the
+    pwwt.cn article, section 01, contrasts with TwELL; value and column-index
+    arrays of the kongchang.com article's ELLPACK passage).
+
+      count[t]     number of active columns (z > 0) in row t, uncapped;
+      idx[t, s]    for s < min(count, width): the s-th active column,
+                   ascending; -1 in unused slots;
+      val[t, s]    h at that column; 0 in unused slots.
+    The classic format sets width to the longest row, max_t count[t].
+    """
+    z = _f64(z)
+    T, d_ff = z.shape
+    count = np.zeros(T, dtype=np.int64)
+    idx = np.full((T, width), -1, dtype=np.int64)
+    val = np.zeros((T, width), dtype=np.float64)
+    for t in range(T):
+        cols = np.nonzero(z[t] > 0.0)[0]
+        count[t] = len(cols)
+        keep = cols[:width]
+        idx[t, :len(keep)] = keep
+        val[t, :len(keep)] = z[t, keep]
+    return count, idx, val
+
+
+def ell_unpack(count, idx, val, d_ff: int) -> np.ndarray:
+    """Dense [T, d_ff] matrix holding the live row-ELLPACK entries."""
+    count = np.asarray(count)
+    idx = np.asarray(idx)
+    val = _f64(val)
+    T, width = idx.shape
+    h = np.zeros((T, d_ff), dtype=np.float64)
+    live = np.arange(width)[None, :] < np.minimum(count, width)[:, None]
+    rr, ss = np.nonzero(live)
+    h[rr, idx[rr, ss]] = val[rr, ss]
+    return h
+
+
 def route(count, cap: int) -> np.ndarray:
     """Rows sent to the dense path: any tile with more active columns than the
     capacity (hybrid routing, pwwt.cn article section 03).  Ascending."""

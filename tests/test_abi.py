@@ -124,3 +124,30 @@ def test_strerror(sffn):
     for code in (0, -1, -2, -3, -4, 5):
         assert isinstance(sffn.strerror(code), str) and sffn.strerror(code)
     assert sffn.strerror(-3) != sffn.strerror(-1)
+
+
+def test_conversion_baseline_errors(sffn):
+    lib = sffn._lib
+    s = _shape(sffn)
+    ws_n = sffn.workspace_bytes(s, sffn.WS_CONVERT)
+    assert ws_n >= (64 + 512) * 4
+    sf = _shape(sffn, dtype=sffn.SFFN_F32)
+    assert lib.gate_preact(ctypes.byref(sf), P, P, None, P, None) == -2
+    assert lib.gate_preact(ctypes.byref(_shape(sffn, d_model=264)), P, P, None, P, None) == -2
+    assert lib.gate_preact(ctypes.byref(s), P, P, None, None, None) == -1
+    assert lib.twell_from_preact(ctypes.byref(s), P, P, P, None, None, P, P, P, WS, ws_n - 1,
+                                 None) == -3
+    assert lib.twell_from_preact(ctypes.byref(s), None, P, P, None, None, P, P, P, WS, ws_n,
+                                 None) == -1
+    assert lib.ell_from_preact(ctypes.byref(s), -1, P, P, P, None, None, P, P, P, WS, ws_n,
+                               None) == -1
+    assert lib.ell_from_preact(ctypes.byref(s), 513, P, P, P, None, None, P, P, P, WS, ws_n,
+                               None) == -1
+    assert lib.ell_from_preact(ctypes.byref(s), 4, P, P, P, None, None, P, None, P, WS, ws_n,
+                               None) == -1
+    assert lib.ell_from_preact(ctypes.byref(sf), 4, P, P, P, None, None, P, P, P, WS, ws_n,
+                               None) == -2
+    s0 = _shape(sffn, T=0)
+    assert lib.ell_from_preact(ctypes.byref(s0), 0, None, None, None, None, None, None, None,
+                               None, None, 0, None) == 0
+

@@ -44,11 +44,13 @@ def brute_force(x, wg, b, wu, wd, tile, cap):
                 if z[t][j] > 0:
                     count[t][kt] += 1
                     lists[t][kt].append(j)
+    row_lists = [[j for j in range(d_ff) if z[t][j] > 0] for t in range(T)]
     routed = [t for t in range(T) if any(c > cap for c in count[t])]
     u = [[sum(X[t][k] * U_[j][k] for k in range(K)) for j in range(d_ff)] for t in range(T)]
     y = [[sum((z[t][j] if z[t][j] > 0 else 0) * u[t][j] * D[j][c] for j in range(d_ff))
           for c in range(dm)] for t in range(T)]
-    return {"z": z, "count": count, "lists": lists, "routed": routed, "y": y}
+    return {"z": z, "count": count, "lists": lists, "row_lists": row_lists, "routed": routed,
+            "y": y}
 
 
 def _bf16(a):
@@ -110,6 +112,21 @@ def check_against_brute(x, wg, b, wu, wd, tile, cap):
     Hr = oracle.relu(out["z"])
     keep = np.setdiff1d(np.arange(T), out["routed"])
     assert np.array_equal(H[keep], Hr[keep])
+    # row-wise ELLPACK: row counts, ascending live columns, values equal h;
+    # the widest row fixes the classic width, which makes it lossless
+    longest = max(len(r) for r in ref["row_lists"])
+    for width in sorted({0, 1, 3, longest, longest + 2}):
+        ec, ei, ev = oracle.ell_pack(out["z"], width)
+        assert ei.shape == (T, width)
+        for t in range(T):
+            assert ec[t] == len(ref["row_lists"][t])
+            live = ref["row_lists"][t][:width]
+            assert list(ei[t, :len(live)]) == live
+            assert all(v == -1 for v in ei[t, len(live):])
+            for s, j in enumerate(live):
+                assert ev[t, s] == out["z"][t, j]
+        if width >= longest:
+            assert np.array_equal(oracle.ell_unpack(ec, ei, ev, d_ff), oracle.relu(out["z"]))
     # dense and sparse y against the exact result
     yex = np.array([[float(v) for v in row] for row in ref["y"]])
     scale = max(1e-300, float(np.abs(yex).max()))
@@ -288,6 +305,33 @@ def _mut_pack_descending(orig):
     return f
 
 
+def _mut_ell_count_capped(orig):
+    def f(z, width):
+        c, i, v = orig(z, width)
+        return np.minimum(c, width), i, v
+    return f
+
+
+def _mut_ell_zero_active(orig):
+    return lambda z, width: orig(np.where(np.asarray(z) == 0, 1e-300, z), width)
+
+
+def _mut_ell_no_running_slot(orig):
+    # every 4-column tile writes its list from slot 0 (a converter that forgets
+    # the running count across tiles): later tiles overwrite earlier ones
+    def f(z, width):
+        z = np.asarray(z, float)
+        c, i, v = orig(z, width)
+        i, v = np.full_like(i, -1), np.zeros_like(v)
+        for t in range(z.shape[0]):
+            for lo in range(0, z.shape[1], 4):
+                cols = [lo + j for j in np.nonzero(z[t, lo:lo + 4] > 0)[0]][:width]
+                i[t, :len(cols)] = cols
+                v[t, :len(cols)] = z[t, cols]
+        return c, i, v
+    return f
+
+
 def _mut_route_ge(orig):
     return lambda count, cap: np.nonzero(np.asarray(count).max(1) >= cap)[0]
 
@@ -323,6 +367,9 @@ MUTATIONS = {
     "pack_local_index": ("twell_pack", _mut_pack_local_index),
     "pack_descending": ("twell_pack", _mut_pack_descending),
     "route_ge": ("route", _mut_route_ge),
+    "ell_count_capped": ("ell_pack", _mut_ell_count_capped),
+    "ell_zero_active": ("ell_pack", _mut_ell_zero_active),
+    "ell_no_running_slot": ("ell_pack", _mut_ell_no_running_slot),
     "gate_naive_sum": ("gate_preact", _mut_gate_naive),
     "gate_bias_sign": ("gate_preact", _mut_gate_bias_sign),
     "up_from_gate": ("ffn_sparse", _mut_up_from_gate),
