@@ -88,20 +88,21 @@ def measured_traffic(workload: str):
 
 
 def gpu_clocks():
-    """Current GPU clocks as reported by rocm-smi (None if it is unavailable)."""
-    import shutil
-    import subprocess
-    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
-    if exe is None:
-        return None
-    try:
-        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout)
-        card = next(iter(d.values()))
-        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()
-                or "fclk" in k.lower()}
-    except Exception:  # noqa: BLE001 - the clocks are context, never a reason to fail
-        return None
+    """Current DPM clock levels of the GPU from sysfs (the entries marked '*'
+    in pp_dpm_sclk / pp_dpm_mclk / pp_dpm_fclk); None where unavailable.  Read
+    as plain files: no helper program is started from this GPU process."""
+    import glob
+    out = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_*clk")):
+        try:
+            with open(path) as f:
+                cur = [ln.split(":", 1)[1].strip(" *\n") for ln in f if ln.rstrip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            card = path.split("/")[4]
+            out[f"{card}.{os.path.basename(path)[7:]}"] = cur[0]
+    return out or None
 
 
 def cpu_baseline(inp, rows: int) -> dict:
