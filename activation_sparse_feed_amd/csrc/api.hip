@@ -63,6 +63,12 @@ size_t hybrid_ws(const sffn_shape* s) {
   return n;
 }
 
+// twell_pack_l1: the pack workspace, then the per-(row, tile) L1 sums and the
+// reduction's block sums.
+size_t pack_l1_ws(const sffn_shape* s) {
+  return pack_ws(s) + align256((size_t)s->T * (s->d_ff / 128) * 4) + align256(l1_ws_bytes());
+}
+
 size_t convert_ws(const sffn_shape* s) {
   return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4);
 }
@@ -92,19 +98,12 @@ int32_t twell_weight_norms(const sffn_shape* shape, const void* wg_t, float* wg_
                                      nullptr, shape->d_model, (hipStream_t)stream));
 }
 
-int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
-                   const float* wg_norms, uint16_t* count, uint16_t* idx, void* val,
-                   void* workspace, size_t ws_bytes, void* stream) {
-  int32_t st = check_shape(shape);
-  if (st != SFFN_OK) return st;
-  if (shape->T == 0) return SFFN_OK;
-  if (!ptrs_ok({x, wg_t, count}) || (b_g && !aligned16(b_g)) || (wg_norms && !aligned16(wg_norms)))
-    return SFFN_ERR_ARG;
-  if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
-  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < pack_ws(shape))
-    return SFFN_ERR_WORKSPACE;
-  if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
+namespace {
+
+// twell_pack, with the L1 regulariser's per-(row, tile) sums when l1_part is set.
+int32_t pack_impl(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                  const float* wg_norms, uint16_t* count, uint16_t* idx, void* val,
+                  void* workspace, float* l1_part, size_t* l1_n, hipStream_t s) {
   float* xn = (float*)workspace;
   float* wn = (float*)((char*)workspace + align256((size_t)shape->T * 4));
   void* gws = (char*)wn + align256((size_t)shape->d_ff * 4);
@@ -114,7 +113,58 @@ int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t, con
   if (e != hipSuccess) return SFFN_ERR_HIP;
   return hip_status(launch_gate_twell(shape->dtype, x, wg_t, b_g, xn, wg_norms ? wg_norms : wn,
                                       count, idx, val, shape->T, shape->d_model, shape->d_ff,
-                                      shape->cap, guard_band(shape), gws, s));
+                                      shape->cap, guard_band(shape), gws, l1_part, l1_n, s));
+}
+
+int32_t check_pack(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                   const float* wg_norms, uint16_t* count, uint16_t* idx, void* val) {
+  if (!ptrs_ok({x, wg_t, count}) || (b_g && !aligned16(b_g)) || (wg_norms && !aligned16(wg_norms)))
+    return SFFN_ERR_ARG;
+  if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
+  return SFFN_OK;
+}
+
+}  // namespace
+
+int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                   const float* wg_norms, uint16_t* count, uint16_t* idx, void* val,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  st = check_pack(shape, x, wg_t, b_g, wg_norms, count, idx, val);
+  if (st != SFFN_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < pack_ws(shape))
+    return SFFN_ERR_WORKSPACE;
+  if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
+  return pack_impl(shape, x, wg_t, b_g, wg_norms, count, idx, val, workspace, nullptr, nullptr,
+                   (hipStream_t)stream);
+}
+
+int32_t twell_pack_l1(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                      const float* wg_norms, uint16_t* count, uint16_t* idx, void* val,
+                      float lambda, float* l1_value, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (!ptrs_ok({l1_value}) || !(lambda == lambda)) return SFFN_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (shape->T == 0) {
+    return hip_status(launch_l1_zero(l1_value, s));  // the mean over no tokens: 0
+  }
+  st = check_pack(shape, x, wg_t, b_g, wg_norms, count, idx, val);
+  if (st != SFFN_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < pack_l1_ws(shape))
+    return SFFN_ERR_WORKSPACE;
+  if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
+  float* part = (float*)((char*)workspace + pack_ws(shape));
+  const size_t n = (size_t)shape->T * (shape->d_ff / 128);
+  void* red = (char*)part + align256(n * 4);
+  size_t parts = n;
+  st = pack_impl(shape, x, wg_t, b_g, wg_norms, count, idx, val, workspace, part, &parts, s);
+  if (st != SFFN_OK) return st;
+  return hip_status(launch_l1_reduce(part, parts, (double)lambda / (double)shape->T, red, l1_value,
+                                     s));
 }
 
 int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t, const void* wd,
@@ -276,6 +326,7 @@ size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
                                     shape->cap);
     case SFFN_WS_PACK: return pack_ws(shape);
     case SFFN_WS_CONVERT: return convert_ws(shape);
+    case SFFN_WS_PACK_L1: return pack_l1_ws(shape);
     default: return 0;
   }
 }

@@ -23,7 +23,15 @@ bool gate_needs_xnorm(int dtype, int T, int K);
 hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const float* b_g,
                              const float* xnorm, const float* wnorm, uint16_t* count,
                              uint16_t* idx, void* val, int T, int K, int N, int cap,
-                             GuardBand gb, void* gate_ws, hipStream_t stream);
+                             GuardBand gb, void* gate_ws, float* l1_part, size_t* l1_n,
+                             hipStream_t stream);
+
+// L1 regulariser value: *out = scale * (sum of the n per-(row, tile) sums in
+// part), summed in float64 in a fixed order (two launches; ws: l1_ws_bytes()).
+size_t l1_ws_bytes();
+hipError_t launch_l1_zero(float* out, hipStream_t stream);
+hipError_t launch_l1_reduce(const float* part, size_t n, double scale, void* ws, float* out,
+                            hipStream_t stream);
 
 // Separate-conversion baseline (bf16, K a multiple of 32): the gate GEMM
 // storing the float32 pre-activation z [T, N] (bias added), and converters

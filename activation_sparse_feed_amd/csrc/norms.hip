@@ -48,6 +48,53 @@ __global__ __launch_bounds__(256) void row_norms_kernel(const T* __restrict__ a,
   }
 }
 
+// L1 regulariser reduction: block b sums its contiguous slice of the
+// per-(row, tile) sums in float64 (each thread a fixed stride, then a fixed
+// butterfly and wave order); the final launch sums the block results the same
+// way.  Deterministic.
+constexpr int kL1Blocks = 256;
+
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+  v = wave_sum(v);
+  const int w = (int)(threadIdx.x >> 6);
+  if (lane_id() == 0) red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
+  return t;
+}
+
+__global__ __launch_bounds__(256) void l1_partial_sums(const float* __restrict__ part, size_t n,
+                                                       double* __restrict__ blk) {
+  __shared__ double red[4];
+  const size_t chunk = (n + kL1Blocks - 1) / kL1Blocks;
+  const size_t lo = (size_t)blockIdx.x * chunk, hi = min(n, lo + chunk);
+  double s = 0.0;
+  for (size_t i = lo + threadIdx.x; i < hi; i += blockDim.x) s += (double)part[i];
+  const double t = block_sum_f64(s, red);
+  if (threadIdx.x == 0) blk[blockIdx.x] = t;
+}
+
+// One workgroup for up to kL1Single sums: each thread a fixed stride, then the
+// same fixed butterfly and wave order.
+constexpr size_t kL1Single = 65536;
+
+__global__ __launch_bounds__(1024) void l1_single(const float* __restrict__ part, size_t n,
+                                                  double scale, float* __restrict__ out) {
+  __shared__ double red[16];
+  double s = 0.0;
+  for (size_t i = threadIdx.x; i < n; i += blockDim.x) s += (double)part[i];
+  const double t = block_sum_f64(s, red);
+  if (threadIdx.x == 0) *out = (float)(t * scale);
+}
+
+__global__ __launch_bounds__(256) void l1_final(const double* __restrict__ blk, double scale,
+                                                float* __restrict__ out) {
+  __shared__ double red[4];
+  const double t = block_sum_f64(threadIdx.x < kL1Blocks ? blk[threadIdx.x] : 0.0, red);
+  if (threadIdx.x == 0) *out = (float)(t * scale);
+}
+
 }  // namespace
 
 hipError_t launch_row_norms(int dtype, const void* a, int rows_a, float* out_a, const void* b,
@@ -62,6 +109,30 @@ hipError_t launch_row_norms(int dtype, const void* a, int rows_a, float* out_a, 
     hipLaunchKernelGGL(row_norms_kernel<float>, grid, dim3(256), 0, stream, (const float*)a,
                        rows_a, out_a, (const float*)b, rows_b, out_b, K);
   }
+  return hipGetLastError();
+}
+
+size_t l1_ws_bytes() { return (size_t)kL1Blocks * sizeof(double); }
+
+namespace {
+__global__ void l1_set_zero(float* out) { *out = 0.f; }
+}  // namespace
+
+hipError_t launch_l1_zero(float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(l1_set_zero, dim3(1), dim3(1), 0, stream, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_l1_reduce(const float* part, size_t n, double scale, void* ws, float* out,
+                            hipStream_t stream) {
+  if (n <= kL1Single) {
+    hipLaunchKernelGGL(l1_single, dim3(1), dim3(1024), 0, stream, part, n, scale, out);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(l1_partial_sums, dim3(kL1Blocks), dim3(256), 0, stream, part, n, (double*)ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(l1_final, dim3(1), dim3(256), 0, stream, (const double*)ws, scale, out);
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ struct GateArgs {
   const float* wnorm;  // ||wg_t[j]||, [N]
   int T, K, N, cap;
   GuardBand gb;
+  float* l1_part;  // [T, n_tiles] sums of ReLU(z) over each (row, tile), or null
 };
 
 // Copy the row norms of a tile into LDS (rows past T read as 0).
@@ -92,6 +93,10 @@ __device__ __forceinline__ void emit_row(const GateArgs& a, const RowCtx& c, int
     }
   }
   if (lane == 0) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)(c0 + __popcll(m1m));
+  if (a.l1_part) {  // L1 regulariser: the row's ReLU sum over this tile, fixed order
+    const float s = wave_sum((act0 ? z0 : 0.f) + (act1 ? z1 : 0.f));
+    if (lane == 0) a.l1_part[(size_t)t * c.nt + c.kt] = s;
+  }
 }
 
 // bias_lds (optional): the tile's 128 bias values already staged in LDS.

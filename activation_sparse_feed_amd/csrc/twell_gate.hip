@@ -89,13 +89,14 @@ struct AccEpi {
   float bias[GateGemm::FN], nw[GateGemm::FN];
   const float* rn_a;
   uint32_t* exact_lds;  // this wave's exact-stage area
+  float l1;             // L1 regulariser: this lane's ReLU sum over its rows and columns
 };
 
 // One accumulator row group (fm, r): 4 rows of the wave, all 128 columns of
 // its TwELL tile.  Template indices keep every accumulator access static (no
 // spill of the accumulator array to scratch).
 template <int FM, int R>
-__device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, const AccEpi& c) {
+__device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, AccEpi& c) {
   constexpr int FN = GateGemm::FN;
   const int row = c.wm * GateGemm::WM + FM * 16 + 4 * c.gi + R;
   const int t = c.m0 + row;
@@ -146,11 +147,23 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, const 
     running += __builtin_popcount(seg);
   }
   if (c.li == 0 && valid) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)running;
+  if (a.l1_part) {  // L1 regulariser, fixed order
+    float s = 0.f;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) s += act[fn] ? v[fn] : 0.f;
+    if constexpr (GateGemm::BN == kTile) {
+      if (valid) c.l1 += s;  // per lane over its rows; one value per workgroup after the walk
+    } else {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 16);
+      if (c.li == 0 && valid) a.l1_part[(size_t)t * c.nt + c.kt] = s;
+    }
+  }
 }
 
 template <int FM, int R>
 struct EpiLoop {
-  __device__ static __forceinline__ void run(const GateArgs& a, GateGemm& g, const AccEpi& c) {
+  __device__ static __forceinline__ void run(const GateArgs& a, GateGemm& g, AccEpi& c) {
     epi_group<FM, R>(a, g, c);
     if constexpr (R + 1 < 4) EpiLoop<FM, R + 1>::run(a, g, c);
     else if constexpr (FM + 1 < GateGemm::FM) EpiLoop<FM + 1, 0>::run(a, g, c);
@@ -196,6 +209,7 @@ __global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twel
   c.li = c.lane & 15;
   c.cw = 0.f;
   c.cb = 0.f;
+  c.l1 = 0.f;
 #pragma unroll
   for (int fn = 0; fn < G::FN; ++fn) {
     const int col = fn * 16 + c.li;
@@ -210,6 +224,20 @@ __global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twel
     c.cb = fmaxf(c.cb, __shfl_xor(c.cb, o, kWave));
   }
   EpiLoop<0, 0>::run(a, g, c);
+  if constexpr (G::BN == kTile) {
+    if (a.l1_part) {  // L1 regulariser: the workgroup's sum, fixed order, one store
+      float* red = (float*)(lds + kExactOff + G::NWAVES * kExactLdsWords * 4);
+      static_assert(G::LDS_BYTES >= kExactOff + G::NWAVES * (kExactLdsWords + 1) * 4, "fits");
+      const float s = wave_sum_uniform(c.l1);
+      if (c.lane == 0) red[w] = s;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float t = 0.f;
+        for (int i = 0; i < G::NWAVES; ++i) t += red[i];
+        a.l1_part[blockIdx.x] = t;
+      }
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void gate_twell_f32(GateArgs a) {
@@ -557,9 +585,11 @@ bool gate_needs_xnorm(int dtype, int T, int K) { return !use_skinny(dtype, T, K)
 hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const float* b_g,
                              const float* xnorm, const float* wnorm, uint16_t* count,
                              uint16_t* idx, void* val, int T, int K, int N, int cap,
-                             GuardBand gb, void* gate_ws, hipStream_t stream) {
-  GateArgs a{x, wg_t, b_g, count, idx, val, xnorm, wnorm, T, K, N, cap, gb};
+                             GuardBand gb, void* gate_ws, float* l1_part, size_t* l1_n,
+                             hipStream_t stream) {
+  GateArgs a{x, wg_t, b_g, count, idx, val, xnorm, wnorm, T, K, N, cap, gb, l1_part};
   const int nt = N / kTile;
+  if (l1_n) *l1_n = (size_t)T * nt;  // one sum per (row, tile), except the 256-row kernel
   if (use_skinny(dtype, T, K)) {
     // Guard band for this summation order: the MFMA steps of a split (at most
     // kSkinnySteps per wave and two adds across the waves for the partial
@@ -585,6 +615,7 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
     const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
                              ((N + GateGemm::BN - 1) / GateGemm::BN)));
     hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(64 * GateGemm::NWAVES), 0, stream, a);
+    if (l1_n && GateGemm::BN == kTile) *l1_n = g2.x;  // one sum per workgroup
   } else if (dtype == 1) {
     hipLaunchKernelGGL(gate_twell_bf16, dim3((unsigned)(((T + 127) / 128) * nt)), dim3(256), 0,
                        stream, a);

@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libsffn.so")
 
 SFFN_OK, SFFN_ERR_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ERR_HIP = 0, -1, -2, -3, -4
 SFFN_F32, SFFN_BF16 = 0, 1
-WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK, WS_CONVERT = 0, 1, 2, 3, 4
+WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK, WS_CONVERT, WS_PACK_L1 = 0, 1, 2, 3, 4, 5
 TILE = 128
 
-EXPORTED = ("twell_weight_norms", "twell_pack", "sparse_ffn_fwd", "hybrid_route",
+EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
             "dense_ffn_ref", "gate_preact", "twell_from_preact", "ell_from_preact",
             "sffn_workspace_bytes", "sffn_strerror")
 
@@ -46,13 +46,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sp = ctypes.POINTER(Shape)
     lib.twell_weight_norms.argtypes = [sp, vp, vp, vp]
     lib.twell_pack.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.twell_pack_l1.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.sparse_ffn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.gate_preact.argtypes = [sp, vp, vp, vp, vp, vp]
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for fn in ("twell_weight_norms", "twell_pack", "sparse_ffn_fwd", "hybrid_route",
+    for fn in ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
                "dense_ffn_ref", "gate_preact", "twell_from_preact", "ell_from_preact"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
@@ -142,6 +143,16 @@ def twell_pack(shape: Shape, x, wg_t, b_g, count, idx, val, workspace, wg_norms=
     _check("twell_pack", _lib.twell_pack(ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g),
                                          _ptr(wg_norms), _ptr(count), _ptr(idx), _ptr(val),
                                          _ptr(workspace), ws_n, _stream(stream)))
+
+
+def twell_pack_l1(shape: Shape, x, wg_t, b_g, count, idx, val, lam: float, l1_value, workspace,
+                  wg_norms=None, stream=None) -> None:
+    if l1_value.dtype != torch.float32 or l1_value.numel() < 1:
+        raise ValueError("l1_value must be a float32 device tensor with one element")
+    ws_n = workspace.numel() * workspace.element_size()
+    _check("twell_pack_l1", _lib.twell_pack_l1(
+        ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wg_norms), _ptr(count),
+        _ptr(idx), _ptr(val), float(lam), _ptr(l1_value), _ptr(workspace), ws_n, _stream(stream)))
 
 
 def sparse_ffn_fwd(shape: Shape, x, wu_t, wd, count, idx, val, y, workspace=None,

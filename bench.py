@@ -40,6 +40,8 @@ def parse_args():
     p.add_argument("--cpu-rows", type=int, default=None,
                    help="rows of the CPU oracle sample (default: whole batch, at most 4096)")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-l1", action="store_true",
+                   help="skip timing twell_pack_l1 (the L1 regulariser fused into the gate epilogue)")
     p.add_argument("--no-conversion", action="store_true",
                    help="skip the separate-conversion baseline (gate GEMM storing z, then "
                         "standalone TwELL and row-ELLPACK conversions)")
@@ -388,6 +390,31 @@ def main() -> int:
         }
         del z, tw, ell, ws_c
 
+    # ---- the L1 regulariser fused into the gate epilogue: twell_pack_l1 against
+    # twell_pack, K calls each back to back
+    l1 = None
+    if not args.no_l1:
+        l1_out = torch.empty(1, dtype=torch.float32, device="cuda")
+        ws_l1 = sffn.alloc_workspace(s, sffn.WS_PACK_L1)
+        tw1 = sffn.alloc_twell(s)
+        lam = 1.0
+        for _ in range(2):
+            sffn.twell_pack_l1(s, x, wg, b, *tw1, lam, l1_out, ws_l1, wg_norms)
+        l0, l1e, l2e = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
+        torch.cuda.synchronize()
+        l0.record()
+        for _ in range(K):
+            sffn.twell_pack_l1(s, x, wg, b, *tw1, lam, l1_out, ws_l1, wg_norms)
+        l1e.record()
+        for _ in range(K):
+            sffn.twell_pack(s, x, wg, b, ffn.count, ffn.idx, ffn.val, ffn.ws_pack, wg_norms)
+        l2e.record()
+        torch.cuda.synchronize()
+        t_l1, t_p = l0.elapsed_time(l1e) / K, l1e.elapsed_time(l2e) / K
+        l1 = {"lambda": lam, "value": float(l1_out.item()), "twell_pack_l1_ms": t_l1,
+              "twell_pack_ms": t_p, "overhead": t_l1 / t_p - 1.0}
+        del ws_l1, tw1
+
     count = ffn.count.to(torch.int64)
     nnz_live = int(torch.clamp(count, max=w.cap).sum().item()) if w.cap > 0 else 0
     n_routed = int(ffn.n_routed.item())
@@ -451,6 +478,7 @@ def main() -> int:
         "cold": cold,
         "torch_dense_ms": t_torch,
         "separate_conversion": conversion,
+        "l1_regulariser": l1,
         "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,
         "speedup_vs_dense": (t_dense / ms_step) if t_dense else None,
         "dense_tflops": (3 * gate_flop / (t_dense * 1e-3) / 1e12) if t_dense else None,

@@ -71,7 +71,8 @@ typedef enum {
   SFFN_WS_DENSE = 1,
   SFFN_WS_SPARSE = 2,
   SFFN_WS_PACK = 3,
-  SFFN_WS_CONVERT = 4
+  SFFN_WS_CONVERT = 4,
+  SFFN_WS_PACK_L1 = 5
 } sffn_ws_kind;
 
 typedef struct {
@@ -119,6 +120,30 @@ int32_t twell_weight_norms(const sffn_shape* shape, const void* wg_t, float* wg_
 int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t,
                    const float* b_g, const float* wg_norms, uint16_t* count, uint16_t* idx,
                    void* val, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * twell_pack_l1 -- twell_pack plus the L1 activation regulariser that drives
+ * the sparsity in training (pwwt.cn article, section 04: a light L1 penalty on
+ * the FFN activations; the besthub.dev page), summed in the same gate
+ * epilogue from the same z as the TwELL lists:
+ *
+ *   *l1_value = lambda / T * sum_t sum_j ReLU(z[t, j])      (float32, device)
+ *
+ * Every active entry counts, also those past the capacity.  The gate kernels
+ * sum in float32 in a fixed order (the 256-row kernel over its whole tile of
+ * up to 256 x 128 entries, at most about 30 additions deep; the others per
+ * row and tile), and those partial sums are added in float64 in a fixed
+ * order, so the value is deterministic.  The
+ * gradient of the term with respect to z is lambda / T on exactly the active
+ * entries (the uncapped TwELL support) and 0 elsewhere, so it needs no output
+ * of its own.  T == 0 writes 0.  Outputs and arguments otherwise as
+ * twell_pack; lambda must not be NaN (else SFFN_ERR_ARG); workspace: at least
+ * sffn_workspace_bytes(shape, SFFN_WS_PACK_L1) bytes, no initial contents.
+ */
+int32_t twell_pack_l1(const sffn_shape* shape, const void* x, const void* wg_t,
+                      const float* b_g, const float* wg_norms, uint16_t* count, uint16_t* idx,
+                      void* val, float lambda, float* l1_value, void* workspace, size_t ws_bytes,
+                      void* stream);
 
 /*
  * sparse_ffn_fwd -- fused up(.)gate -> down over the TwELL nonzeros (pwwt.cn

@@ -178,6 +178,20 @@ def ell_unpack(count, idx, val, d_ff: int) -> np.ndarray:
     return h
 
 
+def l1_term(z, lam: float) -> float:
+    """L1 activation regulariser of the sparse training recipe (pwwt.cn article,
+    section 04; besthub.dev page): lam times the mean over tokens of the summed
+    ReLU activations, lam / T * sum_t sum_j h[t, j].  The formula itself was lost
+    from the pages; this is the plainest reading of an L1 penalty on the FFN
+    activations averaged over tokens.  Its gradient with respect to z is lam / T
+    wherever z > 0.  No tokens: 0."""
+    z = _f64(z)
+    T = z.shape[0]
+    if T == 0:
+        return 0.0
+    return float(lam) * math.fsum(z[z > 0.0].tolist()) / T
+
+
 def route(count, cap: int) -> np.ndarray:
     """Rows sent to the dense path: any tile with more active columns than the
     capacity (hybrid routing, pwwt.cn article section 03).  Ascending."""

@@ -151,3 +151,19 @@ def test_conversion_baseline_errors(sffn):
     assert lib.ell_from_preact(ctypes.byref(s0), 0, None, None, None, None, None, None, None,
                                None, None, 0, None) == 0
 
+
+def test_pack_l1_errors(sffn):
+    lib = sffn._lib
+    s = _shape(sffn)
+    need = sffn.workspace_bytes(s, sffn.WS_PACK_L1)
+    assert need > sffn.workspace_bytes(s, sffn.WS_PACK) + 64 * 4 * 4
+    nan = float("nan")
+    assert lib.twell_pack_l1(ctypes.byref(s), P, P, None, None, P, P, P, 1.0, P, WS, need - 1,
+                             None) == -3
+    assert lib.twell_pack_l1(ctypes.byref(s), P, P, None, None, P, P, P, 1.0, None, WS, need,
+                             None) == -1
+    assert lib.twell_pack_l1(ctypes.byref(s), P, P, None, None, P, P, P, nan, P, WS, need,
+                             None) == -1
+    assert lib.twell_pack_l1(ctypes.byref(_shape(sffn, tile=64)), P, P, None, None, P, P, P, 1.0,
+                             P, WS, need, None) == -2
+

@@ -127,6 +127,11 @@ def check_against_brute(x, wg, b, wu, wd, tile, cap):
                 assert ev[t, s] == out["z"][t, j]
         if width >= longest:
             assert np.array_equal(oracle.ell_unpack(ec, ei, ev, d_ff), oracle.relu(out["z"]))
+    # L1 regulariser: lam / T times the exact sum of the positive z
+    for lam in (1.0, 0.25):
+        exact = Fr(lam) * sum((v for row in ref["z"] for v in row if v > 0), Fr(0)) / T
+        got = oracle.l1_term(out["z"], lam)
+        assert abs(Fr(got) - exact) <= Fr(2.0 ** -50) * (abs(exact) + 1)
     # dense and sparse y against the exact result
     yex = np.array([[float(v) for v in row] for row in ref["y"]])
     scale = max(1e-300, float(np.abs(yex).max()))
@@ -332,6 +337,14 @@ def _mut_ell_no_running_slot(orig):
     return f
 
 
+def _mut_l1_abs(orig):
+    return lambda z, lam: float(lam) * float(np.abs(np.asarray(z, float)).sum()) / max(1, len(z))
+
+
+def _mut_l1_no_mean(orig):
+    return lambda z, lam: orig(z, lam) * max(1, len(z))
+
+
 def _mut_route_ge(orig):
     return lambda count, cap: np.nonzero(np.asarray(count).max(1) >= cap)[0]
 
@@ -367,6 +380,8 @@ MUTATIONS = {
     "pack_local_index": ("twell_pack", _mut_pack_local_index),
     "pack_descending": ("twell_pack", _mut_pack_descending),
     "route_ge": ("route", _mut_route_ge),
+    "l1_sums_abs": ("l1_term", _mut_l1_abs),
+    "l1_no_token_mean": ("l1_term", _mut_l1_no_mean),
     "ell_count_capped": ("ell_pack", _mut_ell_count_capped),
     "ell_zero_active": ("ell_pack", _mut_ell_zero_active),
     "ell_no_running_slot": ("ell_pack", _mut_ell_no_running_slot),
@@ -392,3 +407,28 @@ def test_planted_mistake_is_caught(name, monkeypatch):
             caught = True
             break
     assert caught, f"planted mistake {name} was not detected"
+
+
+# ------------------------------------------------------------ L1 regulariser
+def test_l1_closed_form_when_every_entry_is_active():
+    """With a bias large enough that every z > 0, sum_tj z = sum_t x_t . (sum_j w_j)
+    + T sum_j b_j: an independent closed form of the L1 sum."""
+    rng = np.random.default_rng(7)
+    T, K, d_ff = 5, 16, 12
+    x = _bf16(rng.standard_normal((T, K)))
+    w = _bf16(rng.standard_normal((d_ff, K)) / 4)
+    b = np.full(d_ff, 64.0)
+    z = oracle.gate_preact(x, w, b)
+    assert (z > 0).all()
+    closed = (sum((Fr(float(x[t, k])) * sum(Fr(float(w[j, k])) for j in range(d_ff))
+                   for t in range(T) for k in range(K)), Fr(0)) + T * Fr(float(b.sum())))
+    got = oracle.l1_term(z, 0.5)
+    assert abs(Fr(got) - Fr(1, 2) * closed / T) <= Fr(2.0 ** -48) * abs(closed)
+
+
+def test_l1_special_cases():
+    z = np.array([[-1.0, 0.0, -3.0], [0.0, -0.5, -2.0]])
+    assert oracle.l1_term(z, 3.0) == 0.0          # nothing active (z = 0 is inactive)
+    assert oracle.l1_term(np.zeros((0, 4)), 1.0) == 0.0
+    assert oracle.l1_term(np.array([[2.0, -1.0], [1.0, 4.0]]), 1.0) == 3.5
+
