@@ -69,6 +69,11 @@ size_t pack_l1_ws(const sffn_shape* s) {
   return pack_ws(s) + align256((size_t)s->T * (s->d_ff / 128) * 4) + align256(l1_ws_bytes());
 }
 
+size_t backward_ws(const sffn_shape* s) {
+  return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4) +
+         backward_workspace_bytes(s->T, s->d_ff, s->d_model, s->cap);
+}
+
 size_t convert_ws(const sffn_shape* s) {
   return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4);
 }
@@ -247,7 +252,7 @@ int32_t gate_preact(const sffn_shape* shape, const void* x, const void* wg_t, co
   if (!preact_supported(shape->dtype, shape->d_model) || act_bytes_too_large(shape))
     return SFFN_ERR_UNSUPPORTED;
   return hip_status(launch_gate_preact(x, wg_t, b_g, z, shape->T, shape->d_model, shape->d_ff,
-                                       (hipStream_t)stream));
+                                       nullptr, nullptr, (hipStream_t)stream));
 }
 
 namespace {
@@ -313,7 +318,37 @@ int32_t ell_from_preact(const sffn_shape* shape, int32_t width, const float* z, 
   if (st != SFFN_OK) return st;
   return hip_status(launch_ell_convert(z, x, wg_t, b_g, xn, wn, width, ell_count, ell_idx,
                                        ell_val, shape->T, shape->d_model, shape->d_ff,
-                                       guard_band(shape), s));
+                                       guard_band(shape), nullptr, nullptr, s));
+}
+
+int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                       const void* wu_t, const void* wd, const float* wg_norms,
+                       const uint16_t* count, const uint16_t* idx, const void* val,
+                       const int32_t* routed, const int32_t* n_routed, const void* gy, void* gx,
+                       float* gwg_t, float* gwu_t, float* gwd, float* gb, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({x, wg_t, wu_t, wd, count, routed, n_routed, gy, gx, gwg_t, gwu_t, gwd}) ||
+      (b_g && !aligned16(b_g)) || (wg_norms && !aligned16(wg_norms)) || (gb && !aligned16(gb)))
+    return SFFN_ERR_ARG;
+  if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < backward_ws(shape))
+    return SFFN_ERR_WORKSPACE;
+  if (!backward_supported(shape->dtype, shape->d_model) || act_bytes_too_large(shape))
+    return SFFN_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  float* xn = (float*)workspace;
+  float* wbuf = (float*)((char*)workspace + align256((size_t)shape->T * 4));
+  void* bws = (char*)wbuf + align256((size_t)shape->d_ff * 4);
+  hipError_t e = launch_row_norms(shape->dtype, x, shape->T, xn, wg_t, wg_norms ? 0 : shape->d_ff,
+                                  wbuf, shape->d_model, s);
+  if (e != hipSuccess) return SFFN_ERR_HIP;
+  return hip_status(launch_backward(x, wg_t, b_g, wu_t, wd, xn, wg_norms ? wg_norms : wbuf, count,
+                                    idx, val, routed, n_routed, gy, gx, gwg_t, gwu_t, gwd, gb,
+                                    shape->T, shape->d_model, shape->d_ff, shape->cap,
+                                    guard_band(shape), bws, s));
 }
 
 size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
@@ -327,6 +362,7 @@ size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
     case SFFN_WS_PACK: return pack_ws(shape);
     case SFFN_WS_CONVERT: return convert_ws(shape);
     case SFFN_WS_PACK_L1: return pack_l1_ws(shape);
+    case SFFN_WS_BACKWARD: return backward_ws(shape);
     default: return 0;
   }
 }

@@ -1,0 +1,545 @@
+// Backward of the activation-sparse gated FFN through TwELL and the hybrid
+// routing (training through the format: pwwt.cn article, sections 03-04).
+//
+// For an upstream gradient gy = dL/dy of y = (ReLU(x wg_t^T + b) * x wu_t^T) wd,
+// only the active entries (t, j) carry gradient.  Per entry, with h its TwELL
+// value:
+//   u  = x_t . wu_t[j],  ga = gy_t . wd[j]
+//   gz = ga u,  gu = ga h,  a = h u
+//   gx_t     += gz wg_t[j] + gu wu_t[j]
+//   gwg_t[j] += gz x_t,  gwu_t[j] += gu x_t,  gwd[j] += a gy_t,  gb[j] += gz
+// Rows within capacity take their entries from the forward's TwELL lists;
+// routed rows (a tile over capacity) from complete activity lists rebuilt here
+// (their gate recomputed with the same GEMM and the same exact activity
+// decision).
+//
+// Kernels, in stream order:
+//   bwd_prep   one wave per row: tile-major copies of the counts and live
+//              indices of rows within capacity (0 for routed rows), and the
+//              start of every tile in a routed row's complete list;
+//   bwd_rows   one wave per row within capacity: walks the row's entries in
+//              order, computes the two dot products and gz, gu, a per entry
+//              (stored for the weight gradients) and accumulates gx_t in
+//              registers;
+//   bwd_routed_items, bwd_routed, bwd_routed_gx
+//              the same for the routed rows, whose long lists are cut into up
+//              to eight parts (one wave each) whose partial gx are summed in
+//              part order;
+//   bwd_cols   one wave per (column, d chunk): finds the column's entries by
+//              scanning the tile-major lists (staged in LDS) in row order,
+//              then the routed rows, and sums the weight-gradient rows in
+//              registers; every column is written (zero when inactive).
+// Every sum runs in a fixed order, so the gradients are deterministic.
+#include "common.cuh"
+#include "launch.h"
+
+namespace sffn {
+
+namespace {
+
+constexpr int kBTile = 128;
+
+struct BwdArgs {
+  const uint16_t* x;
+  const uint16_t* wg;
+  const uint16_t* wu;
+  const uint16_t* wd;
+  const uint16_t* gy;
+  const uint16_t* count;   // forward TwELL [T, nt] (uncapped)
+  const uint16_t* idx;     // [T, nt, cap]
+  const uint16_t* val;     // [T, nt, cap] bf16 h
+  const int32_t* routed;   // ascending routed rows
+  const int32_t* n_routed;
+  const uint16_t* ecount;  // routed row r: complete list length
+  const uint16_t* eidx;    // [T, N] complete lists of the routed rows (row r = routed[r])
+  const uint16_t* eval;    // [T, N] bf16 h
+  int32_t* eoff;           // [T, nt] start of tile k in routed row r's list
+  uint16_t* count_t;       // [nt, T] counts of rows within capacity, 0 for routed rows
+  uint16_t* idx_t;         // [nt, T, cap] their live indices
+  f32x4_t* co;             // [T, nt, cap] (gz, gu, a, 0) of the TwELL entries
+  f32x4_t* co_r;           // [T, N] (gz, gu, a, 0) of the routed rows' entries
+  uint16_t* gx;            // [T, D] bf16
+  float* gwg;              // [N, D]
+  float* gwu;              // [N, D]
+  float* gwd;              // [N, D]
+  float* gb;               // [N] or null
+  int T, D, N, nt, cap;
+};
+
+// Position of row t in the ascending routed list (binary search), or -1.
+__device__ __forceinline__ int routed_index(const int32_t* routed, int n, int t) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (routed[mid] < t) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < n && routed[lo] == t) ? lo : -1;
+}
+
+// A row is routed when some tile count exceeds the capacity.
+__device__ __forceinline__ bool row_is_routed(const BwdArgs& a, int t) {
+  bool over = false;
+  for (int k = lane_id(); k < a.nt; k += kWave) over |= (int)a.count[(size_t)t * a.nt + k] > a.cap;
+  return __ballot(over) != 0ull;
+}
+
+__global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int lane = lane_id();
+  const int t = (int)blockIdx.x * 4 + w;
+  if (t >= a.T) return;
+  const bool routed = row_is_routed(a, t);
+  if (!routed) {
+    for (int k = lane; k < a.nt; k += kWave) {
+      const int c = (int)a.count[(size_t)t * a.nt + k];
+      a.count_t[(size_t)k * a.T + t] = (uint16_t)c;
+      const uint16_t* src = a.idx + ((size_t)t * a.nt + k) * a.cap;
+      uint16_t* dst = a.idx_t + ((size_t)k * a.T + t) * a.cap;
+      for (int s = 0; s < c; ++s) dst[s] = src[s];
+    }
+    return;
+  }
+  for (int k = lane; k < a.nt; k += kWave) a.count_t[(size_t)k * a.T + t] = 0;
+  const int r = uniform(routed_index(a.routed, min(*a.n_routed, a.T), t));
+  if (r < 0) return;  // not in the routed list: the row keeps no entries
+  int carry = 0;
+  for (int k0 = 0; k0 < a.nt; k0 += kWave) {
+    const int k = k0 + lane;
+    const int c = k < a.nt ? (int)a.count[(size_t)t * a.nt + k] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (k < a.nt) a.eoff[(size_t)r * a.nt + k] = carry + incl - c;
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+}
+
+// gx_t (bf16) from this lane's float32 chunks.
+template <int P>
+__device__ __forceinline__ void store_gx(const BwdArgs& a, int t, float (*gxa)[8]) {
+  const size_t xo = (size_t)t * a.D + (size_t)lane_id() * 8;
+#pragma unroll
+  for (int c = 0; c < P; ++c) {
+    u32x4_t o;
+    o.x = (uint32_t)f32_to_bf16(gxa[c][0]) | ((uint32_t)f32_to_bf16(gxa[c][1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(gxa[c][2]) | ((uint32_t)f32_to_bf16(gxa[c][3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(gxa[c][4]) | ((uint32_t)f32_to_bf16(gxa[c][5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(gxa[c][6]) | ((uint32_t)f32_to_bf16(gxa[c][7]) << 16);
+    *(u32x4_t*)(a.gx + xo + c * 512) = o;
+  }
+}
+
+// One entry of row t: the two dot products, the per-entry gradients (stored
+// at *out by lane 0) and the gx accumulation.  xc / gyc: this lane's chunks of
+// x_t and gy_t (8 bf16 each, at c * 512 + lane * 8).
+template <int P>
+__device__ __forceinline__ void bwd_entry(const BwdArgs& a, int j, float h, const u32x4_t* xc,
+                                          const u32x4_t* gyc, float (*gxa)[8], f32x4_t* out) {
+  const int lane = lane_id();
+  const size_t rowo = (size_t)j * a.D + (size_t)lane * 8;
+  u32x4_t uw[P], dw[P], gw[P];
+#pragma unroll
+  for (int c = 0; c < P; ++c) {
+    uw[c] = ldg16(a.wu + rowo + c * 512);
+    dw[c] = ldg16(a.wd + rowo + c * 512);
+    gw[c] = ldg16(a.wg + rowo + c * 512);
+  }
+  float su = 0.f, sg = 0.f;
+#pragma unroll
+  for (int c = 0; c < P; ++c) {
+    float xf[8], uf[8], gf[8], df[8];
+    Elt<uint16_t>::unpack(xc[c], xf);
+    Elt<uint16_t>::unpack(uw[c], uf);
+    Elt<uint16_t>::unpack(gyc[c], gf);
+    Elt<uint16_t>::unpack(dw[c], df);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      su = fmaf(xf[e], uf[e], su);
+      sg = fmaf(gf[e], df[e], sg);
+    }
+  }
+  const float u = wave_sum_uniform(su);
+  const float ga = wave_sum_uniform(sg);
+  const float gz = ga * u, gu = ga * h;
+#pragma unroll
+  for (int c = 0; c < P; ++c) {
+    float uf[8], wf[8];
+    Elt<uint16_t>::unpack(uw[c], uf);
+    Elt<uint16_t>::unpack(gw[c], wf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gxa[c][e] = fmaf(gu, uf[e], fmaf(gz, wf[e], gxa[c][e]));
+  }
+  if (lane == 0) *out = f32x4_t{gz, gu, h * u, 0.f};
+}
+
+template <int P>
+__device__ __forceinline__ void load_row(const uint16_t* base, int t, int D, u32x4_t* c8) {
+  const size_t o = (size_t)t * D + (size_t)lane_id() * 8;
+#pragma unroll
+  for (int c = 0; c < P; ++c) c8[c] = ldg16(base + o + c * 512);
+}
+
+// Rows within capacity: one wave walks the row's TwELL entries in order and
+// writes gx_t.  Routed rows are left to bwd_routed.
+template <int P>
+__global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int lane = lane_id();
+  const int t = (int)blockIdx.x * 4 + w;
+  if (t >= a.T) return;
+  if (row_is_routed(a, t)) return;
+  u32x4_t xc[P], gyc[P];
+  load_row<P>(a.x, t, a.D, xc);
+  load_row<P>(a.gy, t, a.D, gyc);
+  float gxa[P][8];
+#pragma unroll
+  for (int c = 0; c < P; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gxa[c][e] = 0.f;
+  for (int k = 0; k < a.nt; ++k) {
+    const size_t tk = (size_t)t * a.nt + k;
+    const int c = uniform(min((int)a.count[tk], a.cap));
+    for (int s = 0; s < c; ++s) {
+      const size_t pos = tk * a.cap + s;
+      const int j = uniform(min((int)a.idx[pos], a.N - 1));  // valid lists: j < N already
+      bwd_entry<P>(a, j, bf16_to_f32(a.val[pos]), xc, gyc, gxa, a.co + pos);
+    }
+  }
+  store_gx<P>(a, t, gxa);
+}
+
+// Routed rows: their complete lists are long (a routed row is a heavy one),
+// so each list of n entries is cut into min(kRoutedSplit, ceil(n /
+// kRoutedChunk)) equal parts, one wave per part over a persistent grid; each
+// part writes its partial gx (float32) and bwd_routed_gx sums a row's parts in
+// order.  item_start[r]: first part of routed row r (exclusive prefix of the
+// part counts, bwd_routed_items); item_start[n_routed]: all parts.
+constexpr int kRoutedChunk = 64;
+constexpr int kRoutedSplit = 8;
+constexpr int kRoutedWaves = 4096;
+
+__device__ __forceinline__ int routed_parts(int n) {
+  return min(kRoutedSplit, (n + kRoutedChunk - 1) / kRoutedChunk);
+}
+
+__global__ __launch_bounds__(1024) void bwd_routed_items(BwdArgs a, int32_t* item_start) {
+  __shared__ int wsum[16];
+  const int nr = uniform(min(*a.n_routed, a.T));
+  const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+  int carry = 0;
+  for (int r0 = 0; r0 < nr; r0 += 1024) {
+    const int r = r0 + (int)threadIdx.x;
+    const int c = r < nr ? routed_parts(min((int)a.ecount[r], a.N)) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    int before = carry, total = carry;
+    for (int i = 0; i < 16; ++i) {
+      before += i < w ? wsum[i] : 0;
+      total += wsum[i];
+    }
+    if (r < nr) item_start[r] = before + incl - c;
+    __syncthreads();
+    carry = total;
+  }
+  if (threadIdx.x == 0) item_start[nr] = carry;
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void bwd_routed(BwdArgs a, const int32_t* item_start,
+                                                  float* part) {
+  const int nr = uniform(min(*a.n_routed, a.T));
+  const int items = uniform(item_start[nr]);
+  const int lane = lane_id();
+  for (int it = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); it < items; it += kRoutedWaves) {
+    // routed row of this chunk: the last r with item_start[r] <= it
+    int lo = 0, hi = nr - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (item_start[mid] <= it) lo = mid;
+      else hi = mid - 1;
+    }
+    const int r = uniform(lo);
+    const int t = uniform(min(max(a.routed[r], 0), a.T - 1));
+    const int n = uniform(min((int)a.ecount[r], a.N));
+    const int np = routed_parts(n), pi = it - item_start[r];
+    const int s0 = (int)((long)pi * n / np), s1 = (int)((long)(pi + 1) * n / np);
+    u32x4_t xc[P], gyc[P];
+    load_row<P>(a.x, t, a.D, xc);
+    load_row<P>(a.gy, t, a.D, gyc);
+    float gxa[P][8];
+#pragma unroll
+    for (int c = 0; c < P; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gxa[c][e] = 0.f;
+    for (int s = s0; s < s1; ++s) {
+      const size_t pos = (size_t)r * a.N + s;
+      const int j = uniform(min((int)a.eidx[pos], a.N - 1));
+      bwd_entry<P>(a, j, bf16_to_f32(a.eval[pos]), xc, gyc, gxa, a.co_r + pos);
+    }
+    float* dst = part + (size_t)it * a.D + (size_t)lane * 8;
+#pragma unroll
+    for (int c = 0; c < P; ++c) {
+      *(f32x4_t*)(dst + c * 512) = f32x4_t{gxa[c][0], gxa[c][1], gxa[c][2], gxa[c][3]};
+      *(f32x4_t*)(dst + c * 512 + 4) = f32x4_t{gxa[c][4], gxa[c][5], gxa[c][6], gxa[c][7]};
+    }
+  }
+}
+
+// gx of routed row r = the sum of its parts' partials, in part order (a
+// routed row without entries gets zero).  Workgroups loop over the rows.
+__global__ __launch_bounds__(256) void bwd_routed_gx(BwdArgs a, const int32_t* item_start,
+                                                     const float* part) {
+  const int nr = uniform(min(*a.n_routed, a.T));
+  for (int r = (int)blockIdx.y; r < nr; r += (int)gridDim.y) {
+    const int t = min(max(a.routed[r], 0), a.T - 1);
+    const int i0 = item_start[r], i1 = item_start[r + 1];
+    for (int d = ((int)blockIdx.x * 256 + (int)threadIdx.x) * 2; d < a.D;
+         d += (int)gridDim.x * 512) {
+      float v0 = 0.f, v1 = 0.f;
+      for (int it = i0; it < i1; ++it) {
+        v0 += part[(size_t)it * a.D + d];
+        v1 += part[(size_t)it * a.D + d + 1];
+      }
+      *(uint32_t*)(a.gx + (size_t)t * a.D + d) =
+          (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+    }
+  }
+}
+
+// Weight gradients.  Workgroup = 16 waves = 16 consecutive columns of one
+// tile and one chunk of PC * 512 model dimensions; the tile's tile-major
+// counts and indices are staged in LDS a block of rows at a time and every
+// wave scans them for its own column (ascending rows, so the sums run in row
+// order), then scans the routed rows' lists (binary search per row).
+constexpr int kColWaves = 16;
+constexpr int kColLdsHalves = 16384;  // 32 KB of u16: counts and indices of a row block
+
+// acc += coef * (this lane's chunks of row t), for one matched entry.
+template <int PC>
+__device__ __forceinline__ void col_accumulate(const BwdArgs& a, int t, int d0, f32x4_t coef,
+                                               float (*ag)[8], float (*au)[8], float (*ad)[8],
+                                               float& gbs) {
+  const size_t ro = (size_t)t * a.D + d0 + (size_t)lane_id() * 8;
+  u32x4_t xc[PC], gc[PC];
+#pragma unroll
+  for (int c = 0; c < PC; ++c) {
+    xc[c] = ldg16(a.x + ro + c * 512);
+    gc[c] = ldg16(a.gy + ro + c * 512);
+  }
+#pragma unroll
+  for (int c = 0; c < PC; ++c) {
+    float xf[8], gf[8];
+    Elt<uint16_t>::unpack(xc[c], xf);
+    Elt<uint16_t>::unpack(gc[c], gf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ag[c][e] = fmaf(coef[0], xf[e], ag[c][e]);
+      au[c][e] = fmaf(coef[1], xf[e], au[c][e]);
+      ad[c][e] = fmaf(coef[2], gf[e], ad[c][e]);
+    }
+  }
+  gbs += coef[0];
+}
+
+template <int PC>
+__global__ __launch_bounds__(64 * kColWaves) void bwd_cols(BwdArgs a, int rows_per_block) {
+  __shared__ uint16_t lds[kColLdsHalves];
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int lane = lane_id();
+  const int dchunks = a.D / (PC * 512);
+  const int bid = (int)blockIdx.x;
+  const int dc = bid % dchunks;
+  const int cg = (bid / dchunks) % (kBTile / kColWaves);
+  const int k = bid / (dchunks * (kBTile / kColWaves));
+  const int j = k * kBTile + cg * kColWaves + w;
+  const int d0 = dc * PC * 512;
+  uint16_t* cnt_s = lds;
+  uint16_t* idx_s = lds + rows_per_block;
+  float ag[PC][8], au[PC][8], ad[PC][8];
+#pragma unroll
+  for (int c = 0; c < PC; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[c][e] = au[c][e] = ad[c][e] = 0.f;
+  float gbs = 0.f;
+  for (int row0 = 0; row0 < a.T; row0 += rows_per_block) {
+    const int nrow = min(rows_per_block, a.T - row0);
+    __syncthreads();  // the previous block's scan is done
+    for (int i = (int)threadIdx.x; i < nrow; i += (int)blockDim.x) {
+      const size_t g = (size_t)k * a.T + row0 + i;
+      const int c = (int)a.count_t[g];
+      cnt_s[i] = (uint16_t)c;
+      for (int s = 0; s < c; ++s) idx_s[i * a.cap + s] = a.idx_t[g * a.cap + s];
+    }
+    __syncthreads();
+    for (int rb = 0; rb < nrow; rb += kWave) {
+      const int i = rb + lane;
+      int match = -1;
+      if (i < nrow) {
+        const int c = (int)cnt_s[i];
+        for (int s = 0; s < c; ++s) {
+          const int v = (int)idx_s[i * a.cap + s];
+          if (v >= j) {
+            if (v == j) match = s;
+            break;
+          }
+        }
+      }
+      uint64_t m = __ballot(match >= 0);
+      while (m) {
+        const int L = __builtin_ctzll(m);
+        m &= m - 1;
+        const int t = row0 + rb + L;
+        const int s = __shfl(match, L, kWave);
+        const f32x4_t coef = a.co[((size_t)t * a.nt + k) * a.cap + s];
+        col_accumulate<PC>(a, t, d0, coef, ag, au, ad, gbs);
+      }
+    }
+  }
+  // routed rows: their complete lists, one binary search per row
+  const int nr = uniform(min(*a.n_routed, a.T));
+  for (int r0 = 0; r0 < nr; r0 += kWave) {
+    const int r = r0 + lane;
+    int match = -1, tr = 0;
+    if (r < nr) {
+      tr = a.routed[r];
+      // the tile's range of the row's list, kept inside the list's N slots
+      const int beg = min(max(a.eoff[(size_t)r * a.nt + k], 0), a.N);
+      const int end = min(beg + (int)a.count[(size_t)tr * a.nt + k], a.N);
+      const uint16_t* li = a.eidx + (size_t)r * a.N;
+      int lo = beg, hi = end;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)li[mid] < j) lo = mid + 1;
+        else hi = mid;
+      }
+      if (lo < end && (int)li[lo] == j) match = lo;
+    }
+    uint64_t m = __ballot(match >= 0);
+    while (m) {
+      const int L = __builtin_ctzll(m);
+      m &= m - 1;
+      const int t = min(max(__shfl(tr, L, kWave), 0), a.T - 1);
+      const int s = __shfl(match, L, kWave);
+      const f32x4_t coef = a.co_r[(size_t)(r0 + L) * a.N + s];
+      col_accumulate<PC>(a, t, d0, coef, ag, au, ad, gbs);
+    }
+  }
+  const size_t wo = (size_t)j * a.D + d0 + (size_t)lane * 8;
+#pragma unroll
+  for (int c = 0; c < PC; ++c) {
+    *(f32x4_t*)(a.gwg + wo + c * 512) = f32x4_t{ag[c][0], ag[c][1], ag[c][2], ag[c][3]};
+    *(f32x4_t*)(a.gwg + wo + c * 512 + 4) = f32x4_t{ag[c][4], ag[c][5], ag[c][6], ag[c][7]};
+    *(f32x4_t*)(a.gwu + wo + c * 512) = f32x4_t{au[c][0], au[c][1], au[c][2], au[c][3]};
+    *(f32x4_t*)(a.gwu + wo + c * 512 + 4) = f32x4_t{au[c][4], au[c][5], au[c][6], au[c][7]};
+    *(f32x4_t*)(a.gwd + wo + c * 512) = f32x4_t{ad[c][0], ad[c][1], ad[c][2], ad[c][3]};
+    *(f32x4_t*)(a.gwd + wo + c * 512 + 4) = f32x4_t{ad[c][4], ad[c][5], ad[c][6], ad[c][7]};
+  }
+  if (a.gb && dc == 0 && lane == 0) a.gb[j] = gbs;
+}
+
+size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool backward_supported(int dtype, int d_model) {
+  return dtype == 1 && d_model % 512 == 0 && d_model <= 4096;
+}
+
+// Workspace of the backward: the routed rows' z (later reused for their
+// per-entry gradients), their complete lists and tile offsets, the tile-major
+// copies and the per-entry gradients of the TwELL entries.
+size_t backward_workspace_bytes(int T, int N, int D, int cap) {
+  const size_t nt = (size_t)N / kBTile;
+  return al256((size_t)T * N * 16) + 2 * al256((size_t)T * N * 2) + al256((size_t)T * 2) +
+         al256((size_t)T * nt * 4) + al256(nt * T * 2) + al256(nt * T * cap * 2) +
+         al256((size_t)T * nt * cap * 16) + al256(((size_t)T + 1) * 4) +
+         al256((size_t)T * kRoutedSplit * D * 4);
+}
+
+hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
+                           const void* wd, const float* xnorm, const float* wnorm,
+                           const uint16_t* count, const uint16_t* idx, const void* val,
+                           const int32_t* routed, const int32_t* n_routed, const void* gy,
+                           void* gx, float* gwg_t, float* gwu_t, float* gwd, float* gb, int T,
+                           int D, int N, int cap, GuardBand band, void* ws, hipStream_t stream) {
+  const int nt = N / kBTile;
+  char* p = (char*)ws;
+  float* z_r = (float*)p;          // routed rows' z, then (same bytes) their entry gradients
+  f32x4_t* co_r = (f32x4_t*)p;
+  p += al256((size_t)T * N * 16);
+  uint16_t* eidx = (uint16_t*)p;
+  p += al256((size_t)T * N * 2);
+  uint16_t* eval = (uint16_t*)p;
+  p += al256((size_t)T * N * 2);
+  uint16_t* ecount = (uint16_t*)p;
+  p += al256((size_t)T * 2);
+  int32_t* eoff = (int32_t*)p;
+  p += al256((size_t)T * nt * 4);
+  uint16_t* count_t = (uint16_t*)p;
+  p += al256((size_t)nt * T * 2);
+  uint16_t* idx_t = (uint16_t*)p;
+  p += al256((size_t)nt * T * cap * 2);
+  f32x4_t* co = (f32x4_t*)p;
+  p += al256((size_t)T * nt * cap * 16);
+  int32_t* item_start = (int32_t*)p;
+  p += al256(((size_t)T + 1) * 4);
+  float* part = (float*)p;
+
+  // routed rows: z with the gate GEMM, then complete activity lists
+  hipError_t e = launch_gate_preact(x, wg_t, b_g, z_r, T, D, N, routed, n_routed, stream);
+  if (e != hipSuccess) return e;
+  e = launch_ell_convert(z_r, x, wg_t, b_g, xnorm, wnorm, N, ecount, eidx, eval, T, D, N, band,
+                         routed, n_routed, stream);
+  if (e != hipSuccess) return e;
+
+  BwdArgs a{(const uint16_t*)x, (const uint16_t*)wg_t, (const uint16_t*)wu_t,
+            (const uint16_t*)wd, (const uint16_t*)gy, count, idx, (const uint16_t*)val,
+            routed, n_routed, ecount, eidx, eval, eoff, count_t, idx_t, co, co_r,
+            (uint16_t*)gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, cap};
+  const dim3 rows_grid((unsigned)((T + 3) / 4));
+  hipLaunchKernelGGL(bwd_prep, rows_grid, dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (D / 512) {
+#define SFFN_BWD_ROWS(P)                                                                        \
+  case P:                                                                                        \
+    hipLaunchKernelGGL(bwd_rows<P>, rows_grid, dim3(256), 0, stream, a);                         \
+    hipLaunchKernelGGL(bwd_routed_items, dim3(1), dim3(1024), 0, stream, a, item_start);         \
+    hipLaunchKernelGGL(bwd_routed<P>, dim3(kRoutedWaves / 4), dim3(256), 0, stream, a,           \
+                       (const int32_t*)item_start, part);                                        \
+    break;
+    SFFN_BWD_ROWS(1) SFFN_BWD_ROWS(2) SFFN_BWD_ROWS(3) SFFN_BWD_ROWS(4)
+    SFFN_BWD_ROWS(5) SFFN_BWD_ROWS(6) SFFN_BWD_ROWS(7) SFFN_BWD_ROWS(8)
+#undef SFFN_BWD_ROWS
+    default: return hipErrorInvalidValue;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_routed_gx, dim3((unsigned)((D + 511) / 512), 256), dim3(256), 0, stream,
+                     a, (const int32_t*)item_start, (const float*)part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // rows per staged block: counts + cap indices each, in 32 KB of LDS, a
+  // multiple of the wave width
+  const int rpb = max(kWave, (kColLdsHalves / (1 + max(cap, 1))) / kWave * kWave);
+  if (D % 1024 == 0) {
+    const dim3 g((unsigned)(nt * (kBTile / kColWaves) * (D / 1024)));
+    hipLaunchKernelGGL(bwd_cols<2>, g, dim3(64 * kColWaves), 0, stream, a, rpb);
+  } else {
+    const dim3 g((unsigned)(nt * (kBTile / kColWaves) * (D / 512)));
+    hipLaunchKernelGGL(bwd_cols<1>, g, dim3(64 * kColWaves), 0, stream, a, rpb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sffn

@@ -23,17 +23,21 @@ namespace {
 // fused epilogue sees and the converters reach the same exact activity
 // decision with the same guard band.
 
-// z[t, j] = acc + b_g[j] (float32, row-major [T, N]).
-__global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_preact_bf16(GateArgs a,
-                                                                                        float* z) {
+// z[m, j] = acc + b_g[j] (float32, row-major [rows, N]) for the x rows
+// rowmap[m] (rowmap null: row m), m < rows (n_rows_dev null: T; else the
+// count on the device).
+__global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_preact_bf16(
+    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev) {
   using G = GateGemm;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   int mi, ni;
   tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, (a.N + G::BN - 1) / G::BN, &mi, &ni);
   const int m0 = mi * G::BM, n0 = ni * G::BN;
+  const int mv = uniform(n_rows_dev ? min(*n_rows_dev, a.T) : a.T);
+  if (m0 >= mv) return;
   G g;
   const uint16_t* B[1] = {(const uint16_t*)a.wg};
-  g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, m0, a.T, B, n0, a.N, a.K);
+  g.init((const uint16_t*)a.x, (size_t)a.T, rowmap, m0, mv, B, n0, a.N, a.K);
   g.run_pipe(lds, a.K);
   const int lane = lane_id();
   const int w = uniform((int)(threadIdx.x >> 6));
@@ -48,7 +52,7 @@ __global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_prea
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * G::WM + fm * 16 + 4 * (lane >> 4) + r;
-        if (cv && m < a.T) z[(size_t)m * a.N + col] = g.acc[0][fm][fn][r] + bb;
+        if (cv && m < mv) z[(size_t)m * a.N + col] = g.acc[0][fm][fn][r] + bb;
       }
   }
 }
@@ -156,19 +160,24 @@ __device__ __forceinline__ void ell_emit(uint16_t* eidx, uint16_t* eval, size_t 
   running += __popcll(m0) + __popcll(m1);
 }
 
+// Row m of z and of the output is x row rowmap[m] (rowmap null: m), for
+// m < rows (n_rows_dev null: T; else the count on the device).
 template <int U>
 __global__ __launch_bounds__(256) void ell_convert_bf16(GateArgs a, const float* z, int width,
                                                         uint16_t* ecount, uint16_t* eidx,
-                                                        uint16_t* eval) {
+                                                        uint16_t* eval, const int* rowmap,
+                                                        const int* n_rows_dev) {
   __shared__ uint32_t exact_lds[4 * kExactLdsWords];
   const int w = uniform((int)(threadIdx.x >> 6));
   const int lane = lane_id();
-  const int t = (int)blockIdx.x * 4 + w;
-  if (t >= a.T) return;
+  const int m = (int)blockIdx.x * 4 + w;
+  const int mv = uniform(n_rows_dev ? min(*n_rows_dev, a.T) : a.T);
+  if (m >= mv) return;
+  const int t = uniform(rowmap ? rowmap[m] : m);
   const int nt = a.N / kTile;
   const float nx = a.xnorm[t];
-  const float* zr = z + (size_t)t * a.N;
-  const size_t ebase = (size_t)t * width;
+  const float* zr = z + (size_t)m * a.N;
+  const size_t ebase = (size_t)m * width;
   int running = 0;
   for (int k0 = 0; k0 < nt; k0 += U) {
     float zv[U][2], dv[U][2];
@@ -223,17 +232,19 @@ __global__ __launch_bounds__(256) void ell_convert_bf16(GateArgs a, const float*
       ell_emit(eidx, eval, ebase, width, c0, act[0], act[1], zz[0], zz[1], running);
     }
   }
-  if (lane == 0) ecount[t] = (uint16_t)running;
+  if (lane == 0) ecount[m] = (uint16_t)running;
 }
 
 }  // namespace
 
 hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g, float* z, int T,
-                              int K, int N, hipStream_t stream) {
+                              int K, int N, const int* rowmap, const int* n_rows_dev,
+                              hipStream_t stream) {
   GateArgs a{x, wg_t, b_g, nullptr, nullptr, nullptr, nullptr, nullptr, T, K, N, 0, GuardBand{}};
   const dim3 g((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
                           ((N + GateGemm::BN - 1) / GateGemm::BN)));
-  hipLaunchKernelGGL(gate_preact_bf16, g, dim3(64 * GateGemm::NWAVES), 0, stream, a, z);
+  hipLaunchKernelGGL(gate_preact_bf16, g, dim3(64 * GateGemm::NWAVES), 0, stream, a, z, rowmap,
+                     n_rows_dev);
   return hipGetLastError();
 }
 
@@ -253,10 +264,11 @@ hipError_t launch_twell_convert(const float* z, const void* x, const void* wg_t,
 hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, const float* b_g,
                               const float* xnorm, const float* wnorm, int width,
                               uint16_t* ecount, uint16_t* eidx, void* eval, int T, int K, int N,
-                              GuardBand gb, hipStream_t stream) {
+                              GuardBand gb, const int* rowmap, const int* n_rows_dev,
+                              hipStream_t stream) {
   GateArgs a{x, wg_t, b_g, nullptr, nullptr, nullptr, xnorm, wnorm, T, K, N, 0, gb};
   hipLaunchKernelGGL(ell_convert_bf16<16>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, a,
-                     z, width, ecount, eidx, (uint16_t*)eval);
+                     z, width, ecount, eidx, (uint16_t*)eval, rowmap, n_rows_dev);
   return hipGetLastError();
 }
 

@@ -37,9 +37,12 @@ hipError_t launch_l1_reduce(const float* part, size_t n, double scale, void* ws,
 // storing the float32 pre-activation z [T, N] (bias added), and converters
 // from z to TwELL and to a row-wise ELLPACK of the given width (ecount [T],
 // eidx / eval [T, width]).  Same activity decision as launch_gate_twell.
+// With rowmap / n_rows_dev (both may be null): output row m < *n_rows_dev is
+// x row rowmap[m] (the backward's routed rows).
 bool preact_supported(int dtype, int K);
 hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g, float* z, int T,
-                              int K, int N, hipStream_t stream);
+                              int K, int N, const int* rowmap, const int* n_rows_dev,
+                              hipStream_t stream);
 hipError_t launch_twell_convert(const float* z, const void* x, const void* wg_t, const float* b_g,
                                 const float* xnorm, const float* wnorm, uint16_t* count,
                                 uint16_t* idx, void* val, int T, int K, int N, int cap,
@@ -47,7 +50,21 @@ hipError_t launch_twell_convert(const float* z, const void* x, const void* wg_t,
 hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, const float* b_g,
                               const float* xnorm, const float* wnorm, int width,
                               uint16_t* ecount, uint16_t* eidx, void* eval, int T, int K, int N,
-                              GuardBand gb, hipStream_t stream);
+                              GuardBand gb, const int* rowmap, const int* n_rows_dev,
+                              hipStream_t stream);
+
+// Backward through TwELL and the hybrid routing (bf16, d_model % 512 == 0,
+// d_model <= 4096): gx [T, D] bf16, float32 weight gradients [N, D] and gb
+// [N] (may be null).  xnorm: ||x_t|| of every row; wnorm: ||wg_t[j]||.  ws:
+// backward_workspace_bytes().
+bool backward_supported(int dtype, int d_model);
+size_t backward_workspace_bytes(int T, int N, int D, int cap);
+hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
+                           const void* wd, const float* xnorm, const float* wnorm,
+                           const uint16_t* count, const uint16_t* idx, const void* val,
+                           const int32_t* routed, const int32_t* n_routed, const void* gy,
+                           void* gx, float* gwg_t, float* gwu_t, float* gwd, float* gb, int T,
+                           int D, int N, int cap, GuardBand band, void* ws, hipStream_t stream);
 
 // Row norms of a [rows_a, K] and a [rows_b, K] matrix in one launch.
 hipError_t launch_row_norms(int dtype, const void* a, int rows_a, float* out_a, const void* b,

@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libsffn.so")
 
 SFFN_OK, SFFN_ERR_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ERR_HIP = 0, -1, -2, -3, -4
 SFFN_F32, SFFN_BF16 = 0, 1
-WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK, WS_CONVERT, WS_PACK_L1 = 0, 1, 2, 3, 4, 5
+WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK, WS_CONVERT, WS_PACK_L1, WS_BACKWARD = 0, 1, 2, 3, 4, 5, 6
 TILE = 128
 
 EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
-            "dense_ffn_ref", "gate_preact", "twell_from_preact", "ell_from_preact",
-            "sffn_workspace_bytes", "sffn_strerror")
+            "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
+            "ell_from_preact", "sffn_workspace_bytes", "sffn_strerror")
 
 
 class SffnError(RuntimeError):
@@ -51,10 +51,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.gate_preact.argtypes = [sp, vp, vp, vp, vp, vp]
+    lib.sparse_ffn_bwd.argtypes = [sp] + [vp] * 17 + [vp, sz, vp]
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
-               "dense_ffn_ref", "gate_preact", "twell_from_preact", "ell_from_preact"):
+               "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
+               "ell_from_preact"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
     lib.sffn_workspace_bytes.restype = sz
@@ -176,6 +178,20 @@ def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=Non
     _check("dense_ffn_ref", _lib.dense_ffn_ref(
         ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd),
         _ptr(workspace), ws_n, _ptr(y), _stream(stream)))
+
+
+def sparse_ffn_bwd(shape: Shape, x, wg_t, b_g, wu_t, wd, count, idx, val, routed, n_routed, gy,
+                   gx, gwg_t, gwu_t, gwd, gb, workspace, wg_norms=None, stream=None) -> None:
+    for name, t in (("gwg_t", gwg_t), ("gwu_t", gwu_t), ("gwd", gwd)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (shape.d_ff, shape.d_model):
+            raise ValueError(f"{name} must be float32 [d_ff, d_model]")
+    if gb is not None and (gb.dtype != torch.float32 or gb.numel() != shape.d_ff):
+        raise ValueError("gb must be float32 [d_ff]")
+    ws_n = workspace.numel() * workspace.element_size()
+    _check("sparse_ffn_bwd", _lib.sparse_ffn_bwd(
+        ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd), _ptr(wg_norms),
+        _ptr(count), _ptr(idx), _ptr(val), _ptr(routed), _ptr(n_routed), _ptr(gy), _ptr(gx),
+        _ptr(gwg_t), _ptr(gwu_t), _ptr(gwd), _ptr(gb), _ptr(workspace), ws_n, _stream(stream)))
 
 
 def gate_preact(shape: Shape, x, wg_t, b_g, z, stream=None) -> None:

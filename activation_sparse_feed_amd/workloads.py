@@ -35,7 +35,7 @@ import math
 
 import numpy as np
 
-SEED_OFFSETS = {"x": 1, "wg": 2, "wu": 3, "wd": 4, "rows": 5}
+SEED_OFFSETS = {"x": 1, "wg": 2, "wu": 3, "wd": 4, "rows": 5, "gy": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -200,3 +200,10 @@ def generate_custom(T: int, d_model: int, d_ff: int, dtype: str, beta: float,
     w = Workload("custom", T=T, d_model=d_model, d_ff=d_ff, dtype=dtype,
                  beta=beta, cap=cap, seed_base=seed_base, rows=rows, **kw)
     return generate(w)
+
+
+def upstream_grad(w: Workload) -> np.ndarray:
+    """A seeded upstream gradient dL/dy for the backward, [T, d_model]: unit
+    normals in the workload's storage format (bf16 bit patterns or float32)."""
+    return _store(_normal(w.seed_base + SEED_OFFSETS["gy"], (w.T, w.d_model), 1.0), w.dtype)
+

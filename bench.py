@@ -40,6 +40,8 @@ def parse_args():
     p.add_argument("--cpu-rows", type=int, default=None,
                    help="rows of the CPU oracle sample (default: whole batch, at most 4096)")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip timing the sparse backward (sparse_ffn_bwd) and the dense one")
     p.add_argument("--no-l1", action="store_true",
                    help="skip timing twell_pack_l1 (the L1 regulariser fused into the gate epilogue)")
     p.add_argument("--no-conversion", action="store_true",
@@ -415,6 +417,58 @@ def main() -> int:
               "twell_pack_ms": t_p, "overhead": t_l1 / t_p - 1.0}
         del ws_l1, tw1
 
+    # ---- backward through TwELL and the routing (sparse_ffn_bwd), against a
+    # dense backward from torch's GEMMs (hipBLASLt) given the forward's dense
+    # activations; both after the same forward, K calls each
+    backward = None
+    if not args.no_backward and w.dtype == "bf16" and w.d_model % 512 == 0 and w.d_model <= 4096:
+        gy = dev(wl.upstream_grad(w))
+        ws_b = sffn.alloc_workspace(s, sffn.WS_BACKWARD)
+        gx = torch.empty_like(x)
+        gw3 = [torch.empty((w.d_ff, w.d_model), device="cuda") for _ in range(3)]
+        gbv = torch.empty(w.d_ff, device="cuda")
+        ffn.forward(x, wg, b, wu, wd, wg_norms)
+
+        def bwd():
+            sffn.sparse_ffn_bwd(s, x, wg, b, wu, wd, ffn.count, ffn.idx, ffn.val, ffn.routed,
+                                ffn.n_routed, gy, gx, *gw3, gbv, ws_b, wg_norms)
+        # dense backward from activations saved in [d_ff, T] layout and weights
+        # prepared in [d_model, d_ff] layout (one-time), so that no GEMM
+        # operand is a transposed view
+        wg_tt, wu_tt = wg.t().contiguous(), wu.t().contiguous()
+        zT = (torch.nn.functional.linear(x, wg) + b.to(dt)).t().contiguous()
+        uT = torch.nn.functional.linear(x, wu).t().contiguous()
+        actT = zT > 0
+        hT = torch.where(actT, zT, torch.zeros_like(zT))
+
+        def dense_bwd():
+            gyT = gy.t().contiguous()
+            gaT = torch.mm(wd, gyT)
+            gzT = torch.where(actT, gaT * uT, torch.zeros_like(gaT))
+            guT = gaT * hT
+            gx_d = (torch.mm(wg_tt, gzT) + torch.mm(wu_tt, guT)).t().contiguous()
+            return (gx_d, torch.mm(gzT, x), torch.mm(guT, x), torch.mm(hT * uT, gy),
+                    gzT.float().sum(1))
+        for _ in range(2):
+            bwd()
+            dense_bwd()
+        b0, b1, b2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record()
+        for _ in range(K):
+            bwd()
+        b1.record()
+        for _ in range(K):
+            dense_bwd()
+        b2.record()
+        torch.cuda.synchronize()
+        t_b, t_db = b0.elapsed_time(b1) / K, b1.elapsed_time(b2) / K
+        backward = {"sparse_ffn_bwd_ms": t_b, "torch_dense_backward_ms": t_db,
+                    "speedup_vs_torch_dense": t_db / t_b,
+                    "weight_grad_bytes": 3.0 * w.d_ff * w.d_model * 4,
+                    "note": "dense: 6 hipBLASLt bf16 GEMMs from saved dense activations"}
+        del ws_b, gw3, zT, uT, hT, actT, wg_tt, wu_tt
+
     count = ffn.count.to(torch.int64)
     nnz_live = int(torch.clamp(count, max=w.cap).sum().item()) if w.cap > 0 else 0
     n_routed = int(ffn.n_routed.item())
@@ -479,6 +533,7 @@ def main() -> int:
         "torch_dense_ms": t_torch,
         "separate_conversion": conversion,
         "l1_regulariser": l1,
+        "backward": backward,
         "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,
         "speedup_vs_dense": (t_dense / ms_step) if t_dense else None,
         "dense_tflops": (3 * gate_flop / (t_dense * 1e-3) / 1e12) if t_dense else None,

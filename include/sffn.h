@@ -72,7 +72,8 @@ typedef enum {
   SFFN_WS_SPARSE = 2,
   SFFN_WS_PACK = 3,
   SFFN_WS_CONVERT = 4,
-  SFFN_WS_PACK_L1 = 5
+  SFFN_WS_PACK_L1 = 5,
+  SFFN_WS_BACKWARD = 6
 } sffn_ws_kind;
 
 typedef struct {
@@ -184,6 +185,40 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
                      const float* b_g, const void* wu_t, const void* wd,
                      const uint16_t* count, int32_t* routed, int32_t* n_routed,
                      void* workspace, size_t ws_bytes, void* y, void* stream);
+
+/*
+ * sparse_ffn_bwd -- backward of the sparse forward (training through TwELL
+ * and the hybrid routing: pwwt.cn article, sections 03-04).  For the upstream
+ * gradient gy = dL/dy and the forward's count/idx/val (from twell_pack) and
+ * routed/n_routed (from hybrid_route), by the chain rule on the gated FFN:
+ *
+ *   gx[t, :]    = sum_j gz[t,j] wg_t[j, :] + gu[t,j] wu_t[j, :]     (dtype)
+ *   gwg_t[j, :] = sum_t gz[t,j] x[t, :]      gwu_t[j, :] = sum_t gu[t,j] x[t, :]
+ *   gwd[j, :]   = sum_t a[t,j] gy[t, :]      gb[j] = sum_t gz[t,j]  (float32)
+ *
+ * over the active entries only (gz = ga u, gu = ga h, a = h u with
+ * ga = gy_t . wd[j], u = x_t . wu_t[j]; ReLU' is 0 elsewhere).  Rows within
+ * capacity use their TwELL entries (h = val); routed rows use complete
+ * activity lists rebuilt from x with twell_pack's GEMM and exact activity
+ * decision (h rounded to bf16 like val).  Every sum runs in a fixed order:
+ * the result is deterministic.  Every element of the outputs is written
+ * (weight-gradient rows of inactive columns are zero); gb may be NULL.
+ *
+ * bf16 only, d_model % 512 == 0 and d_model <= 4096 (else
+ * SFFN_ERR_UNSUPPORTED), plus twell_pack's size limits.  gy, gx: [T, d_model]
+ * dtype; gwg_t, gwu_t, gwd: float32 [d_ff, d_model]; gb: float32 [d_ff].
+ * wg_norms as for twell_pack (or NULL).  workspace: at least
+ * sffn_workspace_bytes(shape, SFFN_WS_BACKWARD) bytes (sized for every row
+ * routed: about 20 * T * d_ff + 32 * T * d_model bytes), no initial contents;
+ * the routed and n_routed of the same forward; calls sharing it
+ * must be stream-ordered.
+ */
+int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
+                       const void* wu_t, const void* wd, const float* wg_norms,
+                       const uint16_t* count, const uint16_t* idx, const void* val,
+                       const int32_t* routed, const int32_t* n_routed, const void* gy, void* gx,
+                       float* gwg_t, float* gwu_t, float* gwd, float* gb, void* workspace,
+                       size_t ws_bytes, void* stream);
 
 /*
  * dense_ffn_ref -- the dense gated FFN used as the speed-up reference

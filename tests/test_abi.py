@@ -167,3 +167,28 @@ def test_pack_l1_errors(sffn):
     assert lib.twell_pack_l1(ctypes.byref(_shape(sffn, tile=64)), P, P, None, None, P, P, P, 1.0,
                              P, WS, need, None) == -2
 
+
+def test_backward_errors(sffn):
+    lib = sffn._lib
+    s = _shape(sffn, d_model=512)
+    need = sffn.workspace_bytes(s, sffn.WS_BACKWARD)
+    assert need >= 20 * 64 * 512
+    args = [P] * 17
+    args[2] = None   # b_g
+    args[5] = None   # wg_norms
+    args[16] = None  # gb
+    assert lib.sparse_ffn_bwd(ctypes.byref(s), *args, WS, need - 1, None) == -3
+    bad = list(args)
+    bad[12] = None   # gx
+    assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
+    bad = list(args)
+    bad[9] = MISALIGNED  # routed
+    assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
+    s264 = _shape(sffn, d_model=264)
+    n264 = sffn.workspace_bytes(s264, sffn.WS_BACKWARD)
+    assert lib.sparse_ffn_bwd(ctypes.byref(s264), *args, WS, n264, None) == -2
+    sf = _shape(sffn, d_model=512, dtype=sffn.SFFN_F32)
+    assert lib.sparse_ffn_bwd(ctypes.byref(sf), *args, WS, sffn.workspace_bytes(sf, 6), None) == -2
+    s0 = _shape(sffn, T=0)
+    assert lib.sparse_ffn_bwd(ctypes.byref(s0), *([None] * 17), None, 0, None) == 0
+

@@ -1,0 +1,122 @@
+"""GPU parity of the sparse backward (sparse_ffn_bwd) against the oracle.
+
+The forward runs first (twell_pack, sparse_ffn_fwd, hybrid_route) and its
+TwELL arrays and routed rows feed the backward, as in training.  Each gradient
+is compared with the oracle's sparse backward on the same TwELL values and with
+its dense backward (exact h), by relative Frobenius error within the bf16
+tolerance 5e-3; gx separately over routed and non-routed rows.  The weight
+gradients are float32 sums in a fixed order: two calls give the same bits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_feed_amd import workloads as wl
+from helpers import device_inputs, rel_fro, sample_rows, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+
+
+def _sffn():
+    from activation_sparse_feed_amd import sffn
+    return sffn
+
+
+def run_backward(inp: wl.Inputs, cap: int, gy_np: np.ndarray, repeat: int = 1):
+    sffn = _sffn()
+    w = inp.workload
+    d = device_inputs(inp)
+    ffn = sffn.SparseFFN(w.T, w.d_model, w.d_ff, cap, torch.bfloat16)
+    ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    s = ffn.shape
+    gy = to_device(gy_np, "bf16")
+    ws = sffn.alloc_workspace(s, sffn.WS_BACKWARD)
+    outs = []
+    for _ in range(repeat):
+        gx = torch.empty((w.T, w.d_model), dtype=torch.bfloat16, device="cuda")
+        g = [torch.full((w.d_ff, w.d_model), float("nan"), device="cuda") for _ in range(3)]
+        gb = torch.full((w.d_ff,), float("nan"), device="cuda")
+        sffn.sparse_ffn_bwd(s, d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], ffn.count, ffn.idx,
+                            ffn.val, ffn.routed, ffn.n_routed, gy, gx, *g, gb, ws)
+        outs.append({"gx": gx, "gwg_t": g[0], "gwu_t": g[1], "gwd": g[2], "gb": gb})
+    torch.cuda.synchronize()
+    return ffn, outs
+
+
+def check(inp: wl.Inputs, cap: int, dense: bool, rows=None):
+    w = inp.workload
+    gy_np = wl.upstream_grad(w)
+    ffn, outs = run_backward(inp, cap, gy_np, repeat=2)
+    o = outs[0]
+    for k in o:  # deterministic
+        assert torch.equal(o[k].view(torch.int16) if o[k].dtype == torch.bfloat16 else o[k],
+                           outs[1][k].view(torch.int16) if o[k].dtype == torch.bfloat16 else outs[1][k]), k
+    x, wg, wu, wd = inp.as_f64("x"), inp.as_f64("wg_t"), inp.as_f64("wu_t"), inp.as_f64("wd")
+    gy = wl.bf16_bits_to_f32(gy_np).astype(np.float64)
+    n_r = int(ffn.n_routed.item())
+    routed = ffn.routed[:n_r].cpu().numpy().astype(np.int64)
+    ref = oracle.ffn_sparse_backward(x, wg, inp.b_g, wu, wd, gy, ffn.count.cpu().numpy(),
+                                     ffn.idx.cpu().numpy().astype(np.int64), to_f64(ffn.val), cap)
+    refs = [ref]
+    if dense:
+        refs.append(oracle.ffn_dense_backward(x, wg, inp.b_g, wu, wd, gy))
+    got = {k: to_f64(v) for k, v in o.items()}
+    mask = np.zeros(w.T, dtype=bool)
+    mask[routed] = True
+    errs = {}
+    for r in refs:
+        for k in ("gwg_t", "gwu_t", "gwd", "gb"):
+            errs[k] = rel_fro(got[k], r[k])
+            assert errs[k] <= TOL, (k, errs[k])
+        sel = np.arange(w.T) if rows is None else rows
+        errs["gx"] = rel_fro(got["gx"][sel], r["gx"][sel])
+        assert errs["gx"] <= TOL, errs
+        for name, m in (("routed", mask[sel]), ("not_routed", ~mask[sel])):
+            if m.any():
+                errs["gx_" + name] = rel_fro(got["gx"][sel][m], r["gx"][sel][m])
+                assert errs["gx_" + name] <= TOL, errs
+    errs["n_routed"] = n_r
+    return errs
+
+
+@pytest.mark.parametrize("T,d_model,d_ff,beta,cap", [
+    (300, 512, 1024, 1.9, 4),     # ragged rows, routed rows (complete lists)
+    (64, 1024, 512, 1.2, 8),      # two 512-wide chunks, many routed rows
+    (33, 512, 256, 2.0, 8),       # few tokens (the forward's split-K gate)
+    (130, 1536, 384, 1.5, 0),     # capacity 0: every active row routed
+])
+def test_backward_small(T, d_model, d_ff, beta, cap):
+    inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype="bf16", beta=beta,
+                             seed_base=60 + T, cap=cap)
+    e = check(inp, cap, dense=True)
+    if cap == 0:
+        assert e["n_routed"] > 0
+
+
+def test_backward_hybrid_mix_full_size():
+    w = wl.WORKLOADS["hybrid_mix"]
+    inp = wl.generate(w)
+    e = check(inp, w.cap, dense=False, rows=sample_rows(w.T, 256, seed=4))
+    assert e["n_routed"] > 60
+
+
+def test_backward_rejects_unsupported_width():
+    sffn = _sffn()
+    s = sffn.make_shape(64, 264, 256, 8, sffn.SFFN_BF16)
+    ws = torch.empty(max(sffn.workspace_bytes(s, sffn.WS_BACKWARD), 16), dtype=torch.uint8,
+                     device="cuda")
+    b = torch.zeros((64, 264), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((256, 264), dtype=torch.bfloat16, device="cuda")
+    g = [torch.zeros((256, 264), device="cuda") for _ in range(3)]
+    c = torch.zeros((64, 2), dtype=torch.uint16, device="cuda")
+    i = torch.zeros((64, 2, 8), dtype=torch.uint16, device="cuda")
+    v = torch.zeros((64, 2, 8), dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros(64, dtype=torch.int32, device="cuda")
+    with pytest.raises(sffn.SffnError) as ei:
+        sffn.sparse_ffn_bwd(s, b, w, None, w, w, c, i, v, r, r[:1], b, b, *g, None, ws)
+    assert ei.value.status == sffn.SFFN_ERR_UNSUPPORTED
