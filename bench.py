@@ -463,10 +463,20 @@ def main() -> int:
         b2.record()
         torch.cuda.synchronize()
         t_b, t_db = b0.elapsed_time(b1) / K, b1.elapsed_time(b2) / K
+        # activations kept between forward and backward (x and the weights are
+        # kept by both): the sparse path keeps the TwELL arrays and the routed
+        # list (u and the routed rows' gate are recomputed in the backward); a
+        # dense backward keeps h and u, T x d_ff each
+        nt_ = w.d_ff // w.tile
+        sparse_saved = (w.T * nt_ * 2 + w.T * nt_ * max(w.cap, 1) * (2 + 2) + 4 * (w.T + 1))
+        dense_saved = 2 * w.T * w.d_ff * 2
         backward = {"sparse_ffn_bwd_ms": t_b, "torch_dense_backward_ms": t_db,
                     "speedup_vs_torch_dense": t_db / t_b,
                     "weight_grad_bytes": 3.0 * w.d_ff * w.d_model * 4,
-                    "note": "dense: 6 hipBLASLt bf16 GEMMs from saved dense activations"}
+                    "note": "dense: 6 hipBLASLt bf16 GEMMs from saved dense activations",
+                    "saved_activation_bytes": {"sparse_twell_and_routing": sparse_saved,
+                                               "dense_h_and_u": dense_saved,
+                                               "reduction": 1.0 - sparse_saved / dense_saved}}
         del ws_b, gw3, zT, uT, hT, actT, wg_tt, wu_tt
 
     count = ffn.count.to(torch.int64)
