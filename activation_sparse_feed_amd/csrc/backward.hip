@@ -213,27 +213,37 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
 }
 
 // Routed rows: their complete lists are long (a routed row is a heavy one),
-// so each list of n entries is cut into min(kRoutedSplit, ceil(n /
-// kRoutedChunk)) equal parts, one wave per part over a persistent grid; each
-// part writes its partial gx (float32) and bwd_routed_gx sums a row's parts in
-// order.  item_start[r]: first part of routed row r (exclusive prefix of the
-// part counts, bwd_routed_items); item_start[n_routed]: all parts.
+// so the lists are cut into parts of `chunk` entries, one wave per part over a
+// persistent grid; each part writes its partial gx (float32) and
+// bwd_routed_gx sums a row's parts in order.  chunk = max(kRoutedChunk,
+// ceil(E / (7 T))) for E routed entries in all, so there are at most 8 T
+// parts (the partial buffer's size).  item_start[r]: first part of routed row
+// r (exclusive prefix of the part counts, bwd_routed_items);
+// item_start[n_routed]: all parts; item_start[n_routed + 1]: chunk.
 constexpr int kRoutedChunk = 64;
-constexpr int kRoutedSplit = 8;
+constexpr int kRoutedSplit = 8;  // parts per row that the partial buffer holds
 constexpr int kRoutedWaves = 4096;
-
-__device__ __forceinline__ int routed_parts(int n) {
-  return min(kRoutedSplit, (n + kRoutedChunk - 1) / kRoutedChunk);
-}
 
 __global__ __launch_bounds__(1024) void bwd_routed_items(BwdArgs a, int32_t* item_start) {
   __shared__ int wsum[16];
   const int nr = uniform(min(*a.n_routed, a.T));
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+  // all routed entries, then the part size
+  int e = 0;
+  for (int r = (int)threadIdx.x; r < nr; r += 1024) e += min((int)a.ecount[r], a.N);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) e += __shfl_xor(e, o, kWave);
+  if (lane == 0) wsum[w] = e;
+  __syncthreads();
+  int etot = 0;
+  for (int i = 0; i < 16; ++i) etot += wsum[i];
+  __syncthreads();
+  const int budget = max(1, (kRoutedSplit - 1) * a.T);
+  const int chunk = max(kRoutedChunk, (int)(((long)etot + budget - 1) / budget));
   int carry = 0;
   for (int r0 = 0; r0 < nr; r0 += 1024) {
     const int r = r0 + (int)threadIdx.x;
-    const int c = r < nr ? routed_parts(min((int)a.ecount[r], a.N)) : 0;
+    const int c = r < nr ? (min((int)a.ecount[r], a.N) + chunk - 1) / chunk : 0;
     int incl = c;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -251,7 +261,10 @@ __global__ __launch_bounds__(1024) void bwd_routed_items(BwdArgs a, int32_t* ite
     __syncthreads();
     carry = total;
   }
-  if (threadIdx.x == 0) item_start[nr] = carry;
+  if (threadIdx.x == 0) {
+    item_start[nr] = carry;
+    item_start[nr + 1] = chunk;
+  }
 }
 
 template <int P>
@@ -271,8 +284,8 @@ __global__ __launch_bounds__(256) void bwd_routed(BwdArgs a, const int32_t* item
     const int r = uniform(lo);
     const int t = uniform(min(max(a.routed[r], 0), a.T - 1));
     const int n = uniform(min((int)a.ecount[r], a.N));
-    const int np = routed_parts(n), pi = it - item_start[r];
-    const int s0 = (int)((long)pi * n / np), s1 = (int)((long)(pi + 1) * n / np);
+    const int chunk = item_start[nr + 1], pi = it - item_start[r];
+    const int s0 = min(pi * chunk, n), s1 = min(s0 + chunk, n);
     u32x4_t xc[P], gyc[P];
     load_row<P>(a.x, t, a.D, xc);
     load_row<P>(a.gy, t, a.D, gyc);
@@ -462,7 +475,7 @@ size_t backward_workspace_bytes(int T, int N, int D, int cap) {
   const size_t nt = (size_t)N / kBTile;
   return al256((size_t)T * N * 16) + 2 * al256((size_t)T * N * 2) + al256((size_t)T * 2) +
          al256((size_t)T * nt * 4) + al256(nt * T * 2) + al256(nt * T * cap * 2) +
-         al256((size_t)T * nt * cap * 16) + al256(((size_t)T + 1) * 4) +
+         al256((size_t)T * nt * cap * 16) + al256(((size_t)T + 2) * 4) +
          al256((size_t)T * kRoutedSplit * D * 4);
 }
 
@@ -492,7 +505,7 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   f32x4_t* co = (f32x4_t*)p;
   p += al256((size_t)T * nt * cap * 16);
   int32_t* item_start = (int32_t*)p;
-  p += al256(((size_t)T + 1) * 4);
+  p += al256(((size_t)T + 2) * 4);
   float* part = (float*)p;
 
   // routed rows: z with the gate GEMM, then complete activity lists

@@ -25,10 +25,14 @@ namespace {
 
 // z[m, j] = acc + b_g[j] (float32, row-major [rows, N]) for the x rows
 // rowmap[m] (rowmap null: row m), m < rows (n_rows_dev null: T; else the
-// count on the device).
-__global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_preact_bf16(
+// count on the device).  G: GateGemm (the TwELL kernel's own tiles, for the
+// baseline) or RowsGemm (64-row tiles, for a few mapped rows).  Both chain
+// 16x16x32 MFMAs over K, K / 32 roundings: the same guard band holds.
+using RowsGemm = Gemm2<1, kTile, false, 64, 4, false, 64, 4, 4>;
+
+template <class G>
+__global__ __launch_bounds__(64 * G::NWAVES) void gate_preact_bf16(
     GateArgs a, float* z, const int* rowmap, const int* n_rows_dev) {
-  using G = GateGemm;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   int mi, ni;
   tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, (a.N + G::BN - 1) / G::BN, &mi, &ni);
@@ -137,9 +141,8 @@ __global__ __launch_bounds__(256) void twell_convert_bf16(GateArgs a, const floa
 
 // Classic row-wise ELLPACK from z: one wavefront per row walks the column
 // tiles in order with a running slot count across tiles, U tiles of loads in
-// flight per round.  A round with no entry inside the guard band (the common
-// case) is emitted straight from registers; a round with one is redone tile by
-// tile with the exact re-evaluation.  ecount[t] = active columns of the row
+// flight per round, emitted straight from registers; a tile with an entry
+// inside the guard band first gets its exact re-evaluation.  ecount[t] = active columns of the row
 // (uncapped); slots s < min(ecount, width) hold the ascending columns and
 // their values.
 __device__ __forceinline__ void ell_emit(uint16_t* eidx, uint16_t* eval, size_t ebase, int width,
@@ -162,6 +165,34 @@ __device__ __forceinline__ void ell_emit(uint16_t* eidx, uint16_t* eval, size_t 
 
 // Row m of z and of the output is x row rowmap[m] (rowmap null: m), for
 // m < rows (n_rows_dev null: T; else the count on the device).
+// The exact re-evaluation of one tile's flagged entries (|z| not above the
+// band d), out of line so the unrolled round keeps one copy of it.
+struct TileFix {
+  float z0, z1;
+  int a0, a1;
+};
+
+__device__ __noinline__ TileFix ell_fix_tile(const uint16_t* xrow, const uint16_t* wg,
+                                             const float* b, int K, int c0, float z0, float z1,
+                                             float d0, float d1, uint32_t* exact_lds) {
+  const int lane = lane_id();
+  TileFix f{z0, z1, z0 > 0.f, z1 > 0.f};
+  uint64_t fl[2] = {__ballot(!(fabsf(z0) > d0)), __ballot(!(fabsf(z1) > d1))};
+  while (fl[0] | fl[1]) {
+    const int h = fl[0] ? 0 : 1;
+    const int L = __builtin_ctzll(fl[h]);
+    fl[h] &= fl[h] - 1;
+    const int col = c0 + 64 * h + L;
+    const ExactResult e = exact_gate_value<uint16_t, 2>(xrow, wg + (size_t)col * K,
+                                                        b ? b[col] : 0.f, K, exact_lds);
+    if (lane == L) {
+      if (h == 0) { f.a0 = e.sign > 0; f.z0 = (float)e.value; }
+      else        { f.a1 = e.sign > 0; f.z1 = (float)e.value; }
+    }
+  }
+  return f;
+}
+
 template <int U>
 __global__ __launch_bounds__(256) void ell_convert_bf16(GateArgs a, const float* z, int width,
                                                         uint16_t* ecount, uint16_t* eidx,
@@ -191,45 +222,27 @@ __global__ __launch_bounds__(256) void ell_convert_bf16(GateArgs a, const float*
         dv[u][h] = a.gb.coef_xw * nx * a.wnorm[col] + (a.b ? a.gb.coef_b * fabsf(a.b[col]) : 0.f);
       }
     }
-    bool flag = false;
+    uint32_t fm = 0;  // tiles of the round with an entry inside the guard band
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (k0 + u < nt) flag |= !(fabsf(zv[u][0]) > dv[u][0]) || !(fabsf(zv[u][1]) > dv[u][1]);
-    if (!__ballot(flag)) {
+      if (k0 + u < nt &&
+          __ballot(!(fabsf(zv[u][0]) > dv[u][0]) || !(fabsf(zv[u][1]) > dv[u][1])))
+        fm |= 1u << u;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (k0 + u < nt)
-          ell_emit(eidx, eval, ebase, width, (k0 + u) * kTile, zv[u][0] > 0.f, zv[u][1] > 0.f,
-                   zv[u][0], zv[u][1], running);
-      continue;
-    }
-    // rare: this round again, tile by tile, with the exact re-evaluation
-#pragma unroll 1
-    for (int kt = k0; kt < min(k0 + U, nt); ++kt) {
-      const int c0 = kt * kTile;
-      float zz[2] = {zr[c0 + lane], zr[c0 + 64 + lane]};
-      bool act[2] = {zz[0] > 0.f, zz[1] > 0.f};
-      uint64_t fl[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int col = c0 + 64 * h + lane;
-        const float d = a.gb.coef_xw * nx * a.wnorm[col] + (a.b ? a.gb.coef_b * fabsf(a.b[col]) : 0.f);
-        fl[h] = __ballot(!(fabsf(zz[h]) > d));
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u >= nt) break;
+      float z0 = zv[u][0], z1 = zv[u][1];
+      bool a0 = z0 > 0.f, a1 = z1 > 0.f;
+      if ((fm >> u) & 1u) {  // rare: exact re-evaluation of the tile's flagged entries
+        const TileFix f = ell_fix_tile((const uint16_t*)a.x + (size_t)t * a.K,
+                                       (const uint16_t*)a.wg, a.b, a.K, (k0 + u) * kTile, z0, z1,
+                                       dv[u][0], dv[u][1], exact_lds + w * kExactLdsWords);
+        z0 = f.z0;
+        z1 = f.z1;
+        a0 = f.a0 != 0;
+        a1 = f.a1 != 0;
       }
-      while (fl[0] | fl[1]) {
-        const int h = fl[0] ? 0 : 1;
-        const int L = __builtin_ctzll(fl[h]);
-        fl[h] &= fl[h] - 1;
-        const int col = c0 + 64 * h + L;
-        const ExactResult e = exact_gate_value<uint16_t, 2>(
-            (const uint16_t*)a.x + (size_t)t * a.K, (const uint16_t*)a.wg + (size_t)col * a.K,
-            a.b ? a.b[col] : 0.f, a.K, exact_lds + w * kExactLdsWords);
-        if (lane == L) {
-          if (h == 0) { act[0] = e.sign > 0; zz[0] = (float)e.value; }
-          else        { act[1] = e.sign > 0; zz[1] = (float)e.value; }
-        }
-      }
-      ell_emit(eidx, eval, ebase, width, c0, act[0], act[1], zz[0], zz[1], running);
+      ell_emit(eidx, eval, ebase, width, (k0 + u) * kTile, a0, a1, z0, z1, running);
     }
   }
   if (lane == 0) ecount[m] = (uint16_t)running;
@@ -241,10 +254,16 @@ hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g,
                               int K, int N, const int* rowmap, const int* n_rows_dev,
                               hipStream_t stream) {
   GateArgs a{x, wg_t, b_g, nullptr, nullptr, nullptr, nullptr, nullptr, T, K, N, 0, GuardBand{}};
-  const dim3 g((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
-                          ((N + GateGemm::BN - 1) / GateGemm::BN)));
-  hipLaunchKernelGGL(gate_preact_bf16, g, dim3(64 * GateGemm::NWAVES), 0, stream, a, z, rowmap,
-                     n_rows_dev);
+  if (rowmap) {
+    const dim3 g((unsigned)(((T + RowsGemm::BM - 1) / RowsGemm::BM) * (N / RowsGemm::BN)));
+    hipLaunchKernelGGL(gate_preact_bf16<RowsGemm>, g, dim3(64 * RowsGemm::NWAVES), 0, stream, a,
+                       z, rowmap, n_rows_dev);
+  } else {
+    const dim3 g((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
+                            ((N + GateGemm::BN - 1) / GateGemm::BN)));
+    hipLaunchKernelGGL(gate_preact_bf16<GateGemm>, g, dim3(64 * GateGemm::NWAVES), 0, stream, a,
+                       z, rowmap, n_rows_dev);
+  }
   return hipGetLastError();
 }
 
