@@ -35,7 +35,15 @@ __global__ __launch_bounds__(64 * G::NWAVES) void gate_preact_bf16(
     GateArgs a, float* z, const int* rowmap, const int* n_rows_dev) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   int mi, ni;
-  tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, (a.N + G::BN - 1) / G::BN, &mi, &ni);
+  const int ntn = (a.N + G::BN - 1) / G::BN;
+  if (n_rows_dev) {
+    // few mapped rows: the active tiles are the first ones, spread over the
+    // XCDs in dispatch order (the XCD-aware map would put them all on one)
+    mi = (int)blockIdx.x / ntn;
+    ni = (int)blockIdx.x - mi * ntn;
+  } else {
+    tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, ntn, &mi, &ni);
+  }
   const int m0 = mi * G::BM, n0 = ni * G::BN;
   const int mv = uniform(n_rows_dev ? min(*n_rows_dev, a.T) : a.T);
   if (m0 >= mv) return;
