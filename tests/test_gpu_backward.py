@@ -89,6 +89,8 @@ def check(inp: wl.Inputs, cap: int, dense: bool, rows=None):
     (64, 1024, 512, 1.2, 8),      # two 512-wide chunks, many routed rows
     (33, 512, 256, 2.0, 8),       # few tokens (the forward's split-K gate)
     (130, 1536, 384, 1.5, 0),     # capacity 0: every active row routed
+    (40, 4096, 640, 2.0, 4),      # the widest model dimension (eight 512-wide chunks)
+    (97, 2560, 256, 1.7, 2),      # five chunks, odd d-chunk count for the weight gradients
 ])
 def test_backward_small(T, d_model, d_ff, beta, cap):
     inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype="bf16", beta=beta,
@@ -96,6 +98,11 @@ def test_backward_small(T, d_model, d_ff, beta, cap):
     e = check(inp, cap, dense=True)
     if cap == 0:
         assert e["n_routed"] > 0
+
+
+def test_backward_decode_full_size():
+    w = wl.WORKLOADS["decode_1pct"]
+    check(wl.generate(w), w.cap, dense=True)
 
 
 def test_backward_hybrid_mix_full_size():
