@@ -212,6 +212,66 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
   store_gx<P>(a, t, gxa);
 }
 
+// Few tokens (T <= kSplitMaxT): one wave per row would leave the GPU almost
+// idle, so each row's tiles are cut into kRowParts equal ranges, one wave per
+// range, each writing its partial gx (float32); bwd_rows_combine sums a row's
+// ranges in order.  Routed rows are skipped (bwd_routed writes them).
+constexpr int kSplitMaxT = 256;
+constexpr int kRowParts = 16;
+
+template <int P>
+__global__ __launch_bounds__(256) void bwd_rows_split(BwdArgs a, float* rpart) {
+  const int item = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int t = item / kRowParts, pi = item - t * kRowParts;
+  if (t >= a.T || row_is_routed(a, t)) return;
+  u32x4_t xc[P], gyc[P];
+  load_row<P>(a.x, t, a.D, xc);
+  load_row<P>(a.gy, t, a.D, gyc);
+  float gxa[P][8];
+#pragma unroll
+  for (int c = 0; c < P; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gxa[c][e] = 0.f;
+  const int k0 = (int)((long)pi * a.nt / kRowParts), k1 = (int)((long)(pi + 1) * a.nt / kRowParts);
+  for (int k = k0; k < k1; ++k) {
+    const size_t tk = (size_t)t * a.nt + k;
+    const int c = uniform(min((int)a.count[tk], a.cap));
+    for (int s = 0; s < c; ++s) {
+      const size_t pos = tk * a.cap + s;
+      const int j = uniform(min((int)a.idx[pos], a.N - 1));  // valid lists: j < N already
+      bwd_entry<P>(a, j, bf16_to_f32(a.val[pos]), xc, gyc, gxa, a.co + pos);
+    }
+  }
+  float* dst = rpart + (size_t)item * a.D + (size_t)lane_id() * 8;
+#pragma unroll
+  for (int c = 0; c < P; ++c) {
+    *(f32x4_t*)(dst + c * 512) = f32x4_t{gxa[c][0], gxa[c][1], gxa[c][2], gxa[c][3]};
+    *(f32x4_t*)(dst + c * 512 + 4) = f32x4_t{gxa[c][4], gxa[c][5], gxa[c][6], gxa[c][7]};
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_rows_combine(BwdArgs a, const float* rpart) {
+  const int t = (int)blockIdx.y;
+  // routed rows: written by bwd_routed_gx (their flag: some count over cap)
+  __shared__ int routed_s;
+  if (threadIdx.x < kWave) {
+    const bool r = row_is_routed(a, t);
+    if (threadIdx.x == 0) routed_s = r;
+  }
+  __syncthreads();
+  if (routed_s) return;
+  for (int d = ((int)blockIdx.x * 256 + (int)threadIdx.x) * 2; d < a.D; d += (int)gridDim.x * 512) {
+    float v0 = 0.f, v1 = 0.f;
+    for (int p = 0; p < kRowParts; ++p) {
+      const float* src = rpart + ((size_t)t * kRowParts + p) * a.D + d;
+      v0 += src[0];
+      v1 += src[1];
+    }
+    *(uint32_t*)(a.gx + (size_t)t * a.D + d) =
+        (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
+  }
+}
+
 // Routed rows: their complete lists are long (a routed row is a heavy one),
 // so the lists are cut into parts of `chunk` entries, one wave per part over a
 // persistent grid; each part writes its partial gx (float32) and
@@ -476,7 +536,8 @@ size_t backward_workspace_bytes(int T, int N, int D, int cap) {
   return al256((size_t)T * N * 16) + 2 * al256((size_t)T * N * 2) + al256((size_t)T * 2) +
          al256((size_t)T * nt * 4) + al256(nt * T * 2) + al256(nt * T * cap * 2) +
          al256((size_t)T * nt * cap * 16) + al256(((size_t)T + 2) * 4) +
-         al256((size_t)T * kRoutedSplit * D * 4);
+         al256((size_t)T * kRoutedSplit * D * 4) +
+         (T <= kSplitMaxT ? al256((size_t)T * kRowParts * D * 4) : 0);
 }
 
 hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
@@ -507,6 +568,8 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   int32_t* item_start = (int32_t*)p;
   p += al256(((size_t)T + 2) * 4);
   float* part = (float*)p;
+  p += al256((size_t)T * kRoutedSplit * D * 4);
+  float* rpart = (float*)p;  // few tokens only
 
   // routed rows: z with the gate GEMM, then complete activity lists
   hipError_t e = launch_gate_preact(x, wg_t, b_g, z_r, T, D, N, routed, n_routed, stream);
@@ -526,7 +589,11 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   switch (D / 512) {
 #define SFFN_BWD_ROWS(P)                                                                        \
   case P:                                                                                        \
-    hipLaunchKernelGGL(bwd_rows<P>, rows_grid, dim3(256), 0, stream, a);                         \
+    if (T <= kSplitMaxT)                                                                         \
+      hipLaunchKernelGGL(bwd_rows_split<P>, dim3((unsigned)((T * kRowParts + 3) / 4)),           \
+                         dim3(256), 0, stream, a, rpart);                                        \
+    else                                                                                         \
+      hipLaunchKernelGGL(bwd_rows<P>, rows_grid, dim3(256), 0, stream, a);                       \
     hipLaunchKernelGGL(bwd_routed_items, dim3(1), dim3(1024), 0, stream, a, item_start);         \
     hipLaunchKernelGGL(bwd_routed<P>, dim3(kRoutedWaves / 4), dim3(256), 0, stream, a,           \
                        (const int32_t*)item_start, part);                                        \
@@ -542,6 +609,12 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
                      a, (const int32_t*)item_start, (const float*)part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (T <= kSplitMaxT) {
+    hipLaunchKernelGGL(bwd_rows_combine, dim3((unsigned)((D + 511) / 512), (unsigned)T), dim3(256),
+                       0, stream, a, (const float*)rpart);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // rows per staged block: counts + cap indices each, in 32 KB of LDS, a
   // multiple of the wave width
   const int rpb = max(kWave, (kColLdsHalves / (1 + max(cap, 1))) / kWave * kWave);
