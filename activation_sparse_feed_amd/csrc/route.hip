@@ -4,7 +4,7 @@
 // A row is routed when any of its TwELL tiles holds more active columns than
 // the capacity.  Two small kernels, no atomics, deterministic:
 //   route_flags    per row (lanes over the tiles): flag = OR_k (count[t, k] > cap),
-//                  and the number of flagged rows of each 64-row group
+//                  and the number of flagged rows of each 16-row group
 //   route_compact  each 256-row block adds the group counts before it, then
 //                  writes its flagged rows in ascending order; the last block
 //                  writes n_routed.
@@ -19,7 +19,7 @@ namespace {
 
 constexpr int kBlock = 256;
 
-constexpr int kFlagRows = 64;  // rows per workgroup of route_flags (16 per wave)
+constexpr int kFlagRows = 16;  // rows per workgroup of route_flags (4 per wave)
 
 __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict__ count, int T,
                                                       int nt, int cap, int* __restrict__ flags,
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ 
   __shared__ int prefix_s;
   const int b = blockIdx.x;
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  // flagged rows before this block: the counts of the 64-row groups before it
+  // flagged rows before this block: the counts of the 16-row groups before it
   int acc = 0;
   for (int i = threadIdx.x; i < b * (kBlock / kFlagRows); i += kBlock) acc += group_count[i];
 #pragma unroll
