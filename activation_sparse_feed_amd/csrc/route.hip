@@ -24,8 +24,8 @@ constexpr int kFlagRows = 16;  // rows per workgroup of route_flags (4 per wave)
 __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict__ count, int T,
                                                       int nt, int cap, int* __restrict__ flags,
                                                       int* __restrict__ group_count) {
-  // wave w takes rows w, w + 4, ... of the workgroup's 64; for each row the
-  // lanes read the tiles' counts side by side (coalesced), all sixteen rows'
+  // wave w takes rows w, w + 4, ... of the workgroup's 16; for each row the
+  // lanes read the tiles' counts side by side (coalesced), all four rows'
   // loads in flight together
   const int lane = lane_id(), w = threadIdx.x >> 6;
   constexpr int R = kFlagRows / 4;
