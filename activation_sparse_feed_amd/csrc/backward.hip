@@ -25,10 +25,13 @@
 //              the same for the routed rows, whose long lists are cut into up
 //              to eight parts (one wave each) whose partial gx are summed in
 //              part order;
-//   bwd_cols   one wave per (column, d chunk): finds the column's entries by
-//              scanning the tile-major lists (staged in LDS) in row order,
-//              then the routed rows, and sums the weight-gradient rows in
-//              registers; every column is written (zero when inactive).
+//   csc_count, csc_colscan, csc_ptr, csc_fill
+//              the TwELL entries regrouped by column (row order within a
+//              column), deterministic;
+//   bwd_cols   one wave per (column, d chunk): the column's entries from its
+//              list, then the routed rows' (binary search in their lists),
+//              summed into the weight-gradient rows in registers; every column
+//              is written (zero when inactive).
 // Every sum runs in a fixed order, so the gradients are deterministic.
 #include "common.cuh"
 #include "launch.h"
@@ -389,13 +392,124 @@ __global__ __launch_bounds__(256) void bwd_routed_gx(BwdArgs a, const int32_t* i
   }
 }
 
-// Weight gradients.  Workgroup = 16 waves = 16 consecutive columns of one
-// tile and one chunk of PC * 512 model dimensions; the tile's tile-major
-// counts and indices are staged in LDS a block of rows at a time and every
-// wave scans them for its own column (ascending rows, so the sums run in row
-// order), then scans the routed rows' lists (binary search per row).
-constexpr int kColWaves = 16;
-constexpr int kColLdsHalves = 16384;  // 32 KB of u16: counts and indices of a row block
+// Column lists of the TwELL entries (rows within capacity), built once so
+// that each column's weight-gradient sums read its entries as one contiguous
+// list in row order: csc_count counts the entries of every column per block
+// of kCscRows rows, csc_colscan turns the counts into each block's start
+// within its column and the column totals, csc_ptr scans the totals into
+// col_ptr, and csc_fill places every entry (row, gz, gu, a).  Inside a 64-row
+// chunk an entry's rank among its column's entries is the number of lower
+// lanes (rows) that hold the column, read from a per-column lane mask in LDS,
+// so the lists are in row order and the build is deterministic.
+constexpr int kCscRows = 256;
+
+__device__ __forceinline__ int tile_col(const BwdArgs& a, size_t g, int s, int k) {
+  return min(max((int)a.idx_t[g * a.cap + s] - k * kBTile, 0), kBTile - 1);
+}
+
+__global__ __launch_bounds__(64) void csc_count(BwdArgs a, int* hist) {
+  __shared__ int cnt[kBTile];
+  const int lane = lane_id();
+  const int k = (int)blockIdx.x % a.nt, rb = (int)blockIdx.x / a.nt;
+  cnt[lane] = 0;
+  cnt[lane + kWave] = 0;
+  __syncthreads();
+  const int r1 = min((rb + 1) * kCscRows, a.T);
+  for (int t = rb * kCscRows + lane; t < r1; t += kWave) {
+    const size_t g = (size_t)k * a.T + t;
+    const int c = (int)a.count_t[g];
+    for (int s = 0; s < c; ++s) atomicAdd(&cnt[tile_col(a, g, s, k)], 1);
+  }
+  __syncthreads();
+  int* h = hist + (size_t)rb * a.N + k * kBTile;
+  h[lane] = cnt[lane];
+  h[lane + kWave] = cnt[lane + kWave];
+}
+
+__global__ __launch_bounds__(256) void csc_colscan(BwdArgs a, int* hist, int* total, int nblk) {
+  const int j = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (j >= a.N) return;
+  int run = 0;
+  for (int b = 0; b < nblk; ++b) {
+    const int v = hist[(size_t)b * a.N + j];
+    hist[(size_t)b * a.N + j] = run;
+    run += v;
+  }
+  total[j] = run;
+}
+
+__global__ __launch_bounds__(1024) void csc_ptr(const int* total, int N, int* col_ptr) {
+  __shared__ int wsum[16];
+  const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+  const int per = (N + 1023) / 1024;
+  const int lo = min((int)threadIdx.x * per, N), hi = min(lo + per, N);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += total[i];
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == kWave - 1) wsum[w] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int i = 0; i < w; ++i) run += wsum[i];
+  for (int i = lo; i < hi; ++i) {
+    col_ptr[i] = run;
+    run += total[i];
+  }
+  if (threadIdx.x == 1023) col_ptr[N] = run;
+}
+
+__global__ __launch_bounds__(64) void csc_fill(BwdArgs a, const int* hist, const int* col_ptr,
+                                               f32x4_t* csc) {
+  __shared__ int run[kBTile];
+  __shared__ uint32_t mlo[kBTile], mhi[kBTile];
+  const int lane = lane_id();
+  const int k = (int)blockIdx.x % a.nt, rb = (int)blockIdx.x / a.nt;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int jl = lane + kWave * h;
+    run[jl] = col_ptr[k * kBTile + jl] + hist[(size_t)rb * a.N + k * kBTile + jl];
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int r1 = min((rb + 1) * kCscRows, a.T);
+  for (int t0 = rb * kCscRows; t0 < r1; t0 += kWave) {
+    const int t = t0 + lane;
+    const size_t g = (size_t)k * a.T + t;
+    const int c = t < r1 ? (int)a.count_t[g] : 0;
+    mlo[lane] = mlo[lane + kWave] = 0u;
+    mhi[lane] = mhi[lane + kWave] = 0u;
+    __syncthreads();
+    for (int s = 0; s < c; ++s) {
+      const int jl = tile_col(a, g, s, k);
+      if (lane < 32) atomicOr(&mlo[jl], 1u << lane);
+      else atomicOr(&mhi[jl], 1u << (lane - 32));
+    }
+    __syncthreads();
+    for (int s = 0; s < c; ++s) {
+      const int jl = tile_col(a, g, s, k);
+      const uint64_t m = ((uint64_t)mhi[jl] << 32) | mlo[jl];
+      const int pos = run[jl] + __popcll(m & below);
+      const f32x4_t co = a.co[((size_t)t * a.nt + k) * a.cap + s];
+      csc[pos] = f32x4_t{__int_as_float(t), co[0], co[1], co[2]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int jl = lane + kWave * h;
+      run[jl] += __popcll(((uint64_t)mhi[jl] << 32) | mlo[jl]);
+    }
+    __syncthreads();
+  }
+}
+
+// Weight gradients: one wave per (column, chunk of PC * 512 model dimensions).
+// The column's TwELL entries come from its list (row order), kColBatch
+// entries' x and gy rows loaded together; then the routed rows' entries (one
+// binary search per routed row in its complete list, ascending rows).  Every
+// column is written (zero when inactive).
 
 // acc += coef * (this lane's chunks of row t), for one matched entry.
 template <int PC>
@@ -424,61 +538,71 @@ __device__ __forceinline__ void col_accumulate(const BwdArgs& a, int t, int d0, 
   gbs += coef[0];
 }
 
+// The same for kColBatch entries (rows t[i], coefficients coef[i] = (gz, gu,
+// a); entries past the list carry 0), their rows loaded together, summed in
+// batch order.
+constexpr int kColBatch = 4;
+
 template <int PC>
-__global__ __launch_bounds__(64 * kColWaves) void bwd_cols(BwdArgs a, int rows_per_block) {
-  __shared__ uint16_t lds[kColLdsHalves];
+__device__ __forceinline__ void col_accumulate_batch(const BwdArgs& a, const int* t, int d0,
+                                                     const f32x4_t* coef, float (*ag)[8],
+                                                     float (*au)[8], float (*ad)[8], float& gbs) {
+  u32x4_t xc[kColBatch][PC], gc[kColBatch][PC];
+#pragma unroll
+  for (int i = 0; i < kColBatch; ++i) {
+    const size_t ro = (size_t)t[i] * a.D + d0 + (size_t)lane_id() * 8;
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      xc[i][c] = ldg16(a.x + ro + c * 512);
+      gc[i][c] = ldg16(a.gy + ro + c * 512);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kColBatch; ++i) {
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      float xf[8], gf[8];
+      Elt<uint16_t>::unpack(xc[i][c], xf);
+      Elt<uint16_t>::unpack(gc[i][c], gf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ag[c][e] = fmaf(coef[i][0], xf[e], ag[c][e]);
+        au[c][e] = fmaf(coef[i][1], xf[e], au[c][e]);
+        ad[c][e] = fmaf(coef[i][2], gf[e], ad[c][e]);
+      }
+    }
+    gbs += coef[i][0];
+  }
+}
+
+template <int PC>
+__global__ __launch_bounds__(256) void bwd_cols(BwdArgs a, const int* col_ptr, const f32x4_t* csc) {
   const int w = uniform((int)(threadIdx.x >> 6));
   const int lane = lane_id();
   const int dchunks = a.D / (PC * 512);
-  const int bid = (int)blockIdx.x;
-  const int dc = bid % dchunks;
-  const int cg = (bid / dchunks) % (kBTile / kColWaves);
-  const int k = bid / (dchunks * (kBTile / kColWaves));
-  const int j = k * kBTile + cg * kColWaves + w;
+  const int dc = (int)blockIdx.x % dchunks;
+  const int j = ((int)blockIdx.x / dchunks) * 4 + w;
   const int d0 = dc * PC * 512;
-  uint16_t* cnt_s = lds;
-  uint16_t* idx_s = lds + rows_per_block;
   float ag[PC][8], au[PC][8], ad[PC][8];
 #pragma unroll
   for (int c = 0; c < PC; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) ag[c][e] = au[c][e] = ad[c][e] = 0.f;
   float gbs = 0.f;
-  for (int row0 = 0; row0 < a.T; row0 += rows_per_block) {
-    const int nrow = min(rows_per_block, a.T - row0);
-    __syncthreads();  // the previous block's scan is done
-    for (int i = (int)threadIdx.x; i < nrow; i += (int)blockDim.x) {
-      const size_t g = (size_t)k * a.T + row0 + i;
-      const int c = (int)a.count_t[g];
-      cnt_s[i] = (uint16_t)c;
-      for (int s = 0; s < c; ++s) idx_s[i * a.cap + s] = a.idx_t[g * a.cap + s];
+  const int e0 = uniform(col_ptr[j]), e1 = uniform(col_ptr[j + 1]);
+  for (int e = e0; e < e1; e += kColBatch) {
+    int tb[kColBatch];
+    f32x4_t cb[kColBatch];
+#pragma unroll
+    for (int i = 0; i < kColBatch; ++i) {
+      const f32x4_t v = csc[min(e + i, e1 - 1)];
+      tb[i] = min(max(__float_as_int(v[0]), 0), a.T - 1);
+      cb[i] = e + i < e1 ? f32x4_t{v[1], v[2], v[3], 0.f} : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
-    for (int rb = 0; rb < nrow; rb += kWave) {
-      const int i = rb + lane;
-      int match = -1;
-      if (i < nrow) {
-        const int c = (int)cnt_s[i];
-        for (int s = 0; s < c; ++s) {
-          const int v = (int)idx_s[i * a.cap + s];
-          if (v >= j) {
-            if (v == j) match = s;
-            break;
-          }
-        }
-      }
-      uint64_t m = __ballot(match >= 0);
-      while (m) {
-        const int L = __builtin_ctzll(m);
-        m &= m - 1;
-        const int t = row0 + rb + L;
-        const int s = __shfl(match, L, kWave);
-        const f32x4_t coef = a.co[((size_t)t * a.nt + k) * a.cap + s];
-        col_accumulate<PC>(a, t, d0, coef, ag, au, ad, gbs);
-      }
-    }
+    col_accumulate_batch<PC>(a, tb, d0, cb, ag, au, ad, gbs);
   }
   // routed rows: their complete lists, one binary search per row
+  const int k = j / kBTile;
   const int nr = uniform(min(*a.n_routed, a.T));
   for (int r0 = 0; r0 < nr; r0 += kWave) {
     const int r = r0 + lane;
@@ -487,7 +611,7 @@ __global__ __launch_bounds__(64 * kColWaves) void bwd_cols(BwdArgs a, int rows_p
       tr = a.routed[r];
       // the tile's range of the row's list, kept inside the list's N slots
       const int beg = min(max(a.eoff[(size_t)r * a.nt + k], 0), a.N);
-      const int end = min(beg + (int)a.count[(size_t)tr * a.nt + k], a.N);
+      const int end = min(beg + (int)a.count[(size_t)min(max(tr, 0), a.T - 1) * a.nt + k], a.N);
       const uint16_t* li = a.eidx + (size_t)r * a.N;
       int lo = beg, hi = end;
       while (lo < hi) {
@@ -537,7 +661,9 @@ size_t backward_workspace_bytes(int T, int N, int D, int cap) {
          al256((size_t)T * nt * 4) + al256(nt * T * 2) + al256(nt * T * cap * 2) +
          al256((size_t)T * nt * cap * 16) + al256(((size_t)T + 2) * 4) +
          al256((size_t)T * kRoutedSplit * D * 4) +
-         (T <= kSplitMaxT ? al256((size_t)T * kRowParts * D * 4) : 0);
+         (T <= kSplitMaxT ? al256((size_t)T * kRowParts * D * 4) : 0) +
+         al256((size_t)((T + kCscRows - 1) / kCscRows) * N * 4) + al256((size_t)N * 4) +
+         al256(((size_t)N + 1) * 4) + al256((size_t)T * nt * cap * 16);
 }
 
 hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
@@ -570,6 +696,15 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   float* part = (float*)p;
   p += al256((size_t)T * kRoutedSplit * D * 4);
   float* rpart = (float*)p;  // few tokens only
+  p += T <= kSplitMaxT ? al256((size_t)T * kRowParts * D * 4) : 0;
+  const int nblk = (T + kCscRows - 1) / kCscRows;
+  int* hist = (int*)p;
+  p += al256((size_t)nblk * N * 4);
+  int* total = (int*)p;
+  p += al256((size_t)N * 4);
+  int* col_ptr = (int*)p;
+  p += al256(((size_t)N + 1) * 4);
+  f32x4_t* csc = (f32x4_t*)p;
 
   // routed rows: z with the gate GEMM, then complete activity lists
   hipError_t e = launch_gate_preact(x, wg_t, b_g, z_r, T, D, N, routed, n_routed, stream);
@@ -615,16 +750,22 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // rows per staged block: counts + cap indices each, in 32 KB of LDS, a
-  // multiple of the wave width
-  const int rpb = max(kWave, (kColLdsHalves / (1 + max(cap, 1))) / kWave * kWave);
-  if (D % 1024 == 0) {
-    const dim3 g((unsigned)(nt * (kBTile / kColWaves) * (D / 1024)));
-    hipLaunchKernelGGL(bwd_cols<2>, g, dim3(64 * kColWaves), 0, stream, a, rpb);
-  } else {
-    const dim3 g((unsigned)(nt * (kBTile / kColWaves) * (D / 512)));
-    hipLaunchKernelGGL(bwd_cols<1>, g, dim3(64 * kColWaves), 0, stream, a, rpb);
-  }
+  // the TwELL entries' column lists, then the weight gradients
+  const dim3 tiles_blocks((unsigned)(nt * nblk));
+  hipLaunchKernelGGL(csc_count, tiles_blocks, dim3(64), 0, stream, a, hist);
+  hipLaunchKernelGGL(csc_colscan, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, a, hist,
+                     total, nblk);
+  hipLaunchKernelGGL(csc_ptr, dim3(1), dim3(1024), 0, stream, (const int*)total, N, col_ptr);
+  hipLaunchKernelGGL(csc_fill, tiles_blocks, dim3(64), 0, stream, a, (const int*)hist,
+                     (const int*)col_ptr, csc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (D % 1024 == 0)
+    hipLaunchKernelGGL(bwd_cols<2>, dim3((unsigned)(N / 4 * (D / 1024))), dim3(256), 0, stream, a,
+                       (const int*)col_ptr, (const f32x4_t*)csc);
+  else
+    hipLaunchKernelGGL(bwd_cols<1>, dim3((unsigned)(N / 4 * (D / 512))), dim3(256), 0, stream, a,
+                       (const int*)col_ptr, (const f32x4_t*)csc);
   return hipGetLastError();
 }
 
