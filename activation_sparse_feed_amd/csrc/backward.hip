@@ -462,8 +462,10 @@ __global__ __launch_bounds__(1024) void csc_ptr(const int* total, int N, int* co
   if (threadIdx.x == 1023) col_ptr[N] = run;
 }
 
+// Entries: (row, gz, gu, a) when the per-entry gradients exist already
+// (with_grads), else (row, TwELL position, h) for bwd_cols_fused.
 __global__ __launch_bounds__(64) void csc_fill(BwdArgs a, const int* hist, const int* col_ptr,
-                                               f32x4_t* csc) {
+                                               f32x4_t* csc, int with_grads) {
   __shared__ int run[kBTile];
   __shared__ uint32_t mlo[kBTile], mhi[kBTile];
   const int lane = lane_id();
@@ -492,8 +494,13 @@ __global__ __launch_bounds__(64) void csc_fill(BwdArgs a, const int* hist, const
       const int jl = tile_col(a, g, s, k);
       const uint64_t m = ((uint64_t)mhi[jl] << 32) | mlo[jl];
       const int pos = run[jl] + __popcll(m & below);
-      const f32x4_t co = a.co[((size_t)t * a.nt + k) * a.cap + s];
-      csc[pos] = f32x4_t{__int_as_float(t), co[0], co[1], co[2]};
+      const size_t tp = ((size_t)t * a.nt + k) * a.cap + s;
+      if (with_grads) {
+        const f32x4_t co = a.co[tp];
+        csc[pos] = f32x4_t{__int_as_float(t), co[0], co[1], co[2]};
+      } else {
+        csc[pos] = f32x4_t{__int_as_float(t), __int_as_float((int)tp), bf16_to_f32(a.val[tp]), 0.f};
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -644,6 +651,201 @@ __global__ __launch_bounds__(256) void bwd_cols(BwdArgs a, const int* col_ptr, c
   if (a.gb && dc == 0 && lane == 0) a.gb[j] = gbs;
 }
 
+// Fused order for d_model <= 2048 and more than kSplitMaxT tokens.  The
+// column pass already loads x_t and gy_t for every entry of a column, so with
+// the column's wu_t and wd rows held in registers it computes the entry's dot
+// products itself (gz, gu, a, stored at the entry's TwELL position) and sums
+// the weight gradients in the same step; the row pass (bwd_gx) then only
+// gathers wg_t and wu_t rows per entry for gx, with no reduction in its chain.
+// Four gathered rows per entry instead of five.
+constexpr int kFusedBatch = 2;
+
+template <int P>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_cols_fused(BwdArgs a, const int* col_ptr,
+                                                      const f32x4_t* csc) {
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int lane = lane_id();
+  const int j = (int)blockIdx.x * 4 + w;
+  // the column's wu_t and wd rows, each lane's 8-element pieces kept in LDS
+  // (read back by the same lane only, so no barrier) to leave registers for
+  // two waves per SIMD
+  __shared__ u32x4_t wrow_s[4][2][P][kWave];
+  {
+    u32x4_t uw[P], dw[P];
+    load_row<P>(a.wu, j, a.D, uw);
+    load_row<P>(a.wd, j, a.D, dw);
+#pragma unroll
+    for (int c = 0; c < P; ++c) {
+      wrow_s[w][0][c][lane] = uw[c];
+      wrow_s[w][1][c][lane] = dw[c];
+    }
+  }
+  float ag[P][8], au[P][8], ad[P][8];
+#pragma unroll
+  for (int c = 0; c < P; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[c][e] = au[c][e] = ad[c][e] = 0.f;
+  float gbs = 0.f;
+  const int e0 = uniform(col_ptr[j]), e1 = uniform(col_ptr[j + 1]);
+  for (int e = e0; e < e1; e += kFusedBatch) {
+    u32x4_t xc[kFusedBatch][P], gc[kFusedBatch][P];
+    int pos[kFusedBatch];
+    float h[kFusedBatch];
+#pragma unroll
+    for (int i = 0; i < kFusedBatch; ++i) {
+      const f32x4_t v = csc[min(e + i, e1 - 1)];
+      const int t = min(max(__float_as_int(v[0]), 0), a.T - 1);
+      pos[i] = __float_as_int(v[1]);
+      h[i] = v[2];
+      load_row<P>(a.x, t, a.D, xc[i]);
+      load_row<P>(a.gy, t, a.D, gc[i]);
+    }
+    // an opaque zero offset: keeps the compiler from hoisting the LDS reads
+    // (and the registers they would hold) out of the loop
+    int lofs = 0;
+    asm volatile("" : "+v"(lofs));
+    const u32x4_t* wu_l = &wrow_s[w][0][0][lane + lofs];
+    const u32x4_t* wd_l = &wrow_s[w][1][0][lane + lofs];
+#pragma unroll
+    for (int i = 0; i < kFusedBatch; ++i) {
+      float su = 0.f, sg = 0.f;
+#pragma unroll
+      for (int c = 0; c < P; ++c) {
+        float xf[8], uf[8], gf[8], df[8];
+        Elt<uint16_t>::unpack(xc[i][c], xf);
+        Elt<uint16_t>::unpack(wu_l[c * kWave], uf);
+        Elt<uint16_t>::unpack(gc[i][c], gf);
+        Elt<uint16_t>::unpack(wd_l[c * kWave], df);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          su = fmaf(xf[q], uf[q], su);
+          sg = fmaf(gf[q], df[q], sg);
+        }
+      }
+      const float u = wave_sum_uniform(su);
+      const float ga = wave_sum_uniform(sg);
+      const bool live = e + i < e1;
+      const float gz = live ? ga * u : 0.f, gu = live ? ga * h[i] : 0.f;
+      const float aa = live ? h[i] * u : 0.f;
+      if (live && lane == 0) a.co[pos[i]] = f32x4_t{gz, gu, aa, 0.f};
+#pragma unroll
+      for (int c = 0; c < P; ++c) {
+        float xf[8], gf[8];
+        Elt<uint16_t>::unpack(xc[i][c], xf);
+        Elt<uint16_t>::unpack(gc[i][c], gf);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          ag[c][q] = fmaf(gz, xf[q], ag[c][q]);
+          au[c][q] = fmaf(gu, xf[q], au[c][q]);
+          ad[c][q] = fmaf(aa, gf[q], ad[c][q]);
+        }
+      }
+      gbs += gz;
+    }
+  }
+  // routed rows: their entries' gradients come from bwd_routed
+  const int k = j / kBTile;
+  const int nr = uniform(min(*a.n_routed, a.T));
+  for (int r0 = 0; r0 < nr; r0 += kWave) {
+    const int r = r0 + lane;
+    int match = -1, tr = 0;
+    if (r < nr) {
+      tr = a.routed[r];
+      const int beg = min(max(a.eoff[(size_t)r * a.nt + k], 0), a.N);
+      const int end = min(beg + (int)a.count[(size_t)min(max(tr, 0), a.T - 1) * a.nt + k], a.N);
+      const uint16_t* li = a.eidx + (size_t)r * a.N;
+      int lo = beg, hi = end;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)li[mid] < j) lo = mid + 1;
+        else hi = mid;
+      }
+      if (lo < end && (int)li[lo] == j) match = lo;
+    }
+    uint64_t m = __ballot(match >= 0);
+    while (m) {
+      const int L = __builtin_ctzll(m);
+      m &= m - 1;
+      const int t = min(max(__shfl(tr, L, kWave), 0), a.T - 1);
+      const int s = __shfl(match, L, kWave);
+      const f32x4_t coef = a.co_r[(size_t)(r0 + L) * a.N + s];
+      col_accumulate<P>(a, t, 0, coef, ag, au, ad, gbs);
+    }
+  }
+  const size_t wo = (size_t)j * a.D + (size_t)lane * 8;
+#pragma unroll
+  for (int c = 0; c < P; ++c) {
+    *(f32x4_t*)(a.gwg + wo + c * 512) = f32x4_t{ag[c][0], ag[c][1], ag[c][2], ag[c][3]};
+    *(f32x4_t*)(a.gwg + wo + c * 512 + 4) = f32x4_t{ag[c][4], ag[c][5], ag[c][6], ag[c][7]};
+    *(f32x4_t*)(a.gwu + wo + c * 512) = f32x4_t{au[c][0], au[c][1], au[c][2], au[c][3]};
+    *(f32x4_t*)(a.gwu + wo + c * 512 + 4) = f32x4_t{au[c][4], au[c][5], au[c][6], au[c][7]};
+    *(f32x4_t*)(a.gwd + wo + c * 512) = f32x4_t{ad[c][0], ad[c][1], ad[c][2], ad[c][3]};
+    *(f32x4_t*)(a.gwd + wo + c * 512 + 4) = f32x4_t{ad[c][4], ad[c][5], ad[c][6], ad[c][7]};
+  }
+  if (a.gb && lane == 0) a.gb[j] = gbs;
+}
+
+// gx of the rows within capacity from the stored per-entry gradients: the
+// row's entries are gathered a group of tiles at a time into a per-wave list
+// (TwELL positions, ascending) and taken kGxBatch at a time, their wg_t and
+// wu_t rows loaded together.
+constexpr int kGxList = 512;
+constexpr int kGxBatch = 4;
+
+template <int P>
+__global__ __launch_bounds__(256) void bwd_gx(BwdArgs a) {
+  __shared__ int list_s[4][kGxList];
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int lane = lane_id();
+  const int t = (int)blockIdx.x * 4 + w;
+  if (t >= a.T || row_is_routed(a, t)) return;
+  int* list = list_s[w];
+  float gxa[P][8];
+#pragma unroll
+  for (int c = 0; c < P; ++c)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) gxa[c][q] = 0.f;
+  const int G = min(kWave, max(1, kGxList / max(a.cap, 1)));  // tiles per group
+  for (int kb = 0; kb < a.nt; kb += G) {
+    const int k = kb + lane;
+    const int c = (lane < G && k < a.nt) ? min((int)a.count[(size_t)t * a.nt + k], a.cap) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    const int n = uniform(__shfl(incl, kWave - 1, kWave));
+    for (int s = 0; s < c; ++s) list[incl - c + s] = (int)(((size_t)t * a.nt + k) * a.cap + s);
+    __builtin_amdgcn_wave_barrier();
+    for (int e0 = 0; e0 < n; e0 += kGxBatch) {
+      u32x4_t gw[kGxBatch][P], uw[kGxBatch][P];
+      f32x4_t co[kGxBatch];
+#pragma unroll
+      for (int i = 0; i < kGxBatch; ++i) {
+        const int pos = uniform(list[min(e0 + i, n - 1)]);
+        const int j = uniform(min((int)a.idx[pos], a.N - 1));  // valid lists: j < N already
+        co[i] = e0 + i < n ? a.co[pos] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        load_row<P>(a.wg, j, a.D, gw[i]);
+        load_row<P>(a.wu, j, a.D, uw[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kGxBatch; ++i)
+#pragma unroll
+        for (int cc = 0; cc < P; ++cc) {
+          float gf[8], uf[8];
+          Elt<uint16_t>::unpack(gw[i][cc], gf);
+          Elt<uint16_t>::unpack(uw[i][cc], uf);
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            gxa[cc][q] = fmaf(co[i][1], uf[q], fmaf(co[i][0], gf[q], gxa[cc][q]));
+        }
+    }
+    __builtin_amdgcn_wave_barrier();  // the list is rewritten by the next group
+  }
+  store_gx<P>(a, t, gxa);
+}
+
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -721,13 +923,18 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   hipLaunchKernelGGL(bwd_prep, rows_grid, dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // the fused order keeps TwELL positions in 31 bits and a row's group of
+  // tiles inside bwd_gx's list
+  const bool fused = D <= 2048 && T > kSplitMaxT && cap <= kGxList &&
+                     (size_t)T * nt * (size_t)cap < ((size_t)1 << 31);
+  const dim3 tiles_blocks((unsigned)(nt * nblk));
   switch (D / 512) {
 #define SFFN_BWD_ROWS(P)                                                                        \
   case P:                                                                                        \
-    if (T <= kSplitMaxT)                                                                         \
+    if (!fused && T <= kSplitMaxT)                                                               \
       hipLaunchKernelGGL(bwd_rows_split<P>, dim3((unsigned)((T * kRowParts + 3) / 4)),           \
                          dim3(256), 0, stream, a, rpart);                                        \
-    else                                                                                         \
+    else if (!fused)                                                                             \
       hipLaunchKernelGGL(bwd_rows<P>, rows_grid, dim3(256), 0, stream, a);                       \
     hipLaunchKernelGGL(bwd_routed_items, dim3(1), dim3(1024), 0, stream, a, item_start);         \
     hipLaunchKernelGGL(bwd_routed<P>, dim3(kRoutedWaves / 4), dim3(256), 0, stream, a,           \
@@ -744,22 +951,32 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
                      a, (const int32_t*)item_start, (const float*)part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (T <= kSplitMaxT) {
+  if (!fused && T <= kSplitMaxT) {
     hipLaunchKernelGGL(bwd_rows_combine, dim3((unsigned)((D + 511) / 512), (unsigned)T), dim3(256),
                        0, stream, a, (const float*)rpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // the TwELL entries' column lists, then the weight gradients
-  const dim3 tiles_blocks((unsigned)(nt * nblk));
+  // the TwELL entries' column lists, then the weight gradients (and, fused,
+  // the per-entry gradients, then gx)
   hipLaunchKernelGGL(csc_count, tiles_blocks, dim3(64), 0, stream, a, hist);
   hipLaunchKernelGGL(csc_colscan, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, a, hist,
                      total, nblk);
   hipLaunchKernelGGL(csc_ptr, dim3(1), dim3(1024), 0, stream, (const int*)total, N, col_ptr);
   hipLaunchKernelGGL(csc_fill, tiles_blocks, dim3(64), 0, stream, a, (const int*)hist,
-                     (const int*)col_ptr, csc);
+                     (const int*)col_ptr, csc, fused ? 0 : 1);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (fused) {
+    const dim3 cg((unsigned)(N / 4));
+    switch (D / 512) {
+      case 1: hipLaunchKernelGGL(bwd_cols_fused<1>, cg, dim3(256), 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc); hipLaunchKernelGGL(bwd_gx<1>, rows_grid, dim3(256), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(bwd_cols_fused<2>, cg, dim3(256), 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc); hipLaunchKernelGGL(bwd_gx<2>, rows_grid, dim3(256), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL(bwd_cols_fused<3>, cg, dim3(256), 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc); hipLaunchKernelGGL(bwd_gx<3>, rows_grid, dim3(256), 0, stream, a); break;
+      default: hipLaunchKernelGGL(bwd_cols_fused<4>, cg, dim3(256), 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc); hipLaunchKernelGGL(bwd_gx<4>, rows_grid, dim3(256), 0, stream, a); break;
+    }
+    return hipGetLastError();
+  }
   if (D % 1024 == 0)
     hipLaunchKernelGGL(bwd_cols<2>, dim3((unsigned)(N / 4 * (D / 1024))), dim3(256), 0, stream, a,
                        (const int*)col_ptr, (const f32x4_t*)csc);

@@ -91,6 +91,11 @@ def check(inp: wl.Inputs, cap: int, dense: bool, rows=None):
     (130, 1536, 384, 1.5, 0),     # capacity 0: every active row routed
     (40, 4096, 640, 2.0, 4),      # the widest model dimension (eight 512-wide chunks)
     (97, 2560, 256, 1.7, 2),      # five chunks, odd d-chunk count for the weight gradients
+    # more than 256 tokens, d_model <= 2048: per-entry gradients in the column pass
+    (400, 1024, 512, 1.2, 8),     # two chunks
+    (280, 1536, 384, 1.5, 0),     # three chunks, capacity 0: empty column lists
+    (270, 2048, 384, 2.0, 3),     # four chunks, ragged rows
+    (300, 2560, 256, 1.7, 2),     # wider than 2048: row pass and column pass
 ])
 def test_backward_small(T, d_model, d_ff, beta, cap):
     inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype="bf16", beta=beta,
