@@ -190,6 +190,11 @@ __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, 
 using GateGemm = Gemm2<1, SFFN_GATE_BN, false, SFFN_GATE_BK, SFFN_GATE_WN, false, SFFN_GATE_BM,
                        SFFN_GATE_STAGES, SFFN_GATE_WAVES>;
 static_assert(GateGemm::WN == kTile, "each wave holds one TwELL column tile");
+// 256 x 256 tiles of the same kernel: eight waves as 4 x 2, each 64 rows x one
+// TwELL tile (a quarter fewer LDS fragment bytes per MFMA than 32 x 128).
+using GateGemmWide = Gemm2<1, 256, false, SFFN_GATE_BK, 2, false, 256, SFFN_GATE_STAGES,
+                           SFFN_GATE_WAVES>;
+static_assert(GateGemmWide::WN == kTile, "each wave holds one TwELL column tile");
 
 }  // namespace
 

@@ -57,15 +57,15 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 }
 
 // bf16, d_model % 32 == 0: 256-row tiles on the buffer-load main loop, TwELL
-// built straight from the MFMA accumulators.  Default: 256 x 128 tiles, eight
-// waves, two per SIMD, one workgroup per CU (one A tile of 256 rows feeds the
-// whole TwELL tile, a quarter less L2-to-LDS traffic than two 128-row
-// workgroups); each wave holds 32 rows x the 128 columns of the TwELL tile.
-// The same code also builds 256 x 256 tiles of four waves as 2 x 2, each
-// holding 128 rows x one TwELL tile (SFFN_GATE_BN=256 SFFN_GATE_WN=2
-// SFFN_GATE_WAVES=4): fewer LDS reads per MFMA, but with one wave per SIMD the
-// buffer loads stall the MFMA stream, so it is slower at 4096 tokens and
-// about even at 16384.
+// built straight from the MFMA accumulators; eight waves, two per SIMD, one
+// workgroup per CU.  Two tile shapes in one grid: 256 x 256 (GateGemmWide,
+// waves as 4 x 2, each 64 rows x one TwELL tile) wherever they fill whole
+// rounds of the CUs, and 256 x 128 (GateGemm, waves as 8 x 1, each 32 rows x
+// the TwELL tile) for a remainder that would leave a last round of wide tiles
+// at most half full.  The wide tile reads 12 KB of LDS fragments per wave and
+// K step for 64 x 128 outputs where the narrow one reads 10 KB for 32 x 128.
+// (256 x 256 tiles of four waves as 2 x 2, one wave per SIMD, let the buffer
+// loads stall the MFMA stream: slower.)
 //
 // A wave holds rows WM wm + 16 fm + 4 g + r and columns WN wn + 16 fn + i of
 // the workgroup tile, for lane 16 g + i and accumulator (fm, fn, r).  For a
@@ -83,10 +83,11 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 #define SFFN_EPI_EXACT_U 4  // exact re-evaluation: 16-byte chunks per lane loaded together
 #endif
 
+template <class G>
 struct AccEpi {
   int m0, n0, nt, kt, wm, lane, gi, li;  // n0: first column of the wave's TwELL tile
   float cw, cb;
-  float bias[GateGemm::FN], nw[GateGemm::FN];
+  float bias[G::FN], nw[G::FN];
   const float* rn_a;
   uint32_t* exact_lds;  // this wave's exact-stage area
   float l1;             // L1 regulariser: this lane's ReLU sum over its rows and columns
@@ -95,10 +96,10 @@ struct AccEpi {
 // One accumulator row group (fm, r): 4 rows of the wave, all 128 columns of
 // its TwELL tile.  Template indices keep every accumulator access static (no
 // spill of the accumulator array to scratch).
-template <int FM, int R>
-__device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, AccEpi& c) {
-  constexpr int FN = GateGemm::FN;
-  const int row = c.wm * GateGemm::WM + FM * 16 + 4 * c.gi + R;
+template <class G, int FM, int R>
+__device__ __forceinline__ void epi_group(const GateArgs& a, G& g, AccEpi<G>& c) {
+  constexpr int FN = G::FN;
+  const int row = c.wm * G::WM + FM * 16 + 4 * c.gi + R;
   const int t = c.m0 + row;
   const bool valid = t < a.T;
   const float nx = c.rn_a[row];
@@ -120,7 +121,7 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, AccEpi
       while (fb) {
         const int L = __builtin_ctzll(fb);
         fb &= fb - 1;
-        const int lrow = c.wm * GateGemm::WM + FM * 16 + 4 * (L >> 4) + R;
+        const int lrow = c.wm * G::WM + FM * 16 + 4 * (L >> 4) + R;
         const int lcol = fn * 16 + (L & 15);
         const float bl = a.b ? a.b[c.n0 + lcol] : 0.f;
         const ExactResult e = exact_gate_value<uint16_t, SFFN_EPI_EXACT_U>(
@@ -147,36 +148,29 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, GateGemm& g, AccEpi
     running += __builtin_popcount(seg);
   }
   if (c.li == 0 && valid) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)running;
-  if (a.l1_part) {  // L1 regulariser, fixed order
-    float s = 0.f;
+  if (a.l1_part) {  // L1 regulariser, fixed order: per lane over its rows,
+    float s = 0.f;     // one value per workgroup after the walk
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) s += act[fn] ? v[fn] : 0.f;
-    if constexpr (GateGemm::BN == kTile) {
-      if (valid) c.l1 += s;  // per lane over its rows; one value per workgroup after the walk
-    } else {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 16);
-      if (c.li == 0 && valid) a.l1_part[(size_t)t * c.nt + c.kt] = s;
-    }
+    if (valid) c.l1 += s;
   }
 }
 
-template <int FM, int R>
+template <class G, int FM, int R>
 struct EpiLoop {
-  __device__ static __forceinline__ void run(const GateArgs& a, GateGemm& g, AccEpi& c) {
-    epi_group<FM, R>(a, g, c);
-    if constexpr (R + 1 < 4) EpiLoop<FM, R + 1>::run(a, g, c);
-    else if constexpr (FM + 1 < GateGemm::FM) EpiLoop<FM + 1, 0>::run(a, g, c);
+  __device__ static __forceinline__ void run(const GateArgs& a, G& g, AccEpi<G>& c) {
+    epi_group<G, FM, R>(a, g, c);
+    if constexpr (R + 1 < 4) EpiLoop<G, FM, R + 1>::run(a, g, c);
+    else if constexpr (FM + 1 < G::FM) EpiLoop<G, FM + 1, 0>::run(a, g, c);
   }
 };
 
-__global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twell_bf16_v2(GateArgs a) {
-  using G = GateGemm;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
+// One output tile (rows m0.., columns n0..) of configuration G: main loop,
+// then the TwELL epilogue from the accumulators.  Every wave's TwELL tile lies
+// inside [0, N) (the launcher never lets a tile hang over the last column).
+template <class G>
+__device__ __forceinline__ void gate_tile(const GateArgs& a, uint8_t* lds, int m0, int n0) {
   const int nt = a.N / kTile;
-  int mi, ni;
-  tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, (a.N + G::BN - 1) / G::BN, &mi, &ni);
-  const int m0 = mi * G::BM, n0 = ni * G::BN;
   G g;
   const uint16_t* B[1] = {(const uint16_t*)a.wg};
   g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, m0, a.T, B, n0, a.N, a.K);
@@ -195,10 +189,9 @@ __global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twel
   __syncthreads();
   const int w = uniform((int)(threadIdx.x >> 6));
   const int wn = w / G::WAVES_M;
-  AccEpi c;
+  AccEpi<G> c;
   c.m0 = m0;
   c.n0 = n0 + wn * G::WN;
-  if (c.n0 >= a.N) return;  // the half of a 256-wide tile past the last column
   c.nt = nt;
   c.kt = c.n0 / kTile;
   c.rn_a = rn_a;
@@ -223,20 +216,43 @@ __global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twel
     c.cw = fmaxf(c.cw, __shfl_xor(c.cw, o, kWave));
     c.cb = fmaxf(c.cb, __shfl_xor(c.cb, o, kWave));
   }
-  EpiLoop<0, 0>::run(a, g, c);
-  if constexpr (G::BN == kTile) {
-    if (a.l1_part) {  // L1 regulariser: the workgroup's sum, fixed order, one store
-      float* red = (float*)(lds + kExactOff + G::NWAVES * kExactLdsWords * 4);
-      static_assert(G::LDS_BYTES >= kExactOff + G::NWAVES * (kExactLdsWords + 1) * 4, "fits");
-      const float s = wave_sum_uniform(c.l1);
-      if (c.lane == 0) red[w] = s;
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        float t = 0.f;
-        for (int i = 0; i < G::NWAVES; ++i) t += red[i];
-        a.l1_part[blockIdx.x] = t;
-      }
+  EpiLoop<G, 0, 0>::run(a, g, c);
+  if (a.l1_part) {  // L1 regulariser: the workgroup's sum, fixed order, one store
+    float* red = (float*)(lds + kExactOff + G::NWAVES * kExactLdsWords * 4);
+    static_assert(G::LDS_BYTES >= kExactOff + G::NWAVES * (kExactLdsWords + 1) * 4, "fits");
+    const float s = wave_sum_uniform(c.l1);
+    if (c.lane == 0) red[w] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = 0.f;
+      for (int i = 0; i < G::NWAVES; ++i) t += red[i];
+      a.l1_part[blockIdx.x] = t;
     }
+  }
+}
+
+// The grid: the first mt * wide_nt workgroups take 256 x 256 tiles
+// (GateGemmWide) of columns [0, 256 wide_nt), the rest 256 x 128 tiles
+// (GateGemm) of the columns after.  The wide tiles read a quarter fewer LDS
+// bytes per MFMA; the narrow ones fill what would otherwise be a part-empty
+// last round of wide tiles.
+__global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twell_bf16_v2(
+    GateArgs a, int wide_nt, int narrow_nt) {
+  static_assert(GateGemm::NWAVES == GateGemmWide::NWAVES, "one block size");
+  static_assert(GateGemm::BM == GateGemmWide::BM, "one row tiling");
+  constexpr size_t kLds = GateGemm::LDS_BYTES > GateGemmWide::LDS_BYTES ? GateGemm::LDS_BYTES
+                                                                         : GateGemmWide::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  const int mt = (a.T + GateGemm::BM - 1) / GateGemm::BM;
+  const int n_wide = mt * wide_nt;
+  const int bid = (int)blockIdx.x;
+  int mi, ni;
+  if (bid < n_wide) {
+    tile_of(bid, mt, wide_nt, &mi, &ni);
+    gate_tile<GateGemmWide>(a, lds, mi * GateGemmWide::BM, ni * GateGemmWide::BN);
+  } else {
+    tile_of(bid - n_wide, mt, narrow_nt, &mi, &ni);
+    gate_tile<GateGemm>(a, lds, mi * GateGemm::BM, wide_nt * GateGemmWide::BN + ni * GateGemm::BN);
   }
 }
 
@@ -570,6 +586,23 @@ int stream_splits(int K, int N) {
 
 int few_token_splits(int K, int N) { return use_stream(K) ? stream_splits(K, N) : skinny_splits(K, N); }
 
+// Columns of 256-wide tiles (wide_nt, counted in 256-column tiles) and of
+// 128-wide tiles after them (narrow_nt) for the 256-row gate kernel, one
+// workgroup per CU.  Wide tiles everywhere, unless the last round of them
+// would hold at most half a round (then that remainder, rounded up to whole
+// columns of tiles, runs as twice as many narrow tiles, each half as long).
+// Any split gives the same results; this only sets the schedule.
+constexpr int kGateCUs = 256;
+void gate_tile_split(int T, int N, int* wide_nt, int* narrow_nt) {
+  const int mt = (T + GateGemm::BM - 1) / GateGemm::BM;
+  const int nt = N / kTile;
+  int wide = nt / 2;
+  const long rem = ((long)mt * wide) % kGateCUs;
+  if (rem != 0 && rem <= kGateCUs / 2) wide = max(0, wide - (int)((rem + mt - 1) / mt));
+  *wide_nt = wide;
+  *narrow_nt = nt - 2 * wide;
+}
+
 }  // namespace
 
 size_t gate_workspace_bytes(int dtype, int T, int K, int N) {
@@ -612,10 +645,13 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
       hipLaunchKernelGGL(gate_skinny_epilogue<4>, dim3((unsigned)(nt * 4)), blk, 0, stream, a, partial, S);
     }
   } else if (dtype == 1 && K % GateGemm::BK == 0) {
-    const dim3 g2((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
-                             ((N + GateGemm::BN - 1) / GateGemm::BN)));
-    hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(64 * GateGemm::NWAVES), 0, stream, a);
-    if (l1_n && GateGemm::BN == kTile) *l1_n = g2.x;  // one sum per workgroup
+    int wide_nt, narrow_nt;
+    gate_tile_split(T, N, &wide_nt, &narrow_nt);
+    const int mt = (T + GateGemm::BM - 1) / GateGemm::BM;
+    const dim3 g2((unsigned)(mt * (wide_nt + narrow_nt)));
+    hipLaunchKernelGGL(gate_twell_bf16_v2, g2, dim3(64 * GateGemm::NWAVES), 0, stream, a, wide_nt,
+                       narrow_nt);
+    if (l1_n) *l1_n = g2.x;  // one sum per workgroup
   } else if (dtype == 1) {
     hipLaunchKernelGGL(gate_twell_bf16, dim3((unsigned)(((T + 127) / 128) * nt)), dim3(256), 0,
                        stream, a);
