@@ -21,32 +21,19 @@ namespace {
 // section 01 and of the kongchang.com article).  The GEMM is the TwELL
 // kernel's own main loop (GateGemm), so z holds exactly the float32 values the
 // fused epilogue sees and the converters reach the same exact activity
-// decision with the same guard band.
+// decision with the same guard band; it also runs the same mix of 256 x 256
+// and 256 x 128 tiles, so the two designs differ only after the main loop.
 
-// z[m, j] = acc + b_g[j] (float32, row-major [rows, N]) for the x rows
-// rowmap[m] (rowmap null: row m), m < rows (n_rows_dev null: T; else the
-// count on the device).  G: GateGemm (the TwELL kernel's own tiles, for the
-// baseline) or RowsGemm (64-row tiles, for a few mapped rows).  Both chain
-// 16x16x32 MFMAs over K, K / 32 roundings: the same guard band holds.
+// One tile of z[m, j] = acc + b_g[j] (float32, row-major [rows, N]) for the
+// x rows rowmap[m] (rowmap null: row m), m < mv.  G: GateGemmWide or GateGemm
+// (the TwELL kernel's own tiles, for the baseline) or RowsGemm (64-row tiles,
+// for a few mapped rows).  All chain 16x16x32 MFMAs over K, K / 32 roundings:
+// the same guard band holds.
 using RowsGemm = Gemm2<1, kTile, false, 64, 4, false, 64, 4, 4>;
 
 template <class G>
-__global__ __launch_bounds__(64 * G::NWAVES) void gate_preact_bf16(
-    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
-  int mi, ni;
-  const int ntn = (a.N + G::BN - 1) / G::BN;
-  if (n_rows_dev) {
-    // few mapped rows: the active tiles are the first ones, spread over the
-    // XCDs in dispatch order (the XCD-aware map would put them all on one)
-    mi = (int)blockIdx.x / ntn;
-    ni = (int)blockIdx.x - mi * ntn;
-  } else {
-    tile_of((int)blockIdx.x, (a.T + G::BM - 1) / G::BM, ntn, &mi, &ni);
-  }
-  const int m0 = mi * G::BM, n0 = ni * G::BN;
-  const int mv = uniform(n_rows_dev ? min(*n_rows_dev, a.T) : a.T);
-  if (m0 >= mv) return;
+__device__ __forceinline__ void preact_tile(const GateArgs& a, uint8_t* lds, float* z,
+                                            const int* rowmap, int mv, int m0, int n0) {
   G g;
   const uint16_t* B[1] = {(const uint16_t*)a.wg};
   g.init((const uint16_t*)a.x, (size_t)a.T, rowmap, m0, mv, B, n0, a.N, a.K);
@@ -66,6 +53,42 @@ __global__ __launch_bounds__(64 * G::NWAVES) void gate_preact_bf16(
         const int m = m0 + wm * G::WM + fm * 16 + 4 * (lane >> 4) + r;
         if (cv && m < mv) z[(size_t)m * a.N + col] = g.acc[0][fm][fn][r] + bb;
       }
+  }
+}
+
+// Mapped rows (the routed rows of the backward), 64-row tiles.
+__global__ __launch_bounds__(64 * RowsGemm::NWAVES) void gate_preact_rows(
+    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RowsGemm::LDS_BYTES];
+  // the active tiles are the first ones, spread over the XCDs in dispatch
+  // order (the XCD-aware map would put them all on one)
+  const int ntn = a.N / RowsGemm::BN;
+  const int mi = (int)blockIdx.x / ntn, ni = (int)blockIdx.x - mi * ntn;
+  const int m0 = mi * RowsGemm::BM;
+  const int mv = uniform(min(*n_rows_dev, a.T));
+  if (m0 >= mv) return;
+  preact_tile<RowsGemm>(a, lds, z, rowmap, mv, m0, ni * RowsGemm::BN);
+}
+
+// All rows: the TwELL kernel's grid (wide tiles, then narrow ones).
+__global__ __launch_bounds__(64 * GateGemm::NWAVES) void gate_preact_bf16(GateArgs a, float* z,
+                                                                         int wide_nt,
+                                                                         int narrow_nt) {
+  constexpr size_t kLds = GateGemm::LDS_BYTES > GateGemmWide::LDS_BYTES ? GateGemm::LDS_BYTES
+                                                                         : GateGemmWide::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  const int mt = (a.T + GateGemm::BM - 1) / GateGemm::BM;
+  const int n_wide = mt * wide_nt;
+  const int bid = (int)blockIdx.x;
+  int mi, ni;
+  if (bid < n_wide) {
+    tile_of(bid, mt, wide_nt, &mi, &ni);
+    preact_tile<GateGemmWide>(a, lds, z, nullptr, a.T, mi * GateGemmWide::BM,
+                              ni * GateGemmWide::BN);
+  } else {
+    tile_of(bid - n_wide, mt, narrow_nt, &mi, &ni);
+    preact_tile<GateGemm>(a, lds, z, nullptr, a.T, mi * GateGemm::BM,
+                          wide_nt * GateGemmWide::BN + ni * GateGemm::BN);
   }
 }
 
@@ -263,14 +286,16 @@ hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g,
                               hipStream_t stream) {
   GateArgs a{x, wg_t, b_g, nullptr, nullptr, nullptr, nullptr, nullptr, T, K, N, 0, GuardBand{}};
   if (rowmap) {
+    if (!n_rows_dev) return hipErrorInvalidValue;
     const dim3 g((unsigned)(((T + RowsGemm::BM - 1) / RowsGemm::BM) * (N / RowsGemm::BN)));
-    hipLaunchKernelGGL(gate_preact_bf16<RowsGemm>, g, dim3(64 * RowsGemm::NWAVES), 0, stream, a,
-                       z, rowmap, n_rows_dev);
+    hipLaunchKernelGGL(gate_preact_rows, g, dim3(64 * RowsGemm::NWAVES), 0, stream, a, z, rowmap,
+                       n_rows_dev);
   } else {
-    const dim3 g((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) *
-                            ((N + GateGemm::BN - 1) / GateGemm::BN)));
-    hipLaunchKernelGGL(gate_preact_bf16<GateGemm>, g, dim3(64 * GateGemm::NWAVES), 0, stream, a,
-                       z, rowmap, n_rows_dev);
+    int wide_nt, narrow_nt;
+    gate_tile_split(T, N, &wide_nt, &narrow_nt);
+    const dim3 g((unsigned)(((T + GateGemm::BM - 1) / GateGemm::BM) * (wide_nt + narrow_nt)));
+    hipLaunchKernelGGL(gate_preact_bf16, g, dim3(64 * GateGemm::NWAVES), 0, stream, a, z, wide_nt,
+                       narrow_nt);
   }
   return hipGetLastError();
 }

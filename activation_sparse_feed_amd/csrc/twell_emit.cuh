@@ -196,6 +196,23 @@ using GateGemmWide = Gemm2<1, 256, false, SFFN_GATE_BK, 2, false, 256, SFFN_GATE
                            SFFN_GATE_WAVES>;
 static_assert(GateGemmWide::WN == kTile, "each wave holds one TwELL column tile");
 
+// Columns of 256-wide tiles (wide_nt, counted in 256-column tiles) and of
+// 128-wide tiles after them (narrow_nt) for the 256-row gate kernels, one
+// workgroup per CU.  Wide tiles everywhere, unless the last round of them
+// would hold at most half a round (then that remainder, rounded up to whole
+// columns of tiles, runs as twice as many narrow tiles, each half as long).
+// Any split gives the same results; this only sets the schedule.
+constexpr int kGateCUs = 256;
+inline void gate_tile_split(int T, int N, int* wide_nt, int* narrow_nt) {
+  const int mt = (T + GateGemm::BM - 1) / GateGemm::BM;
+  const int nt = N / kTile;
+  int wide = nt / 2;
+  const long rem = ((long)mt * wide) % kGateCUs;
+  if (rem != 0 && rem <= kGateCUs / 2) wide = max(0, wide - (int)((rem + mt - 1) / mt));
+  *wide_nt = wide;
+  *narrow_nt = nt - 2 * wide;
+}
+
 }  // namespace
 
 }  // namespace sffn

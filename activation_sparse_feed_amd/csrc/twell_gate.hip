@@ -586,22 +586,6 @@ int stream_splits(int K, int N) {
 
 int few_token_splits(int K, int N) { return use_stream(K) ? stream_splits(K, N) : skinny_splits(K, N); }
 
-// Columns of 256-wide tiles (wide_nt, counted in 256-column tiles) and of
-// 128-wide tiles after them (narrow_nt) for the 256-row gate kernel, one
-// workgroup per CU.  Wide tiles everywhere, unless the last round of them
-// would hold at most half a round (then that remainder, rounded up to whole
-// columns of tiles, runs as twice as many narrow tiles, each half as long).
-// Any split gives the same results; this only sets the schedule.
-constexpr int kGateCUs = 256;
-void gate_tile_split(int T, int N, int* wide_nt, int* narrow_nt) {
-  const int mt = (T + GateGemm::BM - 1) / GateGemm::BM;
-  const int nt = N / kTile;
-  int wide = nt / 2;
-  const long rem = ((long)mt * wide) % kGateCUs;
-  if (rem != 0 && rem <= kGateCUs / 2) wide = max(0, wide - (int)((rem + mt - 1) / mt));
-  *wide_nt = wide;
-  *narrow_nt = nt - 2 * wide;
-}
 
 }  // namespace
 
