@@ -123,6 +123,18 @@ def test_large_lognormal_full_size_sampled():
     compare(inp, w.cap, rows, ffn, y)
 
 
+def test_gate_tile_mix_with_odd_tile_count():
+    # 129 row tiles (the last ragged) x 3 TwELL tiles: the 256-row gate kernel
+    # runs one column of 256-wide tiles and one column of 128-wide tiles
+    inp = wl.generate_custom(T=33000, d_model=256, d_ff=384, dtype="bf16", beta=1.5,
+                             seed_base=70, cap=8)
+    ffn, y, _ = run_sparse(inp, 8)
+    n_r = int(ffn.n_routed.item())
+    rows = np.unique(np.concatenate([sample_rows(33000, 48, must=ffn.routed[:min(n_r, 8)].cpu().numpy(), seed=5),
+                                     np.arange(32768, 33000, 29), [32999]]))
+    compare(inp, 8, rows, ffn, y)
+
+
 # ------------------------------------------------------------- dense reference
 @pytest.mark.parametrize("name,T", [("tiny_f32", None), ("prefill_1pct", 512),
                                     ("decode_1pct", None)])
