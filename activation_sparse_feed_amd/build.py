@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsffn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "twell_gate.hip", "convert.hip", "dense.hip", "dense_skinny.hip", "sparse.hip",
-           "route.hip", "norms.hip", "backward.hip"]
+           "route.hip", "norms.hip", "backward.hip", "probe.hip"]
 ARCH = os.environ.get("SFFN_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 instructions are kept out of the generated code.

@@ -23,7 +23,8 @@ TILE = 128
 
 EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
             "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
-            "ell_from_preact", "sffn_workspace_bytes", "sffn_strerror")
+            "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_workspace_bytes",
+            "sffn_strerror")
 
 
 class SffnError(RuntimeError):
@@ -52,11 +53,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.gate_preact.argtypes = [sp, vp, vp, vp, vp, vp]
     lib.sparse_ffn_bwd.argtypes = [sp] + [vp] * 17 + [vp, sz, vp]
+    lib.sffn_probe_hbm.argtypes = [vp, vp, sz, i32, vp]
+    lib.sffn_probe_mfma.argtypes = [vp, i32, i32, vp]
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
                "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
-               "ell_from_preact"):
+               "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
     lib.sffn_workspace_bytes.restype = sz
@@ -171,6 +174,20 @@ def hybrid_route(shape: Shape, x, wg_t, b_g, wu_t, wd, count, routed, n_routed, 
     _check("hybrid_route", _lib.hybrid_route(
         ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd), _ptr(count),
         _ptr(routed), _ptr(n_routed), _ptr(workspace), ws_n, _ptr(y), _stream(stream)))
+
+
+def probe_hbm(src, dst=None, workgroups: int = 4096, stream=None) -> None:
+    """One streaming pass over src (copied to dst, or only read when dst is None)."""
+    n = src.numel() * src.element_size()
+    _check("sffn_probe_hbm", _lib.sffn_probe_hbm(_ptr(src), _ptr(dst), n, int(workgroups),
+                                                 _stream(stream)))
+
+
+def probe_mfma(out, iters: int, stream=None) -> None:
+    """out: float32 with a multiple of 256 elements (one workgroup per 256)."""
+    wgs = out.numel() // 256
+    _check("sffn_probe_mfma", _lib.sffn_probe_mfma(_ptr(out), int(wgs), int(iters),
+                                                   _stream(stream)))
 
 
 def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=None) -> None:

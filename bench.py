@@ -50,10 +50,51 @@ def parse_args():
     p.add_argument("--cold-steps", type=int, default=10,
                    help="steps of the cold pass (a 512 MiB read between steps evicts the "
                         "Infinity Cache); 0 skips it")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the peak probes (measured HBM bandwidth and bf16 MFMA rate)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device copies of MIB MiB (reference for the HBM byte "
                         "counters of a profiling run) and exit")
     return p.parse_args()
+
+
+def measured_peaks() -> dict:
+    """Achievable HBM bandwidth and bf16 MFMA rate on this GPU, from the
+    library's probe kernels (best of five timed calls each): a read-only pass
+    and a copy over 1 GiB buffers (four times the Infinity Cache), and 16
+    independent MFMA chains per wave on 16 workgroups per CU."""
+    import torch
+    from activation_sparse_feed_amd import sffn
+    E = torch.cuda.Event
+
+    def best(fn, reps=5):
+        fn()
+        times = []
+        for _ in range(reps):
+            a, b = E(enable_timing=True), E(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        return min(times)
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    wg_hbm = nbytes // (16 * 4 * 256)  # one pass of four 16-byte chunks per lane
+    t_read = best(lambda: sffn.probe_hbm(src, None, workgroups=wg_hbm))
+    t_copy = best(lambda: sffn.probe_hbm(src, dst, workgroups=wg_hbm))
+    ok_copy = bool(torch.equal(src[:1 << 20], dst[:1 << 20]))
+    del src, dst
+    wgs, iters = 256 * 16, 1024
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    t_mfma = best(lambda: sffn.probe_mfma(out, iters))
+    ok_mfma = bool(torch.all(out == 2048.0 * iters).item())
+    flops = wgs * 4 * 16 * iters * 16384.0
+    return {"hbm_read_gb_s": nbytes / t_read / 1e9, "hbm_copy_gb_s": 2 * nbytes / t_copy / 1e9,
+            "mfma_bf16_tflop_s": flops / t_mfma / 1e12, "checks_passed": ok_copy and ok_mfma,
+            "probe": "sffn_probe_hbm over 1 GiB, 65536 workgroups (read-only; copy counts read + write), "
+                     "sffn_probe_mfma 4096 workgroups x 4 waves x 16 chains x 1024 MFMAs"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_twell_pack_prefill_1pct.md")
@@ -502,6 +543,11 @@ def main() -> int:
         roofline = {"kernel": "twell_pack (gate weight stream + TwELL epilogue)", "bound": "hbm",
                     "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": gbs / PEAK_HBM_GBS}
+    peaks = None if args.no_peaks else measured_peaks()
+    if peaks is not None and w.dtype == "bf16":
+        mp = peaks["mfma_bf16_tflop_s"] if roofline["bound"] == "mfma" else peaks["hbm_read_gb_s"]
+        roofline["measured_peak"] = mp
+        roofline["frac_of_measured"] = roofline["achieved"] / mp
     roofline["traffic"] = measured_traffic(w.name)
     roofline["traffic_unit"] = "bytes per launch (HBM, counter-derived)"
     # fused kernel: algorithmic bytes = x + y + live TwELL + distinct gathered rows
@@ -534,6 +580,8 @@ def main() -> int:
                        "dense_ffn_ref": t_dense},
         "sparse_ffn_fwd": {"algorithmic_bytes": sparse_bytes, "gb_per_s": sparse_bytes / (t_sparse * 1e-3) / 1e9,
                            "hbm_frac": sparse_bytes / (t_sparse * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "hbm_frac_of_measured": (sparse_bytes / (t_sparse * 1e-3) / 1e9
+                                                    / peaks["hbm_read_gb_s"]) if peaks else None,
                            "flop": sparse_flop, "tflop_per_s": sparse_flop / (t_sparse * 1e-3) / 1e12,
                            "distinct_columns": uniq},
         "step_ms_percentiles": {"p10": float(np.percentile(step_ev, 10)),
@@ -547,6 +595,7 @@ def main() -> int:
         "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,
         "speedup_vs_dense": (t_dense / ms_step) if t_dense else None,
         "dense_tflops": (3 * gate_flop / (t_dense * 1e-3) / 1e12) if t_dense else None,
+        "measured_peaks": peaks,
         "activity": {"nnz_per_row": nnz_total / T, "density": nnz_total / (T * n),
                      "routed_rows": n_routed},
         "device": torch.cuda.get_device_name(0),

@@ -281,6 +281,33 @@ int32_t ell_from_preact(const sffn_shape* shape, int32_t width, const float* z, 
                         uint16_t* ell_count, uint16_t* ell_idx, void* ell_val, void* workspace,
                         size_t ws_bytes, void* stream);
 
+/*
+ * Peak probes: measured denominators for the roofline fractions (the
+ * published MI355X peaks are 8 TB/s of HBM and 2.5 PFLOP/s of dense bf16
+ * MFMA; these report what kernels of the hot path's kind reach on this GPU).
+ *
+ * sffn_probe_hbm -- one grid-stride pass over `bytes` bytes of src with
+ * 16-byte loads, four in flight per lane, `workgroups` workgroups of 256
+ * threads.  dst != NULL: copies src to dst (bytes read + bytes written);
+ * dst == NULL: reads only.  Time it with events around the call; use buffers
+ * much larger than the 256 MB Infinity Cache to measure HBM.  src and dst
+ * device pointers, 16-byte aligned, not overlapping; bytes % 16 == 0;
+ * workgroups > 0 (else SFFN_ERR_ARG).  bytes == 0 is a no-op.
+ */
+int32_t sffn_probe_hbm(const void* src, void* dst, size_t bytes, int32_t workgroups,
+                       void* stream);
+
+/*
+ * sffn_probe_mfma -- `workgroups` workgroups of 256 threads; every wave issues
+ * iters x 16 independent v_mfma_f32_16x16x32_bf16 (16384 flops each) on
+ * operands of ones: 4 * 16 * 16384 * iters flops per workgroup (use at least
+ * 8 workgroups per CU: several waves per SIMD).  out: float32
+ * [workgroups * 256], each set to 2048 * iters (exact), a check that every
+ * MFMA ran.  out != NULL, workgroups > 0, 0 < iters < 8192 (else
+ * SFFN_ERR_ARG).
+ */
+int32_t sffn_probe_mfma(float* out, int32_t workgroups, int32_t iters, void* stream);
+
 /* Workspace bytes needed by one call for this shape (0 if the shape is invalid). */
 size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which);
 

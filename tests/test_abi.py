@@ -192,3 +192,18 @@ def test_backward_errors(sffn):
     s0 = _shape(sffn, T=0)
     assert lib.sparse_ffn_bwd(ctypes.byref(s0), *([None] * 17), None, 0, None) == 0
 
+
+
+def test_probe_errors(sffn):
+    lib = sffn._lib
+    ARG = sffn.SFFN_ERR_ARG
+    assert lib.sffn_probe_hbm(None, None, 1024, 64, None) == ARG
+    assert lib.sffn_probe_hbm(MISALIGNED, None, 1024, 64, None) == ARG
+    assert lib.sffn_probe_hbm(P, MISALIGNED, 1024, 64, None) == ARG
+    assert lib.sffn_probe_hbm(P, None, 1000, 64, None) == ARG      # not a multiple of 16
+    assert lib.sffn_probe_hbm(P, None, 1024, 0, None) == ARG
+    assert lib.sffn_probe_hbm(P, None, 0, 64, None) == sffn.SFFN_OK  # nothing to do
+    assert lib.sffn_probe_mfma(None, 4, 16, None) == ARG
+    assert lib.sffn_probe_mfma(P, 0, 16, None) == ARG
+    assert lib.sffn_probe_mfma(P, 4, 0, None) == ARG
+    assert lib.sffn_probe_mfma(P, 4, 8192, None) == ARG
