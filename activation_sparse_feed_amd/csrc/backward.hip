@@ -32,6 +32,11 @@
 //              list, then the routed rows' (binary search in their lists),
 //              summed into the weight-gradient rows in registers; every column
 //              is written (zero when inactive).
+// With d_model <= 2048 and more than kSplitMaxT tokens the order is fused
+// instead: no bwd_rows; the column lists carry each entry's TwELL position and
+// h, bwd_cols_fused (one wave per column over the whole d_model) computes the
+// per-entry gradients itself while summing the weight gradients, and bwd_gx
+// then gathers the wg_t and wu_t rows for gx.
 // Every sum runs in a fixed order, so the gradients are deterministic.
 #include "common.cuh"
 #include "launch.h"
@@ -653,7 +658,7 @@ __global__ __launch_bounds__(256) void bwd_cols(BwdArgs a, const int* col_ptr, c
 
 // Fused order for d_model <= 2048 and more than kSplitMaxT tokens.  The
 // column pass already loads x_t and gy_t for every entry of a column, so with
-// the column's wu_t and wd rows held in registers it computes the entry's dot
+// the column's wu_t and wd rows at hand (in LDS) it computes the entry's dot
 // products itself (gz, gu, a, stored at the entry's TwELL position) and sums
 // the weight gradients in the same step; the row pass (bwd_gx) then only
 // gathers wg_t and wu_t rows per entry for gx, with no reduction in its chain.
