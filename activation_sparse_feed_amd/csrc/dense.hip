@@ -451,10 +451,16 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
   if (e != hipSuccess) return e;
   // y rows = h wd
   DenseArgs d{h, wd, nullptr, nullptr, y, routed, n_routed, T, d_ff, d_model};
-  hipLaunchKernelGGL(down_routed, dim3(kRoutedGrid), dim3(256), 0, stream, d, partial);
+  // grids no larger than the most work the row count allows (few tokens: the
+  // launches that find no routed row dispatch fewer workgroups)
+  const long down_items = (long)((T + 127) / 128) * ((d_model + 127) / 128) * kRoutedMaxSplit;
+  const long red_blocks = ((long)T * d_model / 4 + 255) / 256;
+  hipLaunchKernelGGL(down_routed, dim3((unsigned)std::min<long>(kRoutedGrid, down_items)),
+                     dim3(256), 0, stream, d, partial);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(down_routed_reduce, dim3(256), dim3(256), 0, stream, d, (const float*)partial);
+  hipLaunchKernelGGL(down_routed_reduce, dim3((unsigned)std::max<long>(1, std::min<long>(256, red_blocks))),
+                     dim3(256), 0, stream, d, (const float*)partial);
   return hipGetLastError();
 }
 
