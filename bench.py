@@ -105,26 +105,39 @@ GATE_SOURCES = ("activation_sparse_feed_amd/csrc/twell_gate.hip",
                 "activation_sparse_feed_amd/csrc/common.cuh")
 
 
-def gate_source_digest() -> str:
+SPARSE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_prefill_1pct.md")
+SPARSE_SOURCES = ("activation_sparse_feed_amd/csrc/sparse.hip",
+                  "activation_sparse_feed_amd/csrc/common.cuh")
+
+
+def source_digest(files) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in GATE_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per twell_pack launch from the stored counter summary (its
+def gate_source_digest() -> str:
+    return source_digest(GATE_SOURCES)
+
+
+def sparse_source_digest() -> str:
+    return source_digest(SPARSE_SOURCES)
+
+
+def measured_traffic(workload: str, path: str = TRAFFIC_FILE, digest=gate_source_digest):
+    """HBM bytes per launch of a kernel from its stored counter summary (its
     'key: value' lines), or None when the counters were taken on another
     workload or on different kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             kv = dict(line.split(": ", 1) for line in f.read().splitlines()
                       if line.count(": ") == 1 and " " not in line.split(": ", 1)[0])
     except OSError:
         return None
-    if kv.get("workload") != workload or kv.get("source_digest") != gate_source_digest():
+    if kv.get("workload") != workload or kv.get("source_digest") != digest():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -550,6 +563,7 @@ def main() -> int:
         roofline["frac_of_measured"] = roofline["achieved"] / mp
     roofline["traffic"] = measured_traffic(w.name)
     roofline["traffic_unit"] = "bytes per launch (HBM, counter-derived)"
+    roof_gate = roofline
     # fused kernel: algorithmic bytes = x + y + live TwELL + distinct gathered rows
     routed_mask = torch.zeros(T, dtype=torch.bool, device="cuda")
     routed_mask[ffn.routed[:n_routed].long()] = True
@@ -558,6 +572,25 @@ def main() -> int:
     uniq = int(torch.unique(ffn.idx.to(torch.int64)[live]).numel()) if w.cap > 0 else 0
     sparse_bytes = 2.0 * T * d * eb + nnz_live * (2 + eb) + T * (n // 128) * 2 + uniq * 2.0 * d * eb
     sparse_flop = 4.0 * d * int(live.sum().item())
+    # the fused kernel's own roofline: the larger of its vector-ALU time (packed
+    # bf16 dot2 and float32 FMA at the 157.3 TFLOP/s vector peak) and its HBM
+    # time on the algorithmic bytes
+    t_s = t_sparse * 1e-3
+    if sparse_flop / (PEAK_F32_TFLOPS * 1e12) >= sparse_bytes / (PEAK_HBM_GBS * 1e9):
+        roof_sparse = {"kernel": "sparse_ffn_fwd (fused up*gate -> down over TwELL)", "bound": "alu",
+                       "achieved": sparse_flop / t_s / 1e12, "peak": PEAK_F32_TFLOPS,
+                       "unit": "TFLOP/s"}
+    else:
+        roof_sparse = {"kernel": "sparse_ffn_fwd (fused up*gate -> down over TwELL)", "bound": "hbm",
+                       "achieved": sparse_bytes / t_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        if peaks is not None:
+            roof_sparse["measured_peak"] = peaks["hbm_read_gb_s"]
+            roof_sparse["frac_of_measured"] = roof_sparse["achieved"] / peaks["hbm_read_gb_s"]
+    roof_sparse["frac"] = roof_sparse["achieved"] / roof_sparse["peak"]
+    roof_sparse["traffic"] = measured_traffic(w.name, SPARSE_TRAFFIC_FILE, sparse_source_digest)
+    roof_sparse["traffic_unit"] = "bytes per launch (HBM, counter-derived)"
+    # the line's roofline is the dominant (longer) kernel's; both are kept
+    roofline = roof_sparse if t_sparse > t_gate else roof_gate
 
     out = {
         "metric": "sparse gated-FFN tokens/s (1 GPU)",
@@ -575,6 +608,8 @@ def main() -> int:
         "config": {"workload": w.name, "tokens": T, "d_model": d, "d_ff": n, "beta": beta,
                    "tile": w.tile, "cap": w.cap, "rows": w.rows},
         "roofline": roofline,
+        "roofline_twell_pack": roof_gate,
+        "roofline_sparse_ffn_fwd": roof_sparse,
         "kernels_ms": {"twell_pack": t_gate, "sparse_ffn_fwd": t_sparse,
                        "hybrid_route": t_hybrid, "events_step": t_events,
                        "dense_ffn_ref": t_dense},
