@@ -152,15 +152,24 @@ __global__ __launch_bounds__(256) void down_f32(DenseArgs a) {
 }
 
 // ------------------------------------------------ bf16, buffer-load main loop
-// gate+up: 256 x 64 output tile of both z and u (2 x 2 waves of 128 x (32 + 32)).
-__global__ __launch_bounds__(256, 2) void gateup_bf16_v2(DenseArgs a) {
-  using G = Gemm2<2, 64, false, 32, 2>;
+// gate+up: 256 x 64 output tile of both z and u (2 x 2 waves of 128 x (32 + 32)),
+// two workgroups per CU; or (DenseWide) 256 x 128 of both, eight waves as
+// 4 x 2 of 64 x (64 + 64), one workgroup per CU: a quarter fewer LDS fragment
+// bytes per MFMA, used when the tiles fill at least two rounds of the CUs.
+using DenseNarrow = Gemm2<2, 64, false, 32, 2>;
+using DenseWide = Gemm2<2, 128, false, 32, 2, false, 256, 4, 8>;
+
+template <class G>
+__global__ __launch_bounds__(64 * G::NWAVES, G::NWAVES == 8 ? 1 : 2) void gateup_bf16_v2(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
-  const int nt = a.N / 64;
+  // each of the two B matrices (wg_t, wu_t) contributes BN / 2 columns of the tile
+  static_assert(G::BN % 2 == 0, "two B matrices");
+  constexpr int TW = G::BN / 2;
+  const int nt = a.N / TW;
   const int mv = rows_valid(a);
   int mi, ni;
   tile_of((int)blockIdx.x, (a.M + G::BM - 1) / G::BM, nt, &mi, &ni);
-  const int m0 = mi * G::BM, n0 = ni * 64;
+  const int m0 = mi * G::BM, n0 = ni * TW;
   if (m0 >= mv) return;
   G g;
   const uint16_t* B[2] = {(const uint16_t*)a.b0, (const uint16_t*)a.b1};
@@ -385,8 +394,16 @@ hipError_t launch_dense_gateup(int dtype, const void* x, const void* wg_t, const
                                const int* n_rows_dev, int K, int N, hipStream_t stream) {
   DenseArgs a{x, wg_t, wu_t, b_g, h, rowmap, n_rows_dev, M, K, N};
   if (dtype == 1 && K % 32 == 0) {
-    hipLaunchKernelGGL(gateup_bf16_v2, dim3((unsigned)(((M + 255) / 256) * (N / 64))), dim3(256), 0,
-                       stream, a);
+#ifndef SFFN_DENSE_WIDE
+#define SFFN_DENSE_WIDE 1
+#endif
+    const long wide_tiles = (long)((M + 255) / 256) * (N / 128);
+    if (SFFN_DENSE_WIDE && N % 128 == 0 && wide_tiles >= 2 * 256)
+      hipLaunchKernelGGL(gateup_bf16_v2<DenseWide>, dim3((unsigned)wide_tiles), dim3(512), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL(gateup_bf16_v2<DenseNarrow>, dim3((unsigned)(((M + 255) / 256) * (N / 64))),
+                         dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(((M + 127) / 128) * (N / 64)));

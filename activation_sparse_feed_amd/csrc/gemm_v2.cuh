@@ -97,7 +97,7 @@ struct Gemm2 {
   static constexpr int WM = BM / WAVES_M, WN = BNW / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
-  static_assert(BN == 128 || (BN == 256 && NB == 1 && !B_KN), "workgroup N tile");
+  static_assert(BN == 128 || (BN == 256 && !B_KN), "workgroup N tile");
   static_assert(BM == 256 || BM == 128 || BM == 64 || BM == 32, "workgroup M tile");
   static_assert(BLOCKS % NWAVES == 0, "load blocks per wave");
   static_assert(!NORMS || NWAVES == 4, "norm split assumes 4 waves");

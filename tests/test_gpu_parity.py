@@ -153,6 +153,19 @@ def test_dense_reference(name, T):
     check_y(w.dtype, y, ref["y_dense"], np.zeros(w.T, dtype=bool))
 
 
+def test_dense_reference_prefill_full_size_sampled():
+    # 4096 tokens: the dense gate+up runs its 256 x 128 (eight-wave) tiles
+    sffn = _sffn()
+    w = wl.WORKLOADS["prefill_1pct"]
+    inp = wl.generate(w)
+    d = device_inputs(inp)
+    dense = sffn.DenseFFN(w.T, w.d_model, w.d_ff, torch.bfloat16)
+    y = to_f64(dense.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"]))
+    rows = sample_rows(w.T, 64, seed=6)
+    ref = oracle_rows(inp, rows, w.tile, w.cap)
+    check_y(w.dtype, y[rows], ref["y_dense"], np.zeros(len(rows), dtype=bool))
+
+
 @pytest.mark.parametrize("T,K,N", [(1, 256, 512), (7, 384, 1280), (32, 1024, 4096)])
 def test_dense_reference_few_tokens(T, K, N):
     """Split-K dense kernels (few tokens), ragged row fragments included."""
