@@ -39,6 +39,10 @@ struct DenseArgs {
   int route_nt = 0, route_cap = 0;
   int32_t* routed_out = nullptr;
   int32_t* n_routed_out = nullptr;
+  // fused route only: per-output-tile split counters of the down GEMM, zeroed
+  // by workgroup 0 of the routed gate+up before the down GEMM runs
+  int* tile_count = nullptr;
+  int tile_count_n = 0;
 };
 
 __device__ __forceinline__ int rows_valid(const DenseArgs& a) {
@@ -295,6 +299,7 @@ __global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
     if (blockIdx.x == 0) {
       if ((int)threadIdx.x < mv) a.routed_out[threadIdx.x] = rows_s[threadIdx.x];
       if (threadIdx.x == 0) *a.n_routed_out = mv;
+      for (int i = (int)threadIdx.x; i < a.tile_count_n; i += (int)blockDim.x) a.tile_count[i] = 0;
     }
     a.rowmap = rows_s;
     gateup_routed_tiles<RoutedFused>(a, mv, lds);
@@ -362,6 +367,31 @@ __global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partia
         const int m = m0 + row, n = n0 + col;
         if (m < mv && n < a.N) part[(size_t)m * a.N + n] = v;
       });
+      if (a.tile_count) {
+        // the tile's last split to finish sums the splits' partials in split
+        // order and writes y (no reduction launch): agent-scope fences make the
+        // partials visible across the XCDs' L2s; nothing waits
+        __shared__ int last_s;
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) last_s = atomicAdd(&a.tile_count[mi + mt * ni], 1) == S - 1;
+        __syncthreads();
+        if (last_s) {
+          __threadfence();
+          const size_t per = (size_t)mt * G::BM * a.N;
+          for (int q = (int)threadIdx.x; q < G::BM * 32; q += (int)blockDim.x) {
+            const int m = m0 + q / 32, n = n0 + 4 * (q % 32);
+            if (m >= mv || n >= a.N) continue;
+            const size_t off = (size_t)m * a.N + n;
+            f32x4_t v = *(const f32x4_t*)(partial + off);
+            for (int s2 = 1; s2 < S; ++s2) v += *(const f32x4_t*)(partial + s2 * per + off);
+            uint16_t* dst = y + (size_t)a.rowmap[m] * a.N + n;
+            *(uint2*)dst = make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                      (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+          }
+        }
+        __syncthreads();  // last_s is reused by the next item
+      }
     }
   }
 }
@@ -431,7 +461,7 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
 
 namespace sffn {
 
-size_t routed_partial_bytes(int T, int N, int K) {
+size_t routed_partial_core_bytes(int T, int N, int K) {
   // the largest S * mt of routed_down_splits over every possible row count
   // (S > 1 only: one split writes y directly)
   const int nt = (N + 127) / 128;
@@ -440,7 +470,13 @@ size_t routed_partial_bytes(int T, int N, int K) {
     const int S = routed_down_splits(mt, nt, K);
     if (S > 1) rows = std::max(rows, (size_t)S * mt * 128);
   }
-  return rows * (size_t)N * 4;
+  return (rows * (size_t)N * 4 + 255) & ~(size_t)255;
+}
+
+// the partials, then the fused route's per-tile split counters
+size_t routed_partial_bytes(int T, int N, int K) {
+  return routed_partial_core_bytes(T, N, K) +
+         (size_t)((T + 127) / 128) * ((N + 127) / 128) * sizeof(int);
 }
 
 hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
@@ -450,12 +486,19 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
                              hipStream_t stream) {
   // h [rows, d_ff] = gate+up of the routed rows of x
   DenseArgs g{x, wg_t, wu_t, b_g, h, routed, n_routed, T, d_model, d_ff};
+  // fused route (few tokens): the down GEMM's splits are summed by the last
+  // split of each tile, with counters after the partials in the workspace
+  int* tile_count = nullptr;
+  const int count_n = ((T + 127) / 128) * ((d_model + 127) / 128);
   if (route_count) {
     g.route_count = route_count;
     g.route_nt = route_nt;
     g.route_cap = route_cap;
     g.routed_out = routed;
     g.n_routed_out = n_routed;
+    tile_count = (int*)((char*)partial + routed_partial_core_bytes(T, d_model, d_ff));
+    g.tile_count = tile_count;
+    g.tile_count_n = count_n;
   }
   const int tiles_max = ((T + 127) / 128) * (d_ff / 64);
   if (route_count)
@@ -468,6 +511,7 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
   if (e != hipSuccess) return e;
   // y rows = h wd
   DenseArgs d{h, wd, nullptr, nullptr, y, routed, n_routed, T, d_ff, d_model};
+  d.tile_count = tile_count;
   // grids no larger than the most work the row count allows (few tokens: the
   // launches that find no routed row dispatch fewer workgroups)
   const long down_items = (long)((T + 127) / 128) * ((d_model + 127) / 128) * kRoutedMaxSplit;
@@ -476,6 +520,7 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
                      dim3(256), 0, stream, d, partial);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (tile_count) return hipSuccess;  // the down GEMM summed its own splits
   hipLaunchKernelGGL(down_routed_reduce, dim3((unsigned)std::max<long>(1, std::min<long>(256, red_blocks))),
                      dim3(256), 0, stream, d, (const float*)partial);
   return hipGetLastError();
