@@ -337,6 +337,10 @@ __host__ __device__ inline int routed_down_splits(int mt, int nt, int K) {
 
 // y rows of the routed list: with one split, written directly (rounded);
 // with S > 1, float32 partials [S][mt * 128][N] that down_routed_reduce sums.
+// FOLD (few tokens, a.tile_count set): the tile's last split sums the
+// partials; a template flag so that the many-token instantiation keeps its
+// registers (and occupancy) free of the summation.
+template <bool FOLD>
 __global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partial) {
   using G = Gemm2<1, 128, false, 32, 2, true, 128, SFFN_ROUTED_STAGES>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partia
         const int m = m0 + row, n = n0 + col;
         if (m < mv && n < a.N) part[(size_t)m * a.N + n] = v;
       });
-      if (a.tile_count) {
+      if (FOLD) {
         // the tile's last split to finish sums the splits' partials in split
         // order and writes y (no reduction launch): agent-scope fences make the
         // partials visible across the XCDs' L2s; nothing waits
@@ -516,8 +520,12 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
   // launches that find no routed row dispatch fewer workgroups)
   const long down_items = (long)((T + 127) / 128) * ((d_model + 127) / 128) * kRoutedMaxSplit;
   const long red_blocks = ((long)T * d_model / 4 + 255) / 256;
-  hipLaunchKernelGGL(down_routed, dim3((unsigned)std::min<long>(kRoutedGrid, down_items)),
-                     dim3(256), 0, stream, d, partial);
+  if (tile_count)
+    hipLaunchKernelGGL(down_routed<true>, dim3((unsigned)std::min<long>(kRoutedGrid, down_items)),
+                       dim3(256), 0, stream, d, partial);
+  else
+    hipLaunchKernelGGL(down_routed<false>, dim3((unsigned)std::min<long>(kRoutedGrid, down_items)),
+                       dim3(256), 0, stream, d, partial);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (tile_count) return hipSuccess;  // the down GEMM summed its own splits
