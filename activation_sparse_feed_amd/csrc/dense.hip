@@ -233,9 +233,7 @@ __global__ __launch_bounds__(256, 2) void down_bf16_v2(DenseArgs a) {
 // active tiles are spread over all XCDs by the round-robin dispatch.  128-row tiles and a deeper LDS
 // pipeline than the full-size kernels: with few tiles there are few
 // workgroups per CU to hide memory latency with.
-#ifndef SFFN_ROUTED_STAGES
-#define SFFN_ROUTED_STAGES 5
-#endif
+constexpr int kRoutedStages = 5;     // LDS ring depth of the 128-row routed gate+up
 constexpr int kRoutedGrid = 512;     // workgroups of the routed kernels
 constexpr int kRoutedMaxSplit = 8;   // K splits of the routed down GEMM
 
@@ -276,11 +274,11 @@ __device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, 
 // to hide memory latency with); many: the 256-row tiles of the full-size
 // kernel.
 constexpr int kRoutedBigRows = 1024;
-using RoutedSmall = Gemm2<2, 64, false, 32, 2, false, 128, SFFN_ROUTED_STAGES>;
+using RoutedSmall = Gemm2<2, 64, false, 32, 2, false, 128, kRoutedStages>;
 using RoutedBig = Gemm2<2, 64, false, 32, 2>;
 // With the fused route (at most kRouteBlock rows): one stage less, so that the
 // row list fits beside the ring and two workgroups still share a CU.
-using RoutedFused = Gemm2<2, 64, false, 32, 2, false, 128, SFFN_ROUTED_STAGES - 1>;
+using RoutedFused = Gemm2<2, 64, false, 32, 2, false, 128, kRoutedStages - 1>;
 
 template <bool FUSED>
 __global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
@@ -342,7 +340,7 @@ __host__ __device__ inline int routed_down_splits(int mt, int nt, int K) {
 // registers (and occupancy) free of the summation.
 template <bool FOLD>
 __global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partial) {
-  using G = Gemm2<1, 128, false, 32, 2, true, 128, SFFN_ROUTED_STAGES>;
+  using G = Gemm2<1, 128, false, 32, 2, true, 128, kRoutedStages>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   const int mv = uniform(rows_valid(a));
   const int mt = (mv + G::BM - 1) / G::BM, nt = (a.N + 127) / 128;
@@ -428,11 +426,8 @@ hipError_t launch_dense_gateup(int dtype, const void* x, const void* wg_t, const
                                const int* n_rows_dev, int K, int N, hipStream_t stream) {
   DenseArgs a{x, wg_t, wu_t, b_g, h, rowmap, n_rows_dev, M, K, N};
   if (dtype == 1 && K % 32 == 0) {
-#ifndef SFFN_DENSE_WIDE
-#define SFFN_DENSE_WIDE 1
-#endif
     const long wide_tiles = (long)((M + 255) / 256) * (N / 128);
-    if (SFFN_DENSE_WIDE && N % 128 == 0 && wide_tiles >= 2 * 256)
+    if (N % 128 == 0 && wide_tiles >= 2 * 256)
       hipLaunchKernelGGL(gateup_bf16_v2<DenseWide>, dim3((unsigned)wide_tiles), dim3(512), 0,
                          stream, a);
     else

@@ -14,6 +14,12 @@
 //                 the time, two or more keep it busy.  Each lane's sum of its
 //                 accumulators is stored (2048 * iters, exact in float32 for
 //                 iters < 8192), which also checks that every MFMA ran.
+//   probe_mfma_step
+//                 one v_mfma_f32_16x16x32_bf16 per wave on caller-given
+//                 operand registers, so a test can compare the instruction's
+//                 result with the exact C + A.B: the error model that the
+//                 TwELL epilogue's guard band assumes (one rounding of the
+//                 result per instruction) is checked on the hardware itself.
 #include "common.cuh"
 #include "sffn.h"
 
@@ -69,6 +75,19 @@ __global__ __launch_bounds__(kProbeBlock) void probe_mfma(float* __restrict__ ou
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Wave w, lane l: A and B operand registers a/b[(w * 64 + l) * 8 .. + 8]
+// (bf16 bits), accumulator c[(w * 64 + l) * 4 .. + 4]; d receives the MFMA's
+// four accumulator registers at the same place.
+__global__ __launch_bounds__(64) void probe_mfma_step(const u32x4_t* __restrict__ a,
+                                                      const u32x4_t* __restrict__ b,
+                                                      const f32x4_t* __restrict__ c,
+                                                      f32x4_t* __restrict__ d) {
+  const size_t i = (size_t)blockIdx.x * 64 + threadIdx.x;
+  const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[i]);
+  const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, b[i]);
+  d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c[i], 0, 0, 0);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -91,5 +110,16 @@ extern "C" int32_t sffn_probe_mfma(float* out, int32_t workgroups, int32_t iters
   if (!out || workgroups <= 0 || iters <= 0 || iters >= 8192) return SFFN_ERR_ARG;
   hipLaunchKernelGGL(probe_mfma, dim3((unsigned)workgroups), dim3(kProbeBlock), 0,
                      (hipStream_t)stream, out, (int)iters, 0x3F803F80u, 0x3F803F80u);
+  return hipGetLastError() == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
+}
+
+extern "C" int32_t sffn_probe_mfma_step(const void* a, const void* b, const float* c, float* d,
+                                        int32_t waves, void* stream) {
+  using namespace sffn;
+  if (!a || !b || !c || !d || !aligned16(a) || !aligned16(b) || !aligned16(c) || !aligned16(d) ||
+      waves <= 0)
+    return SFFN_ERR_ARG;
+  hipLaunchKernelGGL(probe_mfma_step, dim3((unsigned)waves), dim3(64), 0, (hipStream_t)stream,
+                     (const u32x4_t*)a, (const u32x4_t*)b, (const f32x4_t*)c, (f32x4_t*)d);
   return hipGetLastError() == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
 }

@@ -10,9 +10,11 @@
 //   y += (h * u) * wd[j]    16-byte loads of the wd row, float32 FMA into the
 //                           lane's slice of y_t held in registers
 // With S == 1 the wave writes y_t once, rounded to dtype.  With S > 1 (few
-// tokens, e.g. decode) each split writes a float32 partial; the last split to
-// finish a token (ticket counter) sums the partials in split order, writes
-// y_t and re-arms the ticket, so the result does not depend on timing.
+// tokens) each split writes a float32 partial; the last split to finish a
+// token (ticket counter) sums the partials in split order and writes y_t, so
+// the result does not depend on timing.  The tickets are cleared by a small
+// kernel at the start of every call: the workspace carries nothing from one
+// call to the next.
 // Rows with any tile over capacity are skipped (the hybrid route owns them).
 #include "common.cuh"
 #include "launch.h"
@@ -158,7 +160,11 @@ __global__ __launch_bounds__(256) void sparse_updown(SparseArgs a) {
 #pragma unroll
       for (int q = 0; q < E; ++q) Elt<T>::store1(a.y, (size_t)t * a.K + (size_t)ch * E + q, yv[c][q]);
   }
-  if (lane == 0) a.tickets[t] = 0;
+}
+
+__global__ void clear_tickets(int* tickets, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) tickets[i] = 0;
 }
 
 // Many tokens (prefill): one token per wave, WAVES tokens per workgroup.  The
@@ -170,10 +176,7 @@ __global__ __launch_bounds__(256) void sparse_updown(SparseArgs a) {
 // processes them two at a time so that four row loads are in flight:
 //   u = x_t . wu_t[j] with packed bf16 dot2, uniform DPP reduction;
 //   y_t += (h * u) * wd[j] in float32 registers.
-#ifndef SFFN_WIN_TILES
-#define SFFN_WIN_TILES 4
-#endif
-constexpr int kWinTiles = SFFN_WIN_TILES;
+constexpr int kWinTiles = 4;
 
 template <int NCH, int WAVES, bool FULL>
 __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
@@ -306,11 +309,7 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
       }
       __builtin_amdgcn_wave_barrier();
     }
-#ifndef SFFN_WIN_SYNC_EVERY
-#define SFFN_WIN_SYNC_EVERY 1
-#endif
-    if (SFFN_WIN_SYNC_EVERY > 0 && ((k0 / kWinTiles + 1) % (SFFN_WIN_SYNC_EVERY > 0 ? SFFN_WIN_SYNC_EVERY : 1)) == 0)
-      __syncthreads();
+    __syncthreads();
   }
   if (!active) return;
 #pragma unroll
@@ -361,14 +360,8 @@ struct TwoPassArgs {
   int T, K, nt, cap;
 };
 
-#ifndef SFFN_UP_SLOTS
-#define SFFN_UP_SLOTS 16
-#endif
-#ifndef SFFN_UP_BATCH
-#define SFFN_UP_BATCH 4
-#endif
-constexpr int kUpSlots = SFFN_UP_SLOTS;  // slots per wave in pass 1 (<= 64)
-constexpr int kUpBatch = SFFN_UP_BATCH;  // wu_t rows in flight per wave
+constexpr int kUpSlots = 16;  // slots per wave in pass 1 (<= 64)
+constexpr int kUpBatch = 4;   // wu_t rows in flight per wave
 
 // Tiles per group for a given number of lanes: whole tiles, at least one.
 __host__ __device__ inline int tiles_per_group(int lanes, int cap) {
@@ -459,10 +452,7 @@ __global__ __launch_bounds__(256) void sparse_up_pass(TwoPassArgs a, int groups)
 
 constexpr int kDownCols = 512;  // output columns per workgroup of pass 2
 constexpr int kDownWaves = 8;   // waves per workgroup of pass 2
-#ifndef SFFN_DOWN_INFLIGHT
-#define SFFN_DOWN_INFLIGHT 8
-#endif
-constexpr int kDownInflight = SFFN_DOWN_INFLIGHT;  // wd row loads in flight per wave
+constexpr int kDownInflight = 8;  // wd row loads in flight per wave
 
 __global__ __launch_bounds__(kDownWaves * 64) void sparse_down_pass(TwoPassArgs a, int groups,
                                                                     int chunks) {
@@ -590,10 +580,7 @@ hipError_t launch_window(const SparseArgs& a, int nch, hipStream_t stream) {
   switch (nch) {
     case 1: launch_win<1, 16>(a, stream); break;
     case 2: launch_win<2, 16>(a, stream); break;
-#ifndef SFFN_WIN_WAVES4
-#define SFFN_WIN_WAVES4 16
-#endif
-    case 4: launch_win<4, SFFN_WIN_WAVES4>(a, stream); break;
+    case 4: launch_win<4, 16>(a, stream); break;
     case 8: launch_win<8, 8>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
@@ -608,11 +595,8 @@ int pow2_at_least(int v) {
 
 }  // namespace
 
-#ifndef SFFN_TWO_PASS_MAX_T
-#define SFFN_TWO_PASS_MAX_T 256
-#endif
 // bf16 with few tokens takes the two-pass kernels.
-static bool use_two_pass(int dtype, int T) { return dtype == 1 && T <= SFFN_TWO_PASS_MAX_T; }
+static bool use_two_pass(int dtype, int T) { return dtype == 1 && T <= 256; }
 
 int sparse_splits(int T, int n_tiles, int /*d_model*/) {
   // enough wavefronts to cover the chip (~2048) when there are few tokens
@@ -645,6 +629,8 @@ hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, cons
   if (S > 1) {
     a.tickets = (int*)ws;
     a.partial = (float*)((char*)ws + align256((size_t)T * 4));
+    hipLaunchKernelGGL(clear_tickets, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream,
+                       a.tickets, T);
   }
   if (dtype == 1) {
     const int nch = pow2_at_least((K / 8 + 63) / 64);

@@ -166,34 +166,14 @@ __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, 
 }
 
 // Configuration of the 256-row gate GEMM (gate_twell_bf16_v2 and gate_preact_bf16).
-#ifndef SFFN_GATE_BN
-#define SFFN_GATE_BN 128
-#endif
-#ifndef SFFN_GATE_BM
-#define SFFN_GATE_BM 256
-#endif
-#ifndef SFFN_GATE_STAGES
-#define SFFN_GATE_STAGES 4
-#endif
-#ifndef SFFN_GATE_BK
-#define SFFN_GATE_BK 32
-#endif
-#ifndef SFFN_GATE_WAVES
-#define SFFN_GATE_WAVES 8
-#endif
-#ifndef SFFN_GATE_WN
-#define SFFN_GATE_WN 1
-#endif
-#ifndef SFFN_GATE_OCC
-#define SFFN_GATE_OCC 1
-#endif
-using GateGemm = Gemm2<1, SFFN_GATE_BN, false, SFFN_GATE_BK, SFFN_GATE_WN, false, SFFN_GATE_BM,
-                       SFFN_GATE_STAGES, SFFN_GATE_WAVES>;
+constexpr int kGateBK = 32;      // K depth of one pipeline stage
+constexpr int kGateStages = 4;   // LDS ring depth
+constexpr int kGateWaves = 8;    // waves per workgroup (two per SIMD)
+using GateGemm = Gemm2<1, 128, false, kGateBK, 1, false, 256, kGateStages, kGateWaves>;
 static_assert(GateGemm::WN == kTile, "each wave holds one TwELL column tile");
 // 256 x 256 tiles of the same kernel: eight waves as 4 x 2, each 64 rows x one
 // TwELL tile (a quarter fewer LDS fragment bytes per MFMA than 32 x 128).
-using GateGemmWide = Gemm2<1, 256, false, SFFN_GATE_BK, 2, false, 256, SFFN_GATE_STAGES,
-                           SFFN_GATE_WAVES>;
+using GateGemmWide = Gemm2<1, 256, false, kGateBK, 2, false, 256, kGateStages, kGateWaves>;
 static_assert(GateGemmWide::WN == kTile, "each wave holds one TwELL column tile");
 
 // Columns of 256-wide tiles (wide_nt, counted in 256-column tiles) and of

@@ -79,9 +79,7 @@ __global__ __launch_bounds__(256) void gate_twell_bf16(GateArgs a) {
 // Guard band: each entry is first tested against a bound for its whole row
 // (largest column norm and bias of the wave's tile); only entries inside it
 // get the per-entry band, and only those inside that are re-evaluated exactly.
-#ifndef SFFN_EPI_EXACT_U
-#define SFFN_EPI_EXACT_U 4  // exact re-evaluation: 16-byte chunks per lane loaded together
-#endif
+constexpr int kEpiExactChunks = 4;  // exact re-evaluation: 16-byte chunks per lane loaded together
 
 template <class G>
 struct AccEpi {
@@ -124,7 +122,7 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, G& g, AccEpi<G>& c)
         const int lrow = c.wm * G::WM + FM * 16 + 4 * (L >> 4) + R;
         const int lcol = fn * 16 + (L & 15);
         const float bl = a.b ? a.b[c.n0 + lcol] : 0.f;
-        const ExactResult e = exact_gate_value<uint16_t, SFFN_EPI_EXACT_U>(
+        const ExactResult e = exact_gate_value<uint16_t, kEpiExactChunks>(
             (const uint16_t*)a.x + (size_t)(c.m0 + lrow) * a.K,
             (const uint16_t*)a.wg + (size_t)(c.n0 + lcol) * a.K, bl, a.K, c.exact_lds);
         if (c.lane == L) {
@@ -236,7 +234,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, uint8_t* lds, int m
 // (GateGemm) of the columns after.  The wide tiles read a quarter fewer LDS
 // bytes per MFMA; the narrow ones fill what would otherwise be a part-empty
 // last round of wide tiles.
-__global__ __launch_bounds__(64 * SFFN_GATE_WAVES, SFFN_GATE_OCC) void gate_twell_bf16_v2(
+__global__ __launch_bounds__(64 * kGateWaves, 1) void gate_twell_bf16_v2(
     GateArgs a, int wide_nt, int narrow_nt) {
   static_assert(GateGemm::NWAVES == GateGemmWide::NWAVES, "one block size");
   static_assert(GateGemm::BM == GateGemmWide::BM, "one row tiling");
@@ -310,10 +308,7 @@ __global__ __launch_bounds__(256) void gate_twell_f32(GateArgs a) {
 // boundary orders the partial writes before their reads, so no fence or
 // counter is needed, and the sums are in a fixed order: deterministic.
 constexpr int kSkinnyFN = kTile / 16;
-#ifndef SFFN_SKINNY_STEPS
-#define SFFN_SKINNY_STEPS 4
-#endif
-constexpr int kSkinnySteps = SFFN_SKINNY_STEPS;  // max K steps of 32 per wave
+constexpr int kSkinnySteps = 4;  // max K steps of 32 per wave
 
 template <int MF>
 struct Skinny {
@@ -438,11 +433,8 @@ __global__ __launch_bounds__(256) void gate_skinny_partial(GateArgs a, float* pa
 // columns each, so their tiles are disjoint: no reduction across waves, and
 // one workgroup per (tile, split) with S chosen so that the grid fits the chip
 // at once (about one workgroup per CU).  Wave 0 also sums the squares of the x values it feeds to the MFMA.
-#ifndef SFFN_STREAM_STAGES
-#define SFFN_STREAM_STAGES 4
-#endif
 template <int MF>
-using StreamGemm = Gemm2<1, kTile, false, 64, 4, false, 16 * MF, SFFN_STREAM_STAGES, 4>;
+using StreamGemm = Gemm2<1, kTile, false, 64, 4, false, 16 * MF, 4, 4>;
 
 template <int MF>
 __global__ __launch_bounds__(256) void gate_skinny_stream(GateArgs a, float* partial, int S) {
@@ -555,17 +547,15 @@ __global__ __launch_bounds__(256) void gate_skinny_epilogue(GateArgs a, const fl
 }
 
 // Splits of the few-token gate: at least enough that no wave has more than
-// kSkinnySteps K steps, and about SFFN_SKINNY_WGS workgroups when the K
+// kSkinnySteps K steps, and about kSkinnyWgs workgroups when the K
 // range allows it (one step per wave at most that many splits).
-#ifndef SFFN_SKINNY_WGS
-#define SFFN_SKINNY_WGS 512
-#endif
+constexpr int kSkinnyWgs = 512;
 int skinny_splits(int K, int N) {
   const int nt = N / kTile;
   const int nk = K / 32;
   const int s_min = (nk + 4 * kSkinnySteps - 1) / (4 * kSkinnySteps);
   const int s_max = max(1, nk / 4);
-  int S = max(SFFN_SKINNY_WGS / nt, s_min);
+  int S = max(kSkinnyWgs / nt, s_min);
   S = min(S, max(s_max, s_min));
   return max(S, 1);
 }
@@ -573,15 +563,13 @@ int skinny_splits(int K, int N) {
 bool use_skinny(int dtype, int T, int K) { return dtype == 1 && T <= 64 && K % 32 == 0; }
 bool use_stream(int K) { return K % 64 == 0; }
 
-// Splits of the streaming kernel: about one workgroup per CU (SFFN_STREAM_WGS
+// Splits of the streaming kernel: about one workgroup per CU (kStreamWgs
 // in all; fewer, longer streams also leave fewer partials to sum), at most one
 // per 64-wide K chunk.
-#ifndef SFFN_STREAM_WGS
-#define SFFN_STREAM_WGS 256
-#endif
+constexpr int kStreamWgs = 256;
 int stream_splits(int K, int N) {
   const int nt = N / kTile;
-  return max(1, min(SFFN_STREAM_WGS / nt, K / 64));
+  return max(1, min(kStreamWgs / nt, K / 64));
 }
 
 int few_token_splits(int K, int N) { return use_stream(K) ? stream_splits(K, N) : skinny_splits(K, N); }
@@ -611,8 +599,10 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
     // Guard band for this summation order: the MFMA steps of a split (at most
     // kSkinnySteps per wave and two adds across the waves for the partial
     // kernel; the whole split, ceil(nc / S) 64-wide chunks, for the streaming
-    // kernel), S partials and the bias, each with the same 4u margin as the
-    // one-pass kernels.
+    // kernel), S partials and the bias.  With the measured MFMA error (product
+    // truncation at most 8u of sum |x_k w_k| over the whole sum, 2u of
+    // rounding per instruction) the total is below u (2 steps + S + 11)
+    // ||x|| ||w||, which 4u (steps + S + 2) covers.
     const bool strm = use_stream(K);
     const int S = few_token_splits(K, N);
     const int steps = strm ? 2 * ((K / 64 + S - 1) / S) : kSkinnySteps + 2;

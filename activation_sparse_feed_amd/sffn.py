@@ -23,8 +23,8 @@ TILE = 128
 
 EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
             "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
-            "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_workspace_bytes",
-            "sffn_strerror")
+            "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
+            "sffn_workspace_bytes", "sffn_strerror")
 
 
 class SffnError(RuntimeError):
@@ -55,11 +55,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sparse_ffn_bwd.argtypes = [sp] + [vp] * 17 + [vp, sz, vp]
     lib.sffn_probe_hbm.argtypes = [vp, vp, sz, i32, vp]
     lib.sffn_probe_mfma.argtypes = [vp, i32, i32, vp]
+    lib.sffn_probe_mfma_step.argtypes = [vp, vp, vp, vp, i32, vp]
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
                "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
-               "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma"):
+               "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
     lib.sffn_workspace_bytes.restype = sz
@@ -120,8 +121,8 @@ def workspace_bytes(shape: Shape, which: int) -> int:
 
 
 def alloc_workspace(shape: Shape, which: int, device=None) -> torch.Tensor:
-    """Zero-filled device workspace for one call kind (the sparse kernel expects
-    zero on first use and leaves it zero)."""
+    """Device workspace for one call kind (no call needs initial contents; it
+    is zero-filled only so that its bytes are defined)."""
     n = workspace_bytes(shape, which)
     return torch.zeros(max(n, 16), dtype=torch.uint8, device=device or "cuda")
 
@@ -188,6 +189,19 @@ def probe_mfma(out, iters: int, stream=None) -> None:
     wgs = out.numel() // 256
     _check("sffn_probe_mfma", _lib.sffn_probe_mfma(_ptr(out), int(wgs), int(iters),
                                                    _stream(stream)))
+
+
+def probe_mfma_step(a, b, c, d, stream=None) -> None:
+    """a, b: uint16/int16 [waves, 64, 8] operand registers; c, d: float32
+    [waves, 64, 4] accumulators in and out (one MFMA per wave)."""
+    waves = d.numel() // 256
+    if a.numel() != waves * 512 or b.numel() != waves * 512 or c.numel() != waves * 256 \
+            or d.numel() != waves * 256 or waves <= 0:
+        raise ValueError("a, b: [waves, 64, 8]; c, d: [waves, 64, 4]")
+    if c.dtype != torch.float32 or d.dtype != torch.float32:
+        raise TypeError("c and d must be float32")
+    _check("sffn_probe_mfma_step", _lib.sffn_probe_mfma_step(_ptr(a), _ptr(b), _ptr(c), _ptr(d),
+                                                             int(waves), _stream(stream)))
 
 
 def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=None) -> None:

@@ -207,3 +207,45 @@ def upstream_grad(w: Workload) -> np.ndarray:
     normals in the workload's storage format (bf16 bit patterns or float32)."""
     return _store(_normal(w.seed_base + SEED_OFFSETS["gy"], (w.T, w.d_model), 1.0), w.dtype)
 
+
+
+def generate_integer(T: int, d_model: int, d_ff: int, dtype: str, seed: int, m: int,
+                     variant: str = "dense", density: float = 2.0 / 3.0) -> Inputs:
+    """An exact-arithmetic fixture: x, wg_t, wu_t, wd hold only -1, 0 and 1
+    and the gate bias is -(m + 1/2), so every pre-activation is a half-integer
+    (never zero) and every product and sum of the forward is a small dyadic
+    rational.  Draws only; the caller checks that its sizes keep every
+    intermediate exactly representable in the arithmetic under test.
+
+    variant "dense": every entry of x and the three weights is nonzero with
+    probability ``density``, sign uniform.
+    variant "one_hot": x and wg_t as above; each row of wu_t and of wd has a
+    single +1 or -1 at a uniform position, so x_t . wu_t[j] is -1, 0 or 1 and
+    each output column sums few terms (exact in bfloat16 at moderate sizes).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def tern(shape):
+        nz = rng.random(shape) < density
+        sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+        return np.where(nz, sign, 0.0).astype(np.float32)
+
+    def one_hot(rows, cols):
+        a = np.zeros((rows, cols), dtype=np.float32)
+        pos = rng.integers(0, cols, size=rows)
+        a[np.arange(rows), pos] = np.where(rng.random(rows) < 0.5, -1.0, 1.0)
+        return a
+
+    x = tern((T, d_model))
+    wg = tern((d_ff, d_model))
+    if variant == "dense":
+        wu, wd = tern((d_ff, d_model)), tern((d_ff, d_model))
+    elif variant == "one_hot":
+        wu, wd = one_hot(d_ff, d_model), one_hot(d_ff, d_model)
+    else:
+        raise ValueError(f"unknown variant {variant!r}")
+    b = np.full(d_ff, -(m + 0.5), dtype=np.float32)
+    w = Workload("integer", T=T, d_model=d_model, d_ff=d_ff, dtype=dtype, beta=m + 0.5,
+                 seed_base=seed)
+    return Inputs(w, _store(x, dtype), _store(wg, dtype), _store(wu, dtype), _store(wd, dtype), b,
+                  np.ones(T, dtype=np.float32))

@@ -156,9 +156,10 @@ int32_t twell_pack_l1(const sffn_shape* shape, const void* x, const void* wg_t,
  * accumulated in float32 and written once, rounded to dtype.  Rows with any
  * count above cap are not touched (hybrid_route writes them).
  * workspace: at least sffn_workspace_bytes(shape, SFFN_WS_SPARSE) bytes of
- * device memory that the caller zero-fills once before its first use with
- * this library; calls leave it zero-filled where it must be.  May be NULL
- * when that size is 0.  Calls that share a workspace must be stream-ordered.
+ * device memory, no initial contents needed (every call initialises what it
+ * uses, so nothing is carried from one call to the next, also after a call
+ * that failed).  May be NULL when that size is 0.  Calls that share a
+ * workspace must be stream-ordered.
  */
 int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t,
                        const void* wd, const uint16_t* count, const uint16_t* idx,
@@ -307,6 +308,25 @@ int32_t sffn_probe_hbm(const void* src, void* dst, size_t bytes, int32_t workgro
  * SFFN_ERR_ARG).
  */
 int32_t sffn_probe_mfma(float* out, int32_t workgroups, int32_t iters, void* stream);
+
+/*
+ * sffn_probe_mfma_step -- one v_mfma_f32_16x16x32_bf16 per wave on operand
+ * registers given by the caller, so that a test can compare the instruction
+ * with the exact C + A.B.  The TwELL epilogue's guard band (twell_pack)
+ * assumes that each such instruction's float32 result carries at most a few
+ * unit roundoffs of error relative to |C| + sum |a_k b_k|; this probe lets
+ * that assumption be checked on the hardware.  For wave w (0 <= w < waves)
+ * and lane l (0..63): a[(64w + l) * 8 .. + 8] and b[...] are the lane's
+ * eight bf16 A and B operand values (uint16 bit patterns), c[(64w + l) * 4
+ * .. + 4] its four float32 accumulator inputs, and d[(64w + l) * 4 .. + 4]
+ * receives the four accumulator outputs.  The lane layout is the
+ * instruction's own (lane l holds row l % 16 of A, column l % 16 of B, and
+ * k = 8 (l / 16) .. 8 (l / 16) + 7 of both; its outputs are column l % 16,
+ * rows 4 (l / 16) .. 4 (l / 16) + 3).  Device pointers, 16-byte aligned,
+ * sized for `waves` waves; waves > 0 (else SFFN_ERR_ARG).
+ */
+int32_t sffn_probe_mfma_step(const void* a, const void* b, const float* c, float* d,
+                             int32_t waves, void* stream);
 
 /* Workspace bytes needed by one call for this shape (0 if the shape is invalid). */
 size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which);

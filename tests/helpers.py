@@ -36,15 +36,38 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
         return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def oracle_rows(inp: wl.Inputs, rows, tile: int, cap: int) -> dict:
-    """Oracle forward of a subset of rows (rows are independent)."""
+def oracle_rows(inp: wl.Inputs, rows, tile: int, cap: int, dense: bool = True) -> dict:
+    """Oracle forward of a subset of rows (rows are independent).  With
+    dense=False the oracle's dense FFN (y_dense) is not computed."""
     x = inp.rows_f64("x", rows)
     wg, wu, wd = inp.as_f64("wg_t"), inp.as_f64("wu_t"), inp.as_f64("wd")
     out = oracle.sparse_forward(x, wg, inp.b_g, wu, wd, tile, cap)
-    out["y_dense"] = oracle.ffn_dense(x, wg, inp.b_g, wu, wd)
+    if dense:
+        out["y_dense"] = oracle.ffn_dense(x, wg, inp.b_g, wu, wd)
     out["xnorm"] = np.linalg.norm(x, axis=1)
     out["wnorm"] = np.linalg.norm(wg, axis=1)
     return out
+
+
+def oracle_twell_all_rows(inp: wl.Inputs, tile: int, cap: int, chunk: int = 1024) -> dict:
+    """The oracle's gate and TwELL pack over every row, in row chunks (rows are
+    independent), without the up and down projections: count, idx, val and the
+    routed rows, for all-row comparisons at full size."""
+    T = inp.workload.T
+    wg = inp.as_f64("wg_t")
+    counts, idxs, vals = [], [], []
+    for r0 in range(0, T, chunk):
+        rows = np.arange(r0, min(T, r0 + chunk))
+        z = oracle.gate_preact(inp.rows_f64("x", rows), wg, inp.b_g)
+        c, i, v = oracle.twell_pack(z, tile, cap)
+        counts.append(c)
+        idxs.append(i)
+        vals.append(v)
+    count = np.concatenate(counts)
+    return {"count": count, "idx": np.concatenate(idxs), "val": np.concatenate(vals),
+            "routed": oracle.route(count, cap),
+            "xnorm": np.linalg.norm(inp.as_f64("x"), axis=1),
+            "wnorm": np.linalg.norm(wg, axis=1)}
 
 
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
@@ -74,7 +97,20 @@ def check_twell(dt: str, count, idx, val, ref: dict, cap: int) -> None:
     assert not bad.any(), f"{bad.sum()} TwELL values off, worst {err.max()}"
 
 
+def row_rel_err(y: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Relative Euclidean error of every row; rows whose exact output is zero
+    get their absolute error (they must come out exactly zero)."""
+    num = np.linalg.norm(y - y_ref, axis=1)
+    den = np.linalg.norm(y_ref, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
 def check_y(dt: str, y: np.ndarray, y_ref: np.ndarray, routed_mask: np.ndarray) -> dict:
+    """y against the oracle: the relative Frobenius error over all compared
+    rows, separately over routed and non-routed rows, AND on every single row
+    (so that a few wrong rows cannot hide in a block norm); rows whose exact
+    output is zero must be exactly zero.  Returns the errors, including the
+    largest per-row one."""
     tol = Y_TOL[dt]
     out = {"all": rel_fro(y, y_ref)}
     assert out["all"] <= tol, out
@@ -84,6 +120,13 @@ def check_y(dt: str, y: np.ndarray, y_ref: np.ndarray, routed_mask: np.ndarray) 
     if (~routed_mask).any():
         out["not_routed"] = rel_fro(y[~routed_mask], y_ref[~routed_mask])
         assert out["not_routed"] <= tol, out
+    rows = row_rel_err(y, y_ref)
+    out["max_row"] = float(rows.max()) if len(rows) else 0.0
+    out["worst_row"] = int(rows.argmax()) if len(rows) else -1
+    zero = np.linalg.norm(y_ref, axis=1) == 0
+    assert not np.any(rows[zero] != 0.0), f"rows {np.nonzero(zero & (rows != 0))[0][:8]} should be 0"
+    bad = np.nonzero(rows > tol)[0]
+    assert len(bad) == 0, f"{len(bad)} rows over {tol}: {bad[:8]} (max {out['max_row']:.3e})"
     return out
 
 

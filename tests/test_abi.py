@@ -207,3 +207,6 @@ def test_probe_errors(sffn):
     assert lib.sffn_probe_mfma(P, 0, 16, None) == ARG
     assert lib.sffn_probe_mfma(P, 4, 0, None) == ARG
     assert lib.sffn_probe_mfma(P, 4, 8192, None) == ARG
+    assert lib.sffn_probe_mfma_step(None, P, P, P, 1, None) == ARG
+    assert lib.sffn_probe_mfma_step(P, P, P, MISALIGNED, 1, None) == ARG
+    assert lib.sffn_probe_mfma_step(P, P, P, P, 0, None) == ARG

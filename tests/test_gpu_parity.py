@@ -3,9 +3,10 @@
 TwELL counts, live indices, the routed-row set and n_routed are compared bit
 for bit; TwELL values within the storage rounding; y by relative Frobenius
 error (1e-5 float32, 5e-3 bf16 with float32 accumulation), over all compared
-rows and separately over routed and non-routed rows.  Full-size workloads run
-at their real shape on the GPU and are compared on a row sample that always
-includes routed rows.
+rows, separately over routed and non-routed rows, and on every compared row
+by itself.  The prefill and hybrid workloads are compared on all 4096 rows;
+the large workload's counts, live indices and routed set on all 16384 rows,
+its y on a sample of rows that includes routed ones.
 """
 from __future__ import annotations
 
@@ -14,7 +15,8 @@ import pytest
 import torch
 
 from activation_sparse_feed_amd import workloads as wl
-from helpers import (check_twell, check_y, device_inputs, oracle_rows, sample_rows, to_f64)
+from helpers import (check_twell, check_y, device_inputs, oracle_rows, oracle_twell_all_rows,
+                     sample_rows, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +50,7 @@ def compare(inp: wl.Inputs, cap: int, rows=None, ffn=None, y=None) -> dict:
     assert np.array_equal(routed_gpu, np.nonzero(count_all.max(1) > cap)[0])
     if rows is None:
         rows = np.arange(T)
-    ref = oracle_rows(inp, rows, w.tile, cap)
+    ref = oracle_rows(inp, rows, w.tile, cap, dense=False)
     # ... and those counts match the oracle bit for bit on the compared rows
     check_twell(w.dtype, count_all[rows], ffn.idx.cpu().numpy()[rows],
                 to_f64(ffn.val)[rows], ref, cap)
@@ -60,6 +62,8 @@ def compare(inp: wl.Inputs, cap: int, rows=None, ffn=None, y=None) -> dict:
     mask[ref["routed"]] = True
     errs = check_y(w.dtype, to_f64(y[rows]), ref["y"], mask)
     errs["n_routed"] = n_r
+    print(f"{w.name}: rows {len(rows)}/{T} routed {n_r} rel_err {errs['all']:.3e} "
+          f"max_row {errs['max_row']:.3e}")
     return errs
 
 
@@ -84,16 +88,14 @@ def test_f32_ragged_tail_with_routing():
     assert e["n_routed"] > 0
 
 
-def test_prefill_full_size_sampled():
+def test_prefill_full_size_all_rows():
     w = wl.WORKLOADS["prefill_1pct"]
     inp = wl.generate(w)
     ffn, y, _ = run_sparse(inp, w.cap)
-    n_r = int(ffn.n_routed.item())
-    rows = sample_rows(w.T, 160, must=ffn.routed[:n_r].cpu().numpy(), seed=1)
-    compare(inp, w.cap, rows, ffn, y)
+    compare(inp, w.cap, None, ffn, y)
 
 
-def test_hybrid_mix_full_size_sampled():
+def test_hybrid_mix_full_size_all_rows():
     w = wl.WORKLOADS["hybrid_mix"]
     inp = wl.generate(w)
     ffn, y, _ = run_sparse(inp, w.cap)
@@ -102,8 +104,7 @@ def test_hybrid_mix_full_size_sampled():
     routed = ffn.routed[:n_r].cpu().numpy()
     assert set(heavy.tolist()) <= set(routed.tolist())
     assert 60 <= n_r <= 260
-    rows = sample_rows(w.T, 96, must=np.concatenate([heavy, routed[:40]]), seed=2)
-    e = compare(inp, w.cap, rows, ffn, y)
+    e = compare(inp, w.cap, None, ffn, y)
     assert "routed" in e and "not_routed" in e
 
 
@@ -112,14 +113,20 @@ def test_decode_all_rows():
     compare(inp, 8)
 
 
-def test_large_lognormal_full_size_sampled():
+def test_large_lognormal_full_size():
+    """Counts, live indices, values and the routed set on all 16384 rows
+    (the oracle's gate in row chunks); y on 320 rows, 64 of them routed."""
     w = wl.WORKLOADS["large_lognormal"]
     inp = wl.generate(w)
     ffn, y, _ = run_sparse(inp, w.cap)
     n_r = int(ffn.n_routed.item())
     assert 0.08 * w.T < n_r < 0.3 * w.T
-    routed = ffn.routed[:n_r].cpu().numpy()
-    rows = sample_rows(w.T, 40, must=routed[::max(1, n_r // 12)], seed=3)
+    routed = ffn.routed[:n_r].cpu().numpy().astype(np.int64)
+    ref = oracle_twell_all_rows(inp, w.tile, w.cap)
+    check_twell(w.dtype, ffn.count.cpu().numpy(), ffn.idx.cpu().numpy(), to_f64(ffn.val), ref,
+                w.cap)
+    assert np.array_equal(routed, ref["routed"])
+    rows = sample_rows(w.T, 256, must=routed[::max(1, n_r // 64)], seed=3)
     compare(inp, w.cap, rows, ffn, y)
 
 
@@ -129,10 +136,7 @@ def test_gate_tile_mix_with_odd_tile_count():
     inp = wl.generate_custom(T=33000, d_model=256, d_ff=384, dtype="bf16", beta=1.5,
                              seed_base=70, cap=8)
     ffn, y, _ = run_sparse(inp, 8)
-    n_r = int(ffn.n_routed.item())
-    rows = np.unique(np.concatenate([sample_rows(33000, 48, must=ffn.routed[:min(n_r, 8)].cpu().numpy(), seed=5),
-                                     np.arange(32768, 33000, 29), [32999]]))
-    compare(inp, 8, rows, ffn, y)
+    compare(inp, 8, None, ffn, y)
 
 
 # ------------------------------------------------------------- dense reference
@@ -320,9 +324,9 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(y1, y2)
 
 
-def test_decode_split_reduction_repeats():
-    """The split-partial reduction (few tokens) re-arms its tickets: repeated
-    calls give identical results."""
+def test_decode_two_pass_repeats():
+    """The few-token bf16 kernels (two passes through the workspace) give
+    bitwise identical results on repeated calls."""
     inp = wl.generate(wl.WORKLOADS["decode_1pct"])
     ffn, y1, d = run_sparse(inp, 8)
     y1 = y1.clone()
@@ -330,3 +334,53 @@ def test_decode_split_reduction_repeats():
         y2 = ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_f32_split_tickets_repeat():
+    """The float32 few-token path splits each row's tiles and reduces the
+    partials through per-row tickets: repeated calls on one workspace give
+    bitwise identical results that match the oracle."""
+    sffn = _sffn()
+    w = wl.WORKLOADS["tiny_f32"]
+    assert sffn.workspace_bytes(sffn.make_shape(w.T, w.d_model, w.d_ff, w.cap, sffn.SFFN_F32),
+                                sffn.WS_SPARSE) > 0  # the ticket path
+    inp = wl.generate(w)
+    ffn, y1, d = run_sparse(inp, w.cap)
+    y1 = y1.clone()
+    for _ in range(3):
+        y2 = ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+    compare(inp, w.cap, None, ffn, y2)
+
+
+def test_shared_sparse_workspace_across_shapes():
+    """One sparse_ffn_fwd workspace, filled with garbage first, serves calls of
+    different shapes and kernel paths in turn (bf16 two-pass with 32 tokens,
+    bf16 split tickets with 512, float32 tickets with 64, twice each): every
+    call matches a call on a fresh workspace bit for bit and the oracle."""
+    sffn = _sffn()
+    cases = [wl.WORKLOADS["decode_1pct"].replace(d_ff=2048),
+             wl.WORKLOADS["decode_1pct"].replace(T=512, d_ff=2048),
+             wl.WORKLOADS["tiny_f32"]]
+    shapes = [sffn.make_shape(w.T, w.d_model, w.d_ff, w.cap,
+                              sffn.SFFN_BF16 if w.dtype == "bf16" else sffn.SFFN_F32)
+              for w in cases]
+    n = max(sffn.workspace_bytes(s, sffn.WS_SPARSE) for s in shapes)
+    shared = torch.randint(0, 256, (max(n, 16),), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for w, s in zip(cases, shapes):
+            inp = wl.generate(w)
+            d = device_inputs(inp)
+            dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+            ffn = sffn.SparseFFN(w.T, w.d_model, w.d_ff, w.cap, dt)
+            ref_y = ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"]).clone()
+            y = torch.empty_like(ref_y)
+            sffn.sparse_ffn_fwd(s, d["x"], d["wu_t"], d["wd"], ffn.count, ffn.idx, ffn.val, y,
+                                shared)
+            sffn.hybrid_route(s, d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], ffn.count,
+                              ffn.routed, ffn.n_routed, ffn.ws_hybrid, y)
+            torch.cuda.synchronize()
+            assert torch.equal(y, ref_y), (rep, w.name, w.T)
+            if rep == 0:
+                compare(inp, w.cap, None, ffn, y)
