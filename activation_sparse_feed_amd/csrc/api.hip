@@ -3,6 +3,8 @@
 // Nothing here allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "sffn.h"
 #include "launch.h"
 #include "route.cuh"
@@ -80,6 +82,41 @@ size_t convert_ws(const sffn_shape* s) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? SFFN_OK : SFFN_ERR_HIP; }
 
+}  // namespace
+
+// Scratch memory of twell_pack_noalloc: a static device array instead of a
+// caller workspace, for callers that cannot allocate.  Every GPU the library
+// runs on holds its own copy until the process ends.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices];  // device address of `scratch`, per device, set once
+
+// Device address of the scratch array on the device that runs `stream`.  The
+// array's name is only a host-side handle: kernels must be given this address.
+int32_t device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return SFFN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SFFN_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return SFFN_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return SFFN_ERR_HIP;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return SFFN_OK;
+}
+
 // Guard band of the activity decision (see the TwELL epilogue), with
 // u = 2^-24 and S = sum_k |x_k w_k| <= ||x|| ||w||.
 // bf16: one v_mfma_f32_16x16x32_bf16 was measured (sffn_probe_mfma_step) to
@@ -152,6 +189,25 @@ int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t, con
   return pack_impl(shape, x, wg_t, b_g, wg_norms, count, idx, val, workspace, nullptr, nullptr,
                    (hipStream_t)stream);
 }
+
+int32_t twell_pack_noalloc(const sffn_shape* shape, const void* x, const void* wg_t,
+                           const float* b_g, const float* wg_norms, uint16_t* count,
+                           uint16_t* idx, void* val, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (shape->T == 0) return SFFN_OK;
+  st = check_pack(shape, x, wg_t, b_g, wg_norms, count, idx, val);
+  if (st != SFFN_OK) return st;
+  if (act_bytes_too_large(shape)) return SFFN_ERR_UNSUPPORTED;
+  if (pack_ws(shape) > kNoAllocScratchBytes) return SFFN_ERR_TOO_LARGE;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  st = device_scratch(s, &ws);
+  if (st != SFFN_OK) return st;
+  return pack_impl(shape, x, wg_t, b_g, wg_norms, count, idx, val, ws, nullptr, nullptr, s);
+}
+
+size_t twell_pack_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 int32_t twell_pack_l1(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
                       const float* wg_norms, uint16_t* count, uint16_t* idx, void* val,
@@ -381,6 +437,8 @@ const char* sffn_strerror(int32_t status) {
     case SFFN_ERR_UNSUPPORTED: return "shape or parameter outside the supported range";
     case SFFN_ERR_WORKSPACE: return "workspace missing or too small";
     case SFFN_ERR_HIP: return "HIP launch or runtime error";
+    case SFFN_ERR_TOO_LARGE:
+      return "shape needs more scratch than twell_pack_noalloc holds (use twell_pack)";
     default: return "unknown sffn status";
   }
 }

@@ -17,11 +17,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsffn.so")
 
 SFFN_OK, SFFN_ERR_ARG, SFFN_ERR_UNSUPPORTED, SFFN_ERR_WORKSPACE, SFFN_ERR_HIP = 0, -1, -2, -3, -4
+SFFN_ERR_TOO_LARGE = -5
 SFFN_F32, SFFN_BF16 = 0, 1
 WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK, WS_CONVERT, WS_PACK_L1, WS_BACKWARD = 0, 1, 2, 3, 4, 5, 6
 TILE = 128
 
-EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
+EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_noalloc",
+            "twell_pack_noalloc_max_bytes", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
             "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
             "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
             "sffn_workspace_bytes", "sffn_strerror")
@@ -47,6 +49,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sp = ctypes.POINTER(Shape)
     lib.twell_weight_norms.argtypes = [sp, vp, vp, vp]
     lib.twell_pack.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.twell_pack_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.twell_pack_noalloc_max_bytes.argtypes = []
+    lib.twell_pack_noalloc_max_bytes.restype = sz
     lib.twell_pack_l1.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.sparse_ffn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
@@ -58,8 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sffn_probe_mfma_step.argtypes = [vp, vp, vp, vp, i32, vp]
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for fn in ("twell_weight_norms", "twell_pack", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
-               "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
+    for fn in ("twell_weight_norms", "twell_pack", "twell_pack_noalloc", "twell_pack_l1",
+               "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
                "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
@@ -149,6 +154,17 @@ def twell_pack(shape: Shape, x, wg_t, b_g, count, idx, val, workspace, wg_norms=
     _check("twell_pack", _lib.twell_pack(ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g),
                                          _ptr(wg_norms), _ptr(count), _ptr(idx), _ptr(val),
                                          _ptr(workspace), ws_n, _stream(stream)))
+
+
+def twell_pack_noalloc(shape: Shape, x, wg_t, b_g, count, idx, val, wg_norms=None,
+                       stream=None) -> None:
+    _check("twell_pack_noalloc", _lib.twell_pack_noalloc(
+        ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wg_norms), _ptr(count),
+        _ptr(idx), _ptr(val), _stream(stream)))
+
+
+def twell_pack_noalloc_max_bytes() -> int:
+    return int(_lib.twell_pack_noalloc_max_bytes())
 
 
 def twell_pack_l1(shape: Shape, x, wg_t, b_g, count, idx, val, lam: float, l1_value, workspace,

@@ -21,7 +21,8 @@
  *     scalars are passed by value or through the host struct sffn_shape.
  *   - Every call is asynchronous on the given HIP stream (hipStream_t passed
  *     as void*; NULL means the default stream).  The library never allocates,
- *     frees or synchronises.  The caller owns all memory, workspace included.
+ *     frees or synchronises.  The caller owns all memory, workspace included,
+ *     except the static scratch array of twell_pack_noalloc (see there).
  *   - Layouts (row-major):
  *       x, y                  [T, d_model]
  *       wg_t, wu_t, wd        [d_ff, d_model]; row j holds the d_model weights
@@ -60,7 +61,8 @@ typedef enum {
   SFFN_ERR_ARG = -1,         /* null/misaligned pointer, negative or inconsistent size */
   SFFN_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
   SFFN_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than sffn_workspace_bytes */
-  SFFN_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+  SFFN_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+  SFFN_ERR_TOO_LARGE = -5    /* twell_pack_noalloc: shape needs more than its scratch */
 } sffn_status;
 
 typedef enum { SFFN_F32 = 0, SFFN_BF16 = 1 } sffn_dtype;
@@ -121,6 +123,29 @@ int32_t twell_weight_norms(const sffn_shape* shape, const void* wg_t, float* wg_
 int32_t twell_pack(const sffn_shape* shape, const void* x, const void* wg_t,
                    const float* b_g, const float* wg_norms, uint16_t* count, uint16_t* idx,
                    void* val, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * twell_pack_noalloc -- twell_pack without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same computation,
+ * kernels and outputs as twell_pack (bit for bit); the workspace is a static
+ * device array of twell_pack_noalloc_max_bytes() bytes (32 MiB) inside the
+ * library, one per GPU, held until the process ends.  Nothing is allocated
+ * or freed by the call (the first call on a device looks the array's address
+ * up; later calls reuse it).  Shapes whose twell_pack workspace
+ * (sffn_workspace_bytes(shape, SFFN_WS_PACK)) exceeds that size return
+ * SFFN_ERR_TOO_LARGE before anything is launched.  All calls on one GPU share
+ * the array: calls that overlap in time on one GPU (on different streams or
+ * host threads) race and must not be issued; calls ordered on one stream are
+ * safe.  The scratch needs no initial contents.  Arguments and errors
+ * otherwise as twell_pack; the device is the one that runs `stream`.
+ */
+int32_t twell_pack_noalloc(const sffn_shape* shape, const void* x, const void* wg_t,
+                           const float* b_g, const float* wg_norms, uint16_t* count,
+                           uint16_t* idx, void* val, void* stream);
+
+/* Size in bytes of twell_pack_noalloc's static scratch array. */
+size_t twell_pack_noalloc_max_bytes(void);
 
 /*
  * twell_pack_l1 -- twell_pack plus the L1 activation regulariser that drives

@@ -210,3 +210,21 @@ def test_probe_errors(sffn):
     assert lib.sffn_probe_mfma_step(None, P, P, P, 1, None) == ARG
     assert lib.sffn_probe_mfma_step(P, P, P, MISALIGNED, 1, None) == ARG
     assert lib.sffn_probe_mfma_step(P, P, P, P, 0, None) == ARG
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(sffn):
+    """twell_pack_noalloc checks the workspace its shape needs against its
+    static scratch on the host, before any device call."""
+    lib = sffn._lib
+    cap_bytes = sffn.twell_pack_noalloc_max_bytes()
+    assert cap_bytes == 32 << 20
+    big = _shape(sffn, T=9_000_000, d_model=8, d_ff=512)   # row norms alone exceed 32 MiB
+    assert sffn.workspace_bytes(big, sffn.WS_PACK) > cap_bytes
+    assert lib.twell_pack_noalloc(ctypes.byref(big), P, P, None, None, P, P, P, None) == \
+        sffn.SFFN_ERR_TOO_LARGE
+    assert "scratch" in sffn.strerror(sffn.SFFN_ERR_TOO_LARGE)
+    ok = _shape(sffn)
+    assert lib.twell_pack_noalloc(ctypes.byref(ok), None, P, None, None, P, P, P, None) == \
+        sffn.SFFN_ERR_ARG
+    assert lib.twell_pack_noalloc(ctypes.byref(_shape(sffn, T=0)), None, None, None, None, None,
+                                  None, None, None) == sffn.SFFN_OK
