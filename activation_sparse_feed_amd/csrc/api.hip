@@ -387,11 +387,12 @@ int32_t ell_from_preact(const sffn_shape* shape, int32_t width, const float* z, 
 int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
                        const void* wu_t, const void* wd, const float* wg_norms,
                        const uint16_t* count, const uint16_t* idx, const void* val,
-                       const int32_t* routed, const int32_t* n_routed, const void* gy, void* gx,
-                       float* gwg_t, float* gwu_t, float* gwd, float* gb, void* workspace,
-                       size_t ws_bytes, void* stream) {
+                       const int32_t* routed, const int32_t* n_routed, const void* gy,
+                       float l1_lambda, void* gx, float* gwg_t, float* gwu_t, float* gwd,
+                       float* gb, void* workspace, size_t ws_bytes, void* stream) {
   int32_t st = check_shape(shape);
   if (st != SFFN_OK) return st;
+  if (!(l1_lambda == l1_lambda)) return SFFN_ERR_ARG;
   if (shape->T == 0) return SFFN_OK;
   if (!ptrs_ok({x, wg_t, wu_t, wd, count, routed, n_routed, gy, gx, gwg_t, gwu_t, gwd}) ||
       (b_g && !aligned16(b_g)) || (wg_norms && !aligned16(wg_norms)) || (gb && !aligned16(gb)))
@@ -411,6 +412,7 @@ int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t,
   return hip_status(launch_backward(x, wg_t, b_g, wu_t, wd, xn, wg_norms ? wg_norms : wbuf, count,
                                     idx, val, routed, n_routed, gy, gx, gwg_t, gwu_t, gwd, gb,
                                     shape->T, shape->d_model, shape->d_ff, shape->cap,
+                                    (float)((double)l1_lambda / (double)shape->T),
                                     guard_band(shape), bws, s));
 }
 

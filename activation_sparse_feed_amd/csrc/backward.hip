@@ -5,7 +5,9 @@
 // only the active entries (t, j) carry gradient.  Per entry, with h its TwELL
 // value:
 //   u  = x_t . wu_t[j],  ga = gy_t . wd[j]
-//   gz = ga u,  gu = ga h,  a = h u
+//   gz = ga u + l1g,  gu = ga h,  a = h u
+//     (l1g = lambda / T: the gradient of the L1 activation regulariser
+//     lambda / T sum ReLU(z) on an active entry; 0 when it is not trained)
 //   gx_t     += gz wg_t[j] + gu wu_t[j]
 //   gwg_t[j] += gz x_t,  gwu_t[j] += gu x_t,  gwd[j] += a gy_t,  gb[j] += gz
 // Rows within capacity take their entries from the forward's TwELL lists;
@@ -72,6 +74,7 @@ struct BwdArgs {
   float* gwd;              // [N, D]
   float* gb;               // [N] or null
   int T, D, N, nt, cap;
+  float l1g;               // lambda / T, added to gz of every active entry
 };
 
 // Position of row t in the ascending routed list (binary search), or -1.
@@ -172,7 +175,7 @@ __device__ __forceinline__ void bwd_entry(const BwdArgs& a, int j, float h, cons
   }
   const float u = wave_sum_uniform(su);
   const float ga = wave_sum_uniform(sg);
-  const float gz = ga * u, gu = ga * h;
+  const float gz = ga * u + a.l1g, gu = ga * h;
 #pragma unroll
   for (int c = 0; c < P; ++c) {
     float uf[8], wf[8];
@@ -730,7 +733,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       const float u = wave_sum_uniform(su);
       const float ga = wave_sum_uniform(sg);
       const bool live = e + i < e1;
-      const float gz = live ? ga * u : 0.f, gu = live ? ga * h[i] : 0.f;
+      const float gz = live ? ga * u + a.l1g : 0.f, gu = live ? ga * h[i] : 0.f;
       const float aa = live ? h[i] * u : 0.f;
       if (live && lane == 0) a.co[pos[i]] = f32x4_t{gz, gu, aa, 0.f};
 #pragma unroll
@@ -878,7 +881,8 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
                            const uint16_t* count, const uint16_t* idx, const void* val,
                            const int32_t* routed, const int32_t* n_routed, const void* gy,
                            void* gx, float* gwg_t, float* gwu_t, float* gwd, float* gb, int T,
-                           int D, int N, int cap, GuardBand band, void* ws, hipStream_t stream) {
+                           int D, int N, int cap, float l1g, GuardBand band, void* ws,
+                           hipStream_t stream) {
   const int nt = N / kBTile;
   char* p = (char*)ws;
   float* z_r = (float*)p;          // routed rows' z, then (same bytes) their entry gradients
@@ -923,7 +927,7 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   BwdArgs a{(const uint16_t*)x, (const uint16_t*)wg_t, (const uint16_t*)wu_t,
             (const uint16_t*)wd, (const uint16_t*)gy, count, idx, (const uint16_t*)val,
             routed, n_routed, ecount, eidx, eval, eoff, count_t, idx_t, co, co_r,
-            (uint16_t*)gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, cap};
+            (uint16_t*)gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, cap, l1g};
   const dim3 rows_grid((unsigned)((T + 3) / 4));
   hipLaunchKernelGGL(bwd_prep, rows_grid, dim3(256), 0, stream, a);
   e = hipGetLastError();

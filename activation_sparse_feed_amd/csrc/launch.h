@@ -55,7 +55,7 @@ hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, c
 
 // Backward through TwELL and the hybrid routing (bf16, d_model % 512 == 0,
 // d_model <= 4096): gx [T, D] bf16, float32 weight gradients [N, D] and gb
-// [N] (may be null).  xnorm: ||x_t|| of every row; wnorm: ||wg_t[j]||.  ws:
+// [N] (may be null).  l1g is added to gz of every active entry.  xnorm: ||x_t|| of every row; wnorm: ||wg_t[j]||.  ws:
 // backward_workspace_bytes().
 bool backward_supported(int dtype, int d_model);
 size_t backward_workspace_bytes(int T, int N, int D, int cap);
@@ -64,7 +64,8 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
                            const uint16_t* count, const uint16_t* idx, const void* val,
                            const int32_t* routed, const int32_t* n_routed, const void* gy,
                            void* gx, float* gwg_t, float* gwu_t, float* gwd, float* gb, int T,
-                           int D, int N, int cap, GuardBand band, void* ws, hipStream_t stream);
+                           int D, int N, int cap, float l1g, GuardBand band, void* ws,
+                           hipStream_t stream);
 
 // Row norms of a [rows_a, K] and a [rows_b, K] matrix in one launch.
 hipError_t launch_row_norms(int dtype, const void* a, int rows_a, float* out_a, const void* b,

@@ -57,7 +57,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.gate_preact.argtypes = [sp, vp, vp, vp, vp, vp]
-    lib.sparse_ffn_bwd.argtypes = [sp] + [vp] * 17 + [vp, sz, vp]
+    lib.sparse_ffn_bwd.argtypes = [sp] + [vp] * 12 + [ctypes.c_float] + [vp] * 5 + [vp, sz, vp]
     lib.sffn_probe_hbm.argtypes = [vp, vp, sz, i32, vp]
     lib.sffn_probe_mfma.argtypes = [vp, i32, i32, vp]
     lib.sffn_probe_mfma_step.argtypes = [vp, vp, vp, vp, i32, vp]
@@ -228,7 +228,8 @@ def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=Non
 
 
 def sparse_ffn_bwd(shape: Shape, x, wg_t, b_g, wu_t, wd, count, idx, val, routed, n_routed, gy,
-                   gx, gwg_t, gwu_t, gwd, gb, workspace, wg_norms=None, stream=None) -> None:
+                   gx, gwg_t, gwu_t, gwd, gb, workspace, wg_norms=None, l1_lambda: float = 0.0,
+                   stream=None) -> None:
     for name, t in (("gwg_t", gwg_t), ("gwu_t", gwu_t), ("gwd", gwd)):
         if t.dtype != torch.float32 or tuple(t.shape) != (shape.d_ff, shape.d_model):
             raise ValueError(f"{name} must be float32 [d_ff, d_model]")
@@ -237,8 +238,9 @@ def sparse_ffn_bwd(shape: Shape, x, wg_t, b_g, wu_t, wd, count, idx, val, routed
     ws_n = workspace.numel() * workspace.element_size()
     _check("sparse_ffn_bwd", _lib.sparse_ffn_bwd(
         ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd), _ptr(wg_norms),
-        _ptr(count), _ptr(idx), _ptr(val), _ptr(routed), _ptr(n_routed), _ptr(gy), _ptr(gx),
-        _ptr(gwg_t), _ptr(gwu_t), _ptr(gwd), _ptr(gb), _ptr(workspace), ws_n, _stream(stream)))
+        _ptr(count), _ptr(idx), _ptr(val), _ptr(routed), _ptr(n_routed), _ptr(gy),
+        float(l1_lambda), _ptr(gx), _ptr(gwg_t), _ptr(gwu_t), _ptr(gwd), _ptr(gb), _ptr(workspace),
+        ws_n, _stream(stream)))
 
 
 def gate_preact(shape: Shape, x, wg_t, b_g, z, stream=None) -> None:

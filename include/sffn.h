@@ -161,8 +161,8 @@ size_t twell_pack_noalloc_max_bytes(void);
  * row and tile), and those partial sums are added in float64 in a fixed
  * order, so the value is deterministic.  The
  * gradient of the term with respect to z is lambda / T on exactly the active
- * entries (the uncapped TwELL support) and 0 elsewhere, so it needs no output
- * of its own.  T == 0 writes 0.  Outputs and arguments otherwise as
+ * entries (the uncapped TwELL support) and 0 elsewhere; sparse_ffn_bwd adds it
+ * when given the same lambda.  T == 0 writes 0.  Outputs and arguments otherwise as
  * twell_pack; lambda must not be NaN (else SFFN_ERR_ARG); workspace: at least
  * sffn_workspace_bytes(shape, SFFN_WS_PACK_L1) bytes, no initial contents.
  */
@@ -214,16 +214,23 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
 
 /*
  * sparse_ffn_bwd -- backward of the sparse forward (training through TwELL
- * and the hybrid routing: pwwt.cn article, sections 03-04).  For the upstream
- * gradient gy = dL/dy and the forward's count/idx/val (from twell_pack) and
- * routed/n_routed (from hybrid_route), by the chain rule on the gated FFN:
+ * and the hybrid routing: pwwt.cn article, sections 03-04), optionally with
+ * the L1 activation regulariser of the same training recipe (section 04:
+ * the penalty lambda / T * sum_t sum_j ReLU(z[t, j]) whose value
+ * twell_pack_l1 computes).  For the upstream gradient gy = dL/dy, the
+ * regulariser weight l1_lambda (0 for none) and the forward's count/idx/val
+ * (from twell_pack) and routed/n_routed (from hybrid_route), by the chain
+ * rule on the gated FFN:
  *
  *   gx[t, :]    = sum_j gz[t,j] wg_t[j, :] + gu[t,j] wu_t[j, :]     (dtype)
  *   gwg_t[j, :] = sum_t gz[t,j] x[t, :]      gwu_t[j, :] = sum_t gu[t,j] x[t, :]
  *   gwd[j, :]   = sum_t a[t,j] gy[t, :]      gb[j] = sum_t gz[t,j]  (float32)
  *
- * over the active entries only (gz = ga u, gu = ga h, a = h u with
- * ga = gy_t . wd[j], u = x_t . wu_t[j]; ReLU' is 0 elsewhere).  Rows within
+ * over the active entries only (gz = ga u + l1_lambda / T, gu = ga h,
+ * a = h u with ga = gy_t . wd[j], u = x_t . wu_t[j]; ReLU' is 0 elsewhere,
+ * so the regulariser adds l1_lambda / T to gz on exactly the active entries,
+ * those past the capacity included).  l1_lambda must not be NaN (else
+ * SFFN_ERR_ARG).  Rows within
  * capacity use their TwELL entries (h = val); routed rows use complete
  * activity lists rebuilt from x with twell_pack's GEMM and exact activity
  * decision (h rounded to bf16 like val).  Every sum runs in a fixed order:
@@ -242,9 +249,9 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
 int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
                        const void* wu_t, const void* wd, const float* wg_norms,
                        const uint16_t* count, const uint16_t* idx, const void* val,
-                       const int32_t* routed, const int32_t* n_routed, const void* gy, void* gx,
-                       float* gwg_t, float* gwu_t, float* gwd, float* gb, void* workspace,
-                       size_t ws_bytes, void* stream);
+                       const int32_t* routed, const int32_t* n_routed, const void* gy,
+                       float l1_lambda, void* gx, float* gwg_t, float* gwu_t, float* gwd,
+                       float* gb, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * dense_ffn_ref -- the dense gated FFN used as the speed-up reference

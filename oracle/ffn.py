@@ -259,19 +259,29 @@ def sparse_forward(x, wg_t, b_g, wu_t, wd, tile: int, cap: int) -> dict:
     return {"z": z, "count": count, "idx": idx, "val": val, "routed": R, "y": y}
 
 
-def ffn_dense_backward(x, wg_t, b_g, wu_t, wd, gy) -> dict:
+def ffn_dense_backward(x, wg_t, b_g, wu_t, wd, gy, lam: float = 0.0) -> dict:
     """Gradients of the gated FFN y = (ReLU(x W_g + b_g) * x W_u) W_d for an
     upstream gradient gy = dL/dy, by the chain rule on the plain definition
     (the pages give the forward only; training through the format is their
-    pwwt.cn section 03-04 result):
+    pwwt.cn section 03-04 result), with the L1 activation regulariser
+    lam / T * sum_t sum_j ReLU(z) of the training recipe (section 04; see
+    l1_term) added to the loss:
 
       a  = h * u,  h = ReLU(z),  u = x wu_t^T       (forward)
       ga = gy wd^T                                   dL/da
-      gz = ga * u * [z > 0]   (ReLU' = 1 strictly above 0, 0 at and below)
+      gz = (ga * u + lam / T) * [z > 0]   (ReLU' = 1 strictly above 0, 0 at and below)
       gu = ga * h
       gx = gz wg_t + gu wu_t
       g_wg_t = gz^T x,  g_wu_t = gu^T x,  g_wd = a^T gy,  g_b = sum_t gz
     """
+    x = _f64(x)
+    T = x.shape[0]
+    return _dense_backward(x, wg_t, b_g, wu_t, wd, gy, float(lam) / T if T else 0.0)
+
+
+def _dense_backward(x, wg_t, b_g, wu_t, wd, gy, l1g: float) -> dict:
+    """ffn_dense_backward with the regulariser's per-entry gradient l1g given
+    (lam / T of the whole batch, also when x holds only some of its rows)."""
     x = _f64(x)
     z = gate_preact(x, wg_t, b_g)
     act = z > 0.0
@@ -280,20 +290,23 @@ def ffn_dense_backward(x, wg_t, b_g, wu_t, wd, gy) -> dict:
     u = x @ wu.T
     a = h * u
     ga = gy @ wdd.T
-    gz = np.where(act, ga * u, 0.0)
+    gz = np.where(act, ga * u + l1g, 0.0)
     gu = ga * h
     return {"gx": gz @ wg + gu @ wu, "gwg_t": gz.T @ x, "gwu_t": gu.T @ x,
             "gwd": a.T @ gy, "gb": gz.sum(axis=0)}
 
 
-def ffn_sparse_backward(x, wg_t, b_g, wu_t, wd, gy, count, idx, val, cap: int) -> dict:
+def ffn_sparse_backward(x, wg_t, b_g, wu_t, wd, gy, count, idx, val, cap: int,
+                        lam: float = 0.0) -> dict:
     """The same gradients from the forward's TwELL encoding: for rows within
     capacity only the packed entries (j, h) exist, so the up projection, the
     down-projection gradient and every product are taken per entry
     (u_e = x_t . wu_t[j], ga_e = gy_t . wd[j], gz_e = ga_e u_e, gu_e = ga_e h_e,
     a_e = h_e u_e), and the weight gradients are sums over the entries of each
     column; routed rows go through the dense formulas (hybrid routing, pwwt.cn
-    article section 03).  Uses val as h, as the sparse kernels do."""
+    article section 03).  Uses val as h, as the sparse kernels do.  The L1
+    regulariser adds lam / T (T: all rows) to gz of every active entry: the
+    packed ones and, for routed rows, all of theirs."""
     x = _f64(x)
     wg, wu, wdd, gy = _f64(wg_t), _f64(wu_t), _f64(wd), _f64(gy)
     count = np.asarray(count)
@@ -309,9 +322,10 @@ def ffn_sparse_backward(x, wg_t, b_g, wu_t, wd, gy, count, idx, val, cap: int) -
     rr, kk, ss = np.nonzero(live)
     jj = idx[rr, kk, ss]
     hh = val[rr, kk, ss]
+    l1g = float(lam) / T if T else 0.0
     u = np.einsum("ek,ek->e", x[rr], wu[jj]) if len(rr) else np.zeros(0)
     ga = np.einsum("ek,ek->e", gy[rr], wdd[jj]) if len(rr) else np.zeros(0)
-    gz, gu, a = ga * u, ga * hh, hh * u
+    gz, gu, a = ga * u + l1g, ga * hh, hh * u
     GZ = scipy.sparse.csr_matrix((gz, (rr, jj)), shape=(T, d_ff))
     GU = scipy.sparse.csr_matrix((gu, (rr, jj)), shape=(T, d_ff))
     A = scipy.sparse.csr_matrix((a, (rr, jj)), shape=(T, d_ff))
@@ -319,7 +333,7 @@ def ffn_sparse_backward(x, wg_t, b_g, wu_t, wd, gy, count, idx, val, cap: int) -
            "gwg_t": np.asarray(GZ.T @ x), "gwu_t": np.asarray(GU.T @ x),
            "gwd": np.asarray(A.T @ gy), "gb": np.asarray(GZ.sum(axis=0)).ravel()}
     if len(R):
-        d = ffn_dense_backward(x[R], wg_t, b_g, wu_t, wd, gy[R])
+        d = _dense_backward(x[R], wg_t, b_g, wu_t, wd, gy[R], l1g)
         out["gx"][R] = d["gx"]
         for k in ("gwg_t", "gwu_t", "gwd", "gb"):
             out[k] = out[k] + d[k]

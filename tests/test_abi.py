@@ -173,13 +173,16 @@ def test_backward_errors(sffn):
     s = _shape(sffn, d_model=512)
     need = sffn.workspace_bytes(s, sffn.WS_BACKWARD)
     assert need >= 20 * 64 * 512
-    args = [P] * 17
+    args = [P] * 12 + [0.25] + [P] * 5   # ..., gy, l1_lambda, gx, gwg_t, gwu_t, gwd, gb
     args[2] = None   # b_g
     args[5] = None   # wg_norms
-    args[16] = None  # gb
+    args[17] = None  # gb
     assert lib.sparse_ffn_bwd(ctypes.byref(s), *args, WS, need - 1, None) == -3
     bad = list(args)
-    bad[12] = None   # gx
+    bad[13] = None   # gx
+    assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
+    bad = list(args)
+    bad[12] = float("nan")  # l1_lambda
     assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
     bad = list(args)
     bad[9] = MISALIGNED  # routed
@@ -190,7 +193,8 @@ def test_backward_errors(sffn):
     sf = _shape(sffn, d_model=512, dtype=sffn.SFFN_F32)
     assert lib.sparse_ffn_bwd(ctypes.byref(sf), *args, WS, sffn.workspace_bytes(sf, 6), None) == -2
     s0 = _shape(sffn, T=0)
-    assert lib.sparse_ffn_bwd(ctypes.byref(s0), *([None] * 17), None, 0, None) == 0
+    assert lib.sparse_ffn_bwd(ctypes.byref(s0), *([None] * 12), 0.0, *([None] * 5), None, 0,
+                              None) == 0
 
 
 

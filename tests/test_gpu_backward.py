@@ -27,7 +27,7 @@ def _sffn():
     return sffn
 
 
-def run_backward(inp: wl.Inputs, cap: int, gy_np: np.ndarray, repeat: int = 1):
+def run_backward(inp: wl.Inputs, cap: int, gy_np: np.ndarray, repeat: int = 1, lam: float = 0.0):
     sffn = _sffn()
     w = inp.workload
     d = device_inputs(inp)
@@ -42,16 +42,16 @@ def run_backward(inp: wl.Inputs, cap: int, gy_np: np.ndarray, repeat: int = 1):
         g = [torch.full((w.d_ff, w.d_model), float("nan"), device="cuda") for _ in range(3)]
         gb = torch.full((w.d_ff,), float("nan"), device="cuda")
         sffn.sparse_ffn_bwd(s, d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], ffn.count, ffn.idx,
-                            ffn.val, ffn.routed, ffn.n_routed, gy, gx, *g, gb, ws)
+                            ffn.val, ffn.routed, ffn.n_routed, gy, gx, *g, gb, ws, l1_lambda=lam)
         outs.append({"gx": gx, "gwg_t": g[0], "gwu_t": g[1], "gwd": g[2], "gb": gb})
     torch.cuda.synchronize()
     return ffn, outs
 
 
-def check(inp: wl.Inputs, cap: int, dense: bool, rows=None):
+def check(inp: wl.Inputs, cap: int, dense: bool, rows=None, lam: float = 0.0):
     w = inp.workload
     gy_np = wl.upstream_grad(w)
-    ffn, outs = run_backward(inp, cap, gy_np, repeat=2)
+    ffn, outs = run_backward(inp, cap, gy_np, repeat=2, lam=lam)
     o = outs[0]
     for k in o:  # deterministic
         assert torch.equal(o[k].view(torch.int16) if o[k].dtype == torch.bfloat16 else o[k],
@@ -61,10 +61,11 @@ def check(inp: wl.Inputs, cap: int, dense: bool, rows=None):
     n_r = int(ffn.n_routed.item())
     routed = ffn.routed[:n_r].cpu().numpy().astype(np.int64)
     ref = oracle.ffn_sparse_backward(x, wg, inp.b_g, wu, wd, gy, ffn.count.cpu().numpy(),
-                                     ffn.idx.cpu().numpy().astype(np.int64), to_f64(ffn.val), cap)
+                                     ffn.idx.cpu().numpy().astype(np.int64), to_f64(ffn.val), cap,
+                                     lam)
     refs = [ref]
     if dense:
-        refs.append(oracle.ffn_dense_backward(x, wg, inp.b_g, wu, wd, gy))
+        refs.append(oracle.ffn_dense_backward(x, wg, inp.b_g, wu, wd, gy, lam))
     got = {k: to_f64(v) for k, v in o.items()}
     mask = np.zeros(w.T, dtype=bool)
     mask[routed] = True
@@ -132,3 +133,31 @@ def test_backward_rejects_unsupported_width():
     with pytest.raises(sffn.SffnError) as ei:
         sffn.sparse_ffn_bwd(s, b, w, None, w, w, c, i, v, r, r[:1], b, b, *g, None, ws)
     assert ei.value.status == sffn.SFFN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("T,d_model,d_ff,beta,cap", [
+    (300, 512, 1024, 1.9, 4),     # row pass, routed rows (complete lists)
+    (33, 512, 256, 2.0, 8),       # few tokens
+    (400, 1024, 512, 1.2, 8),     # fused column order (per-entry gradients in the column pass)
+    (130, 1536, 384, 1.5, 0),     # capacity 0: every active entry in a routed row
+])
+def test_backward_l1_regulariser(T, d_model, d_ff, beta, cap):
+    """The L1 activation regulariser's gradient (lam / T on every active entry,
+    routed rows' entries past the capacity included) through gz into gb,
+    gwg_t and gx, against the oracle with the same lam; the lam-free
+    gradients (gwu_t, gwd) are unchanged bit for bit."""
+    inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype="bf16", beta=beta,
+                             seed_base=71, cap=cap)
+    lam = 0.5
+    e = check(inp, cap, dense=True, lam=lam)
+    gy_np = wl.upstream_grad(inp.workload)
+    _, (with_l1,) = run_backward(inp, cap, gy_np, lam=lam)
+    _, (without,) = run_backward(inp, cap, gy_np, lam=0.0)
+    for k in ("gwu_t", "gwd"):
+        assert torch.equal(with_l1[k], without[k]), k
+    # gb moves by lam / T times the number of active rows of each column
+    x, wg = inp.as_f64("x"), inp.as_f64("wg_t")
+    act = (oracle.gate_preact(x, wg, inp.b_g) > 0).sum(0)
+    dgb = to_f64(with_l1["gb"]) - to_f64(without["gb"])
+    assert np.allclose(dgb, lam / T * act, rtol=1e-4, atol=1e-4 * (1 + np.abs(to_f64(without["gb"])).max()))
+    print(f"l1 backward T={T} d={d_model}: {e}")

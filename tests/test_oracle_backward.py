@@ -8,7 +8,10 @@ against facts that do not come from the oracle itself:
   * central finite differences of L = sum(y * gy) along random directions,
     on inputs whose pre-activations stay clear of the ReLU kink;
   * the sparse form against the dense one, and planted mistakes that the pins
-    must catch.
+    must catch;
+  * all of the above also with the L1 activation regulariser lam / T *
+    sum ReLU(z) added to the loss (its gradient lam / T on the active
+    entries).
 """
 from __future__ import annotations
 
@@ -23,17 +26,20 @@ from oracle import ffn as offn
 from test_oracle_pins import _bf16, tiny_cases
 
 
-def brute_backward(x, wg, b, wu, wd, gy):
-    """Exact chain rule with nested loops (no numpy arithmetic)."""
+def brute_backward(x, wg, b, wu, wd, gy, lam=0.0):
+    """Exact chain rule with nested loops (no numpy arithmetic); lam weights
+    the L1 term lam / T * sum ReLU(z) added to the loss."""
     F = lambda m: [[Fr(float(v)) for v in row] for row in m]
     X, G, U_, D, GY = F(x), F(wg), F(wu), F(wd), F(gy)
     B = [Fr(float(v)) for v in b]
     T, K, d_ff, dm = len(X), len(X[0]), len(G), len(D[0])
+    l1 = Fr(float(lam)) / T if T else Fr(0)
     z = [[B[j] + sum(X[t][k] * G[j][k] for k in range(K)) for j in range(d_ff)] for t in range(T)]
     u = [[sum(X[t][k] * U_[j][k] for k in range(K)) for j in range(d_ff)] for t in range(T)]
     h = [[z[t][j] if z[t][j] > 0 else Fr(0) for j in range(d_ff)] for t in range(T)]
     ga = [[sum(GY[t][c] * D[j][c] for c in range(dm)) for j in range(d_ff)] for t in range(T)]
-    gz = [[ga[t][j] * u[t][j] if z[t][j] > 0 else Fr(0) for j in range(d_ff)] for t in range(T)]
+    gz = [[ga[t][j] * u[t][j] + l1 if z[t][j] > 0 else Fr(0) for j in range(d_ff)]
+          for t in range(T)]
     gu = [[ga[t][j] * h[t][j] for j in range(d_ff)] for t in range(T)]
     gx = [[sum(gz[t][j] * G[j][k] + gu[t][j] * U_[j][k] for j in range(d_ff)) for k in range(K)]
           for t in range(T)]
@@ -60,22 +66,23 @@ def _gy(case, seed=3):
     return _bf16(np.random.default_rng(seed).standard_normal((x.shape[0], wd.shape[1])))
 
 
-def check_backward_against_brute(case):
+def check_backward_against_brute(case, lam=0.0):
     x, wg, b, wu, wd, tile, cap = case
     gy = _gy(case)
-    ref = brute_backward(x, wg, b, wu, wd, gy)
-    dense = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy)
+    ref = brute_backward(x, wg, b, wu, wd, gy, lam)
+    dense = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy, lam)
     z = oracle.gate_preact(x, wg, b)
     count, idx, val = oracle.twell_pack(z, tile, cap)
-    sparse = oracle.ffn_sparse_backward(x, wg, b, wu, wd, gy, count, idx, val, cap)
+    sparse = oracle.ffn_sparse_backward(x, wg, b, wu, wd, gy, count, idx, val, cap, lam)
     for out in (dense, sparse):
         for k in ("gx", "gwg_t", "gwu_t", "gwd", "gb"):
             _close(out[k], ref[k])
 
 
+@pytest.mark.parametrize("lam", [0.0, 0.75])
 @pytest.mark.parametrize("case", range(len(tiny_cases())))
-def test_backward_brute_force_tiny(case):
-    check_backward_against_brute(tiny_cases()[case])
+def test_backward_brute_force_tiny(case, lam):
+    check_backward_against_brute(tiny_cases()[case], lam)
 
 
 def _moderate(seed=11, T=20, K=32, d_ff=48, dm=None, margin=None):
@@ -97,27 +104,32 @@ def _moderate(seed=11, T=20, K=32, d_ff=48, dm=None, margin=None):
     return x, wg, b, wu, wd, gy
 
 
-def test_backward_matches_torch_autograd_float64():
+@pytest.mark.parametrize("lam", [0.0, 0.3])
+def test_backward_matches_torch_autograd_float64(lam):
     x, wg, b, wu, wd, gy = _moderate()
     t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
          for k, v in dict(x=x, wg=wg, b=b, wu=wu, wd=wd).items()}
-    y = (torch.relu(t["x"] @ t["wg"].T + t["b"]) * (t["x"] @ t["wu"].T)) @ t["wd"]
-    (y * torch.tensor(gy, dtype=torch.float64)).sum().backward()
-    got = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy)
+    h = torch.relu(t["x"] @ t["wg"].T + t["b"])
+    y = (h * (t["x"] @ t["wu"].T)) @ t["wd"]
+    loss = (y * torch.tensor(gy, dtype=torch.float64)).sum() + lam / x.shape[0] * h.sum()
+    loss.backward()
+    got = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy, lam)
     pairs = {"gx": "x", "gwg_t": "wg", "gwu_t": "wu", "gwd": "wd", "gb": "b"}
     for k, tk in pairs.items():
         ref = t[tk].grad.numpy()
         assert np.abs(got[k] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max()), k
 
 
-def test_backward_finite_differences():
+@pytest.mark.parametrize("lam", [0.0, 1.5])
+def test_backward_finite_differences(lam):
     x, wg, b, wu, wd, gy = _moderate(seed=12, T=6, K=8, d_ff=12, dm=5, margin=0.0625)
 
     def loss(x_, wg_, b_, wu_, wd_):
         z = x_ @ wg_.T + b_
-        return float(((np.maximum(z, 0.0) * (x_ @ wu_.T)) @ wd_ * gy).sum())
+        h = np.maximum(z, 0.0)
+        return float(((h * (x_ @ wu_.T)) @ wd_ * gy).sum()) + lam / x_.shape[0] * float(h.sum())
 
-    g = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy)
+    g = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy, lam)
     rng = np.random.default_rng(5)
     args = [x, wg, b, wu, wd]
     names = ["gx", "gwg_t", "gb", "gwu_t", "gwd"]
@@ -133,21 +145,22 @@ def test_backward_finite_differences():
     assert set(names) == set(g)
 
 
-def test_sparse_backward_equals_dense_with_routing():
+@pytest.mark.parametrize("lam", [0.0, 0.5])
+def test_sparse_backward_equals_dense_with_routing(lam):
     x, wg, b, wu, wd, gy = _moderate(seed=13, T=24, K=32, d_ff=64)
     z = oracle.gate_preact(x, wg, b)
     for cap in (0, 2, 4, 64):
         count, idx, val = oracle.twell_pack(z, 16, cap)
-        sp = oracle.ffn_sparse_backward(x, wg, b, wu, wd, gy, count, idx, val, cap)
-        de = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy)
+        sp = oracle.ffn_sparse_backward(x, wg, b, wu, wd, gy, count, idx, val, cap, lam)
+        de = oracle.ffn_dense_backward(x, wg, b, wu, wd, gy, lam)
         for k in de:
             assert np.abs(sp[k] - de[k]).max() <= 1e-12 * max(1.0, np.abs(de[k]).max()), (cap, k)
 
 
 # ------------------------------------------------------------ planted mistakes
 def _mut_no_relu_mask(orig):
-    def f(x, wg_t, b_g, wu_t, wd, gy):
-        out = orig(x, wg_t, b_g, wu_t, wd, gy)
+    def f(x, wg_t, b_g, wu_t, wd, gy, lam=0.0):
+        out = orig(x, wg_t, b_g, wu_t, wd, gy, lam)
         z = offn.gate_preact(x, wg_t, b_g)
         u = np.asarray(x, float) @ np.asarray(wu_t, float).T
         ga = np.asarray(gy, float) @ np.asarray(wd, float).T
@@ -157,8 +170,8 @@ def _mut_no_relu_mask(orig):
 
 
 def _mut_gu_from_u(orig):
-    def f(x, wg_t, b_g, wu_t, wd, gy):
-        out = orig(x, wg_t, b_g, wu_t, wd, gy)
+    def f(x, wg_t, b_g, wu_t, wd, gy, lam=0.0):
+        out = orig(x, wg_t, b_g, wu_t, wd, gy, lam)
         x64 = np.asarray(x, float)
         u = x64 @ np.asarray(wu_t, float).T
         ga = np.asarray(gy, float) @ np.asarray(wd, float).T
@@ -168,8 +181,8 @@ def _mut_gu_from_u(orig):
 
 
 def _mut_gwd_from_h(orig):
-    def f(x, wg_t, b_g, wu_t, wd, gy):
-        out = orig(x, wg_t, b_g, wu_t, wd, gy)
+    def f(x, wg_t, b_g, wu_t, wd, gy, lam=0.0):
+        out = orig(x, wg_t, b_g, wu_t, wd, gy, lam)
         h = offn.relu(offn.gate_preact(x, wg_t, b_g))
         out["gwd"] = h.T @ np.asarray(gy, float)  # a = h * u lost
         return out
@@ -177,8 +190,8 @@ def _mut_gwd_from_h(orig):
 
 
 def _mut_gx_gate_only(orig):
-    def f(x, wg_t, b_g, wu_t, wd, gy):
-        out = orig(x, wg_t, b_g, wu_t, wd, gy)
+    def f(x, wg_t, b_g, wu_t, wd, gy, lam=0.0):
+        out = orig(x, wg_t, b_g, wu_t, wd, gy, lam)
         z = offn.gate_preact(x, wg_t, b_g)
         x64 = np.asarray(x, float)
         u = x64 @ np.asarray(wu_t, float).T
@@ -188,8 +201,25 @@ def _mut_gx_gate_only(orig):
     return f
 
 
+def _mut_l1_everywhere(orig):
+    def f(x, wg_t, b_g, wu_t, wd, gy, lam=0.0):
+        out = orig(x, wg_t, b_g, wu_t, wd, gy, lam)
+        z = offn.gate_preact(x, wg_t, b_g)
+        T = np.asarray(x).shape[0]
+        out["gb"] = out["gb"] + lam / T * (z <= 0).sum(0)  # regulariser on inactive entries too
+        return out
+    return f
+
+
+def _mut_l1_no_mean(orig):
+    def f(x, wg_t, b_g, wu_t, wd, gy, lam=0.0):
+        return orig(x, wg_t, b_g, wu_t, wd, gy, lam * np.asarray(x).shape[0])  # lam, not lam / T
+    return f
+
+
 BWD_MUTATIONS = {"no_relu_mask": _mut_no_relu_mask, "gu_from_u": _mut_gu_from_u,
-                 "gwd_from_h": _mut_gwd_from_h, "gx_gate_only": _mut_gx_gate_only}
+                 "gwd_from_h": _mut_gwd_from_h, "gx_gate_only": _mut_gx_gate_only,
+                 "l1_everywhere": _mut_l1_everywhere, "l1_no_mean": _mut_l1_no_mean}
 
 
 @pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
@@ -197,10 +227,11 @@ def test_backward_planted_mistake_is_caught(name, monkeypatch):
     orig = offn.ffn_dense_backward
     monkeypatch.setattr(offn, "ffn_dense_backward", BWD_MUTATIONS[name](orig))
     monkeypatch.setattr(oracle, "ffn_dense_backward", offn.ffn_dense_backward)
+    lam = 0.75 if name.startswith("l1_") else 0.0
     caught = False
     for case in tiny_cases():
         try:
-            check_backward_against_brute(case)
+            check_backward_against_brute(case, lam)
         except AssertionError:
             caught = True
             break
