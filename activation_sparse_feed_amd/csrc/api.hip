@@ -71,9 +71,9 @@ size_t pack_l1_ws(const sffn_shape* s) {
   return pack_ws(s) + align256((size_t)s->T * (s->d_ff / 128) * 4) + align256(l1_ws_bytes());
 }
 
-size_t backward_ws(const sffn_shape* s) {
+size_t backward_ws(const sffn_shape* s, int max_routed) {
   return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4) +
-         backward_workspace_bytes(s->T, s->d_ff, s->d_model, s->cap);
+         backward_workspace_bytes(s->T, s->d_ff, s->d_model, s->cap, max_routed);
 }
 
 size_t convert_ws(const sffn_shape* s) {
@@ -387,18 +387,18 @@ int32_t ell_from_preact(const sffn_shape* shape, int32_t width, const float* z, 
 int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
                        const void* wu_t, const void* wd, const float* wg_norms,
                        const uint16_t* count, const uint16_t* idx, const void* val,
-                       const int32_t* routed, const int32_t* n_routed, const void* gy,
-                       float l1_lambda, void* gx, float* gwg_t, float* gwu_t, float* gwd,
-                       float* gb, void* workspace, size_t ws_bytes, void* stream) {
+                       const int32_t* routed, const int32_t* n_routed, int32_t max_routed,
+                       const void* gy, float l1_lambda, void* gx, float* gwg_t, float* gwu_t,
+                       float* gwd, float* gb, void* workspace, size_t ws_bytes, void* stream) {
   int32_t st = check_shape(shape);
   if (st != SFFN_OK) return st;
-  if (!(l1_lambda == l1_lambda)) return SFFN_ERR_ARG;
+  if (!(l1_lambda == l1_lambda) || max_routed < 0 || max_routed > shape->T) return SFFN_ERR_ARG;
   if (shape->T == 0) return SFFN_OK;
   if (!ptrs_ok({x, wg_t, wu_t, wd, count, routed, n_routed, gy, gx, gwg_t, gwu_t, gwd}) ||
       (b_g && !aligned16(b_g)) || (wg_norms && !aligned16(wg_norms)) || (gb && !aligned16(gb)))
     return SFFN_ERR_ARG;
   if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
-  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < backward_ws(shape))
+  if (workspace == nullptr || !aligned16(workspace) || ws_bytes < backward_ws(shape, max_routed))
     return SFFN_ERR_WORKSPACE;
   if (!backward_supported(shape->dtype, shape->d_model) || act_bytes_too_large(shape))
     return SFFN_ERR_UNSUPPORTED;
@@ -412,8 +412,13 @@ int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t,
   return hip_status(launch_backward(x, wg_t, b_g, wu_t, wd, xn, wg_norms ? wg_norms : wbuf, count,
                                     idx, val, routed, n_routed, gy, gx, gwg_t, gwu_t, gwd, gb,
                                     shape->T, shape->d_model, shape->d_ff, shape->cap,
-                                    (float)((double)l1_lambda / (double)shape->T),
+                                    (float)((double)l1_lambda / (double)shape->T), max_routed,
                                     guard_band(shape), bws, s));
+}
+
+size_t sparse_ffn_bwd_workspace_bytes(const sffn_shape* shape, int32_t max_routed) {
+  if (check_shape(shape) != SFFN_OK || max_routed < 0 || max_routed > shape->T) return 0;
+  return backward_ws(shape, max_routed);
 }
 
 size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
@@ -427,7 +432,7 @@ size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which) {
     case SFFN_WS_PACK: return pack_ws(shape);
     case SFFN_WS_CONVERT: return convert_ws(shape);
     case SFFN_WS_PACK_L1: return pack_l1_ws(shape);
-    case SFFN_WS_BACKWARD: return backward_ws(shape);
+    case SFFN_WS_BACKWARD: return backward_ws(shape, shape->T);
     default: return 0;
   }
 }

@@ -75,6 +75,7 @@ struct BwdArgs {
   float* gb;               // [N] or null
   int T, D, N, nt, cap;
   float l1g;               // lambda / T, added to gz of every active entry
+  int R;                   // routed rows the workspace holds (<= T)
 };
 
 // Position of row t in the ascending routed list (binary search), or -1.
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     return;
   }
   for (int k = lane; k < a.nt; k += kWave) a.count_t[(size_t)k * a.T + t] = 0;
-  const int r = uniform(routed_index(a.routed, min(*a.n_routed, a.T), t));
+  const int r = uniform(routed_index(a.routed, min(*a.n_routed, a.R), t));
   if (r < 0) return;  // not in the routed list: the row keeps no entries
   int carry = 0;
   for (int k0 = 0; k0 < a.nt; k0 += kWave) {
@@ -297,7 +298,7 @@ constexpr int kRoutedWaves = 4096;
 
 __global__ __launch_bounds__(1024) void bwd_routed_items(BwdArgs a, int32_t* item_start) {
   __shared__ int wsum[16];
-  const int nr = uniform(min(*a.n_routed, a.T));
+  const int nr = uniform(min(*a.n_routed, a.R));
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
   // all routed entries, then the part size
   int e = 0;
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(1024) void bwd_routed_items(BwdArgs a, int32_t* ite
   int etot = 0;
   for (int i = 0; i < 16; ++i) etot += wsum[i];
   __syncthreads();
-  const int budget = max(1, (kRoutedSplit - 1) * a.T);
+  const int budget = max(1, (kRoutedSplit - 1) * a.R);
   const int chunk = max(kRoutedChunk, (int)(((long)etot + budget - 1) / budget));
   int carry = 0;
   for (int r0 = 0; r0 < nr; r0 += 1024) {
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(1024) void bwd_routed_items(BwdArgs a, int32_t* ite
 template <int P>
 __global__ __launch_bounds__(256) void bwd_routed(BwdArgs a, const int32_t* item_start,
                                                   float* part) {
-  const int nr = uniform(min(*a.n_routed, a.T));
+  const int nr = uniform(min(*a.n_routed, a.R));
   const int items = uniform(item_start[nr]);
   const int lane = lane_id();
   for (int it = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); it < items; it += kRoutedWaves) {
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(256) void bwd_routed(BwdArgs a, const int32_t* item
 // routed row without entries gets zero).  Workgroups loop over the rows.
 __global__ __launch_bounds__(256) void bwd_routed_gx(BwdArgs a, const int32_t* item_start,
                                                      const float* part) {
-  const int nr = uniform(min(*a.n_routed, a.T));
+  const int nr = uniform(min(*a.n_routed, a.R));
   for (int r = (int)blockIdx.y; r < nr; r += (int)gridDim.y) {
     const int t = min(max(a.routed[r], 0), a.T - 1);
     const int i0 = item_start[r], i1 = item_start[r + 1];
@@ -618,7 +619,7 @@ __global__ __launch_bounds__(256) void bwd_cols(BwdArgs a, const int* col_ptr, c
   }
   // routed rows: their complete lists, one binary search per row
   const int k = j / kBTile;
-  const int nr = uniform(min(*a.n_routed, a.T));
+  const int nr = uniform(min(*a.n_routed, a.R));
   for (int r0 = 0; r0 < nr; r0 += kWave) {
     const int r = r0 + lane;
     int match = -1, tr = 0;
@@ -753,7 +754,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   }
   // routed rows: their entries' gradients come from bwd_routed
   const int k = j / kBTile;
-  const int nr = uniform(min(*a.n_routed, a.T));
+  const int nr = uniform(min(*a.n_routed, a.R));
   for (int r0 = 0; r0 < nr; r0 += kWave) {
     const int r = r0 + lane;
     int match = -1, tr = 0;
@@ -865,15 +866,28 @@ bool backward_supported(int dtype, int d_model) {
 // Workspace of the backward: the routed rows' z (later reused for their
 // per-entry gradients), their complete lists and tile offsets, the tile-major
 // copies and the per-entry gradients of the TwELL entries.
-size_t backward_workspace_bytes(int T, int N, int D, int cap) {
+// Routed-row buffers are sized for R rows (the routed rows the caller allows
+// for), the others for all T rows.
+size_t backward_workspace_bytes(int T, int N, int D, int cap, int R) {
   const size_t nt = (size_t)N / kBTile;
-  return al256((size_t)T * N * 16) + 2 * al256((size_t)T * N * 2) + al256((size_t)T * 2) +
-         al256((size_t)T * nt * 4) + al256(nt * T * 2) + al256(nt * T * cap * 2) +
-         al256((size_t)T * nt * cap * 16) + al256(((size_t)T + 2) * 4) +
-         al256((size_t)T * kRoutedSplit * D * 4) +
+  return al256((size_t)R * N * 16) + 2 * al256((size_t)R * N * 2) + al256((size_t)R * 2) +
+         al256((size_t)R * nt * 4) + al256(nt * T * 2) + al256(nt * T * cap * 2) +
+         al256((size_t)T * nt * cap * 16) + al256(((size_t)R + 2) * 4) +
+         al256((size_t)R * kRoutedSplit * D * 4) +
          (T <= kSplitMaxT ? al256((size_t)T * kRowParts * D * 4) : 0) +
          al256((size_t)((T + kCscRows - 1) / kCscRows) * N * 4) + al256((size_t)N * 4) +
          al256(((size_t)N + 1) * 4) + al256((size_t)T * nt * cap * 16);
+}
+
+// More routed rows than the workspace holds (the forward routed more than the
+// caller allowed for): the rows past R were not processed, so the result is
+// made unusable in a way no training loop misses: gb (when given) and the
+// first row of gx become NaN.
+__global__ __launch_bounds__(256) void bwd_routed_overflow(BwdArgs a) {
+  if (*a.n_routed <= a.R) return;
+  if (a.gb)
+    for (int j = (int)threadIdx.x; j < a.N; j += 256) a.gb[j] = __builtin_nanf("");
+  for (int d = (int)threadIdx.x; d < a.D; d += 256) a.gx[d] = (uint16_t)0x7fc0u;
 }
 
 hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
@@ -881,21 +895,21 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
                            const uint16_t* count, const uint16_t* idx, const void* val,
                            const int32_t* routed, const int32_t* n_routed, const void* gy,
                            void* gx, float* gwg_t, float* gwu_t, float* gwd, float* gb, int T,
-                           int D, int N, int cap, float l1g, GuardBand band, void* ws,
+                           int D, int N, int cap, float l1g, int R, GuardBand band, void* ws,
                            hipStream_t stream) {
   const int nt = N / kBTile;
   char* p = (char*)ws;
   float* z_r = (float*)p;          // routed rows' z, then (same bytes) their entry gradients
   f32x4_t* co_r = (f32x4_t*)p;
-  p += al256((size_t)T * N * 16);
+  p += al256((size_t)R * N * 16);
   uint16_t* eidx = (uint16_t*)p;
-  p += al256((size_t)T * N * 2);
+  p += al256((size_t)R * N * 2);
   uint16_t* eval = (uint16_t*)p;
-  p += al256((size_t)T * N * 2);
+  p += al256((size_t)R * N * 2);
   uint16_t* ecount = (uint16_t*)p;
-  p += al256((size_t)T * 2);
+  p += al256((size_t)R * 2);
   int32_t* eoff = (int32_t*)p;
-  p += al256((size_t)T * nt * 4);
+  p += al256((size_t)R * nt * 4);
   uint16_t* count_t = (uint16_t*)p;
   p += al256((size_t)nt * T * 2);
   uint16_t* idx_t = (uint16_t*)p;
@@ -903,9 +917,9 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   f32x4_t* co = (f32x4_t*)p;
   p += al256((size_t)T * nt * cap * 16);
   int32_t* item_start = (int32_t*)p;
-  p += al256(((size_t)T + 2) * 4);
+  p += al256(((size_t)R + 2) * 4);
   float* part = (float*)p;
-  p += al256((size_t)T * kRoutedSplit * D * 4);
+  p += al256((size_t)R * kRoutedSplit * D * 4);
   float* rpart = (float*)p;  // few tokens only
   p += T <= kSplitMaxT ? al256((size_t)T * kRowParts * D * 4) : 0;
   const int nblk = (T + kCscRows - 1) / kCscRows;
@@ -918,16 +932,19 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   f32x4_t* csc = (f32x4_t*)p;
 
   // routed rows: z with the gate GEMM, then complete activity lists
-  hipError_t e = launch_gate_preact(x, wg_t, b_g, z_r, T, D, N, routed, n_routed, stream);
-  if (e != hipSuccess) return e;
-  e = launch_ell_convert(z_r, x, wg_t, b_g, xnorm, wnorm, N, ecount, eidx, eval, T, D, N, band,
-                         routed, n_routed, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (R > 0) {
+    e = launch_gate_preact(x, wg_t, b_g, z_r, T, D, N, routed, n_routed, stream, R);
+    if (e != hipSuccess) return e;
+    e = launch_ell_convert(z_r, x, wg_t, b_g, xnorm, wnorm, N, ecount, eidx, eval, T, D, N, band,
+                           routed, n_routed, stream, R);
+    if (e != hipSuccess) return e;
+  }
 
   BwdArgs a{(const uint16_t*)x, (const uint16_t*)wg_t, (const uint16_t*)wu_t,
             (const uint16_t*)wd, (const uint16_t*)gy, count, idx, (const uint16_t*)val,
             routed, n_routed, ecount, eidx, eval, eoff, count_t, idx_t, co, co_r,
-            (uint16_t*)gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, cap, l1g};
+            (uint16_t*)gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, cap, l1g, R};
   const dim3 rows_grid((unsigned)((T + 3) / 4));
   hipLaunchKernelGGL(bwd_prep, rows_grid, dim3(256), 0, stream, a);
   e = hipGetLastError();
@@ -984,14 +1001,16 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
       case 3: hipLaunchKernelGGL(bwd_cols_fused<3>, cg, dim3(256), 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc); hipLaunchKernelGGL(bwd_gx<3>, rows_grid, dim3(256), 0, stream, a); break;
       default: hipLaunchKernelGGL(bwd_cols_fused<4>, cg, dim3(256), 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc); hipLaunchKernelGGL(bwd_gx<4>, rows_grid, dim3(256), 0, stream, a); break;
     }
-    return hipGetLastError();
-  }
-  if (D % 1024 == 0)
+  } else if (D % 1024 == 0) {
     hipLaunchKernelGGL(bwd_cols<2>, dim3((unsigned)(N / 4 * (D / 1024))), dim3(256), 0, stream, a,
                        (const int*)col_ptr, (const f32x4_t*)csc);
-  else
+  } else {
     hipLaunchKernelGGL(bwd_cols<1>, dim3((unsigned)(N / 4 * (D / 512))), dim3(256), 0, stream, a,
                        (const int*)col_ptr, (const f32x4_t*)csc);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (R < T) hipLaunchKernelGGL(bwd_routed_overflow, dim3(1), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -58,14 +58,14 @@ __device__ __forceinline__ void preact_tile(const GateArgs& a, uint8_t* lds, flo
 
 // Mapped rows (the routed rows of the backward), 64-row tiles.
 __global__ __launch_bounds__(64 * RowsGemm::NWAVES) void gate_preact_rows(
-    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev) {
+    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev, int max_rows) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[RowsGemm::LDS_BYTES];
   // the active tiles are the first ones, spread over the XCDs in dispatch
   // order (the XCD-aware map would put them all on one)
   const int ntn = a.N / RowsGemm::BN;
   const int mi = (int)blockIdx.x / ntn, ni = (int)blockIdx.x - mi * ntn;
   const int m0 = mi * RowsGemm::BM;
-  const int mv = uniform(min(*n_rows_dev, a.T));
+  const int mv = uniform(min(*n_rows_dev, max_rows));
   if (m0 >= mv) return;
   preact_tile<RowsGemm>(a, lds, z, rowmap, mv, m0, ni * RowsGemm::BN);
 }
@@ -228,12 +228,12 @@ template <int U>
 __global__ __launch_bounds__(256) void ell_convert_bf16(GateArgs a, const float* z, int width,
                                                         uint16_t* ecount, uint16_t* eidx,
                                                         uint16_t* eval, const int* rowmap,
-                                                        const int* n_rows_dev) {
+                                                        const int* n_rows_dev, int max_rows) {
   __shared__ uint32_t exact_lds[4 * kExactLdsWords];
   const int w = uniform((int)(threadIdx.x >> 6));
   const int lane = lane_id();
   const int m = (int)blockIdx.x * 4 + w;
-  const int mv = uniform(n_rows_dev ? min(*n_rows_dev, a.T) : a.T);
+  const int mv = uniform(n_rows_dev ? min(*n_rows_dev, max_rows) : max_rows);
   if (m >= mv) return;
   const int t = uniform(rowmap ? rowmap[m] : m);
   const int nt = a.N / kTile;
@@ -283,13 +283,15 @@ __global__ __launch_bounds__(256) void ell_convert_bf16(GateArgs a, const float*
 
 hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g, float* z, int T,
                               int K, int N, const int* rowmap, const int* n_rows_dev,
-                              hipStream_t stream) {
+                              hipStream_t stream, int max_rows) {
   GateArgs a{x, wg_t, b_g, nullptr, nullptr, nullptr, nullptr, nullptr, T, K, N, 0, GuardBand{}};
   if (rowmap) {
     if (!n_rows_dev) return hipErrorInvalidValue;
-    const dim3 g((unsigned)(((T + RowsGemm::BM - 1) / RowsGemm::BM) * (N / RowsGemm::BN)));
+    const int rows = max_rows >= 0 ? min(max_rows, T) : T;
+    if (rows == 0) return hipSuccess;
+    const dim3 g((unsigned)(((rows + RowsGemm::BM - 1) / RowsGemm::BM) * (N / RowsGemm::BN)));
     hipLaunchKernelGGL(gate_preact_rows, g, dim3(64 * RowsGemm::NWAVES), 0, stream, a, z, rowmap,
-                       n_rows_dev);
+                       n_rows_dev, rows);
   } else {
     int wide_nt, narrow_nt;
     gate_tile_split(T, N, &wide_nt, &narrow_nt);
@@ -317,10 +319,12 @@ hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, c
                               const float* xnorm, const float* wnorm, int width,
                               uint16_t* ecount, uint16_t* eidx, void* eval, int T, int K, int N,
                               GuardBand gb, const int* rowmap, const int* n_rows_dev,
-                              hipStream_t stream) {
+                              hipStream_t stream, int max_rows) {
   GateArgs a{x, wg_t, b_g, nullptr, nullptr, nullptr, xnorm, wnorm, T, K, N, 0, gb};
-  hipLaunchKernelGGL(ell_convert_bf16<16>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, a,
-                     z, width, ecount, eidx, (uint16_t*)eval, rowmap, n_rows_dev);
+  const int rows = max_rows >= 0 ? min(max_rows, T) : T;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(ell_convert_bf16<16>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
+                     a, z, width, ecount, eidx, (uint16_t*)eval, rowmap, n_rows_dev, rows);
   return hipGetLastError();
 }
 

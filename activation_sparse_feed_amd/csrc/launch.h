@@ -38,11 +38,12 @@ hipError_t launch_l1_reduce(const float* part, size_t n, double scale, void* ws,
 // from z to TwELL and to a row-wise ELLPACK of the given width (ecount [T],
 // eidx / eval [T, width]).  Same activity decision as launch_gate_twell.
 // With rowmap / n_rows_dev (both may be null): output row m < *n_rows_dev is
-// x row rowmap[m] (the backward's routed rows).
+// x row rowmap[m] (the backward's routed rows); max_rows (>= 0) caps the
+// mapped rows (the output holds that many rows), else T.
 bool preact_supported(int dtype, int K);
 hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g, float* z, int T,
                               int K, int N, const int* rowmap, const int* n_rows_dev,
-                              hipStream_t stream);
+                              hipStream_t stream, int max_rows = -1);
 hipError_t launch_twell_convert(const float* z, const void* x, const void* wg_t, const float* b_g,
                                 const float* xnorm, const float* wnorm, uint16_t* count,
                                 uint16_t* idx, void* val, int T, int K, int N, int cap,
@@ -51,20 +52,22 @@ hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, c
                               const float* xnorm, const float* wnorm, int width,
                               uint16_t* ecount, uint16_t* eidx, void* eval, int T, int K, int N,
                               GuardBand gb, const int* rowmap, const int* n_rows_dev,
-                              hipStream_t stream);
+                              hipStream_t stream, int max_rows = -1);
 
 // Backward through TwELL and the hybrid routing (bf16, d_model % 512 == 0,
 // d_model <= 4096): gx [T, D] bf16, float32 weight gradients [N, D] and gb
-// [N] (may be null).  l1g is added to gz of every active entry.  xnorm: ||x_t|| of every row; wnorm: ||wg_t[j]||.  ws:
+// [N] (may be null).  l1g is added to gz of every active entry.  R: routed
+// rows the workspace holds (backward_workspace_bytes(..., R)); if the forward
+// routed more, gb and the first row of gx are set to NaN.  xnorm: ||x_t|| of every row; wnorm: ||wg_t[j]||.  ws:
 // backward_workspace_bytes().
 bool backward_supported(int dtype, int d_model);
-size_t backward_workspace_bytes(int T, int N, int D, int cap);
+size_t backward_workspace_bytes(int T, int N, int D, int cap, int R);
 hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
                            const void* wd, const float* xnorm, const float* wnorm,
                            const uint16_t* count, const uint16_t* idx, const void* val,
                            const int32_t* routed, const int32_t* n_routed, const void* gy,
                            void* gx, float* gwg_t, float* gwu_t, float* gwd, float* gb, int T,
-                           int D, int N, int cap, float l1g, GuardBand band, void* ws,
+                           int D, int N, int cap, float l1g, int R, GuardBand band, void* ws,
                            hipStream_t stream);
 
 // Row norms of a [rows_a, K] and a [rows_b, K] matrix in one launch.

@@ -26,7 +26,7 @@ EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_noalloc",
             "twell_pack_noalloc_max_bytes", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
             "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
             "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
-            "sffn_workspace_bytes", "sffn_strerror")
+            "sffn_workspace_bytes", "sparse_ffn_bwd_workspace_bytes", "sffn_strerror")
 
 
 class SffnError(RuntimeError):
@@ -57,7 +57,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.gate_preact.argtypes = [sp, vp, vp, vp, vp, vp]
-    lib.sparse_ffn_bwd.argtypes = [sp] + [vp] * 12 + [ctypes.c_float] + [vp] * 5 + [vp, sz, vp]
+    lib.sparse_ffn_bwd.argtypes = [sp] + [vp] * 11 + [i32, vp, ctypes.c_float] + [vp] * 5 + [vp, sz, vp]
+    lib.sparse_ffn_bwd_workspace_bytes.argtypes = [sp, i32]
+    lib.sparse_ffn_bwd_workspace_bytes.restype = sz
     lib.sffn_probe_hbm.argtypes = [vp, vp, sz, i32, vp]
     lib.sffn_probe_mfma.argtypes = [vp, i32, i32, vp]
     lib.sffn_probe_mfma_step.argtypes = [vp, vp, vp, vp, i32, vp]
@@ -227,9 +229,16 @@ def dense_ffn_ref(shape: Shape, x, wg_t, b_g, wu_t, wd, workspace, y, stream=Non
         _ptr(workspace), ws_n, _ptr(y), _stream(stream)))
 
 
+def backward_workspace_bytes(shape: Shape, max_routed: int) -> int:
+    return int(_lib.sparse_ffn_bwd_workspace_bytes(ctypes.byref(shape), int(max_routed)))
+
+
 def sparse_ffn_bwd(shape: Shape, x, wg_t, b_g, wu_t, wd, count, idx, val, routed, n_routed, gy,
                    gx, gwg_t, gwu_t, gwd, gb, workspace, wg_norms=None, l1_lambda: float = 0.0,
-                   stream=None) -> None:
+                   max_routed=None, stream=None) -> None:
+    """max_routed: routed rows the workspace holds (default T, the workspace of
+    alloc_workspace(shape, WS_BACKWARD)); see backward_workspace_bytes."""
+    mr = shape.T if max_routed is None else int(max_routed)
     for name, t in (("gwg_t", gwg_t), ("gwu_t", gwu_t), ("gwd", gwd)):
         if t.dtype != torch.float32 or tuple(t.shape) != (shape.d_ff, shape.d_model):
             raise ValueError(f"{name} must be float32 [d_ff, d_model]")
@@ -238,7 +247,7 @@ def sparse_ffn_bwd(shape: Shape, x, wg_t, b_g, wu_t, wd, count, idx, val, routed
     ws_n = workspace.numel() * workspace.element_size()
     _check("sparse_ffn_bwd", _lib.sparse_ffn_bwd(
         ctypes.byref(shape), _ptr(x), _ptr(wg_t), _ptr(b_g), _ptr(wu_t), _ptr(wd), _ptr(wg_norms),
-        _ptr(count), _ptr(idx), _ptr(val), _ptr(routed), _ptr(n_routed), _ptr(gy),
+        _ptr(count), _ptr(idx), _ptr(val), _ptr(routed), _ptr(n_routed), mr, _ptr(gy),
         float(l1_lambda), _ptr(gx), _ptr(gwg_t), _ptr(gwu_t), _ptr(gwd), _ptr(gb), _ptr(workspace),
         ws_n, _stream(stream)))
 

@@ -204,6 +204,98 @@ def cpu_baseline(inp, rows: int) -> dict:
             "oracle_dense_tokens_per_s": len(sel) / t_dense}
 
 
+def training_memory(w, x, wg, b, wu, wd, wg_norms, gy) -> dict:
+    """Device-allocator bytes of one forward + backward step, sparse against
+    dense.  x, the weights, gy, y and the gradient outputs are allocated first
+    (both paths need them) and are not counted.  For each path: the bytes the
+    forward keeps for the backward (allocated after the forward, its
+    transients freed) and the peak over the step (forward transients,
+    workspaces, backward transients).
+      sparse: twell_pack, sparse_ffn_fwd, hybrid_route; the forward keeps the
+              TwELL arrays and the routed list; sparse_ffn_bwd with its
+              workspace sized for the routed rows the forward produced.
+      dense:  the gated FFN on hipBLASLt GEMMs keeping h and u ([d_ff, T]
+              bf16), then the dense backward (six GEMMs).
+    """
+    import torch
+
+    from activation_sparse_feed_amd import sffn
+    dt = x.dtype
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    y = torch.empty_like(x)
+    gx = torch.empty_like(x)
+    gw3 = [torch.empty((w.d_ff, w.d_model), device="cuda") for _ in range(3)]
+    gbv = torch.empty(w.d_ff, device="cuda")
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+
+    def mib(v):
+        return v / 2 ** 20
+
+    # sparse
+    torch.cuda.reset_peak_memory_stats()
+    ffn = sffn.SparseFFN(w.T, w.d_model, w.d_ff, w.cap, dt)
+    s = ffn.shape
+    sffn.twell_pack(s, x, wg, b, ffn.count, ffn.idx, ffn.val, ffn.ws_pack, wg_norms)
+    sffn.sparse_ffn_fwd(s, x, wu, wd, ffn.count, ffn.idx, ffn.val, y, ffn.ws_sparse)
+    sffn.hybrid_route(s, x, wg, b, wu, wd, ffn.count, ffn.routed, ffn.n_routed, ffn.ws_hybrid, y)
+    saved = {k: getattr(ffn, k) for k in ("count", "idx", "val", "routed", "n_routed")}
+    n_r = int(saved["n_routed"].item())
+    del ffn
+    torch.cuda.synchronize()
+    sp_saved = torch.cuda.memory_allocated() - base
+    ws = torch.empty(max(sffn.backward_workspace_bytes(s, n_r), 16), dtype=torch.uint8,
+                     device="cuda")
+    sffn.sparse_ffn_bwd(s, x, wg, b, wu, wd, saved["count"], saved["idx"], saved["val"],
+                        saved["routed"], saved["n_routed"], gy, gx, *gw3, gbv, ws, wg_norms,
+                        max_routed=n_r)
+    torch.cuda.synchronize()
+    sp_peak = torch.cuda.max_memory_allocated() - base
+    ws_bytes = ws.numel()
+    del ws, saved
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # dense
+    torch.cuda.reset_peak_memory_stats()
+    zT = (torch.nn.functional.linear(x, wg) + b.to(dt)).t().contiguous()
+    uT = torch.nn.functional.linear(x, wu).t().contiguous()
+    hT = torch.relu(zT)
+    del zT
+    aT = hT * uT
+    torch.mm(aT.t().contiguous(), wd, out=y)
+    del aT
+    torch.cuda.synchronize()
+    de_saved = torch.cuda.memory_allocated() - base
+    de_fwd_peak = torch.cuda.max_memory_allocated() - base
+    wg_tt, wu_tt = wg.t().contiguous(), wu.t().contiguous()  # prepared weights, not counted
+    pre = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    gyT = gy.t().contiguous()
+    gaT = torch.mm(wd, gyT)
+    gzT = torch.where(hT > 0, gaT * uT, torch.zeros_like(gaT))
+    guT = gaT * hT
+    del gaT
+    gx.copy_((torch.mm(wg_tt, gzT) + torch.mm(wu_tt, guT)).t())
+    gw3[0].copy_(torch.mm(gzT, x))
+    gw3[1].copy_(torch.mm(guT, x))
+    gw3[2].copy_(torch.mm(hT * uT, gy))
+    gbv.copy_(gzT.float().sum(1))
+    torch.cuda.synchronize()
+    de_peak = max(torch.cuda.max_memory_allocated() - pre + de_saved, de_fwd_peak)
+    del gzT, guT, gyT, hT, uT, wg_tt, wu_tt
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"sparse_saved_MiB": mib(sp_saved), "sparse_peak_MiB": mib(sp_peak),
+            "sparse_backward_workspace_MiB": mib(ws_bytes), "routed_rows": n_r,
+            "dense_saved_MiB": mib(de_saved), "dense_peak_MiB": mib(de_peak),
+            "saved_reduction": 1.0 - sp_saved / de_saved if de_saved else None,
+            "peak_reduction": 1.0 - sp_peak / de_peak if de_peak else None,
+            "note": "device allocator (torch.cuda.memory_allocated / max_memory_allocated) over "
+                    "one forward + backward; x, weights, gy, y and the gradient outputs excluded"}
+
+
 def d_model_ok(d_model: int) -> bool:
     """The separate-conversion calls need d_model % 32 == 0."""
     return d_model % 32 == 0
@@ -517,21 +609,14 @@ def main() -> int:
         b2.record()
         torch.cuda.synchronize()
         t_b, t_db = b0.elapsed_time(b1) / K, b1.elapsed_time(b2) / K
-        # activations kept between forward and backward (x and the weights are
-        # kept by both): the sparse path keeps the TwELL arrays and the routed
-        # list (u and the routed rows' gate are recomputed in the backward); a
-        # dense backward keeps h and u, T x d_ff each
-        nt_ = w.d_ff // w.tile
-        sparse_saved = (w.T * nt_ * 2 + w.T * nt_ * max(w.cap, 1) * (2 + 2) + 4 * (w.T + 1))
-        dense_saved = 2 * w.T * w.d_ff * 2
         backward = {"sparse_ffn_bwd_ms": t_b, "torch_dense_backward_ms": t_db,
                     "speedup_vs_torch_dense": t_db / t_b,
                     "weight_grad_bytes": 3.0 * w.d_ff * w.d_model * 4,
-                    "note": "dense: 6 hipBLASLt bf16 GEMMs from saved dense activations",
-                    "saved_activation_bytes": {"sparse_twell_and_routing": sparse_saved,
-                                               "dense_h_and_u": dense_saved,
-                                               "reduction": 1.0 - sparse_saved / dense_saved}}
+                    "note": "dense: 6 hipBLASLt bf16 GEMMs from saved dense activations"}
         del ws_b, gw3, zT, uT, hT, actT, wg_tt, wu_tt
+        # measured memory of a training step: what the forward keeps for the
+        # backward and the peak, sparse (TwELL + routed list) against dense (h, u)
+        backward["memory"] = training_memory(w, x, wg, b, wu, wd, wg_norms, gy)
 
     count = ffn.count.to(torch.int64)
     nnz_live = int(torch.clamp(count, max=w.cap).sum().item()) if w.cap > 0 else 0
@@ -632,6 +717,11 @@ def main() -> int:
         "backward": backward,
         "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,
         "speedup_vs_dense": (t_dense / ms_step) if t_dense else None,
+        # against torch's dense FFN (hipBLASLt GEMMs) too, and against the
+        # faster of the two same-GPU dense FFNs
+        "speedup_vs_torch_dense": (t_torch / ms_step) if t_torch else None,
+        "speedup_vs_best_dense": (min(t for t in (t_dense, t_torch) if t) / ms_step)
+        if (t_dense or t_torch) else None,
         "dense_tflops": (3 * gate_flop / (t_dense * 1e-3) / 1e12) if t_dense else None,
         "measured_peaks": peaks,
         "activity": {"nnz_per_row": nnz_total / T, "density": nnz_total / (T * n),

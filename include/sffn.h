@@ -240,18 +240,28 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
  * bf16 only, d_model % 512 == 0 and d_model <= 4096 (else
  * SFFN_ERR_UNSUPPORTED), plus twell_pack's size limits.  gy, gx: [T, d_model]
  * dtype; gwg_t, gwu_t, gwd: float32 [d_ff, d_model]; gb: float32 [d_ff].
- * wg_norms as for twell_pack (or NULL).  workspace: at least
- * sffn_workspace_bytes(shape, SFFN_WS_BACKWARD) bytes (sized for every row
- * routed: about 20 * T * d_ff + 32 * T * d_model bytes), no initial contents;
- * the routed and n_routed of the same forward; calls sharing it
- * must be stream-ordered.
+ * wg_norms as for twell_pack (or NULL); routed and n_routed of the same
+ * forward.  max_routed (0 <= max_routed <= T, else SFFN_ERR_ARG) bounds the
+ * routed rows the workspace holds: T always suffices; a caller that reads
+ * n_routed after the forward can pass it and keep the workspace small.  If the
+ * forward routed more rows than max_routed, those rows are not processed and
+ * gb (when given) and the first row of gx are set to NaN.  workspace: at
+ * least sparse_ffn_bwd_workspace_bytes(shape, max_routed) bytes (about
+ * 20 max_routed d_ff + 32 max_routed d_model bytes for the routed rows plus
+ * about 20 T n_tiles cap bytes for the TwELL entries), no initial contents;
+ * calls sharing it must be stream-ordered.
  */
 int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
                        const void* wu_t, const void* wd, const float* wg_norms,
                        const uint16_t* count, const uint16_t* idx, const void* val,
-                       const int32_t* routed, const int32_t* n_routed, const void* gy,
-                       float l1_lambda, void* gx, float* gwg_t, float* gwu_t, float* gwd,
-                       float* gb, void* workspace, size_t ws_bytes, void* stream);
+                       const int32_t* routed, const int32_t* n_routed, int32_t max_routed,
+                       const void* gy, float l1_lambda, void* gx, float* gwg_t, float* gwu_t,
+                       float* gwd, float* gb, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sparse_ffn_bwd for this shape and routed-row bound
+ * (0 if the shape is invalid or max_routed is outside 0..T);
+ * sffn_workspace_bytes(shape, SFFN_WS_BACKWARD) is this with max_routed = T. */
+size_t sparse_ffn_bwd_workspace_bytes(const sffn_shape* shape, int32_t max_routed);
 
 /*
  * dense_ffn_ref -- the dense gated FFN used as the speed-up reference

@@ -173,17 +173,29 @@ def test_backward_errors(sffn):
     s = _shape(sffn, d_model=512)
     need = sffn.workspace_bytes(s, sffn.WS_BACKWARD)
     assert need >= 20 * 64 * 512
-    args = [P] * 12 + [0.25] + [P] * 5   # ..., gy, l1_lambda, gx, gwg_t, gwu_t, gwd, gb
+    # ..., routed, n_routed, max_routed, gy, l1_lambda, gx, gwg_t, gwu_t, gwd, gb
+    args = [P] * 11 + [64, P, 0.25] + [P] * 5
     args[2] = None   # b_g
     args[5] = None   # wg_norms
-    args[17] = None  # gb
+    args[18] = None  # gb
     assert lib.sparse_ffn_bwd(ctypes.byref(s), *args, WS, need - 1, None) == -3
     bad = list(args)
-    bad[13] = None   # gx
+    bad[14] = None   # gx
     assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
     bad = list(args)
-    bad[12] = float("nan")  # l1_lambda
+    bad[13] = float("nan")  # l1_lambda
     assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
+    for mr in (-1, 65):   # max_routed outside 0..T
+        bad = list(args)
+        bad[11] = mr
+        assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
+    # a smaller routed-row bound needs a smaller workspace, and that one is enough
+    small = sffn.backward_workspace_bytes(s, 4)
+    assert 0 < small < need and sffn.backward_workspace_bytes(s, 64) == need
+    assert sffn.backward_workspace_bytes(s, 65) == 0
+    bad = list(args)
+    bad[11] = 4
+    assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, small - 1, None) == -3
     bad = list(args)
     bad[9] = MISALIGNED  # routed
     assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
@@ -193,8 +205,8 @@ def test_backward_errors(sffn):
     sf = _shape(sffn, d_model=512, dtype=sffn.SFFN_F32)
     assert lib.sparse_ffn_bwd(ctypes.byref(sf), *args, WS, sffn.workspace_bytes(sf, 6), None) == -2
     s0 = _shape(sffn, T=0)
-    assert lib.sparse_ffn_bwd(ctypes.byref(s0), *([None] * 12), 0.0, *([None] * 5), None, 0,
-                              None) == 0
+    assert lib.sparse_ffn_bwd(ctypes.byref(s0), *([None] * 11), 0, None, 0.0, *([None] * 5), None,
+                              0, None) == 0
 
 
 

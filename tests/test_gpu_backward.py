@@ -161,3 +161,74 @@ def test_backward_l1_regulariser(T, d_model, d_ff, beta, cap):
     dgb = to_f64(with_l1["gb"]) - to_f64(without["gb"])
     assert np.allclose(dgb, lam / T * act, rtol=1e-4, atol=1e-4 * (1 + np.abs(to_f64(without["gb"])).max()))
     print(f"l1 backward T={T} d={d_model}: {e}")
+
+
+@pytest.mark.parametrize("case", ["ragged", "hybrid_mix"])
+def test_backward_from_saved_state_alone(case):
+    """The backward needs nothing of the forward but its TwELL arrays and the
+    routed list: the forward's buffers and workspaces are freed first, and the
+    backward workspace holds exactly the routed rows the forward produced
+    (max_routed = n_routed, read after the forward)."""
+    sffn = _sffn()
+    if case == "ragged":
+        inp = wl.generate_custom(T=300, d_model=512, d_ff=1024, dtype="bf16", beta=1.9,
+                                 seed_base=73, cap=4)
+    else:
+        inp = wl.generate(wl.WORKLOADS["hybrid_mix"])
+    w = inp.workload
+    d = device_inputs(inp)
+    ffn = sffn.SparseFFN(w.T, w.d_model, w.d_ff, w.cap, torch.bfloat16)
+    ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    saved = {k: getattr(ffn, k).clone() for k in ("count", "idx", "val", "routed", "n_routed")}
+    s = ffn.shape
+    del ffn
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    n_r = int(saved["n_routed"].item())
+    assert n_r > 0
+    ws = torch.empty(sffn.backward_workspace_bytes(s, n_r), dtype=torch.uint8, device="cuda")
+    assert ws.numel() < sffn.workspace_bytes(s, sffn.WS_BACKWARD)
+    gy_np = wl.upstream_grad(w)
+    gy = to_device(gy_np, "bf16")
+    gx = torch.empty((w.T, w.d_model), dtype=torch.bfloat16, device="cuda")
+    g = [torch.empty((w.d_ff, w.d_model), device="cuda") for _ in range(3)]
+    gb = torch.empty(w.d_ff, device="cuda")
+    sffn.sparse_ffn_bwd(s, d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], saved["count"],
+                        saved["idx"], saved["val"], saved["routed"], saved["n_routed"], gy, gx, *g,
+                        gb, ws, max_routed=n_r)
+    torch.cuda.synchronize()
+    x, wg, wu, wd = inp.as_f64("x"), inp.as_f64("wg_t"), inp.as_f64("wu_t"), inp.as_f64("wd")
+    gyf = wl.bf16_bits_to_f32(gy_np).astype(np.float64)
+    ref = oracle.ffn_dense_backward(x, wg, inp.b_g, wu, wd, gyf)
+    got = {"gx": gx, "gwg_t": g[0], "gwu_t": g[1], "gwd": g[2], "gb": gb}
+    for k, v in got.items():
+        e = rel_fro(to_f64(v), ref[k])
+        assert e <= TOL, (k, e)
+    print(f"backward from saved state ({case}): {n_r} routed rows, workspace "
+          f"{ws.numel() / 1e6:.1f} MB of {sffn.workspace_bytes(s, sffn.WS_BACKWARD) / 1e6:.1f} MB")
+
+
+def test_backward_routed_overflow_is_flagged():
+    """A routed-row bound below what the forward routed leaves those rows out;
+    the call then sets gb and the first row of gx to NaN (forced from the host:
+    the bound is one row short)."""
+    sffn = _sffn()
+    inp = wl.generate_custom(T=300, d_model=512, d_ff=1024, dtype="bf16", beta=1.9, seed_base=73,
+                             cap=4)
+    w = inp.workload
+    d = device_inputs(inp)
+    ffn = sffn.SparseFFN(w.T, w.d_model, w.d_ff, w.cap, torch.bfloat16)
+    ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    n_r = int(ffn.n_routed.item())
+    assert n_r > 1
+    s = ffn.shape
+    ws = torch.empty(sffn.backward_workspace_bytes(s, n_r - 1), dtype=torch.uint8, device="cuda")
+    gy = to_device(wl.upstream_grad(w), "bf16")
+    gx = torch.zeros((w.T, w.d_model), dtype=torch.bfloat16, device="cuda")
+    g = [torch.zeros((w.d_ff, w.d_model), device="cuda") for _ in range(3)]
+    gb = torch.zeros(w.d_ff, device="cuda")
+    sffn.sparse_ffn_bwd(s, d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], ffn.count, ffn.idx,
+                        ffn.val, ffn.routed, ffn.n_routed, gy, gx, *g, gb, ws, max_routed=n_r - 1)
+    torch.cuda.synchronize()
+    assert torch.isnan(gb).all()
+    assert torch.isnan(gx[0].float()).all()
