@@ -14,6 +14,14 @@
 //                 the time, two or more keep it busy.  Each lane's sum of its
 //                 accumulators is stored (2048 * iters, exact in float32 for
 //                 iters < 8192), which also checks that every MFMA ran.
+//   probe_cached  every workgroup reads the same small window (resident in
+//                 each XCD's L2 after the first pass) many times with 16-byte
+//                 loads, four in flight per lane: the rate at which the
+//                 vector-memory path brings cached data into the CUs, the
+//                 ceiling of any kernel that gathers rows it re-reads from L2.
+//   probe_gather  one wave per listed row reads that row of two matrices
+//                 (16-byte loads, the whole row in flight): the rate of a
+//                 row gather like the sparse kernel's, without arithmetic.
 //   probe_mfma_step
 //                 one v_mfma_f32_16x16x32_bf16 per wave on caller-given
 //                 operand registers, so a test can compare the instruction's
@@ -75,6 +83,41 @@ __global__ __launch_bounds__(kProbeBlock) void probe_mfma(float* __restrict__ ou
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+__global__ __launch_bounds__(kProbeBlock) void probe_cached(const u32x4_t* __restrict__ src,
+                                                            size_t n16, int reps) {
+  uint32_t acc = 0;
+  for (int r = 0; r < reps; ++r) {
+    size_t i = threadIdx.x;
+    for (; i + 3 * kProbeBlock < n16; i += 4 * kProbeBlock) {
+      const u32x4_t v0 = src[i], v1 = src[i + kProbeBlock], v2 = src[i + 2 * kProbeBlock],
+                    v3 = src[i + 3 * kProbeBlock];
+      acc ^= (v0.x ^ v1.y) ^ (v2.z ^ v3.w);
+    }
+    for (; i < n16; i += kProbeBlock) acc ^= src[i].x;
+  }
+  asm volatile("" ::"v"(acc));  // keeps the loads
+}
+
+template <int CH>  // 16-byte chunks per lane per row
+__global__ __launch_bounds__(kProbeBlock) void probe_gather(const u32x4_t* __restrict__ a,
+                                                            const u32x4_t* __restrict__ b,
+                                                            const int* __restrict__ rows,
+                                                            int nrows) {
+  const int item = (int)blockIdx.x * (kProbeBlock / 64) + (int)(threadIdx.x >> 6);
+  if (item >= nrows) return;
+  const size_t base = (size_t)rows[item] * (CH * 64) + (threadIdx.x & 63);
+  u32x4_t va[CH], vb[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    va[c] = a[base + 64 * c];
+    vb[c] = b[base + 64 * c];
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc ^= va[c].x ^ vb[c].w;
+  asm volatile("" ::"v"(acc));
+}
+
 // Wave w, lane l: A and B operand registers a/b[(w * 64 + l) * 8 .. + 8]
 // (bf16 bits), accumulator c[(w * 64 + l) * 4 .. + 4]; d receives the MFMA's
 // four accumulator registers at the same place.
@@ -121,5 +164,34 @@ extern "C" int32_t sffn_probe_mfma_step(const void* a, const void* b, const floa
     return SFFN_ERR_ARG;
   hipLaunchKernelGGL(probe_mfma_step, dim3((unsigned)waves), dim3(64), 0, (hipStream_t)stream,
                      (const u32x4_t*)a, (const u32x4_t*)b, (const f32x4_t*)c, (f32x4_t*)d);
+  return hipGetLastError() == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
+}
+
+extern "C" int32_t sffn_probe_cached(const void* src, size_t window_bytes, int32_t reps,
+                                     int32_t workgroups, void* stream) {
+  using namespace sffn;
+  if (!src || !aligned16(src) || window_bytes % 16 != 0 || window_bytes == 0 || reps <= 0 ||
+      workgroups <= 0)
+    return SFFN_ERR_ARG;
+  hipLaunchKernelGGL(probe_cached, dim3((unsigned)workgroups), dim3(kProbeBlock), 0,
+                     (hipStream_t)stream, (const u32x4_t*)src, window_bytes / 16, (int)reps);
+  return hipGetLastError() == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
+}
+
+extern "C" int32_t sffn_probe_gather(const void* a, const void* b, const int32_t* rows,
+                                     int32_t nrows, int32_t row_bytes, void* stream) {
+  using namespace sffn;
+  if (!a || !b || !rows || !aligned16(a) || !aligned16(b) || nrows < 0) return SFFN_ERR_ARG;
+  if (nrows == 0) return SFFN_OK;
+  const dim3 grid((unsigned)((nrows + 3) / 4)), blk(kProbeBlock);
+  hipStream_t s = (hipStream_t)stream;
+  switch (row_bytes) {
+    case 1024: hipLaunchKernelGGL(probe_gather<1>, grid, blk, 0, s, (const u32x4_t*)a, (const u32x4_t*)b, rows, nrows); break;
+    case 2048: hipLaunchKernelGGL(probe_gather<2>, grid, blk, 0, s, (const u32x4_t*)a, (const u32x4_t*)b, rows, nrows); break;
+    case 4096: hipLaunchKernelGGL(probe_gather<4>, grid, blk, 0, s, (const u32x4_t*)a, (const u32x4_t*)b, rows, nrows); break;
+    case 8192: hipLaunchKernelGGL(probe_gather<8>, grid, blk, 0, s, (const u32x4_t*)a, (const u32x4_t*)b, rows, nrows); break;
+    case 16384: hipLaunchKernelGGL(probe_gather<16>, grid, blk, 0, s, (const u32x4_t*)a, (const u32x4_t*)b, rows, nrows); break;
+    default: return SFFN_ERR_ARG;
+  }
   return hipGetLastError() == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
 }

@@ -26,6 +26,7 @@ EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_noalloc",
             "twell_pack_noalloc_max_bytes", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
             "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
             "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
+            "sffn_probe_cached", "sffn_probe_gather",
             "sffn_workspace_bytes", "sparse_ffn_bwd_workspace_bytes", "sffn_strerror")
 
 
@@ -63,11 +64,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sffn_probe_hbm.argtypes = [vp, vp, sz, i32, vp]
     lib.sffn_probe_mfma.argtypes = [vp, i32, i32, vp]
     lib.sffn_probe_mfma_step.argtypes = [vp, vp, vp, vp, i32, vp]
+    lib.sffn_probe_cached.argtypes = [vp, sz, i32, i32, vp]
+    lib.sffn_probe_gather.argtypes = [vp, vp, vp, i32, i32, vp]
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("twell_weight_norms", "twell_pack", "twell_pack_noalloc", "twell_pack_l1",
                "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
-               "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step"):
+               "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
+               "sffn_probe_cached", "sffn_probe_gather"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
     lib.sffn_workspace_bytes.restype = sz
@@ -207,6 +211,30 @@ def probe_mfma(out, iters: int, stream=None) -> None:
     wgs = out.numel() // 256
     _check("sffn_probe_mfma", _lib.sffn_probe_mfma(_ptr(out), int(wgs), int(iters),
                                                    _stream(stream)))
+
+
+def probe_cached(src, window_bytes: int, reps: int, workgroups: int, stream=None) -> None:
+    """Every workgroup reads src[0:window_bytes] reps times (cached-load rate)."""
+    if window_bytes > src.numel() * src.element_size():
+        raise ValueError("window larger than the buffer")
+    _check("sffn_probe_cached", _lib.sffn_probe_cached(_ptr(src), int(window_bytes), int(reps),
+                                                       int(workgroups), _stream(stream)))
+
+
+def probe_gather(a, b, rows, row_bytes: int, max_row=None, stream=None) -> None:
+    """Read rows[i] of a and of b (row_bytes per row) for every listed row.
+    max_row: the largest entry of rows when the caller knows it (then rows is
+    not read back from the device here, e.g. inside a timed region)."""
+    if rows.dtype != torch.int32:
+        raise TypeError("rows must be int32")
+    n_a = a.numel() * a.element_size() // row_bytes
+    n_b = b.numel() * b.element_size() // row_bytes
+    top = (int(rows.max().item()) if rows.numel() else -1) if max_row is None else int(max_row)
+    if top >= min(n_a, n_b):
+        raise ValueError("row index beyond the matrices")
+    _check("sffn_probe_gather", _lib.sffn_probe_gather(_ptr(a), _ptr(b), _ptr(rows),
+                                                       int(rows.numel()), int(row_bytes),
+                                                       _stream(stream)))
 
 
 def probe_mfma_step(a, b, c, d, stream=None) -> None:

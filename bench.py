@@ -91,10 +91,53 @@ def measured_peaks() -> dict:
     t_mfma = best(lambda: sffn.probe_mfma(out, iters))
     ok_mfma = bool(torch.all(out == 2048.0 * iters).item())
     flops = wgs * 4 * 16 * iters * 16384.0
+    del out
+    # cached loads: every workgroup re-reads one 2 MiB window (resident in each
+    # XCD's L2), 8 workgroups per CU
+    win, reps, cwg = 2 << 20, 24, 2048
+    buf = torch.ones(win // 4, dtype=torch.int32, device="cuda")
+    t_cached = best(lambda: sffn.probe_cached(buf, win, reps, cwg))
+    del buf
     return {"hbm_read_gb_s": nbytes / t_read / 1e9, "hbm_copy_gb_s": 2 * nbytes / t_copy / 1e9,
             "mfma_bf16_tflop_s": flops / t_mfma / 1e12, "checks_passed": ok_copy and ok_mfma,
+            "cached_load_gb_s": float(cwg) * reps * win / t_cached / 1e9,
             "probe": "sffn_probe_hbm over 1 GiB, 65536 workgroups (read-only; copy counts read + write), "
-                     "sffn_probe_mfma 4096 workgroups x 4 waves x 16 chains x 1024 MFMAs"}
+                     "sffn_probe_mfma 4096 workgroups x 4 waves x 16 chains x 1024 MFMAs, "
+                     "sffn_probe_cached 2048 workgroups x 24 passes over one 2 MiB window"}
+
+
+def gather_probe(wu, wd, idx_live, flush) -> dict:
+    """The bare row gather of the sparse step: the wu_t and wd rows of the
+    distinct active columns, read once by sffn_probe_gather with no arithmetic,
+    warm (rows cached by a previous pass) and cold (a 512 MiB read in between
+    evicts the Infinity Cache)."""
+    import torch
+    from activation_sparse_feed_amd import sffn
+    rows = torch.unique(idx_live.to(torch.int64)).to(torch.int32)
+    row_bytes = wu.shape[1] * wu.element_size()
+    if rows.numel() == 0 or row_bytes not in (1024, 2048, 4096, 8192, 16384):
+        return None
+    E = torch.cuda.Event
+
+    def timed(cold):
+        ts = []
+        for _ in range(5):
+            if cold:  # evict, then one gather
+                sffn.probe_hbm(flush, None, workgroups=4096)
+            a, b = E(enable_timing=True), E(enable_timing=True)
+            reps = 1 if cold else 10  # warm: back-to-back gathers of cached rows
+            a.record()
+            for _ in range(reps):
+                sffn.probe_gather(wu, wd, rows, row_bytes, max_row=top)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3 / reps)
+        return min(ts)
+    nb = 2.0 * rows.numel() * row_bytes
+    top = int(rows.max().item())
+    tw, tc = timed(False), timed(True)
+    return {"rows": int(rows.numel()), "bytes": nb, "warm_us": tw * 1e6, "cold_us": tc * 1e6,
+            "warm_gb_s": nb / tw / 1e9, "cold_gb_s": nb / tc / 1e9}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_twell_pack_prefill_1pct.md")
@@ -674,6 +717,21 @@ def main() -> int:
     roof_sparse["frac"] = roof_sparse["achieved"] / roof_sparse["peak"]
     roof_sparse["traffic"] = measured_traffic(w.name, SPARSE_TRAFFIC_FILE, sparse_source_digest)
     roof_sparse["traffic_unit"] = "bytes per launch (HBM, counter-derived)"
+    # the kernel's own bound: every live entry brings its wu_t and wd rows into
+    # the CU; against the measured rate of cached loads (sffn_probe_cached) and
+    # the bare gather of the distinct rows (sffn_probe_gather)
+    n_live = int(live.sum().item())
+    row_bytes_per_call = n_live * 2.0 * d * eb
+    roof_sparse["entry_row_bytes"] = row_bytes_per_call
+    roof_sparse["entry_row_gb_s"] = row_bytes_per_call / t_s / 1e9
+    if peaks is not None:
+        roof_sparse["cached_load_ceiling_gb_s"] = peaks["cached_load_gb_s"]
+        roof_sparse["frac_of_cached_load_ceiling"] = (row_bytes_per_call / t_s / 1e9
+                                                      / peaks["cached_load_gb_s"])
+        if w.dtype == "bf16" and w.cap > 0:
+            flush = torch.empty(128 << 20, dtype=torch.int32, device="cuda")
+            roof_sparse["bare_gather"] = gather_probe(wu, wd, ffn.idx.to(torch.int32)[live], flush)
+            del flush
     # the line's roofline is the dominant (longer) kernel's; both are kept
     roofline = roof_sparse if t_sparse > t_gate else roof_gate
 

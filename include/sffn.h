@@ -352,6 +352,30 @@ int32_t sffn_probe_hbm(const void* src, void* dst, size_t bytes, int32_t workgro
 int32_t sffn_probe_mfma(float* out, int32_t workgroups, int32_t iters, void* stream);
 
 /*
+ * sffn_probe_cached -- `workgroups` workgroups of 256 threads each read the
+ * same window [src, src + window_bytes) `reps` times with 16-byte loads, four
+ * in flight per lane (workgroups * reps * window_bytes bytes in all).  With a
+ * window that fits the L2 of an XCD (a few MiB) this is the rate at which the
+ * vector-memory path brings cached data into the CUs: the ceiling of a kernel
+ * that gathers rows it re-reads from the cache.  src 16-byte aligned,
+ * window_bytes a positive multiple of 16, reps > 0, workgroups > 0 (else
+ * SFFN_ERR_ARG).
+ */
+int32_t sffn_probe_cached(const void* src, size_t window_bytes, int32_t reps, int32_t workgroups,
+                          void* stream);
+
+/*
+ * sffn_probe_gather -- for every i < nrows, one wave reads row rows[i] of
+ * matrix a and of matrix b (rows of row_bytes bytes, row-major, 16-byte loads,
+ * the whole row in flight): a row gather like the sparse kernel's, without
+ * its arithmetic (2 * nrows * row_bytes bytes).  row_bytes one of 1024, 2048,
+ * 4096, 8192, 16384; rows: int32 device array of valid row indices; a, b
+ * 16-byte aligned; nrows >= 0 (else SFFN_ERR_ARG; 0 is a no-op).
+ */
+int32_t sffn_probe_gather(const void* a, const void* b, const int32_t* rows, int32_t nrows,
+                          int32_t row_bytes, void* stream);
+
+/*
  * sffn_probe_mfma_step -- one v_mfma_f32_16x16x32_bf16 per wave on operand
  * registers given by the caller, so that a test can compare the instruction
  * with the exact C + A.B.  The TwELL epilogue's guard band (twell_pack)

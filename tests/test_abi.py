@@ -226,6 +226,13 @@ def test_probe_errors(sffn):
     assert lib.sffn_probe_mfma_step(None, P, P, P, 1, None) == ARG
     assert lib.sffn_probe_mfma_step(P, P, P, MISALIGNED, 1, None) == ARG
     assert lib.sffn_probe_mfma_step(P, P, P, P, 0, None) == ARG
+    assert lib.sffn_probe_cached(None, 1024, 1, 1, None) == ARG
+    assert lib.sffn_probe_cached(P, 1000, 1, 1, None) == ARG
+    assert lib.sffn_probe_cached(P, 1024, 0, 1, None) == ARG
+    assert lib.sffn_probe_cached(P, 1024, 1, 0, None) == ARG
+    assert lib.sffn_probe_gather(P, P, P, -1, 8192, None) == ARG
+    assert lib.sffn_probe_gather(P, P, P, 4, 3000, None) == ARG
+    assert lib.sffn_probe_gather(P, P, P, 0, 8192, None) == sffn.SFFN_OK
 
 
 def test_noalloc_rejects_shapes_beyond_its_scratch(sffn):
