@@ -20,10 +20,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_floa
 
 // Round-to-nearest-even float -> bfloat16 bits (finite inputs; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);  // v_cvt_pk_bf16_f32
 }
 
 // Storage traits: elements per 16-byte chunk and conversion of one chunk.

@@ -159,12 +159,19 @@ __global__ __launch_bounds__(256) void down_f32(DenseArgs a) {
 // gate+up: 256 x 64 output tile of both z and u (2 x 2 waves of 128 x (32 + 32)),
 // two workgroups per CU; or (DenseWide) 256 x 128 of both, eight waves as
 // 4 x 2 of 64 x (64 + 64), one workgroup per CU: a quarter fewer LDS fragment
-// bytes per MFMA, used when the tiles fill at least two rounds of the CUs.
+// bytes per MFMA, used when the tiles fill at least two rounds of the CUs,
+// with each step's loads and fragment reads spread among its MFMAs.
 using DenseNarrow = Gemm2<2, 64, false, 32, 2>;
-using DenseWide = Gemm2<2, 128, false, 32, 2, false, 256, 4, 8>;
+using DenseWide = Gemm2<2, 128, false, 32, 2, false, 256, 4, 8, true>;
+
+// Workgroups per CU that the LDS ring of a configuration allows (one or two).
+template <class G>
+constexpr int wg_per_cu() {
+  return G::LDS_BYTES > 80 * 1024 ? 1 : 2;
+}
 
 template <class G>
-__global__ __launch_bounds__(64 * G::NWAVES, G::NWAVES == 8 ? 1 : 2) void gateup_bf16_v2(DenseArgs a) {
+__global__ __launch_bounds__(64 * G::NWAVES, wg_per_cu<G>()) void gateup_bf16_v2(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   // each of the two B matrices (wg_t, wu_t) contributes BN / 2 columns of the tile
   static_assert(G::BN % 2 == 0, "two B matrices");
@@ -200,17 +207,23 @@ __global__ __launch_bounds__(64 * G::NWAVES, G::NWAVES == 8 ? 1 : 2) void gateup
   }
 }
 
-// down: 128 x 128 output tile (the down GEMM has few N tiles, so 128-row tiles
-// keep two workgroups per CU busy), wd [d_ff, d_model] staged K-major and
-// read with transposing LDS reads.
-__global__ __launch_bounds__(256, 2) void down_bf16_v2(DenseArgs a) {
-  using G = Gemm2<1, 128, false, 32, 2, true, 128>;
+// down: wd [d_ff, d_model] staged K-major and read with transposing LDS
+// reads.  DownNarrow: 128 x 128 output tiles, two workgroups per CU (the down
+// GEMM has few N tiles); DownWide: 256 x 256 tiles, eight waves as 4 x 2 of
+// 64 x 128, one workgroup per CU: a quarter fewer LDS fragment bytes per MFMA
+// and half the staging per output, used when the tiles fill at least two
+// rounds of the CUs (loads and fragment reads spread among the MFMAs).
+using DownNarrow = Gemm2<1, 128, false, 32, 2, true, 128>;
+using DownWide = Gemm2<1, 256, false, 32, 2, true, 256, 4, 8, true>;
+
+template <class G>
+__global__ __launch_bounds__(64 * G::NWAVES, wg_per_cu<G>()) void down_bf16_v2(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
-  const int nt = (a.N + 127) / 128;
+  const int nt = (a.N + G::BN - 1) / G::BN;
   const int mv = rows_valid(a);
   int mi, ni;
   tile_of((int)blockIdx.x, (a.M + G::BM - 1) / G::BM, nt, &mi, &ni);
-  const int m0 = mi * G::BM, n0 = ni * 128;
+  const int m0 = mi * G::BM, n0 = ni * G::BN;
   if (m0 >= mv) return;
   G g;
   const uint16_t* B[1] = {(const uint16_t*)a.b0};
@@ -428,11 +441,11 @@ hipError_t launch_dense_gateup(int dtype, const void* x, const void* wg_t, const
   if (dtype == 1 && K % 32 == 0) {
     const long wide_tiles = (long)((M + 255) / 256) * (N / 128);
     if (N % 128 == 0 && wide_tiles >= 2 * 256)
-      hipLaunchKernelGGL(gateup_bf16_v2<DenseWide>, dim3((unsigned)wide_tiles), dim3(512), 0,
-                         stream, a);
+      hipLaunchKernelGGL(gateup_bf16_v2<DenseWide>, dim3((unsigned)wide_tiles),
+                         dim3(64 * DenseWide::NWAVES), 0, stream, a);
     else
       hipLaunchKernelGGL(gateup_bf16_v2<DenseNarrow>, dim3((unsigned)(((M + 255) / 256) * (N / 64))),
-                         dim3(256), 0, stream, a);
+                         dim3(64 * DenseNarrow::NWAVES), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(((M + 127) / 128) * (N / 64)));
@@ -446,8 +459,14 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
                        hipStream_t stream) {
   DenseArgs a{h, wd, nullptr, nullptr, y, rowmap, n_rows_dev, M, K, N};
   if (dtype == 1 && K % 32 == 0) {
-    hipLaunchKernelGGL(down_bf16_v2, dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))),
-                       dim3(256), 0, stream, a);
+    const long wide_tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+    if (wide_tiles >= 2 * 256)
+      hipLaunchKernelGGL(down_bf16_v2<DownWide>, dim3((unsigned)wide_tiles),
+                         dim3(64 * DownWide::NWAVES), 0, stream, a);
+    else
+      hipLaunchKernelGGL(down_bf16_v2<DownNarrow>,
+                         dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))),
+                         dim3(64 * DownNarrow::NWAVES), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));

@@ -67,12 +67,12 @@ __device__ __forceinline__ void tile_of(int bid, int mt, int nt, int* m, int* n)
 // waves of 64 rows x BNW columns, so that every row of a B matrix's tile lives
 // in one wave).
 // B_KN: the single B matrix is [K, N] (N-contiguous, e.g. the down projection
-// weight).  Its K step is staged as BK rows of BNW columns (256 bytes), with
-// 16-byte chunks XOR-swizzled by row (kn_slot); MFMA B fragments are read with
-// the gfx950 transposing LDS read, which hands each lane four consecutive k of
-// one column per 8-byte read.
+// weight).  Its K step is staged as BK rows of BNW columns (256 or 512 bytes),
+// with 16-byte chunks XOR-swizzled by row (kn_slot); MFMA B fragments are read
+// with the gfx950 transposing LDS read, which hands each lane four consecutive
+// k of one column per 8-byte read.
 template <int NB, int BNW, bool NORMS, int BK_ = 32, int WAVES_N = 2, bool B_KN = false,
-          int BM_ = 256, int STAGES_ = 3, int NWAVES_ = 4>
+          int BM_ = 256, int STAGES_ = 3, int NWAVES_ = 4, bool INTERLEAVE = false>
 struct Gemm2 {
   static constexpr int BM = BM_, BK = BK_, STAGES = STAGES_, NWAVES = NWAVES_;
   static constexpr int BN = NB * BNW;
@@ -85,11 +85,14 @@ struct Gemm2 {
   static constexpr int LOADS = BLOCKS / NWAVES;        // load instructions per wave per stage
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(!NORMS || WAVES_N == 2, "norm split assumes 2 x 2 waves");
-  static_assert(!B_KN || (NB == 1 && BNW == 128 && BK == 32 && !NORMS), "K-major B layout");
+  static_assert(!B_KN || (NB == 1 && (BNW == 128 || BNW == 256) && BK == 32 && !NORMS),
+                "K-major B layout");
   static constexpr int KN_ROWB = BNW * 2;   // bytes per staged k row of a [K, N] B
+  static constexpr int KN_CPR = KN_ROWB / 16;  // 16-byte chunks per staged k row
   // 16-byte chunk q of staged k row k sits at chunk q ^ 2 c(k), c(k) = bits 0, 1 and 3 of k:
   // the rows one transposing read touches at a time (k = 8 g + 0..3, g = 0, 1,
-  // or those + 4) land in 16 distinct chunks, so no two lanes share a bank.
+  // or those + 4) land in 16 distinct chunks modulo 16, so no two lanes share a
+  // bank (the row length is a multiple of the 256 bytes of the 64 banks).
   static __device__ __forceinline__ int kn_slot(int k, int q) {
     return q ^ (2 * ((k & 3) | ((k >> 1) & 4)));
   }
@@ -97,7 +100,7 @@ struct Gemm2 {
   static constexpr int WM = BM / WAVES_M, WN = BNW / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_BYTES;
-  static_assert(BN == 128 || (BN == 256 && !B_KN), "workgroup N tile");
+  static_assert(BN == 128 || BN == 256, "workgroup N tile");
   static_assert(BM == 256 || BM == 128 || BM == 64 || BM == 32, "workgroup M tile");
   static_assert(BLOCKS % NWAVES == 0, "load blocks per wave");
   static_assert(!NORMS || NWAVES == 4, "norm split assumes 4 waves");
@@ -116,6 +119,7 @@ struct Gemm2 {
   __amdgpu_buffer_rsrc_t rb[NB];
   int b_ld;  // B_KN: bytes per row of B
   __amdgpu_buffer_rsrc_t rw;  // WAVE_ALIGNED: the matrix this wave's load blocks come from
+  int kstride;  // WAVE_ALIGNED and B_KN: bytes per K element in that matrix (2, or b_ld)
 
   // A: [*, K] bf16 rows; rows m0 .. m0+255 (gathered through rowmap when
   // given); rows >= m_valid read as zero.  B[b]: [N, K] bf16; rows n0 ..
@@ -157,16 +161,18 @@ struct Gemm2 {
         const int rb_ = row - BM;
         voff[i] = (uint32_t)(rb_ % BNW) * ld + (uint32_t)q * 16u;
       } else {
-        // B block blk - BM/RPB covers k rows 4 b .. 4 b + 3 of 256 bytes
+        // B block bb = blk - BM/RPB covers the 1024 / KN_ROWB k rows from
+        // bb * 1024 / KN_ROWB on; lane l lands in physical chunk l % KN_CPR
         const int bb = blk - BM / RPB;
-        const int kk = 4 * bb + (lane >> 4);
-        const int qq = kn_slot(kk, lane & 15);
+        const int kk = (1024 / KN_ROWB) * bb + lane / KN_CPR;
+        const int qq = kn_slot(kk, lane % KN_CPR);
         voff[i] = (uint32_t)kk * (uint32_t)b_ld + (uint32_t)qq * 16u;
       }
     }
     if constexpr (WAVE_ALIGNED) {
       const int blk0 = w * LOADS;
       rw = blk0 * RPB < BM ? ra : ((NB == 1 || (blk0 * RPB - BM) < BNW) ? rb[0] : rb[NB - 1]);
+      kstride = (B_KN && blk0 * RPB >= BM) ? b_ld : 2;
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -185,11 +191,11 @@ struct Gemm2 {
   // Every load block of a wave comes from the same matrix (chosen once per
   // wave, a uniform branch around whole loops: no per-load descriptor select).
   static constexpr bool WAVE_ALIGNED =
-      !B_KN && (BM / RPB) % LOADS == 0 && (BNW / RPB) % LOADS == 0;
+      (BM / RPB) % LOADS == 0 && (BNW / RPB) % LOADS == 0 && (!B_KN || BM == 256);
 
   __device__ __forceinline__ void issue(uint8_t* stage, int k0) {
     const int w = uniform((int)(threadIdx.x >> 6));
-    const int soff = k0 * 2;
+    const int soff = (WAVE_ALIGNED && B_KN) ? k0 * kstride : k0 * 2;
     if constexpr (WAVE_ALIGNED) {
       // the wave's descriptor was chosen once in init: no branch here, so the
       // loads can be scheduled among the MFMAs of the step
@@ -360,8 +366,54 @@ struct Gemm2 {
       }
   }
 
+  // INTERLEAVE (steady steps): the buffer loads and fragment reads of the step
+  // are spread among its MFMAs (one load or read, then a few MFMAs) instead
+  // of all being issued ahead of them, so that a wave's MFMA issue is not held
+  // up behind a burst of memory instructions.
+  static constexpr int N_DS = KS * FM + (B_KN ? 2 * FN : KS * NB * FN);  // fragment reads per step
+  static constexpr int N_MFMA = KS * FM * NB * FN;                      // MFMAs per step
+  static __device__ __forceinline__ void interleave_schedule() {
+    constexpr int per_load = 1;
+    constexpr int left = N_MFMA - LOADS * per_load;
+    constexpr int per_ds = left / N_DS > 0 ? left / N_DS : 1;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // one buffer load
+      __builtin_amdgcn_sched_group_barrier(0x008, per_load, 0);  // MFMAs
+    }
+#pragma unroll
+    for (int i = 0; i < N_DS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, per_ds, 0);  // MFMAs
+    }
+    if constexpr (left - per_ds * N_DS > 0)
+      __builtin_amdgcn_sched_group_barrier(0x008, left - per_ds * N_DS, 0);
+  }
+
+  // The buffer loads of a step write one LDS stage while its fragment reads
+  // come from another: the restrict qualifiers tell the compiler so (the two
+  // stages are distinct since STAGES >= 3).  Without that knowledge it makes
+  // every transposing read wait for all buffer loads in flight, which would
+  // expose the global-load latency once per step.
+  __device__ __forceinline__ void issue_and_read(uint8_t* __restrict__ dst, int k0,
+                                                 const uint8_t* __restrict__ src, Frags& nxt) {
+    issue(dst, k0);
+    load_frags(nxt, src);
+  }
+
   template <bool STEADY, bool SQA = false>
   __device__ __forceinline__ void pipe_step(uint8_t* lds, int kt, int nk, Frags& cur, Frags& nxt) {
+    if constexpr (INTERLEAVE && STEADY && !SQA) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<(STAGES - 3) * LOADS>());
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_and_read(lds + ((kt + STAGES - 1) % STAGES) * STAGE_BYTES, (kt + STAGES - 1) * BK,
+                     lds + ((kt + 1) % STAGES) * STAGE_BYTES, nxt);
+      mma(cur);
+      interleave_schedule();
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     if (STEADY || kt + 1 < nk) {
       if (STEADY) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm<(STAGES - 3) * LOADS>());
@@ -370,8 +422,10 @@ struct Gemm2 {
       }
       lds_barrier();
       if (STEADY || kt + STAGES - 1 < nk)
-        issue(lds + ((kt + STAGES - 1) % STAGES) * STAGE_BYTES, (kt + STAGES - 1) * BK);
-      load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
+        issue_and_read(lds + ((kt + STAGES - 1) % STAGES) * STAGE_BYTES, (kt + STAGES - 1) * BK,
+                       lds + ((kt + 1) % STAGES) * STAGE_BYTES, nxt);
+      else
+        load_frags(nxt, lds + ((kt + 1) % STAGES) * STAGE_BYTES);
     }
     __builtin_amdgcn_sched_barrier(0);
     mma(cur);

@@ -28,6 +28,8 @@
 //                 result with the exact C + A.B: the error model that the
 //                 TwELL epilogue's guard band assumes (one rounding of the
 //                 result per instruction) is checked on the hardware itself.
+#include <algorithm>
+
 #include "common.cuh"
 #include "sffn.h"
 
@@ -131,6 +133,15 @@ __global__ __launch_bounds__(64) void probe_mfma_step(const u32x4_t* __restrict_
   d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c[i], 0, 0, 0);
 }
 
+// out[i] = the library's float32 -> bfloat16 rounding of in[i].
+__global__ __launch_bounds__(kProbeBlock) void probe_bf16_round(const float* __restrict__ in,
+                                                                uint16_t* __restrict__ out,
+                                                                size_t n) {
+  for (size_t i = (size_t)blockIdx.x * kProbeBlock + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kProbeBlock)
+    out[i] = f32_to_bf16(in[i]);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -193,5 +204,15 @@ extern "C" int32_t sffn_probe_gather(const void* a, const void* b, const int32_t
     case 16384: hipLaunchKernelGGL(probe_gather<16>, grid, blk, 0, s, (const u32x4_t*)a, (const u32x4_t*)b, rows, nrows); break;
     default: return SFFN_ERR_ARG;
   }
+  return hipGetLastError() == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
+}
+
+extern "C" int32_t sffn_probe_bf16_round(const float* in, uint16_t* out, size_t n, void* stream) {
+  using namespace sffn;
+  if (!in || !out) return SFFN_ERR_ARG;
+  if (n == 0) return SFFN_OK;
+  const size_t blocks = std::min<size_t>((n + kProbeBlock - 1) / kProbeBlock, 4096);
+  hipLaunchKernelGGL(probe_bf16_round, dim3((unsigned)blocks), dim3(kProbeBlock), 0,
+                     (hipStream_t)stream, in, out, n);
   return hipGetLastError() == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
 }

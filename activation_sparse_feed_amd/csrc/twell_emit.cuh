@@ -169,11 +169,11 @@ __device__ void twell_rows(const GateArgs& a, const ZT* zs, int zld, int nrows, 
 constexpr int kGateBK = 32;      // K depth of one pipeline stage
 constexpr int kGateStages = 4;   // LDS ring depth
 constexpr int kGateWaves = 8;    // waves per workgroup (two per SIMD)
-using GateGemm = Gemm2<1, 128, false, kGateBK, 1, false, 256, kGateStages, kGateWaves>;
+using GateGemm = Gemm2<1, 128, false, kGateBK, 1, false, 256, kGateStages, kGateWaves, true>;
 static_assert(GateGemm::WN == kTile, "each wave holds one TwELL column tile");
 // 256 x 256 tiles of the same kernel: eight waves as 4 x 2, each 64 rows x one
 // TwELL tile (a quarter fewer LDS fragment bytes per MFMA than 32 x 128).
-using GateGemmWide = Gemm2<1, 256, false, kGateBK, 2, false, 256, kGateStages, kGateWaves>;
+using GateGemmWide = Gemm2<1, 256, false, kGateBK, 2, false, 256, kGateStages, kGateWaves, true>;
 static_assert(GateGemmWide::WN == kTile, "each wave holds one TwELL column tile");
 
 // Columns of 256-wide tiles (wide_nt, counted in 256-column tiles) and of

@@ -89,6 +89,15 @@ struct AccEpi {
   const float* rn_a;
   uint32_t* exact_lds;  // this wave's exact-stage area
   float l1;             // L1 regulariser: this lane's ReLU sum over its rows and columns
+  // Stores: wave-uniform bases (the wave's first row, its TwELL tile) and this
+  // lane's 32-bit byte offsets from them, so that each store takes one
+  // scalar base and one vector offset.
+  uint16_t* idx_w;
+  uint16_t* val_w;
+  uint16_t* cnt_w;
+  uint32_t lane_b;      // bytes from the bases of idx/val to the lane's row group (rows + 4 gi)
+  uint32_t lane_cb;     // bytes from cnt_w to the lane's row group's count
+  uint32_t below;       // bits of the lanes before this one in its 16-lane segment
 };
 
 // One accumulator row group (fm, r): 4 rows of the wave, all 128 columns of
@@ -103,12 +112,10 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, G& g, AccEpi<G>& c)
   const float nx = c.rn_a[row];
   const float dmax = c.cw * nx + c.cb;
   float v[FN];
-  bool act[FN];
   bool fl = false;
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     v[fn] = g.acc[0][FM][fn][R] + c.bias[fn];
-    act[fn] = v[fn] > 0.f;
     fl |= valid && !(fabsf(v[fn]) > dmax);
   }
   if (__ballot(fl)) {
@@ -125,31 +132,35 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, G& g, AccEpi<G>& c)
         const ExactResult e = exact_gate_value<uint16_t, kEpiExactChunks>(
             (const uint16_t*)a.x + (size_t)(c.m0 + lrow) * a.K,
             (const uint16_t*)a.wg + (size_t)(c.n0 + lcol) * a.K, bl, a.K, c.exact_lds);
-        if (c.lane == L) {
-          act[fn] = e.sign > 0;
-          v[fn] = (float)e.value;
-        }
+        // activity is v > 0 from here on: a positive exact z that float32
+        // cannot hold stays positive (its bfloat16 value is 0 either way)
+        if (c.lane == L) v[fn] = e.sign > 0 ? fmaxf((float)e.value, 0x1p-149f) : (float)e.value;
       }
     }
   }
-  const size_t base = ((size_t)t * c.nt + c.kt) * a.cap;
+  // the group's rows (FM * 16 + R + 4 gi of the wave): byte offsets of the
+  // lane's row in idx / val and in count
+  const uint32_t rb = c.lane_b + (uint32_t)((FM * 16 + R) * c.nt * a.cap * 2);
+  const uint32_t cb = c.lane_cb + (uint32_t)((FM * 16 + R) * c.nt * 2);
   int running = 0;
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
-    const uint64_t m = __ballot(act[fn]);
+    const bool act = v[fn] > 0.f;
+    const uint64_t m = __ballot(act);
     const uint32_t seg = (uint32_t)(m >> (16 * c.gi)) & 0xffffu;
-    const int slot = running + __builtin_popcount(seg & ((1u << c.li) - 1u));
-    if (act[fn] && valid && slot < a.cap) {
-      a.idx[base + slot] = (uint16_t)(c.n0 + fn * 16 + c.li);
-      ((uint16_t*)a.val)[base + slot] = f32_to_bf16(v[fn]);
+    const int slot = running + __builtin_popcount(seg & c.below);
+    if (act && valid && slot < a.cap) {
+      const uint32_t o = rb + 2u * (uint32_t)slot;
+      *(uint16_t*)((char*)c.idx_w + o) = (uint16_t)(c.n0 + fn * 16 + c.li);
+      *(uint16_t*)((char*)c.val_w + o) = f32_to_bf16(v[fn]);
     }
     running += __builtin_popcount(seg);
   }
-  if (c.li == 0 && valid) a.count[(size_t)t * c.nt + c.kt] = (uint16_t)running;
+  if (c.li == 0 && valid) *(uint16_t*)((char*)c.cnt_w + cb) = (uint16_t)running;
   if (a.l1_part) {  // L1 regulariser, fixed order: per lane over its rows,
     float s = 0.f;     // one value per workgroup after the walk
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) s += act[fn] ? v[fn] : 0.f;
+    for (int fn = 0; fn < FN; ++fn) s += v[fn] > 0.f ? v[fn] : 0.f;
     if (valid) c.l1 += s;
   }
 }
@@ -201,6 +212,15 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, uint8_t* lds, int m
   c.cw = 0.f;
   c.cb = 0.f;
   c.l1 = 0.f;
+  {
+    const size_t r0 = (size_t)(m0 + c.wm * G::WM);  // the wave's first row
+    c.idx_w = a.idx + (r0 * nt + c.kt) * a.cap;
+    c.val_w = (uint16_t*)a.val + (r0 * nt + c.kt) * a.cap;
+    c.cnt_w = a.count + r0 * nt + c.kt;
+    c.lane_b = (uint32_t)(4 * c.gi * nt * a.cap * 2);
+    c.lane_cb = (uint32_t)(4 * c.gi * nt * 2);
+    c.below = (1u << c.li) - 1u;
+  }
 #pragma unroll
   for (int fn = 0; fn < G::FN; ++fn) {
     const int col = fn * 16 + c.li;

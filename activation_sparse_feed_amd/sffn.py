@@ -26,7 +26,7 @@ EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_noalloc",
             "twell_pack_noalloc_max_bytes", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
             "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
             "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
-            "sffn_probe_cached", "sffn_probe_gather",
+            "sffn_probe_cached", "sffn_probe_gather", "sffn_probe_bf16_round",
             "sffn_workspace_bytes", "sparse_ffn_bwd_workspace_bytes", "sffn_strerror")
 
 
@@ -66,12 +66,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sffn_probe_mfma_step.argtypes = [vp, vp, vp, vp, i32, vp]
     lib.sffn_probe_cached.argtypes = [vp, sz, i32, i32, vp]
     lib.sffn_probe_gather.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.sffn_probe_bf16_round.argtypes = [vp, vp, sz, vp]
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("twell_weight_norms", "twell_pack", "twell_pack_noalloc", "twell_pack_l1",
                "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
                "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
-               "sffn_probe_cached", "sffn_probe_gather"):
+               "sffn_probe_cached", "sffn_probe_gather", "sffn_probe_bf16_round"):
         getattr(lib, fn).restype = i32
     lib.sffn_workspace_bytes.argtypes = [sp, i32]
     lib.sffn_workspace_bytes.restype = sz
@@ -219,6 +220,16 @@ def probe_cached(src, window_bytes: int, reps: int, workgroups: int, stream=None
         raise ValueError("window larger than the buffer")
     _check("sffn_probe_cached", _lib.sffn_probe_cached(_ptr(src), int(window_bytes), int(reps),
                                                        int(workgroups), _stream(stream)))
+
+
+def probe_bf16_round(x, out, stream=None) -> None:
+    """out = the library's float32 -> bfloat16 rounding of x (uint16 bits)."""
+    if x.dtype != torch.float32 or out.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("x must be float32 and out 16-bit integer")
+    if out.numel() < x.numel():
+        raise ValueError("out too small")
+    _check("sffn_probe_bf16_round", _lib.sffn_probe_bf16_round(_ptr(x), _ptr(out), int(x.numel()),
+                                                               _stream(stream)))
 
 
 def probe_gather(a, b, rows, row_bytes: int, max_row=None, stream=None) -> None:

@@ -394,6 +394,16 @@ int32_t sffn_probe_gather(const void* a, const void* b, const int32_t* rows, int
 int32_t sffn_probe_mfma_step(const void* a, const void* b, const float* c, float* d,
                              int32_t waves, void* stream);
 
+/*
+ * sffn_probe_bf16_round -- out[i] = the float32 -> bfloat16 rounding that
+ * every kernel of this library applies when it stores a bfloat16 result
+ * (round to nearest, ties to even; NaN stays NaN), for i < n, so that a test
+ * can compare it with a host rounding of the same inputs.  in: float32 [n],
+ * out: uint16 bit patterns [n], device pointers; NULL pointers are
+ * SFFN_ERR_ARG; n == 0 is a no-op.
+ */
+int32_t sffn_probe_bf16_round(const float* in, uint16_t* out, size_t n, void* stream);
+
 /* Workspace bytes needed by one call for this shape (0 if the shape is invalid). */
 size_t sffn_workspace_bytes(const sffn_shape* shape, int32_t which);
 

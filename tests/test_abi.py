@@ -233,6 +233,9 @@ def test_probe_errors(sffn):
     assert lib.sffn_probe_gather(P, P, P, -1, 8192, None) == ARG
     assert lib.sffn_probe_gather(P, P, P, 4, 3000, None) == ARG
     assert lib.sffn_probe_gather(P, P, P, 0, 8192, None) == sffn.SFFN_OK
+    assert lib.sffn_probe_bf16_round(None, P, 4, None) == ARG
+    assert lib.sffn_probe_bf16_round(P, None, 4, None) == ARG
+    assert lib.sffn_probe_bf16_round(P, P, 0, None) == sffn.SFFN_OK
 
 
 def test_noalloc_rejects_shapes_beyond_its_scratch(sffn):

@@ -170,6 +170,35 @@ def test_dense_reference_prefill_full_size_sampled():
     check_y(w.dtype, y[rows], ref["y_dense"], np.zeros(len(rows), dtype=bool))
 
 
+def test_dense_reference_large_full_size_sampled():
+    # 16384 tokens, 4096 -> 14336: the dense down runs its 256 x 256 (eight-wave)
+    # tiles with the K-major weight staged in 512-byte rows
+    sffn = _sffn()
+    w = wl.WORKLOADS["large_lognormal"]
+    inp = wl.generate(w)
+    d = device_inputs(inp)
+    dense = sffn.DenseFFN(w.T, w.d_model, w.d_ff, torch.bfloat16)
+    y = to_f64(dense.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"]))
+    rows = sample_rows(w.T, 96, seed=8)
+    ref = oracle_rows(inp, rows, w.tile, w.cap)
+    check_y(w.dtype, y[rows], ref["y_dense"], np.zeros(len(rows), dtype=bool))
+
+
+def test_dense_reference_wide_down_ragged():
+    # 256 x 256 down tiles over ragged rows (16000 = 62.5 tiles) and a ragged
+    # last column tile (2184 = 8 x 256 + 136, a partial 16-column fragment)
+    sffn = _sffn()
+    inp = wl.generate_custom(T=16000, d_model=2184, d_ff=1024, dtype="bf16", beta=1.0,
+                             seed_base=80)
+    w = inp.workload
+    d = device_inputs(inp)
+    dense = sffn.DenseFFN(w.T, w.d_model, w.d_ff, torch.bfloat16)
+    y = to_f64(dense.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"]))
+    rows = sample_rows(w.T, 64, must=np.arange(w.T - 130, w.T, 7), seed=9)
+    ref = oracle_rows(inp, rows, w.tile, w.cap, dense=True)
+    check_y(w.dtype, y[rows], ref["y_dense"], np.zeros(len(rows), dtype=bool))
+
+
 @pytest.mark.parametrize("T,K,N", [(1, 256, 512), (7, 384, 1280), (32, 1024, 4096)])
 def test_dense_reference_few_tokens(T, K, N):
     """Split-K dense kernels (few tokens), ragged row fragments included."""
