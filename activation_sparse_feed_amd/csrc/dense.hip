@@ -43,6 +43,9 @@ struct DenseArgs {
   // by workgroup 0 of the routed gate+up before the down GEMM runs
   int* tile_count = nullptr;
   int tile_count_n = 0;
+  // routed rows: the eight-wave kernels (gateup_routed_wide, down_routed_wide)
+  // were launched too and take every count above kRoutedBigRows
+  int routed_wide = 0;
 };
 
 __device__ __forceinline__ int rows_valid(const DenseArgs& a) {
@@ -254,7 +257,8 @@ constexpr int kRoutedMaxSplit = 8;   // K splits of the routed down GEMM
 // blockIdx.x, blockIdx.x + gridDim.x, ... of the mt x nt tiles.
 template <typename G>
 __device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, uint8_t* lds) {
-  const int mt = (mv + G::BM - 1) / G::BM, nt = a.N / 64;
+  constexpr int TW = G::BN / 2;  // columns of each of the two B matrices per tile
+  const int mt = (mv + G::BM - 1) / G::BM, nt = a.N / TW;
   const int lane = lane_id();
   const int w = uniform((int)(threadIdx.x >> 6));
   const int wm = w % G::WAVES_M, wn = w / G::WAVES_M;
@@ -262,7 +266,7 @@ __device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, 
   const uint16_t* B[2] = {(const uint16_t*)a.b0, (const uint16_t*)a.b1};
   G g;
   for (int tile = (int)blockIdx.x; tile < mt * nt; tile += (int)gridDim.x) {
-    const int m0 = (tile % mt) * G::BM, n0 = (tile / mt) * 64;
+    const int m0 = (tile % mt) * G::BM, n0 = (tile / mt) * TW;
     g.init((const uint16_t*)a.a, (size_t)a.M, a.rowmap, m0, mv, B, n0, a.N, a.K);
     g.run_pipe(lds, a.K);
 #pragma unroll
@@ -284,9 +288,16 @@ __device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, 
 }
 
 // Few routed rows: 128-row tiles with a deeper pipeline (few workgroups per CU
-// to hide memory latency with); many: the 256-row tiles of the full-size
-// kernel.
+// to hide memory latency with); more than kRoutedBigRows: 256-row tiles.
+// From kRoutedWideTokens tokens on, those many-row counts go to the eight-wave
+// 256-row tiles of the full-size kernels (DenseWide, DownWide), one workgroup
+// per CU, in kernels of their own (gateup_routed_wide, down_routed_wide) that
+// the launcher adds; each kernel returns at once when the device-side row
+// count is not its own.  Below that token count the extra launches (a few us
+// each when they find nothing to do) would cost more than they can save.
 constexpr int kRoutedBigRows = 1024;
+constexpr int kRoutedWideTokens = 8192;
+constexpr int kWideGrid = 256;  // workgroups of the eight-wave routed kernels
 using RoutedSmall = Gemm2<2, 64, false, 32, 2, false, 128, kRoutedStages>;
 using RoutedBig = Gemm2<2, 64, false, 32, 2>;
 // With the fused route (at most kRouteBlock rows): one stage less, so that the
@@ -316,9 +327,16 @@ __global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
     gateup_routed_tiles<RoutedFused>(a, mv, lds);
   } else {
     const int mv = uniform(rows_valid(a));  // scalar: the tile loop and buffer descriptors stay uniform
-    if (mv > kRoutedBigRows) gateup_routed_tiles<RoutedBig>(a, mv, lds);
-    else gateup_routed_tiles<RoutedSmall>(a, mv, lds);
+    if (mv <= kRoutedBigRows) gateup_routed_tiles<RoutedSmall>(a, mv, lds);
+    else if (!a.routed_wide) gateup_routed_tiles<RoutedBig>(a, mv, lds);
   }
+}
+
+// More than kRoutedBigRows routed rows: 256 x (128 + 128) tiles, eight waves.
+__global__ __launch_bounds__(64 * DenseWide::NWAVES, 1) void gateup_routed_wide(DenseArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DenseWide::LDS_BYTES];
+  const int mv = uniform(rows_valid(a));
+  if (mv > kRoutedBigRows) gateup_routed_tiles<DenseWide>(a, mv, lds);
 }
 
 // K splits of the routed down GEMM for mt x nt output tiles: the fewest splits
@@ -327,15 +345,15 @@ __global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
 // a nearly empty one), else the best filling; at most kRoutedMaxSplit, at least
 // 8 K steps per split, and at most three rounds of items (which bounds the
 // partials at 3 * kRoutedGrid tiles of 128 x 128 floats).
-__host__ __device__ inline int routed_down_splits(int mt, int nt, int K) {
+__host__ __device__ inline int routed_down_splits(int mt, int nt, int K, int grid) {
   const int tiles = max(1, mt * nt);
   const int s_max = max(1, min(kRoutedMaxSplit, K / 256));
   int best = 1;
   int best_num = 0, best_den = 1;  // best filling as a fraction
   for (int s = 1; s <= s_max; ++s) {
     const int items = tiles * s;
-    if (s > 1 && items > 3 * kRoutedGrid) break;
-    const int slots = ((items + kRoutedGrid - 1) / kRoutedGrid) * kRoutedGrid;
+    if (s > 1 && items > 3 * grid) break;
+    const int slots = ((items + grid - 1) / grid) * grid;
     if (10 * items >= 9 * slots) return s;
     if ((long)items * best_den > (long)best_num * slots) {
       best = s;
@@ -346,24 +364,40 @@ __host__ __device__ inline int routed_down_splits(int mt, int nt, int K) {
   return best;
 }
 
+// The routed down GEMM for mv rows: square tiles of bm (128, or 256 on the
+// eight-wave kernel above kRoutedBigRows rows when it runs), mt x nt of them,
+// S K splits over that kernel's grid; partials [S][mt * bm][N] when S > 1.
+struct DownPlan {
+  bool wide;
+  int bm, mt, nt, S;
+};
+__host__ __device__ inline DownPlan routed_down_plan(int mv, int N, int K, bool wide_ok) {
+  DownPlan p;
+  p.wide = wide_ok && mv > kRoutedBigRows;
+  p.bm = p.wide ? 256 : 128;
+  p.mt = (mv + p.bm - 1) / p.bm;
+  p.nt = (N + p.bm - 1) / p.bm;
+  p.S = routed_down_splits(p.mt, p.nt, K, p.wide ? kWideGrid : kRoutedGrid);
+  return p;
+}
+
 // y rows of the routed list: with one split, written directly (rounded);
-// with S > 1, float32 partials [S][mt * 128][N] that down_routed_reduce sums.
+// with S > 1, float32 partials [S][mt * BM][N] that down_routed_reduce sums.
 // FOLD (few tokens, a.tile_count set): the tile's last split sums the
 // partials; a template flag so that the many-token instantiation keeps its
-// registers (and occupancy) free of the summation.
-template <bool FOLD>
-__global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partial) {
-  using G = Gemm2<1, 128, false, 32, 2, true, 128, kRoutedStages>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
-  const int mv = uniform(rows_valid(a));
-  const int mt = (mv + G::BM - 1) / G::BM, nt = (a.N + 127) / 128;
-  const int S = routed_down_splits(mt, nt, a.K);
+// registers (and occupancy) free of the summation.  G: square BM x BN tiles
+// of the K-major down GEMM.
+template <class G, bool FOLD>
+__device__ __forceinline__ void down_routed_items(const DenseArgs& a, float* partial,
+                                                  const DownPlan& p, int mv, uint8_t* lds) {
+  static_assert(G::BM == G::BN, "square tiles");
+  const int mt = p.mt, nt = p.nt, S = p.S;
   const int nks = a.K / 32;
   uint16_t* y = (uint16_t*)a.out;
   for (int item = (int)blockIdx.x; item < mt * nt * S; item += (int)gridDim.x) {
     const int mi = item % mt, rest = item / mt;
     const int ni = rest % nt, si = rest / nt;
-    const int m0 = mi * G::BM, n0 = ni * 128;
+    const int m0 = mi * G::BM, n0 = ni * G::BN;
     const int k_lo = (int)(((long)si * nks) / S) * 32;
     const int k_hi = (int)(((long)(si + 1) * nks) / S) * 32;
     G g;
@@ -385,17 +419,19 @@ __global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partia
       if (FOLD) {
         // the tile's last split to finish sums the splits' partials in split
         // order and writes y (no reduction launch): agent-scope fences make the
-        // partials visible across the XCDs' L2s; nothing waits
-        __shared__ int last_s;
+        // partials visible across the XCDs' L2s; nothing waits.  The flag
+        // lives in the pipeline LDS, free after run_pipe's closing barrier.
+        int* last_s = (int*)lds;
         __threadfence();
         __syncthreads();
-        if (threadIdx.x == 0) last_s = atomicAdd(&a.tile_count[mi + mt * ni], 1) == S - 1;
+        if (threadIdx.x == 0) *last_s = atomicAdd(&a.tile_count[mi + mt * ni], 1) == S - 1;
         __syncthreads();
-        if (last_s) {
+        if (*last_s) {
           __threadfence();
           const size_t per = (size_t)mt * G::BM * a.N;
-          for (int q = (int)threadIdx.x; q < G::BM * 32; q += (int)blockDim.x) {
-            const int m = m0 + q / 32, n = n0 + 4 * (q % 32);
+          constexpr int Q = G::BN / 4;  // float4 columns per tile row
+          for (int q = (int)threadIdx.x; q < G::BM * Q; q += (int)blockDim.x) {
+            const int m = m0 + q / Q, n = n0 + 4 * (q % Q);
             if (m >= mv || n >= a.N) continue;
             const size_t off = (size_t)m * a.N + n;
             f32x4_t v = *(const f32x4_t*)(partial + off);
@@ -405,19 +441,38 @@ __global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partia
                                       (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
           }
         }
-        __syncthreads();  // last_s is reused by the next item
+        __syncthreads();  // the flag's LDS is the next item's first stage
       }
     }
   }
 }
 
+using RoutedDown = Gemm2<1, 128, false, 32, 2, true, 128, kRoutedStages>;
+
+template <bool FOLD>
+__global__ __launch_bounds__(256, 2) void down_routed(DenseArgs a, float* partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RoutedDown::LDS_BYTES];
+  const int mv = uniform(rows_valid(a));
+  const DownPlan p = routed_down_plan(mv, a.N, a.K, a.routed_wide != 0);
+  if (!p.wide) down_routed_items<RoutedDown, FOLD>(a, partial, p, mv, lds);
+}
+
+// More than kRoutedBigRows routed rows: 256 x 256 tiles, eight waves.
+__global__ __launch_bounds__(64 * DownWide::NWAVES, 1) void down_routed_wide(DenseArgs a,
+                                                                             float* partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DownWide::LDS_BYTES];
+  const int mv = uniform(rows_valid(a));
+  const DownPlan p = routed_down_plan(mv, a.N, a.K, a.routed_wide != 0);
+  if (p.wide) down_routed_items<DownWide, false>(a, partial, p, mv, lds);
+}
+
 // y[rowmap[m], n] = sum over splits of the partials, in split order.
 __global__ __launch_bounds__(256) void down_routed_reduce(DenseArgs a, const float* partial) {
   const int mv = uniform(rows_valid(a));
-  const int mt = (mv + 127) / 128, nt = (a.N + 127) / 128;
-  const int S = routed_down_splits(mt, nt, a.K);
+  const DownPlan p = routed_down_plan(mv, a.N, a.K, a.routed_wide != 0);
+  const int S = p.S;
   if (S == 1) return;
-  const size_t per = (size_t)mt * 128 * a.N;  // floats per split
+  const size_t per = (size_t)p.mt * p.bm * a.N;  // floats per split
   const size_t n4 = (size_t)mv * a.N / 4;     // N % 8 == 0
   uint16_t* y = (uint16_t*)a.out;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
@@ -480,13 +535,18 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
 namespace sffn {
 
 size_t routed_partial_core_bytes(int T, int N, int K) {
-  // the largest S * mt of routed_down_splits over every possible row count
-  // (S > 1 only: one split writes y directly)
-  const int nt = (N + 127) / 128;
+  const bool wide_ok = T >= kRoutedWideTokens;  // as launch_routed_ffn decides
+  // the largest S * mt * bm of routed_down_plan over every possible row count
+  // (S > 1 only: one split writes y directly); the plan depends on the row
+  // count through mt (and the tile kind), so one count per (kind, mt) suffices
   size_t rows = 0;
-  for (int mt = 1; mt <= (T + 127) / 128; ++mt) {
-    const int S = routed_down_splits(mt, nt, K);
-    if (S > 1) rows = std::max(rows, (size_t)S * mt * 128);
+  for (int bm = 128; bm <= 256; bm += 128) {
+    for (int mt = 1; mt <= (T + bm - 1) / bm; ++mt) {
+      const int mv = std::min(T, mt * bm);
+      const DownPlan p = routed_down_plan(mv, N, K, wide_ok);
+      if (p.bm != bm || p.mt != mt) continue;
+      if (p.S > 1) rows = std::max(rows, (size_t)p.S * p.mt * p.bm);
+    }
   }
   return (rows * (size_t)N * 4 + 255) & ~(size_t)255;
 }
@@ -518,6 +578,11 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
     g.tile_count = tile_count;
     g.tile_count_n = count_n;
   }
+  // from kRoutedWideTokens tokens on, counts above kRoutedBigRows go to the
+  // eight-wave kernels launched after the four-wave ones (which then return
+  // at once for such counts; the eight-wave ones return for the others)
+  const bool wide = route_count == nullptr && T >= kRoutedWideTokens;
+  g.routed_wide = wide;
   const int tiles_max = ((T + 127) / 128) * (d_ff / 64);
   if (route_count)
     hipLaunchKernelGGL(gateup_routed<true>, dim3((unsigned)min(tiles_max, kRoutedGrid)), dim3(256),
@@ -527,9 +592,17 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
                        0, stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (wide) {
+    const long wide_tiles = (long)((T + 255) / 256) * (d_ff / 128);
+    hipLaunchKernelGGL(gateup_routed_wide, dim3((unsigned)std::min<long>(kWideGrid, wide_tiles)),
+                       dim3(64 * DenseWide::NWAVES), 0, stream, g);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // y rows = h wd
   DenseArgs d{h, wd, nullptr, nullptr, y, routed, n_routed, T, d_ff, d_model};
   d.tile_count = tile_count;
+  d.routed_wide = wide;
   // grids no larger than the most work the row count allows (few tokens: the
   // launches that find no routed row dispatch fewer workgroups)
   const long down_items = (long)((T + 127) / 128) * ((d_model + 127) / 128) * kRoutedMaxSplit;
@@ -542,6 +615,12 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
                        dim3(256), 0, stream, d, partial);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (wide) {
+    hipLaunchKernelGGL(down_routed_wide, dim3((unsigned)kWideGrid), dim3(64 * DownWide::NWAVES), 0,
+                       stream, d, partial);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (tile_count) return hipSuccess;  // the down GEMM summed its own splits
   hipLaunchKernelGGL(down_routed_reduce, dim3((unsigned)std::max<long>(1, std::min<long>(256, red_blocks))),
                      dim3(256), 0, stream, d, (const float*)partial);

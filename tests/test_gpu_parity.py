@@ -271,6 +271,18 @@ def test_many_routed_rows_use_the_large_tile_fallback():
     assert e["n_routed"] == 1200
 
 
+def test_many_routed_rows_wide_tiles_ragged():
+    # 8200 tokens (the eight-wave fallback kernels are launched from 8192 on)
+    # and nearly every row routed: 256-row tiles with a ragged last row tile
+    # (8200 = 32 x 256 + 8), a ragged last column tile of the down GEMM
+    # (2080 = 8 x 256 + 32) and K splits of the down GEMM; y on 300 rows
+    inp = wl.generate_custom(T=8200, d_model=2080, d_ff=1024, dtype="bf16", beta=1.0,
+                             seed_base=90, cap=2)
+    rows = sample_rows(8200, 300, must=np.arange(8190, 8200), seed=4)
+    e = compare(inp, 2, rows)
+    assert e["n_routed"] > 1024
+
+
 def test_zero_tokens_is_a_noop():
     sffn = _sffn()
     s = sffn.make_shape(0, 256, 512, 8, sffn.SFFN_BF16)
