@@ -434,13 +434,18 @@ struct Gemm2 {
   }
 
   // SQA: the waves with wn == 0 also accumulate the sums of squares of the A
-  // rows (sqa, per lane as in sq_a).
-  template <bool SQA = false>
-  __device__ __forceinline__ void run_pipe(uint8_t* lds, int K) {
+  // rows (sqa, per lane as in sq_a).  after_issue() runs once the first
+  // stages' loads are in flight, before the wait for them: work whose own
+  // memory latency can hide behind theirs (its LDS writes, outside the
+  // pipeline's stages, are visible to the whole workgroup after the loop's
+  // first barrier).
+  template <bool SQA = false, typename F>
+  __device__ __forceinline__ void run_pipe(uint8_t* lds, int K, F&& after_issue) {
     static_assert(STAGES >= 3, "stages");
     const int nk = K / BK;
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(lds + s * STAGE_BYTES, s * BK);
+    after_issue();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
     lds_barrier();
     Frags f0, f1;
@@ -457,6 +462,11 @@ struct Gemm2 {
       if (kt + 1 < nk) pipe_step<false, SQA>(lds, kt + 1, nk, f1, f0);
     }
     __syncthreads();
+  }
+
+  template <bool SQA = false>
+  __device__ __forceinline__ void run_pipe(uint8_t* lds, int K) {
+    run_pipe<SQA>(lds, K, [] {});
   }
 
   // Full K loop; K must be a multiple of 64.  lds must hold LDS_BYTES.

@@ -177,25 +177,35 @@ struct EpiLoop {
 // One output tile (rows m0.., columns n0..) of configuration G: main loop,
 // then the TwELL epilogue from the accumulators.  Every wave's TwELL tile lies
 // inside [0, N) (the launcher never lets a tile hang over the last column).
+// epi: LDS outside the pipeline for the tile's row norms [BM], column norms
+// [BN] and biases [BN]; they are loaded while the first stages are in flight.
 template <class G>
-__device__ __forceinline__ void gate_tile(const GateArgs& a, uint8_t* lds, int m0, int n0) {
+__device__ __forceinline__ void gate_tile(const GateArgs& a, uint8_t* lds, float* epi, int m0,
+                                          int n0) {
   const int nt = a.N / kTile;
+  float* rn_a = epi;            // [BM]
+  float* rn_b = rn_a + G::BM;   // [BN]
+  float* bias_s = rn_b + G::BN;  // [BN]
   G g;
   const uint16_t* B[1] = {(const uint16_t*)a.wg};
   g.init((const uint16_t*)a.x, (size_t)a.T, nullptr, m0, a.T, B, n0, a.N, a.K);
-  g.run_pipe(lds, a.K);
+  static_assert(G::BM <= 64 * G::NWAVES && G::BN <= 64 * G::NWAVES, "one element per thread");
+  g.run_pipe(lds, a.K, [&] {
+    const int i = (int)threadIdx.x;
+    const float xn = (i < G::BM && m0 + i < a.T) ? a.xnorm[m0 + i] : 0.f;
+    const float wn = i < G::BN ? a.wnorm[n0 + i] : 0.f;
+    const float bb = (i < G::BN && a.b) ? a.b[n0 + i] : 0.f;
+    if (i < G::BM) rn_a[i] = xn;
+    if (i < G::BN) {
+      rn_b[i] = wn;
+      bias_s[i] = bb;
+    }
+  });
 
   // epilogue LDS (the pipeline stages are free after run_pipe's barrier):
-  // row norms, column norms, one exact-stage area per wave
-  float* rn_a = (float*)lds;     // [BM]
-  float* rn_b = rn_a + G::BM;    // [BN]
-  constexpr int kExactOff = (G::BM + G::BN) * 4;
+  // one exact-stage area per wave
+  constexpr int kExactOff = 0;
   static_assert(G::LDS_BYTES >= kExactOff + G::NWAVES * kExactLdsWords * 4, "epilogue LDS fits");
-  for (int i = threadIdx.x; i < G::BM; i += blockDim.x)
-    rn_a[i] = (m0 + i < a.T) ? a.xnorm[m0 + i] : 0.f;
-  for (int i = threadIdx.x; i < G::BN; i += blockDim.x)
-    rn_b[i] = (n0 + i < a.N) ? a.wnorm[n0 + i] : 0.f;
-  __syncthreads();
   const int w = uniform((int)(threadIdx.x >> 6));
   const int wn = w / G::WAVES_M;
   AccEpi<G> c;
@@ -224,7 +234,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, uint8_t* lds, int m
 #pragma unroll
   for (int fn = 0; fn < G::FN; ++fn) {
     const int col = fn * 16 + c.li;
-    c.bias[fn] = a.b ? a.b[c.n0 + col] : 0.f;
+    c.bias[fn] = bias_s[wn * G::WN + col];
     c.nw[fn] = rn_b[wn * G::WN + col];
     c.cw = fmaxf(c.cw, a.gb.coef_xw * c.nw[fn]);
     c.cb = fmaxf(c.cb, a.gb.coef_b * fabsf(c.bias[fn]));
@@ -260,17 +270,24 @@ __global__ __launch_bounds__(64 * kGateWaves, 1) void gate_twell_bf16_v2(
   static_assert(GateGemm::BM == GateGemmWide::BM, "one row tiling");
   constexpr size_t kLds = GateGemm::LDS_BYTES > GateGemmWide::LDS_BYTES ? GateGemm::LDS_BYTES
                                                                          : GateGemmWide::LDS_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  // one LDS object: the pipeline stages, then the epilogue's norms and biases
+  // (a second __shared__ array would cost the compiler its proof that the
+  // fragment reads do not alias the buffer loads in flight)
+  constexpr size_t kEpiFloats = GateGemmWide::BM + 2 * GateGemmWide::BN;
+  static_assert(GateGemmWide::BN >= GateGemm::BN, "epilogue area sized by the wide tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds + kEpiFloats * 4];
+  float* epi = (float*)(lds + kLds);
   const int mt = (a.T + GateGemm::BM - 1) / GateGemm::BM;
   const int n_wide = mt * wide_nt;
   const int bid = (int)blockIdx.x;
   int mi, ni;
   if (bid < n_wide) {
     tile_of(bid, mt, wide_nt, &mi, &ni);
-    gate_tile<GateGemmWide>(a, lds, mi * GateGemmWide::BM, ni * GateGemmWide::BN);
+    gate_tile<GateGemmWide>(a, lds, epi, mi * GateGemmWide::BM, ni * GateGemmWide::BN);
   } else {
     tile_of(bid - n_wide, mt, narrow_nt, &mi, &ni);
-    gate_tile<GateGemm>(a, lds, mi * GateGemm::BM, wide_nt * GateGemmWide::BN + ni * GateGemm::BN);
+    gate_tile<GateGemm>(a, lds, epi, mi * GateGemm::BM,
+                        wide_nt * GateGemmWide::BN + ni * GateGemm::BN);
   }
 }
 
