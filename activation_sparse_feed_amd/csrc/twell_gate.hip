@@ -147,6 +147,10 @@ __device__ __forceinline__ void epi_group(const GateArgs& a, G& g, AccEpi<G>& c)
   for (int fn = 0; fn < FN; ++fn) {
     const bool act = v[fn] > 0.f;
     const uint64_t m = __ballot(act);
+    // at low density most 16-column groups of the four rows hold no active
+    // entry: a uniform branch skips their slot arithmetic (the epilogue is
+    // bound by VALU issue, all eight waves reaching it together)
+    if (m == 0) continue;
     const uint32_t seg = (uint32_t)(m >> (16 * c.gi)) & 0xffffu;
     const int slot = running + __builtin_popcount(seg & c.below);
     if (act && valid && slot < a.cap) {
