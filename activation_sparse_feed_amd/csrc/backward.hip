@@ -40,6 +40,8 @@
 // per-entry gradients itself while summing the weight gradients, and bwd_gx
 // then gathers the wg_t and wu_t rows for gx.
 // Every sum runs in a fixed order, so the gradients are deterministic.
+#include <algorithm>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -76,7 +78,14 @@ struct BwdArgs {
   int T, D, N, nt, cap;
   float l1g;               // lambda / T, added to gz of every active entry
   int R;                   // routed rows the workspace holds (<= T)
+  int routed_dense;        // the MFMA kernels of backward_routed.hip were launched too
 };
+
+// The routed rows go to the MFMA kernels (backward_routed.hip) instead of the
+// per-entry ones below: launched, and enough routed rows on the device.
+__device__ __forceinline__ bool routed_on_tiles(const BwdArgs& a, int nr) {
+  return a.routed_dense && nr >= kDenseRoutedRows;
+}
 
 // Position of row t in the ascending routed list (binary search), or -1.
 __device__ __forceinline__ int routed_index(const int32_t* routed, int n, int t) {
@@ -299,6 +308,7 @@ constexpr int kRoutedWaves = 4096;
 __global__ __launch_bounds__(1024) void bwd_routed_items(BwdArgs a, int32_t* item_start) {
   __shared__ int wsum[16];
   const int nr = uniform(min(*a.n_routed, a.R));
+  if (routed_on_tiles(a, nr)) return;
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
   // all routed entries, then the part size
   int e = 0;
@@ -343,6 +353,7 @@ template <int P>
 __global__ __launch_bounds__(256) void bwd_routed(BwdArgs a, const int32_t* item_start,
                                                   float* part) {
   const int nr = uniform(min(*a.n_routed, a.R));
+  if (routed_on_tiles(a, nr)) return;
   const int items = uniform(item_start[nr]);
   const int lane = lane_id();
   for (int it = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); it < items; it += kRoutedWaves) {
@@ -385,6 +396,7 @@ __global__ __launch_bounds__(256) void bwd_routed(BwdArgs a, const int32_t* item
 __global__ __launch_bounds__(256) void bwd_routed_gx(BwdArgs a, const int32_t* item_start,
                                                      const float* part) {
   const int nr = uniform(min(*a.n_routed, a.R));
+  if (routed_on_tiles(a, nr)) return;
   for (int r = (int)blockIdx.y; r < nr; r += (int)gridDim.y) {
     const int t = min(max(a.routed[r], 0), a.T - 1);
     const int i0 = item_start[r], i1 = item_start[r + 1];
@@ -617,9 +629,11 @@ __global__ __launch_bounds__(256) void bwd_cols(BwdArgs a, const int* col_ptr, c
     }
     col_accumulate_batch<PC>(a, tb, d0, cb, ag, au, ad, gbs);
   }
-  // routed rows: their complete lists, one binary search per row
+  // routed rows: their complete lists, one binary search per row (unless
+  // their products run on MFMA tiles and are added afterwards)
   const int k = j / kBTile;
-  const int nr = uniform(min(*a.n_routed, a.R));
+  const int nr0 = uniform(min(*a.n_routed, a.R));
+  const int nr = routed_on_tiles(a, nr0) ? 0 : nr0;
   for (int r0 = 0; r0 < nr; r0 += kWave) {
     const int r = r0 + lane;
     int match = -1, tr = 0;
@@ -752,9 +766,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       gbs += gz;
     }
   }
-  // routed rows: their entries' gradients come from bwd_routed
+  // routed rows: their entries' gradients come from bwd_routed (unless their
+  // products run on MFMA tiles and are added afterwards)
   const int k = j / kBTile;
-  const int nr = uniform(min(*a.n_routed, a.R));
+  const int nr0 = uniform(min(*a.n_routed, a.R));
+  const int nr = routed_on_tiles(a, nr0) ? 0 : nr0;
   for (int r0 = 0; r0 < nr; r0 += kWave) {
     const int r = r0 + lane;
     int match = -1, tr = 0;
@@ -868,9 +884,17 @@ bool backward_supported(int dtype, int d_model) {
 // copies and the per-entry gradients of the TwELL entries.
 // Routed-row buffers are sized for R rows (the routed rows the caller allows
 // for), the others for all T rows.
+// The first region holds the routed rows' z, then their per-entry gradients,
+// or (MFMA path) the dense buffers of backward_routed.hip.
+size_t routed_region_bytes(int T, int N, int D, int R) {
+  size_t n = al256((size_t)R * N * 16);
+  if (routed_dense_launch(T, R)) n = std::max(n, routed_dense_workspace_bytes(N, D, R));
+  return n;
+}
+
 size_t backward_workspace_bytes(int T, int N, int D, int cap, int R) {
   const size_t nt = (size_t)N / kBTile;
-  return al256((size_t)R * N * 16) + 2 * al256((size_t)R * N * 2) + al256((size_t)R * 2) +
+  return routed_region_bytes(T, N, D, R) + 2 * al256((size_t)R * N * 2) + al256((size_t)R * 2) +
          al256((size_t)R * nt * 4) + al256(nt * T * 2) + al256(nt * T * cap * 2) +
          al256((size_t)T * nt * cap * 16) + al256(((size_t)R + 2) * 4) +
          al256((size_t)R * kRoutedSplit * D * 4) +
@@ -901,7 +925,9 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   char* p = (char*)ws;
   float* z_r = (float*)p;          // routed rows' z, then (same bytes) their entry gradients
   f32x4_t* co_r = (f32x4_t*)p;
-  p += al256((size_t)R * N * 16);
+  void* dense_ws = p;              // or the MFMA path's buffers
+  const bool dense = routed_dense_launch(T, R);
+  p += routed_region_bytes(T, N, D, R);
   uint16_t* eidx = (uint16_t*)p;
   p += al256((size_t)R * N * 2);
   uint16_t* eval = (uint16_t*)p;
@@ -944,11 +970,17 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   BwdArgs a{(const uint16_t*)x, (const uint16_t*)wg_t, (const uint16_t*)wu_t,
             (const uint16_t*)wd, (const uint16_t*)gy, count, idx, (const uint16_t*)val,
             routed, n_routed, ecount, eidx, eval, eoff, count_t, idx_t, co, co_r,
-            (uint16_t*)gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, cap, l1g, R};
+            (uint16_t*)gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, cap, l1g, R, dense ? 1 : 0};
   const dim3 rows_grid((unsigned)((T + 3) / 4));
   hipLaunchKernelGGL(bwd_prep, rows_grid, dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dense) {  // the routed rows' u, ga, per-entry gradients and gx on MFMA tiles
+    e = launch_backward_routed_dense(x, gy, wg_t, wu_t, wd, routed, n_routed, ecount, eidx, eval,
+                                     gx, gwg_t, gwu_t, gwd, gb, T, D, N, R, l1g, dense_ws, 0,
+                                     stream);
+    if (e != hipSuccess) return e;
+  }
   // the fused order keeps TwELL positions in 31 bits and a row's group of
   // tiles inside bwd_gx's list
   const bool fused = D <= 2048 && T > kSplitMaxT && cap <= kGxList &&
@@ -1010,6 +1042,12 @@ hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, co
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dense) {  // the routed rows' weight gradients and gb, added to the sums above
+    e = launch_backward_routed_dense(x, gy, wg_t, wu_t, wd, routed, n_routed, ecount, eidx, eval,
+                                     gx, gwg_t, gwu_t, gwd, gb, T, D, N, R, l1g, dense_ws, 1,
+                                     stream);
+    if (e != hipSuccess) return e;
+  }
   if (R < T) hipLaunchKernelGGL(bwd_routed_overflow, dim3(1), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

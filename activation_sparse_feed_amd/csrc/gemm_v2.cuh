@@ -126,9 +126,11 @@ struct Gemm2 {
   // K is the length of the K loop.  lda (0: K) is the row stride in elements
   // of A and of a K-contiguous B; a_skip is the number of elements of each A
   // row before A (a split of a longer K range starts inside the rows).
+  // zero: clear the accumulators (false: a further K range adds to them).
   __device__ __forceinline__ void init(const uint16_t* A, size_t a_rows_total, const int* rowmap,
                                        int m0, int m_valid, const uint16_t* const* B, int n0,
-                                       int N, int K, int lda = 0, int a_skip = 0) {
+                                       int N, int K, int lda = 0, int a_skip = 0,
+                                       bool zero = true) {
     const int lane = lane_id();
     const int w = uniform((int)(threadIdx.x >> 6));
     const int ldk = lda > 0 ? lda : K;
@@ -174,6 +176,7 @@ struct Gemm2 {
       rw = blk0 * RPB < BM ? ra : ((NB == 1 || (blk0 * RPB - BM) < BNW) ? rb[0] : rb[NB - 1]);
       kstride = (B_KN && blk0 * RPB >= BM) ? b_ld : 2;
     }
+    if (!zero) return;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll

@@ -62,6 +62,27 @@ hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, c
 // backward_workspace_bytes().
 bool backward_supported(int dtype, int d_model);
 size_t backward_workspace_bytes(int T, int N, int D, int cap, int R);
+
+// The routed rows' backward on MFMA tiles (backward_routed.hip): launched when
+// at least kDenseRoutedTokens tokens and room for kDenseRoutedRows routed
+// rows; it takes the routed rows when the device-side count reaches
+// kDenseRoutedRows (the per-entry kernels take them otherwise).
+constexpr int kDenseRoutedRows = 1024;
+constexpr int kDenseRoutedTokens = 8192;
+inline bool routed_dense_launch(int T, int R) {
+  return T >= kDenseRoutedTokens && R >= kDenseRoutedRows;
+}
+size_t routed_dense_workspace_bytes(int N, int D, int R);
+// stage 0: gathers, u and ga, per-entry gradients, gx of the routed rows
+// (after the routed rows' complete lists exist); stage 1: the weight
+// gradients and gb, added to what the column walk wrote (after it).
+hipError_t launch_backward_routed_dense(const void* x, const void* gy, const void* wg_t,
+                                        const void* wu_t, const void* wd, const int32_t* routed,
+                                        const int32_t* n_routed, const uint16_t* ecount,
+                                        const uint16_t* eidx, const void* eval, void* gx,
+                                        float* gwg_t, float* gwu_t, float* gwd, float* gb,
+                                        int T, int D, int N, int R, float l1g, void* ws,
+                                        int stage, hipStream_t stream);
 hipError_t launch_backward(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
                            const void* wd, const float* xnorm, const float* wnorm,
                            const uint16_t* count, const uint16_t* idx, const void* val,

@@ -111,11 +111,43 @@ def test_backward_decode_full_size():
     check(wl.generate(w), w.cap, dense=True)
 
 
+def test_backward_prefill_full_size():
+    # 4096 tokens, 2048 -> 5632, no routed rows: the fused column order at full size;
+    # the weight gradients and gb over every column, gx on 256 rows
+    w = wl.WORKLOADS["prefill_1pct"]
+    e = check(wl.generate(w), w.cap, dense=False, rows=sample_rows(w.T, 256, seed=5))
+    assert e["n_routed"] == 0
+
+
 def test_backward_hybrid_mix_full_size():
     w = wl.WORKLOADS["hybrid_mix"]
     inp = wl.generate(w)
     e = check(inp, w.cap, dense=False, rows=sample_rows(w.T, 256, seed=4))
     assert e["n_routed"] > 60
+
+
+@pytest.mark.parametrize("T,d_model,d_ff,beta,cap,lam", [
+    (8200, 1024, 1024, 1.0, 2, 0.0),   # fused column order, ragged row tiles
+    (8192, 2560, 512, 1.0, 2, 0.5),    # row and column walk order, the L1 term
+])
+def test_backward_routed_rows_on_tiles(T, d_model, d_ff, beta, cap, lam):
+    """More than 1024 routed rows with at least 8192 tokens: the routed rows'
+    products run on MFMA tiles (per-entry gradients rounded to bf16 before the
+    weight-gradient and gx products) and are added to the other rows' sums."""
+    inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype="bf16", beta=beta,
+                             seed_base=110 + d_model, cap=cap)
+    e = check(inp, cap, dense=False, rows=sample_rows(T, 300, must=np.arange(T - 9, T), seed=8),
+              lam=lam)
+    assert e["n_routed"] > 1024
+
+
+def test_backward_few_routed_rows_with_tile_kernels_launched():
+    # at least 8192 tokens but few routed rows: the per-entry kernels take them
+    # (the MFMA kernels are launched and return at once)
+    inp = wl.generate_custom(T=8192, d_model=512, d_ff=512, dtype="bf16", beta=2.3,
+                             seed_base=120, cap=4)
+    e = check(inp, 4, dense=False, rows=sample_rows(8192, 300, seed=9))
+    assert 0 < e["n_routed"] < 1024
 
 
 def test_backward_rejects_unsupported_width():
