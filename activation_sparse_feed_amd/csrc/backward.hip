@@ -98,6 +98,18 @@ __device__ __forceinline__ int routed_index(const int32_t* routed, int n, int t)
   return (lo < n && routed[lo] == t) ? lo : -1;
 }
 
+// Eight float32 weight-gradient values of a lane: stored, or added to what is
+// there (the routed rows' part, written before by the MFMA kernels).
+__device__ __forceinline__ void store_w8(float* p, const float* v, bool add) {
+  f32x4_t lo = f32x4_t{v[0], v[1], v[2], v[3]}, hi = f32x4_t{v[4], v[5], v[6], v[7]};
+  if (add) {
+    lo = *(const f32x4_t*)p + lo;
+    hi = *(const f32x4_t*)(p + 4) + hi;
+  }
+  *(f32x4_t*)p = lo;
+  *(f32x4_t*)(p + 4) = hi;
+}
+
 // A row is routed when some tile count exceeds the capacity.
 __device__ __forceinline__ bool row_is_routed(const BwdArgs& a, int t) {
   bool over = false;
@@ -662,14 +674,12 @@ __global__ __launch_bounds__(256) void bwd_cols(BwdArgs a, const int* col_ptr, c
     }
   }
   const size_t wo = (size_t)j * a.D + d0 + (size_t)lane * 8;
+  const bool add = routed_on_tiles(a, nr0);  // the routed rows' sums are there already
 #pragma unroll
   for (int c = 0; c < PC; ++c) {
-    *(f32x4_t*)(a.gwg + wo + c * 512) = f32x4_t{ag[c][0], ag[c][1], ag[c][2], ag[c][3]};
-    *(f32x4_t*)(a.gwg + wo + c * 512 + 4) = f32x4_t{ag[c][4], ag[c][5], ag[c][6], ag[c][7]};
-    *(f32x4_t*)(a.gwu + wo + c * 512) = f32x4_t{au[c][0], au[c][1], au[c][2], au[c][3]};
-    *(f32x4_t*)(a.gwu + wo + c * 512 + 4) = f32x4_t{au[c][4], au[c][5], au[c][6], au[c][7]};
-    *(f32x4_t*)(a.gwd + wo + c * 512) = f32x4_t{ad[c][0], ad[c][1], ad[c][2], ad[c][3]};
-    *(f32x4_t*)(a.gwd + wo + c * 512 + 4) = f32x4_t{ad[c][4], ad[c][5], ad[c][6], ad[c][7]};
+    store_w8(a.gwg + wo + c * 512, ag[c], add);
+    store_w8(a.gwu + wo + c * 512, au[c], add);
+    store_w8(a.gwd + wo + c * 512, ad[c], add);
   }
   if (a.gb && dc == 0 && lane == 0) a.gb[j] = gbs;
 }
@@ -798,14 +808,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
   }
   const size_t wo = (size_t)j * a.D + (size_t)lane * 8;
+  const bool add = routed_on_tiles(a, nr0);  // the routed rows' sums are there already
 #pragma unroll
   for (int c = 0; c < P; ++c) {
-    *(f32x4_t*)(a.gwg + wo + c * 512) = f32x4_t{ag[c][0], ag[c][1], ag[c][2], ag[c][3]};
-    *(f32x4_t*)(a.gwg + wo + c * 512 + 4) = f32x4_t{ag[c][4], ag[c][5], ag[c][6], ag[c][7]};
-    *(f32x4_t*)(a.gwu + wo + c * 512) = f32x4_t{au[c][0], au[c][1], au[c][2], au[c][3]};
-    *(f32x4_t*)(a.gwu + wo + c * 512 + 4) = f32x4_t{au[c][4], au[c][5], au[c][6], au[c][7]};
-    *(f32x4_t*)(a.gwd + wo + c * 512) = f32x4_t{ad[c][0], ad[c][1], ad[c][2], ad[c][3]};
-    *(f32x4_t*)(a.gwd + wo + c * 512 + 4) = f32x4_t{ad[c][4], ad[c][5], ad[c][6], ad[c][7]};
+    store_w8(a.gwg + wo + c * 512, ag[c], add);
+    store_w8(a.gwu + wo + c * 512, au[c], add);
+    store_w8(a.gwd + wo + c * 512, ad[c], add);
   }
   if (a.gb && lane == 0) a.gb[j] = gbs;
 }

@@ -12,16 +12,20 @@
 //             row's list into a dense array hR [r, j]: the bf16 h of an active
 //             entry, -0 (sign bit alone) for an inactive one (an active h is
 //             never negative, so the sign bit marks activity exactly);
-//   rd_ug     per 128 x 128 tile, u = xR wu_t^T and ga = gyR wd^T (two K loops
-//             over d_model), then per entry gz = ga u + lambda/T, gu = ga h,
-//             a = h u on the active entries (0 elsewhere), written as bf16
-//             [r, j] (for gx) and transposed [j, r] (for the weight
-//             gradients), and each tile's column sums of gz;
+//   rd_uga    per 256 x 128 tile, u = xR wu_t^T and ga = gyR wd^T (two K
+//             loops over d_model, two accumulators), then per entry
+//             gz = ga u + lambda/T, gu = ga h, a = h u on the active entries
+//             (0 elsewhere), written as bf16 [r, j] (for gx) and transposed
+//             [j, r] (for the weight gradients), and each tile's column sums
+//             of gz;
 //   rd_gx     gx_r = gz wg_t + gu wu_t (K over d_ff, both products in one
 //             accumulator), written to the routed rows of gx;
-//   rd_gw     gwg_t += gz^T xR, gwu_t += gu^T xR, gwd += a^T gyR (K over the
-//             routed rows), added to the row walk's sums of the other rows;
-//   rd_gb     gb += the tiles' gz column sums, in tile order.
+//   rd_gw     gwg_t = gz^T xR, gwu_t = gu^T xR, gwd = a^T gyR (K over the
+//             routed rows); the column walk of backward.hip then adds the
+//             other rows' sums to these;
+//   rd_gb     gb += the tiles' gz column sums, in tile order (after the
+//             column walk, which writes gb).
+// The GEMMs run eight waves per workgroup (two per SIMD).
 // The per-entry gradients are rounded to bf16 before the three products (the
 // rounding a dense bf16 backward applies too).  Every sum runs in a fixed
 // order: deterministic.  The kernels run only when the routed count reaches
@@ -54,13 +58,13 @@ struct RdArgs {
   uint16_t* gzT;           // [N, ldr]
   uint16_t* guT;           // [N, ldr]
   uint16_t* aT;            // [N, ldr]
-  float* gbp;              // [ldr / 128, N]
+  float* gbp;              // [ldr / 256, N]
   uint16_t* gx;            // [T, D]
   float* gwg;              // [N, D]
   float* gwu;
   float* gwd;
   float* gb;               // [N] or null
-  int T, D, N, R, ldr;     // ldr: R rounded up to a multiple of 128
+  int T, D, N, R, ldr;     // ldr: R rounded up to a multiple of 256
   float l1g;
 };
 
@@ -108,21 +112,23 @@ __global__ __launch_bounds__(256) void rd_prep(RdArgs a) {
   }
 }
 
-// u and ga of one 128 x 128 tile: four waves as 2 x 2 of 64 x 64.
-using RdTile = Gemm2<1, 128, false, 32, 2, false, 128>;
+// 256 x 256 tiles of eight waves as 4 x 2 of 64 x 128, B staged K-major (gx,
+// the weight gradients).
+using RdKN = Gemm2<1, 256, false, 32, 2, true, 256, 4, 8, true>;
 
-__global__ __launch_bounds__(256, 2) void rd_ug(RdArgs a) {
-  using G = RdTile;
-  // one LDS object (a second one costs the fragment reads their no-alias
-  // proof); the column-sum exchange reuses the pipeline's bytes afterwards
+
+// u and ga of one 256 x 128 tile, eight waves as 4 x 2 of 64 x 64, both
+// accumulators in registers.
+using RdUG = Gemm2<1, 128, false, 32, 2, false, 256, 4, 8, true>;
+
+__global__ __launch_bounds__(64 * RdUG::NWAVES, 1) void rd_uga(RdArgs a) {
+  using G = RdUG;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
-  float(*red)[128] = (float(*)[128])lds;
   const int nr = routed_rows(a);
   if (!dense_on(nr)) return;
-  const int mt = (nr + 127) / 128, nt = a.N / 128;
-  const int mi = (int)blockIdx.x % ((a.R + 127) / 128), ni = (int)blockIdx.x / ((a.R + 127) / 128);
-  if (mi >= mt || ni >= nt) return;
-  const int m0 = mi * 128, n0 = ni * 128;
+  const int mi = (int)blockIdx.x % (a.ldr / 256), ni = (int)blockIdx.x / (a.ldr / 256);
+  const int m0 = mi * 256, n0 = ni * 128;
+  if (m0 >= nr || n0 >= a.N) return;
   G gu_, gg_;
   {
     const uint16_t* B[1] = {a.wu};
@@ -134,37 +140,47 @@ __global__ __launch_bounds__(256, 2) void rd_ug(RdArgs a) {
     gg_.init(a.gyR, (size_t)a.ldr, nullptr, m0, nr, B, n0, a.N, a.D);
     gg_.run_pipe(lds, a.D);
   }
+  const uint16_t* __restrict__ hR = a.hR;
+  uint16_t* __restrict__ gzo = a.gz;
+  uint16_t* __restrict__ guo = a.gu;
+  uint16_t* __restrict__ gzT = a.gzT;
+  uint16_t* __restrict__ guT = a.guT;
+  uint16_t* __restrict__ aT = a.aT;
   const int lane = lane_id();
   const int w = uniform((int)(threadIdx.x >> 6));
   const int wm = w % G::WAVES_M, wn = w / G::WAVES_M;
+  const int jl = wn * G::WN + (lane & 15);  // the lane's first column in the tile
   float colsum[G::FN];
 #pragma unroll
   for (int fn = 0; fn < G::FN; ++fn) colsum[fn] = 0.f;
 #pragma unroll
-  for (int fm = 0; fm < G::FM; ++fm)
+  for (int fm = 0; fm < G::FM; ++fm) {
+    const int rb = m0 + wm * G::WM + fm * 16 + 4 * (lane >> 4);  // rows rb .. rb + 3
+    // the block's h values first, all loads in flight together
+    uint16_t hb[G::FN][4];
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hb[fn][i] = rb + i < nr ? hR[(size_t)(rb + i) * a.N + n0 + jl + fn * 16] : (uint16_t)0x8000u;
 #pragma unroll
     for (int fn = 0; fn < G::FN; ++fn) {
-      const int j = n0 + wn * G::WN + fn * 16 + (lane & 15);
-      const int rb = m0 + wm * G::WM + fm * 16 + 4 * (lane >> 4);  // rows rb .. rb + 3
+      const int j = n0 + jl + fn * 16;
       uint32_t pz[2], pu[2], pa[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = rb + i;
         float gz = 0.f, gu = 0.f, av = 0.f;
-        if (r < nr) {
-          const uint16_t hb = a.hR[(size_t)r * a.N + j];
-          if (!(hb & 0x8000u)) {
-            const float h = bf16_to_f32(hb);
-            const float u = gu_.acc[0][fm][fn][i], ga = gg_.acc[0][fm][fn][i];
-            gz = ga * u + a.l1g;
-            gu = ga * h;
-            av = h * u;
-          }
+        if (!(hb[fn][i] & 0x8000u)) {
+          const float h = bf16_to_f32(hb[fn][i]);
+          const float u = gu_.acc[0][fm][fn][i], ga = gg_.acc[0][fm][fn][i];
+          gz = ga * u + a.l1g;
+          gu = ga * h;
+          av = h * u;
         }
         colsum[fn] += gz;
         const uint16_t bz = f32_to_bf16(gz), bu = f32_to_bf16(gu), ba = f32_to_bf16(av);
-        a.gz[(size_t)r * a.N + j] = bz;
-        a.gu[(size_t)r * a.N + j] = bu;
+        gzo[(size_t)(rb + i) * a.N + j] = bz;
+        guo[(size_t)(rb + i) * a.N + j] = bu;
         if (i & 1) {
           pz[i >> 1] |= (uint32_t)bz << 16;
           pu[i >> 1] |= (uint32_t)bu << 16;
@@ -177,12 +193,15 @@ __global__ __launch_bounds__(256, 2) void rd_ug(RdArgs a) {
       }
       // transposed: rows rb .. rb + 3 of column j are 8 contiguous bytes
       const size_t to = (size_t)j * a.ldr + rb;
-      *(uint2*)(a.gzT + to) = make_uint2(pz[0], pz[1]);
-      *(uint2*)(a.guT + to) = make_uint2(pu[0], pu[1]);
-      *(uint2*)(a.aT + to) = make_uint2(pa[0], pa[1]);
+      *(uint2*)(gzT + to) = make_uint2(pz[0], pz[1]);
+      *(uint2*)(guT + to) = make_uint2(pu[0], pu[1]);
+      *(uint2*)(aT + to) = make_uint2(pa[0], pa[1]);
     }
+  }
   // the tile's column sums of gz: lanes 16 apart hold other rows of the same
-  // column, then the two waves of a column half add in wave order
+  // column, then the four waves of a column half add in wave order (in the
+  // pipeline's LDS, free after its closing barrier: one LDS object)
+  float(*red)[128] = (float(*)[128])lds;
 #pragma unroll
   for (int fn = 0; fn < G::FN; ++fn) {
     float s = colsum[fn];
@@ -191,24 +210,21 @@ __global__ __launch_bounds__(256, 2) void rd_ug(RdArgs a) {
     if (lane < 16) red[wm][wn * G::WN + fn * 16 + lane] = s;
   }
   __syncthreads();
-  if ((int)threadIdx.x < 128)
-    a.gbp[(size_t)mi * a.N + n0 + threadIdx.x] = red[0][threadIdx.x] + red[1][threadIdx.x];
+  const int c = (int)threadIdx.x;
+  if (c < 128)
+    a.gbp[(size_t)mi * a.N + n0 + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
 }
 
-// gx of the routed rows: gz wg_t + gu wu_t, 128 x 128 tiles with the weights
-// staged K-major (transposing LDS reads), both products in one accumulator.
-using RdGx = Gemm2<1, 128, false, 32, 2, true, 128>;
-
-__global__ __launch_bounds__(256, 2) void rd_gx(RdArgs a) {
-  using G = RdGx;
+// gx of the routed rows: gz wg_t + gu wu_t, the weights staged K-major
+// (transposing LDS reads), both products in one accumulator.
+__global__ __launch_bounds__(64 * RdKN::NWAVES, 1) void rd_gx(RdArgs a) {
+  using G = RdKN;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   const int nr = routed_rows(a);
   if (!dense_on(nr)) return;
-  const int mt = (nr + 127) / 128, dt = (a.D + 127) / 128;
-  const int mtm = (a.R + 127) / 128;
-  const int mi = (int)blockIdx.x % mtm, di = (int)blockIdx.x / mtm;
-  if (mi >= mt || di >= dt) return;
-  const int m0 = mi * 128, n0 = di * 128;
+  const int mi = (int)blockIdx.x % (a.ldr / 256), di = (int)blockIdx.x / (a.ldr / 256);
+  const int m0 = mi * 256, n0 = di * 256;
+  if (m0 >= nr || n0 >= a.D) return;
   G g;
   {
     const uint16_t* B[1] = {a.wg};
@@ -226,37 +242,33 @@ __global__ __launch_bounds__(256, 2) void rd_gx(RdArgs a) {
   });
 }
 
-// The weight gradients' routed part: out[j, :] += A[j, :] B, K over the
-// routed rows (padded with zeros to a multiple of 32); 256 x 256 tiles of
-// eight waves, B (xR or gyR, [rows, D]) staged K-major.  blockIdx.x: product
-// (gwg_t, gwu_t, gwd) outermost, then column tiles, then row tiles.
-using RdGw = Gemm2<1, 256, false, 32, 2, true, 256, 4, 8, true>;
-
+// The weight gradients' routed part: out[j, :] = A[j, :] B, K over the
+// routed rows (padded with zeros to a multiple of 32), B (xR or gyR,
+// [rows, D]) staged K-major.  blockIdx.x: product (gwg_t, gwu_t, gwd)
+// outermost, then column tiles, then row tiles.
 __device__ __forceinline__ void gw_tile(const RdArgs& a, const uint16_t* A, const uint16_t* Bm,
                                         float* out, int m0, int n0, int kp, uint8_t* lds) {
-  using G = RdGw;
+  using G = RdKN;
   G g;
   const uint16_t* B[1] = {Bm};
   g.init(A, (size_t)a.N, nullptr, m0, a.N, B, n0, a.D, kp, a.ldr);
   g.run_pipe(lds, kp);
   g.for_each([&](int, int row, int col, float v) {
     const int j = m0 + row, d = n0 + col;
-    if (j < a.N && d < a.D) {
-      float* o = out + (size_t)j * a.D + d;
-      *o = *o + v;
-    }
+    if (j < a.N && d < a.D) out[(size_t)j * a.D + d] = v;
   });
 }
 
-__global__ __launch_bounds__(64 * RdGw::NWAVES, 1) void rd_gw(RdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[RdGw::LDS_BYTES];
+__global__ __launch_bounds__(64 * RdKN::NWAVES, 1) void rd_gw(RdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[RdKN::LDS_BYTES];
   const int nr = routed_rows(a);
   if (!dense_on(nr)) return;
   const int kp = (nr + 31) & ~31;
   const int mt = (a.N + 255) / 256, dt = (a.D + 255) / 256;
   const int prod = (int)blockIdx.x / (mt * dt);
-  const int rest = (int)blockIdx.x % (mt * dt);
-  const int m0 = (rest % mt) * 256, n0 = (rest / mt) * 256;
+  int mi, di;
+  tile_of((int)blockIdx.x % (mt * dt), mt, dt, &mi, &di);
+  const int m0 = mi * 256, n0 = di * 256;
   // one call per product, each with its operands straight from the kernel
   // arguments, so that the buffer descriptors stay in scalar registers
   if (prod == 0) gw_tile(a, a.gzT, a.xR, a.gwg, m0, n0, kp, lds);
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(256) void rd_gb(RdArgs a) {
   if (!dense_on(nr) || a.gb == nullptr) return;
   const int j = (int)(blockIdx.x * 256 + threadIdx.x);
   if (j >= a.N) return;
-  const int mt = (nr + 127) / 128;
+  const int mt = (nr + 255) / 256;
   float s = 0.f;
   for (int mi = 0; mi < mt; ++mi) s += a.gbp[(size_t)mi * a.N + j];
   a.gb[j] += s;
@@ -281,9 +293,9 @@ size_t al256r(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t routed_dense_workspace_bytes(int N, int D, int R) {
-  const size_t ldr = ((size_t)R + 127) & ~(size_t)127;
+  const size_t ldr = ((size_t)R + 255) & ~(size_t)255;
   return 2 * al256r(ldr * D * 2) + al256r((size_t)R * N * 2) + 2 * al256r(ldr * N * 2) +
-         3 * al256r((size_t)N * ldr * 2) + al256r(ldr / 128 * N * 4);
+         3 * al256r((size_t)N * ldr * 2) + al256r(ldr / 256 * N * 4);
 }
 
 hipError_t launch_backward_routed_dense(const void* x, const void* gy, const void* wg_t,
@@ -294,7 +306,7 @@ hipError_t launch_backward_routed_dense(const void* x, const void* gy, const voi
                                         int T, int D, int N, int R, float l1g, void* ws,
                                         int stage, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
-  const int ldr = (R + 127) & ~127;
+  const int ldr = (R + 255) & ~255;
   char* p = (char*)ws;
   RdArgs a{};
   a.x = (const uint16_t*)x;
@@ -335,18 +347,19 @@ hipError_t launch_backward_routed_dense(const void* x, const void* gy, const voi
   a.R = R;
   a.ldr = ldr;
   a.l1g = l1g;
+  const unsigned mtw = (unsigned)(ldr / 256);
   if (stage == 0) {
-    // the products that need only the forward's lists: before the row walk
+    // the routed rows' products, before the column walk (which adds the
+    // other rows' weight-gradient sums to rd_gw's)
+    const dim3 blk(64 * RdKN::NWAVES);
     hipLaunchKernelGGL(rd_prep, dim3((unsigned)(((R + 31) / 32) * 32)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(rd_ug, dim3((unsigned)(((R + 127) / 128) * (N / 128))), dim3(256), 0, stream,
-                       a);
-    hipLaunchKernelGGL(rd_gx, dim3((unsigned)(((R + 127) / 128) * ((D + 127) / 128))), dim3(256), 0,
+    hipLaunchKernelGGL(rd_uga, dim3(mtw * (unsigned)(N / 128)), blk, 0, stream, a);
+    hipLaunchKernelGGL(rd_gx, dim3(mtw * (unsigned)((D + 255) / 256)), blk, 0, stream, a);
+    hipLaunchKernelGGL(rd_gw, dim3((unsigned)(3 * ((N + 255) / 256) * ((D + 255) / 256))), blk, 0,
                        stream, a);
     return hipGetLastError();
   }
-  // stage 1: added to the column walk's sums, after it
-  hipLaunchKernelGGL(rd_gw, dim3((unsigned)(3 * ((N + 255) / 256) * ((D + 255) / 256))),
-                     dim3(64 * RdGw::NWAVES), 0, stream, a);
+  // stage 1: gb, added to what the column walk wrote (after it)
   hipLaunchKernelGGL(rd_gb, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
