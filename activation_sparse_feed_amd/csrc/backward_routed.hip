@@ -55,9 +55,9 @@ struct RdArgs {
   uint16_t* hR;            // [R, N]
   uint16_t* gz;            // [ldr, N]
   uint16_t* gu;            // [ldr, N]
-  uint16_t* gzT;           // [N, ldr]
-  uint16_t* guT;           // [N, ldr]
-  uint16_t* aT;            // [N, ldr]
+  uint16_t* gzT;           // [N, ldt]
+  uint16_t* guT;           // [N, ldt]
+  uint16_t* aT;            // [N, ldt]
   float* gbp;              // [ldr / 256, N]
   uint16_t* gx;            // [T, D]
   float* gwg;              // [N, D]
@@ -65,6 +65,7 @@ struct RdArgs {
   float* gwd;
   float* gb;               // [N] or null
   int T, D, N, R, ldr;     // ldr: R rounded up to a multiple of 256
+  int ldt;                 // row stride of the transposed arrays, see transposed_stride
   float l1g;
 };
 
@@ -112,6 +113,20 @@ __global__ __launch_bounds__(256) void rd_prep(RdArgs a) {
   }
 }
 
+// Tile (mi, ni) of workgroup blockIdx.x over the row tiles of the actual
+// routed count (the grid is sized for the largest count; the workgroups past
+// the actual tiles return), through the XCD-aware map.  Numbering the tiles
+// by the actual count keeps the working ones first and spread over the XCDs:
+// numbered by the largest count (a multiple of 8 row tiles when the buffers
+// are sized for every token), every tile of a given row tile landed on one
+// XCD (u/ga 0.90 -> 1.97 ms at 2799 routed rows of d_ff 14336).
+__device__ __forceinline__ bool rd_tile(int nr, int nt, int* mi, int* ni) {
+  const int mt = (nr + 255) / 256, b = (int)blockIdx.x;
+  if (b >= mt * nt) return false;
+  tile_of(b, mt, nt, mi, ni);
+  return true;
+}
+
 // 256 x 256 tiles of eight waves as 4 x 2 of 64 x 128, B staged K-major (gx,
 // the weight gradients).
 using RdKN = Gemm2<1, 256, false, 32, 2, true, 256, 4, 8, true>;
@@ -126,9 +141,9 @@ __global__ __launch_bounds__(64 * RdUG::NWAVES, 1) void rd_uga(RdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   const int nr = routed_rows(a);
   if (!dense_on(nr)) return;
-  const int mi = (int)blockIdx.x % (a.ldr / 256), ni = (int)blockIdx.x / (a.ldr / 256);
+  int mi, ni;
+  if (!rd_tile(nr, a.N / 128, &mi, &ni)) return;
   const int m0 = mi * 256, n0 = ni * 128;
-  if (m0 >= nr || n0 >= a.N) return;
   G gu_, gg_;
   {
     const uint16_t* B[1] = {a.wu};
@@ -192,7 +207,7 @@ __global__ __launch_bounds__(64 * RdUG::NWAVES, 1) void rd_uga(RdArgs a) {
         }
       }
       // transposed: rows rb .. rb + 3 of column j are 8 contiguous bytes
-      const size_t to = (size_t)j * a.ldr + rb;
+      const size_t to = (size_t)j * a.ldt + rb;
       *(uint2*)(gzT + to) = make_uint2(pz[0], pz[1]);
       *(uint2*)(guT + to) = make_uint2(pu[0], pu[1]);
       *(uint2*)(aT + to) = make_uint2(pa[0], pa[1]);
@@ -222,9 +237,9 @@ __global__ __launch_bounds__(64 * RdKN::NWAVES, 1) void rd_gx(RdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::LDS_BYTES];
   const int nr = routed_rows(a);
   if (!dense_on(nr)) return;
-  const int mi = (int)blockIdx.x % (a.ldr / 256), di = (int)blockIdx.x / (a.ldr / 256);
+  int mi, di;
+  if (!rd_tile(nr, (a.D + 255) / 256, &mi, &di)) return;
   const int m0 = mi * 256, n0 = di * 256;
-  if (m0 >= nr || n0 >= a.D) return;
   G g;
   {
     const uint16_t* B[1] = {a.wg};
@@ -251,7 +266,7 @@ __device__ __forceinline__ void gw_tile(const RdArgs& a, const uint16_t* A, cons
   using G = RdKN;
   G g;
   const uint16_t* B[1] = {Bm};
-  g.init(A, (size_t)a.N, nullptr, m0, a.N, B, n0, a.D, kp, a.ldr);
+  g.init(A, (size_t)a.N, nullptr, m0, a.N, B, n0, a.D, kp, a.ldt);
   g.run_pipe(lds, kp);
   g.for_each([&](int, int row, int col, float v) {
     const int j = m0 + row, d = n0 + col;
@@ -290,12 +305,20 @@ __global__ __launch_bounds__(256) void rd_gb(RdArgs a) {
 
 size_t al256r(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Row stride (elements) of gzT, guT and aT: ldr, or ldr + 256 when ldr / 256
+// is even, so that the stride is an odd multiple of 512 bytes.  A stride of
+// a large power of two (ldr = 16384 when the buffers are sized for every
+// token) puts the 256 rows that a weight-gradient tile reads, and the
+// columns that rd_uga stores, on the same few memory channels.
+int transposed_stride(int ldr) { return (ldr / 256) % 2 == 0 ? ldr + 256 : ldr; }
+
 }  // namespace
 
 size_t routed_dense_workspace_bytes(int N, int D, int R) {
   const size_t ldr = ((size_t)R + 255) & ~(size_t)255;
+  const size_t ldt = (size_t)transposed_stride((int)ldr);
   return 2 * al256r(ldr * D * 2) + al256r((size_t)R * N * 2) + 2 * al256r(ldr * N * 2) +
-         3 * al256r((size_t)N * ldr * 2) + al256r(ldr / 256 * N * 4);
+         3 * al256r((size_t)N * ldt * 2) + al256r(ldr / 256 * N * 4);
 }
 
 hipError_t launch_backward_routed_dense(const void* x, const void* gy, const void* wg_t,
@@ -306,7 +329,7 @@ hipError_t launch_backward_routed_dense(const void* x, const void* gy, const voi
                                         int T, int D, int N, int R, float l1g, void* ws,
                                         int stage, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
-  const int ldr = (R + 255) & ~255;
+  const int ldr = (R + 255) & ~255, ldt = transposed_stride(ldr);
   char* p = (char*)ws;
   RdArgs a{};
   a.x = (const uint16_t*)x;
@@ -330,11 +353,11 @@ hipError_t launch_backward_routed_dense(const void* x, const void* gy, const voi
   a.gu = (uint16_t*)p;
   p += al256r((size_t)ldr * N * 2);
   a.gzT = (uint16_t*)p;
-  p += al256r((size_t)N * ldr * 2);
+  p += al256r((size_t)N * ldt * 2);
   a.guT = (uint16_t*)p;
-  p += al256r((size_t)N * ldr * 2);
+  p += al256r((size_t)N * ldt * 2);
   a.aT = (uint16_t*)p;
-  p += al256r((size_t)N * ldr * 2);
+  p += al256r((size_t)N * ldt * 2);
   a.gbp = (float*)p;
   a.gx = (uint16_t*)gx;
   a.gwg = gwg_t;
@@ -346,6 +369,7 @@ hipError_t launch_backward_routed_dense(const void* x, const void* gy, const voi
   a.N = N;
   a.R = R;
   a.ldr = ldr;
+  a.ldt = ldt;
   a.l1g = l1g;
   const unsigned mtw = (unsigned)(ldr / 256);
   if (stage == 0) {

@@ -27,7 +27,10 @@ def _sffn():
     return sffn
 
 
-def run_backward(inp: wl.Inputs, cap: int, gy_np: np.ndarray, repeat: int = 1, lam: float = 0.0):
+def run_backward(inp: wl.Inputs, cap: int, gy_np: np.ndarray, repeat: int = 1, lam: float = 0.0,
+                 exact_ws: bool = False):
+    """exact_ws: size the routed part of the workspace for the forward's own
+    routed count (max_routed = n_routed) instead of for every token."""
     sffn = _sffn()
     w = inp.workload
     d = device_inputs(inp)
@@ -35,23 +38,30 @@ def run_backward(inp: wl.Inputs, cap: int, gy_np: np.ndarray, repeat: int = 1, l
     ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
     s = ffn.shape
     gy = to_device(gy_np, "bf16")
-    ws = sffn.alloc_workspace(s, sffn.WS_BACKWARD)
+    mr = int(ffn.n_routed.item()) if exact_ws else None
+    if exact_ws:
+        ws = torch.empty(max(sffn.backward_workspace_bytes(s, mr), 16), dtype=torch.uint8,
+                         device="cuda")
+    else:
+        ws = sffn.alloc_workspace(s, sffn.WS_BACKWARD)
     outs = []
     for _ in range(repeat):
         gx = torch.empty((w.T, w.d_model), dtype=torch.bfloat16, device="cuda")
         g = [torch.full((w.d_ff, w.d_model), float("nan"), device="cuda") for _ in range(3)]
         gb = torch.full((w.d_ff,), float("nan"), device="cuda")
         sffn.sparse_ffn_bwd(s, d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], ffn.count, ffn.idx,
-                            ffn.val, ffn.routed, ffn.n_routed, gy, gx, *g, gb, ws, l1_lambda=lam)
+                            ffn.val, ffn.routed, ffn.n_routed, gy, gx, *g, gb, ws, l1_lambda=lam,
+                            max_routed=mr)
         outs.append({"gx": gx, "gwg_t": g[0], "gwu_t": g[1], "gwd": g[2], "gb": gb})
     torch.cuda.synchronize()
     return ffn, outs
 
 
-def check(inp: wl.Inputs, cap: int, dense: bool, rows=None, lam: float = 0.0):
+def check(inp: wl.Inputs, cap: int, dense: bool, rows=None, lam: float = 0.0,
+          exact_ws: bool = False):
     w = inp.workload
     gy_np = wl.upstream_grad(w)
-    ffn, outs = run_backward(inp, cap, gy_np, repeat=2, lam=lam)
+    ffn, outs = run_backward(inp, cap, gy_np, repeat=2, lam=lam, exact_ws=exact_ws)
     o = outs[0]
     for k in o:  # deterministic
         assert torch.equal(o[k].view(torch.int16) if o[k].dtype == torch.bfloat16 else o[k],
@@ -126,18 +136,21 @@ def test_backward_hybrid_mix_full_size():
     assert e["n_routed"] > 60
 
 
-@pytest.mark.parametrize("T,d_model,d_ff,beta,cap,lam", [
-    (8200, 1024, 1024, 1.0, 2, 0.0),   # fused column order, ragged row tiles
-    (8192, 2560, 512, 1.0, 2, 0.5),    # row and column walk order, the L1 term
+@pytest.mark.parametrize("T,d_model,d_ff,beta,cap,lam,exact_ws", [
+    (8200, 1024, 1024, 1.0, 2, 0.0, False),  # fused column order, ragged row tiles
+    (8192, 2560, 512, 1.0, 2, 0.5, False),   # row and column walk order, the L1 term
+    (8200, 1024, 1024, 1.0, 2, 0.0, True),   # workspace sized for the routed count only
 ])
-def test_backward_routed_rows_on_tiles(T, d_model, d_ff, beta, cap, lam):
+def test_backward_routed_rows_on_tiles(T, d_model, d_ff, beta, cap, lam, exact_ws):
     """More than 1024 routed rows with at least 8192 tokens: the routed rows'
     products run on MFMA tiles (per-entry gradients rounded to bf16 before the
-    weight-gradient and gx products) and are added to the other rows' sums."""
+    weight-gradient and gx products) and are added to the other rows' sums.
+    The tile grid is sized for the workspace's row bound and numbered by the
+    actual count, so both sizings are checked."""
     inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype="bf16", beta=beta,
                              seed_base=110 + d_model, cap=cap)
     e = check(inp, cap, dense=False, rows=sample_rows(T, 300, must=np.arange(T - 9, T), seed=8),
-              lam=lam)
+              lam=lam, exact_ws=exact_ws)
     assert e["n_routed"] > 1024
 
 
