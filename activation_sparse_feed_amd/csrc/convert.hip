@@ -2,6 +2,8 @@
 // GEMM storing the float32 pre-activation, and standalone conversions of it to
 // TwELL and to a classic row-wise ELLPACK.  Declared in launch.h; the C entry
 // points are gate_preact, twell_from_preact and ell_from_preact.
+#include <climits>
+
 #include "common.cuh"
 #include "exact.cuh"
 #include "gemm_v2.cuh"
@@ -56,9 +58,12 @@ __device__ __forceinline__ void preact_tile(const GateArgs& a, uint8_t* lds, flo
   }
 }
 
-// Mapped rows (the routed rows of the backward), 64-row tiles.
+// Mapped rows (the routed rows of the backward), 64-row tiles.  wide_from:
+// the row count from which gate_preact_rows_wide takes the rows instead (this
+// kernel then returns), or INT_MAX when that kernel is not launched.
 __global__ __launch_bounds__(64 * RowsGemm::NWAVES) void gate_preact_rows(
-    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev, int max_rows) {
+    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev, int max_rows,
+    int wide_from) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[RowsGemm::LDS_BYTES];
   // the active tiles are the first ones, spread over the XCDs in dispatch
   // order (the XCD-aware map would put them all on one)
@@ -66,8 +71,36 @@ __global__ __launch_bounds__(64 * RowsGemm::NWAVES) void gate_preact_rows(
   const int mi = (int)blockIdx.x / ntn, ni = (int)blockIdx.x - mi * ntn;
   const int m0 = mi * RowsGemm::BM;
   const int mv = uniform(min(*n_rows_dev, max_rows));
-  if (m0 >= mv) return;
+  if (m0 >= mv || mv >= wide_from) return;
   preact_tile<RowsGemm>(a, lds, z, rowmap, mv, m0, ni * RowsGemm::BN);
+}
+
+// Many mapped rows (kRowsWideFrom or more): the TwELL kernel's 256 x 256 tiles
+// (256 x 128 for an odd last column tile), numbered by the actual row count
+// through the XCD-aware map so that the working tiles come first and spread
+// over the XCDs.  The 64-row tiles run these at about 0.46 PFLOP/s.
+constexpr int kRowsWideFrom = 1024;
+
+__global__ __launch_bounds__(64 * GateGemm::NWAVES) void gate_preact_rows_wide(
+    GateArgs a, float* z, const int* rowmap, const int* n_rows_dev, int max_rows) {
+  constexpr size_t kLds = GateGemm::LDS_BYTES > GateGemmWide::LDS_BYTES ? GateGemm::LDS_BYTES
+                                                                         : GateGemmWide::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  const int mv = uniform(min(*n_rows_dev, max_rows));
+  if (mv < kRowsWideFrom) return;
+  const int mt = (mv + GateGemm::BM - 1) / GateGemm::BM;
+  const int nt = a.N / kTile, wide_nt = nt / 2, narrow_nt = nt - 2 * wide_nt;
+  const int bid = (int)blockIdx.x, n_wide = mt * wide_nt;
+  int mi, ni;
+  if (bid < n_wide) {
+    tile_of(bid, mt, wide_nt, &mi, &ni);
+    preact_tile<GateGemmWide>(a, lds, z, rowmap, mv, mi * GateGemmWide::BM,
+                              ni * GateGemmWide::BN);
+  } else if (bid - n_wide < mt * narrow_nt) {
+    tile_of(bid - n_wide, mt, narrow_nt, &mi, &ni);
+    preact_tile<GateGemm>(a, lds, z, rowmap, mv, mi * GateGemm::BM,
+                          wide_nt * GateGemmWide::BN + ni * GateGemm::BN);
+  }
 }
 
 // All rows: the TwELL kernel's grid (wide tiles, then narrow ones).
@@ -289,9 +322,18 @@ hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g,
     if (!n_rows_dev) return hipErrorInvalidValue;
     const int rows = max_rows >= 0 ? min(max_rows, T) : T;
     if (rows == 0) return hipSuccess;
+    // the 256-row kernel only where it can matter (below 8192 tokens its
+    // extra launch would cost more than the few routed rows' tiles gain)
+    const bool wide = rows >= kRowsWideFrom && T >= 8192 && N % kTile == 0;
     const dim3 g((unsigned)(((rows + RowsGemm::BM - 1) / RowsGemm::BM) * (N / RowsGemm::BN)));
     hipLaunchKernelGGL(gate_preact_rows, g, dim3(64 * RowsGemm::NWAVES), 0, stream, a, z, rowmap,
-                       n_rows_dev, rows);
+                       n_rows_dev, rows, wide ? kRowsWideFrom : INT_MAX);
+    if (wide) {
+      const int nt = N / kTile;
+      const dim3 gw((unsigned)(((rows + GateGemm::BM - 1) / GateGemm::BM) * (nt / 2 + nt % 2)));
+      hipLaunchKernelGGL(gate_preact_rows_wide, gw, dim3(64 * GateGemm::NWAVES), 0, stream, a, z,
+                         rowmap, n_rows_dev, rows);
+    }
   } else {
     int wide_nt, narrow_nt;
     gate_tile_split(T, N, &wide_nt, &narrow_nt);
