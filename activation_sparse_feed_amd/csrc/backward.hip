@@ -216,10 +216,19 @@ __device__ __forceinline__ void load_row(const uint16_t* base, int t, int D, u32
   for (int c = 0; c < P; ++c) c8[c] = ldg16(base + o + c * 512);
 }
 
+// Entries of one row staged per wave in LDS at a time (column | h << 16, slot
+// k * cap + s in the row's TwELL arrays).
+constexpr int kRowList = 512;
+
 // Rows within capacity: one wave walks the row's TwELL entries in order and
-// writes gx_t.  Routed rows are left to bwd_routed.
+// writes gx_t.  Routed rows are left to bwd_routed.  The entries are staged a
+// group of tiles at a time into a per-wave list in LDS (one lane per tile, all
+// the group's count, idx and val loads in flight together), so that the walk
+// waits on one memory latency per entry (its weight rows), not on the list
+// reads before them.  Waves share no LDS: no barrier.
 template <int P>
 __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
+  __shared__ uint2 list_s[4][kRowList];
   const int w = uniform((int)(threadIdx.x >> 6));
   const int lane = lane_id();
   const int t = (int)blockIdx.x * 4 + w;
@@ -233,14 +242,37 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
   for (int c = 0; c < P; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) gxa[c][e] = 0.f;
-  for (int k = 0; k < a.nt; ++k) {
-    const size_t tk = (size_t)t * a.nt + k;
-    const int c = uniform(min((int)a.count[tk], a.cap));
-    for (int s = 0; s < c; ++s) {
-      const size_t pos = tk * a.cap + s;
-      const int j = uniform(min((int)a.idx[pos], a.N - 1));  // valid lists: j < N already
-      bwd_entry<P>(a, j, bf16_to_f32(a.val[pos]), xc, gyc, gxa, a.co + pos);
+  uint2* list = list_s[w];
+  const int group = max(1, min(kWave, kRowList / max(a.cap, 1)));  // tiles per staging
+  const size_t row0 = (size_t)t * a.nt * a.cap;
+  for (int k0 = 0; k0 < a.nt; k0 += group) {
+    const int k = k0 + lane;
+    const int c = (lane < group && k < a.nt) ? min((int)a.count[(size_t)t * a.nt + k], a.cap) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
     }
+    const int n = uniform(__shfl(incl, kWave - 1, kWave));
+    const uint32_t slot0 = (uint32_t)k * (uint32_t)a.cap;
+    for (int s = 0; s < c; ++s) {
+      const size_t pos = row0 + slot0 + s;
+      list[incl - c + s] = make_uint2((uint32_t)a.idx[pos] | ((uint32_t)a.val[pos] << 16),
+                                      slot0 + (uint32_t)s);
+    }
+    // LDS operations of one wave complete in order: the reads below see the
+    // writes above once the compiler keeps them in program order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int e = 0; e < n; ++e) {
+      const uint2 v = list[e];
+      const int j = uniform(min((int)(v.x & 0xffffu), a.N - 1));  // valid lists: j < N already
+      const float h = bf16_to_f32((uint16_t)uniform((int)(v.x >> 16)));
+      bwd_entry<P>(a, j, h, xc, gyc, gxa, a.co + row0 + uniform((int)v.y));
+    }
+    __builtin_amdgcn_wave_barrier();
   }
   store_gx<P>(a, t, gxa);
 }
