@@ -168,8 +168,9 @@ __device__ __forceinline__ void store_gx(const BwdArgs& a, int t, float (*gxa)[8
 
 // One entry of row t: the two dot products, the per-entry gradients (stored
 // at *out by lane 0) and the gx accumulation.  xc / gyc: this lane's chunks of
-// x_t and gy_t (8 bf16 each, at c * 512 + lane * 8).
-template <int P>
+// x_t and gy_t (8 bf16 each, at c * 512 + lane * 8), chunk c at xc[c * S]
+// (S = 1: registers; S = kWave: a per-wave row copy in LDS).
+template <int P, int S = 1>
 __device__ __forceinline__ void bwd_entry(const BwdArgs& a, int j, float h, const u32x4_t* xc,
                                           const u32x4_t* gyc, float (*gxa)[8], f32x4_t* out) {
   const int lane = lane_id();
@@ -181,19 +182,20 @@ __device__ __forceinline__ void bwd_entry(const BwdArgs& a, int j, float h, cons
     dw[c] = ldg16(a.wd + rowo + c * 512);
     gw[c] = ldg16(a.wg + rowo + c * 512);
   }
+  // the dot products on the packed bf16 pairs (exact products, float32 sums):
+  // no unpacked copies of the weight rows stay live across the reductions
   float su = 0.f, sg = 0.f;
 #pragma unroll
   for (int c = 0; c < P; ++c) {
-    float xf[8], uf[8], gf[8], df[8];
-    Elt<uint16_t>::unpack(xc[c], xf);
-    Elt<uint16_t>::unpack(uw[c], uf);
-    Elt<uint16_t>::unpack(gyc[c], gf);
-    Elt<uint16_t>::unpack(dw[c], df);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      su = fmaf(xf[e], uf[e], su);
-      sg = fmaf(gf[e], df[e], sg);
-    }
+    const u32x4_t xv = xc[c * S], gv = gyc[c * S];
+    su = dot2_bf16(xv.x, uw[c].x, su);
+    su = dot2_bf16(xv.y, uw[c].y, su);
+    su = dot2_bf16(xv.z, uw[c].z, su);
+    su = dot2_bf16(xv.w, uw[c].w, su);
+    sg = dot2_bf16(gv.x, dw[c].x, sg);
+    sg = dot2_bf16(gv.y, dw[c].y, sg);
+    sg = dot2_bf16(gv.z, dw[c].z, sg);
+    sg = dot2_bf16(gv.w, dw[c].w, sg);
   }
   const float u = wave_sum_uniform(su);
   const float ga = wave_sum_uniform(sg);
@@ -218,25 +220,38 @@ __device__ __forceinline__ void load_row(const uint16_t* base, int t, int D, u32
 
 // Entries of one row staged per wave in LDS at a time (column | h << 16, slot
 // k * cap + s in the row's TwELL arrays).
-constexpr int kRowList = 512;
+constexpr int kRowList = 256;
 
 // Rows within capacity: one wave walks the row's TwELL entries in order and
 // writes gx_t.  Routed rows are left to bwd_routed.  The entries are staged a
 // group of tiles at a time into a per-wave list in LDS (one lane per tile, all
 // the group's count, idx and val loads in flight together), so that the walk
 // waits on one memory latency per entry (its weight rows), not on the list
-// reads before them.  Waves share no LDS: no barrier.
+// reads before them.  The row's x_t and gy_t live in LDS too (each lane reads
+// back only the chunks it wrote), which keeps the wave within 256 registers:
+// two waves per SIMD instead of one, twice the weight rows in flight.  Waves
+// share no LDS: no barrier.
 template <int P>
-__global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_rows(BwdArgs a) {
   __shared__ uint2 list_s[4][kRowList];
+  __shared__ u32x4_t rows_s[4][2][P * kWave];
   const int w = uniform((int)(threadIdx.x >> 6));
   const int lane = lane_id();
   const int t = (int)blockIdx.x * 4 + w;
   if (t >= a.T) return;
   if (row_is_routed(a, t)) return;
-  u32x4_t xc[P], gyc[P];
-  load_row<P>(a.x, t, a.D, xc);
-  load_row<P>(a.gy, t, a.D, gyc);
+  u32x4_t* xs = rows_s[w][0] + lane;
+  u32x4_t* gs = rows_s[w][1] + lane;
+  {
+    u32x4_t xc[P], gyc[P];
+    load_row<P>(a.x, t, a.D, xc);
+    load_row<P>(a.gy, t, a.D, gyc);
+#pragma unroll
+    for (int c = 0; c < P; ++c) {
+      xs[c * kWave] = xc[c];
+      gs[c * kWave] = gyc[c];
+    }
+  }
   float gxa[P][8];
 #pragma unroll
   for (int c = 0; c < P; ++c)
@@ -270,7 +285,7 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
       const uint2 v = list[e];
       const int j = uniform(min((int)(v.x & 0xffffu), a.N - 1));  // valid lists: j < N already
       const float h = bf16_to_f32((uint16_t)uniform((int)(v.x >> 16)));
-      bwd_entry<P>(a, j, h, xc, gyc, gxa, a.co + row0 + uniform((int)v.y));
+      bwd_entry<P, kWave>(a, j, h, xs, gs, gxa, a.co + row0 + uniform((int)v.y));
     }
     __builtin_amdgcn_wave_barrier();
   }
