@@ -467,6 +467,7 @@ __global__ __launch_bounds__(64 * DownWide::NWAVES, 1) void down_routed_wide(Den
 }
 
 // y[rowmap[m], n] = sum over splits of the partials, in split order.
+constexpr int kRedUnroll = 4;
 __global__ __launch_bounds__(256) void down_routed_reduce(DenseArgs a, const float* partial) {
   const int mv = uniform(rows_valid(a));
   const DownPlan p = routed_down_plan(mv, a.N, a.K, a.routed_wide != 0);
@@ -475,15 +476,36 @@ __global__ __launch_bounds__(256) void down_routed_reduce(DenseArgs a, const flo
   const size_t per = (size_t)p.mt * p.bm * a.N;  // floats per split
   const size_t n4 = (size_t)mv * a.N / 4;     // N % 8 == 0
   uint16_t* y = (uint16_t*)a.out;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-    f32x4_t v = *(const f32x4_t*)(partial + 4 * i);
-    for (int s = 1; s < S; ++s) v += *(const f32x4_t*)(partial + s * per + 4 * i);
-    const size_t e = 4 * i;
-    const int m = (int)(e / a.N), n = (int)(e - (size_t)m * a.N);
-    uint16_t* dst = y + (size_t)a.rowmap[m] * a.N + n;
-    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    *(uint2*)dst = make_uint2(lo, hi);
+  // kRedUnroll float4 groups per thread at a time, all their loads in flight
+  // together (the grid is small: one launch that finds nothing to do stays cheap)
+  constexpr int U = kRedUnroll;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x; i0 < n4; i0 += U * stride) {
+    f32x4_t v[U];
+    int row[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = min(i0 + u * stride, n4 - 1);
+      v[u] = *(const f32x4_t*)(partial + 4 * i);
+      row[u] = a.rowmap[(int)(4 * i / a.N)];
+    }
+    for (int s = 1; s < S; ++s)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t i = min(i0 + u * stride, n4 - 1);
+        v[u] += *(const f32x4_t*)(partial + s * per + 4 * i);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = i0 + u * stride;
+      if (i >= n4) break;
+      const size_t e = 4 * i;
+      const int m = (int)(e / a.N), n = (int)(e - (size_t)m * a.N);
+      uint16_t* dst = y + (size_t)row[u] * a.N + n;
+      const uint32_t lo = (uint32_t)f32_to_bf16(v[u][0]) | ((uint32_t)f32_to_bf16(v[u][1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(v[u][2]) | ((uint32_t)f32_to_bf16(v[u][3]) << 16);
+      *(uint2*)dst = make_uint2(lo, hi);
+    }
   }
 }
 
