@@ -325,7 +325,11 @@ hipError_t launch_gate_preact(const void* x, const void* wg_t, const float* b_g,
     // the 256-row kernel only where it can matter (below 8192 tokens its
     // extra launch would cost more than the few routed rows' tiles gain)
     const bool wide = rows >= kRowsWideFrom && T >= 8192 && N % kTile == 0;
-    const dim3 g((unsigned)(((rows + RowsGemm::BM - 1) / RowsGemm::BM) * (N / RowsGemm::BN)));
+    // with the 256-row kernel launched, the 64-row one takes fewer than
+    // kRowsWideFrom rows: no larger grid (its workgroups that return at once
+    // still cost their dispatch)
+    const int narrow_rows = wide ? kRowsWideFrom : rows;
+    const dim3 g((unsigned)(((narrow_rows + RowsGemm::BM - 1) / RowsGemm::BM) * (N / RowsGemm::BN)));
     hipLaunchKernelGGL(gate_preact_rows, g, dim3(64 * RowsGemm::NWAVES), 0, stream, a, z, rowmap,
                        n_rows_dev, rows, wide ? kRowsWideFrom : INT_MAX);
     if (wide) {
