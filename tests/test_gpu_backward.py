@@ -140,6 +140,7 @@ def test_backward_hybrid_mix_full_size():
     (8200, 1024, 1024, 1.0, 2, 0.0, False),  # fused column order, ragged row tiles
     (8192, 2560, 512, 1.0, 2, 0.5, False),   # row and column walk order, the L1 term
     (8200, 1024, 1024, 1.0, 2, 0.0, True),   # workspace sized for the routed count only
+    (8192, 1536, 640, 1.0, 2, 0.25, False),  # d_ff not a multiple of 256: half-empty wide tiles
 ])
 def test_backward_routed_rows_on_tiles(T, d_model, d_ff, beta, cap, lam, exact_ws):
     """More than 1024 routed rows with at least 8192 tokens: the routed rows'
