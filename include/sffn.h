@@ -233,8 +233,11 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
  * SFFN_ERR_ARG).  Rows within
  * capacity use their TwELL entries (h = val); routed rows use complete
  * activity lists rebuilt from x with twell_pack's GEMM and exact activity
- * decision (h rounded to bf16 like val).  Every sum runs in a fixed order:
- * the result is deterministic.  Every element of the outputs is written
+ * decision (h rounded to bf16 like val).  With at least 8192 tokens and 1024
+ * routed rows (the count read on the device), the routed rows' products run as
+ * dense bf16 matrix-core tiles instead, with their gz, gu and a rounded to
+ * bf16 before the products (as a dense bf16 backward rounds them).  Every sum
+ * runs in a fixed order: the result is deterministic.  Every element of the outputs is written
  * (weight-gradient rows of inactive columns are zero); gb may be NULL.
  *
  * bf16 only, d_model % 512 == 0 and d_model <= 4096 (else
