@@ -365,6 +365,45 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("name", ["hybrid_mix", "decode_1pct"])
+def test_forward_graph_replay(name):
+    """The three calls of a forward launch kernels only (no allocation, copy,
+    memset or synchronisation), so a caller can capture them in a HIP graph:
+    each replay, with eager forwards and synchronisations between replays,
+    gives the eager result bit for bit (TwELL arrays, routed set, y)."""
+    inp = wl.generate(wl.WORKLOADS[name])
+    cap = inp.workload.cap
+    ffn, y0, d = run_sparse(inp, cap)
+    ref = {"y": y0.clone(), "count": ffn.count.clone(), "idx": ffn.idx.clone(),
+           "val": ffn.val.clone(), "n": int(ffn.n_routed.item()), "routed": ffn.routed.clone()}
+    live = torch.arange(cap, device="cuda")[None, None, :] < torch.clamp(
+        ref["count"].to(torch.int32), max=cap)[:, :, None]
+    args = (d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            ffn.forward(*args, stream=side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ffn.y.zero_()
+        ffn.count.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ffn.y.view(torch.int16), ref["y"].view(torch.int16))
+        assert torch.equal(ffn.count.view(torch.int16), ref["count"].view(torch.int16))
+        assert torch.equal(torch.where(live, ffn.idx.to(torch.int32), -1),
+                           torch.where(live, ref["idx"].to(torch.int32), -1))
+        assert torch.equal(torch.where(live, ffn.val.float(), 0.0),
+                           torch.where(live, ref["val"].float(), 0.0))
+        n = int(ffn.n_routed.item())
+        assert n == ref["n"]
+        assert torch.equal(ffn.routed[:n], ref["routed"][:n])
+        ffn.forward(*args)  # eager work between the replays
+        torch.cuda.synchronize()
+
+
 def test_decode_two_pass_repeats():
     """The few-token bf16 kernels (two passes through the workspace) give
     bitwise identical results on repeated calls."""
