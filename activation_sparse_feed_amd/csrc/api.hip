@@ -71,7 +71,18 @@ size_t pack_l1_ws(const sffn_shape* s) {
   return pack_ws(s) + align256((size_t)s->T * (s->d_ff / 128) * 4) + align256(l1_ws_bytes());
 }
 
+// Float32 backward: the complete lists' arrays (count, idx, float32 val at
+// capacity backward_f32_cap()) after twell_pack's workspace, then the
+// backward's own.
+size_t backward_f32_lists_bytes(const sffn_shape* s) {
+  const size_t nt = (size_t)s->d_ff / 128, cap = (size_t)backward_f32_cap();
+  return align256((size_t)s->T * nt * 2) + align256((size_t)s->T * nt * cap * 2) +
+         align256((size_t)s->T * nt * cap * 4);
+}
+
 size_t backward_ws(const sffn_shape* s, int max_routed) {
+  if (s->dtype == SFFN_F32)
+    return pack_ws(s) + backward_f32_lists_bytes(s) + backward_f32_workspace_bytes(s->T, s->d_ff);
   return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4) +
          backward_workspace_bytes(s->T, s->d_ff, s->d_model, s->cap, max_routed);
 }
@@ -403,6 +414,30 @@ int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t,
   if (!backward_supported(shape->dtype, shape->d_model) || act_bytes_too_large(shape))
     return SFFN_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
+  const float l1g = (float)((double)l1_lambda / (double)shape->T);
+  if (shape->dtype == SFFN_F32) {
+    // complete activity lists of every row: twell_pack's kernels at the full
+    // capacity (rows within the forward's capacity get their forward entries,
+    // routed rows their complete lists; routed, n_routed and max_routed are
+    // not needed)
+    sffn_shape full = *shape;
+    full.cap = backward_f32_cap();
+    const size_t nt = (size_t)shape->d_ff / 128, cap = (size_t)full.cap;
+    char* p = (char*)workspace + pack_ws(shape);
+    uint16_t* count2 = (uint16_t*)p;
+    p += align256((size_t)shape->T * nt * 2);
+    uint16_t* idx2 = (uint16_t*)p;
+    p += align256((size_t)shape->T * nt * cap * 2);
+    float* val2 = (float*)p;
+    p += align256((size_t)shape->T * nt * cap * 4);
+    st = pack_impl(&full, x, wg_t, b_g, wg_norms, count2, idx2, val2, workspace, nullptr,
+                   nullptr, s);
+    if (st != SFFN_OK) return st;
+    return hip_status(launch_backward_f32(
+        (const float*)x, (const float*)wg_t, (const float*)wu_t, (const float*)wd, count2, idx2,
+        val2, (const float*)gy, (float*)gx, gwg_t, gwu_t, gwd, gb, shape->T, shape->d_model,
+        shape->d_ff, l1g, p, s));
+  }
   float* xn = (float*)workspace;
   float* wbuf = (float*)((char*)workspace + align256((size_t)shape->T * 4));
   void* bws = (char*)wbuf + align256((size_t)shape->d_ff * 4);
@@ -411,9 +446,8 @@ int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t,
   if (e != hipSuccess) return SFFN_ERR_HIP;
   return hip_status(launch_backward(x, wg_t, b_g, wu_t, wd, xn, wg_norms ? wg_norms : wbuf, count,
                                     idx, val, routed, n_routed, gy, gx, gwg_t, gwu_t, gwd, gb,
-                                    shape->T, shape->d_model, shape->d_ff, shape->cap,
-                                    (float)((double)l1_lambda / (double)shape->T), max_routed,
-                                    guard_band(shape), bws, s));
+                                    shape->T, shape->d_model, shape->d_ff, shape->cap, l1g,
+                                    max_routed, guard_band(shape), bws, s));
 }
 
 size_t sparse_ffn_bwd_workspace_bytes(const sffn_shape* shape, int32_t max_routed) {

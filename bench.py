@@ -339,6 +339,14 @@ def training_memory(w, x, wg, b, wu, wd, wg_norms, gy) -> dict:
                     "one forward + backward; x, weights, gy, y and the gradient outputs excluded"}
 
 
+def backward_ok(w) -> bool:
+    """Shapes sparse_ffn_bwd takes: bf16 with d_model a multiple of 512 up to
+    4096, float32 with d_model up to 2048."""
+    if w.dtype == "bf16":
+        return w.d_model % 512 == 0 and w.d_model <= 4096
+    return w.d_model % 4 == 0 and w.d_model <= 2048
+
+
 def d_model_ok(d_model: int) -> bool:
     """The separate-conversion calls need d_model % 32 == 0."""
     return d_model % 32 == 0
@@ -610,7 +618,7 @@ def main() -> int:
     # dense backward from torch's GEMMs (hipBLASLt) given the forward's dense
     # activations; both after the same forward, K calls each
     backward = None
-    if not args.no_backward and w.dtype == "bf16" and w.d_model % 512 == 0 and w.d_model <= 4096:
+    if not args.no_backward and backward_ok(w):
         gy = dev(wl.upstream_grad(w))
         ws_b = sffn.alloc_workspace(s, sffn.WS_BACKWARD)
         gx = torch.empty_like(x)
@@ -655,7 +663,7 @@ def main() -> int:
         backward = {"sparse_ffn_bwd_ms": t_b, "torch_dense_backward_ms": t_db,
                     "speedup_vs_torch_dense": t_db / t_b,
                     "weight_grad_bytes": 3.0 * w.d_ff * w.d_model * 4,
-                    "note": "dense: 6 hipBLASLt bf16 GEMMs from saved dense activations"}
+                    "note": f"dense: 6 hipBLASLt {w.dtype} GEMMs from saved dense activations"}
         del ws_b, gw3, zT, uT, hT, actT, wg_tt, wu_tt
         # measured memory of a training step: what the forward keeps for the
         # backward and the peak, sparse (TwELL + routed list) against dense (h, u)

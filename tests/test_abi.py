@@ -202,8 +202,11 @@ def test_backward_errors(sffn):
     s264 = _shape(sffn, d_model=264)
     n264 = sffn.workspace_bytes(s264, sffn.WS_BACKWARD)
     assert lib.sparse_ffn_bwd(ctypes.byref(s264), *args, WS, n264, None) == -2
-    sf = _shape(sffn, d_model=512, dtype=sffn.SFFN_F32)
+    # float32 is taken up to d_model 2048
+    sf = _shape(sffn, d_model=2056, dtype=sffn.SFFN_F32)
     assert lib.sparse_ffn_bwd(ctypes.byref(sf), *args, WS, sffn.workspace_bytes(sf, 6), None) == -2
+    sf512 = _shape(sffn, d_model=512, dtype=sffn.SFFN_F32)
+    assert sffn.workspace_bytes(sf512, 6) >= 40 * 64 * 512  # complete lists and their gradients
     s0 = _shape(sffn, T=0)
     assert lib.sparse_ffn_bwd(ctypes.byref(s0), *([None] * 11), 0, None, 0.0, *([None] * 5), None,
                               0, None) == 0
