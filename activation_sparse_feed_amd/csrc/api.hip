@@ -71,18 +71,19 @@ size_t pack_l1_ws(const sffn_shape* s) {
   return pack_ws(s) + align256((size_t)s->T * (s->d_ff / 128) * 4) + align256(l1_ws_bytes());
 }
 
-// Float32 backward: the complete lists' arrays (count, idx, float32 val at
-// capacity backward_f32_cap()) after twell_pack's workspace, then the
-// backward's own.
-size_t backward_f32_lists_bytes(const sffn_shape* s) {
-  const size_t nt = (size_t)s->d_ff / 128, cap = (size_t)backward_f32_cap();
+// The general backward (float32, bf16 widths not a multiple of 512): the
+// complete lists' arrays (count, idx, val at capacity backward_general_cap())
+// after twell_pack's workspace, then the backward's own.
+size_t backward_general_lists_bytes(const sffn_shape* s) {
+  const size_t nt = (size_t)s->d_ff / 128, cap = (size_t)backward_general_cap();
   return align256((size_t)s->T * nt * 2) + align256((size_t)s->T * nt * cap * 2) +
-         align256((size_t)s->T * nt * cap * 4);
+         align256((size_t)s->T * nt * cap * elt_bytes(s->dtype));
 }
 
 size_t backward_ws(const sffn_shape* s, int max_routed) {
-  if (s->dtype == SFFN_F32)
-    return pack_ws(s) + backward_f32_lists_bytes(s) + backward_f32_workspace_bytes(s->T, s->d_ff);
+  if (backward_general(s->dtype, s->d_model))
+    return pack_ws(s) + backward_general_lists_bytes(s) +
+           backward_general_workspace_bytes(s->T, s->d_ff);
   return align256((size_t)s->T * 4) + align256((size_t)s->d_ff * 4) +
          backward_workspace_bytes(s->T, s->d_ff, s->d_model, s->cap, max_routed);
 }
@@ -415,28 +416,27 @@ int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t,
     return SFFN_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const float l1g = (float)((double)l1_lambda / (double)shape->T);
-  if (shape->dtype == SFFN_F32) {
+  if (backward_general(shape->dtype, shape->d_model)) {
     // complete activity lists of every row: twell_pack's kernels at the full
     // capacity (rows within the forward's capacity get their forward entries,
     // routed rows their complete lists; routed, n_routed and max_routed are
     // not needed)
     sffn_shape full = *shape;
-    full.cap = backward_f32_cap();
+    full.cap = backward_general_cap();
     const size_t nt = (size_t)shape->d_ff / 128, cap = (size_t)full.cap;
     char* p = (char*)workspace + pack_ws(shape);
     uint16_t* count2 = (uint16_t*)p;
     p += align256((size_t)shape->T * nt * 2);
     uint16_t* idx2 = (uint16_t*)p;
     p += align256((size_t)shape->T * nt * cap * 2);
-    float* val2 = (float*)p;
-    p += align256((size_t)shape->T * nt * cap * 4);
+    void* val2 = p;
+    p += align256((size_t)shape->T * nt * cap * elt_bytes(shape->dtype));
     st = pack_impl(&full, x, wg_t, b_g, wg_norms, count2, idx2, val2, workspace, nullptr,
                    nullptr, s);
     if (st != SFFN_OK) return st;
-    return hip_status(launch_backward_f32(
-        (const float*)x, (const float*)wg_t, (const float*)wu_t, (const float*)wd, count2, idx2,
-        val2, (const float*)gy, (float*)gx, gwg_t, gwu_t, gwd, gb, shape->T, shape->d_model,
-        shape->d_ff, l1g, p, s));
+    return hip_status(launch_backward_general(shape->dtype, x, wg_t, wu_t, wd, count2, idx2, val2,
+                                              gy, gx, gwg_t, gwu_t, gwd, gb, shape->T,
+                                              shape->d_model, shape->d_ff, l1g, p, s));
   }
   float* xn = (float*)workspace;
   float* wbuf = (float*)((char*)workspace + align256((size_t)shape->T * 4));

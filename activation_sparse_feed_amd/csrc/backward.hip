@@ -927,28 +927,29 @@ __global__ __launch_bounds__(256) void bwd_gx(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Float32 shapes (d_model up to kF32MaxD).  The entries come from complete
-// activity lists for every row: twell_pack's own kernels run again at the
-// full capacity of 128 per tile (the same exact activity decision, so a row
-// within the forward's capacity gets exactly its forward entries and a routed
-// row its complete list), and no row is routed here.  One wave per row walks
-// its entries for the per-entry gradients and gx (float32 rows, 4 values per
-// lane and chunk); the column lists of the bf16 path (bwd_prep, csc_*) are
-// built on these arrays; one wave per column sums the weight gradients.
-constexpr int kF32Cap = 128;
-constexpr int kF32MaxD = 2048;
+// The general path: float32 shapes, and bf16 widths that are not a multiple
+// of 512 (d_model up to kGenMaxD).  The entries come from complete activity
+// lists for every row: twell_pack's own kernels run again at the full capacity
+// of 128 per tile (the same exact activity decision, so a row within the
+// forward's capacity gets exactly its forward entries and a routed row its
+// complete list), and no row is routed here.  One wave per row walks its
+// entries for the per-entry gradients and gx (rows in 16-byte chunks per lane,
+// the last chunk masked); the column lists of the bf16 path (bwd_prep, csc_*)
+// are built on these arrays; one wave per column sums the weight gradients.
+constexpr int kGenCap = 128;
+constexpr int kGenMaxD = 2048;
 
-struct F32Args {
-  const float* x;
-  const float* wg;
-  const float* wu;
-  const float* wd;
-  const float* gy;
-  const uint16_t* count;  // [T, nt] complete lists (capacity kF32Cap)
-  const uint16_t* idx;    // [T, nt, kF32Cap]
-  const float* val;       // [T, nt, kF32Cap] h
-  f32x4_t* co;            // [T, nt, kF32Cap] (gz, gu, a, 0)
-  float* gx;              // [T, D]
+struct GenArgs {
+  const void* x;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const void* gy;
+  const uint16_t* count;  // [T, nt] complete lists (capacity kGenCap)
+  const uint16_t* idx;    // [T, nt, kGenCap]
+  const void* val;        // [T, nt, kGenCap] h (element type)
+  f32x4_t* co;            // [T, nt, kGenCap] (gz, gu, a, 0)
+  void* gx;               // [T, D] (element type)
   float* gwg;             // [N, D]
   float* gwu;
   float* gwd;
@@ -957,43 +958,51 @@ struct F32Args {
   float l1g;
 };
 
-// this lane's chunks c (4 floats at 4 (64 c + lane)) of a row of D floats
-template <int NCH>
-__device__ __forceinline__ void f32_row(const float* row, int D, f32x4_t* v) {
+// this lane's chunks c (E values at E (64 c + lane)) of a row of D values,
+// unpacked to float32 (zero past D)
+template <typename T, int NCH>
+__device__ __forceinline__ void gen_row(const void* base, size_t row, int D,
+                                        float (*v)[Elt<T>::kPerChunk]) {
+  constexpr int E = Elt<T>::kPerChunk;
+  const T* r = (const T*)base + row * D;
   const int lane = lane_id();
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int e = 4 * (kWave * c + lane);
-    v[c] = e < D ? *(const f32x4_t*)(row + e) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int e = E * (kWave * c + lane);
+    const u32x4_t q = e < D ? ldg16(r + e) : u32x4_t{0u, 0u, 0u, 0u};
+    Elt<T>::unpack(q, v[c]);
   }
 }
 
-template <int NCH>
-__global__ __launch_bounds__(256) void f32_rows(F32Args a) {
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void gen_rows(GenArgs a) {
+  constexpr int E = Elt<T>::kPerChunk;
   const int lane = lane_id();
   const int t = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
   if (t >= a.T) return;
-  f32x4_t xc[NCH], gc[NCH], gxa[NCH];
-  f32_row<NCH>(a.x + (size_t)t * a.D, a.D, xc);
-  f32_row<NCH>(a.gy + (size_t)t * a.D, a.D, gc);
+  float xc[NCH][E], gc[NCH][E], gxa[NCH][E];
+  gen_row<T, NCH>(a.x, t, a.D, xc);
+  gen_row<T, NCH>(a.gy, t, a.D, gc);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) gxa[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < E; ++e) gxa[c][e] = 0.f;
   for (int k = 0; k < a.nt; ++k) {
     const size_t tk = (size_t)t * a.nt + k;
-    const int n = uniform(min((int)a.count[tk], kF32Cap));
+    const int n = uniform(min((int)a.count[tk], kGenCap));
     for (int s = 0; s < n; ++s) {
-      const size_t pos = tk * kF32Cap + s;
+      const size_t pos = tk * kGenCap + s;
       const int j = uniform(min((int)a.idx[pos], a.N - 1));  // valid lists: j < N already
-      const float h = __int_as_float(uniform(__float_as_int(a.val[pos])));
-      f32x4_t uw[NCH], dw[NCH], gw[NCH];
-      f32_row<NCH>(a.wu + (size_t)j * a.D, a.D, uw);
-      f32_row<NCH>(a.wd + (size_t)j * a.D, a.D, dw);
-      f32_row<NCH>(a.wg + (size_t)j * a.D, a.D, gw);
+      const float h = __int_as_float(uniform(__float_as_int(Elt<T>::load1(a.val, pos))));
+      float uw[NCH][E], dw[NCH][E], gw[NCH][E];
+      gen_row<T, NCH>(a.wu, j, a.D, uw);
+      gen_row<T, NCH>(a.wd, j, a.D, dw);
+      gen_row<T, NCH>(a.wg, j, a.D, gw);
       float su = 0.f, sg = 0.f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < E; ++e) {
           su = fmaf(xc[c][e], uw[c][e], su);
           sg = fmaf(gc[c][e], dw[c][e], sg);
         }
@@ -1002,39 +1011,44 @@ __global__ __launch_bounds__(256) void f32_rows(F32Args a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gxa[c][e] = fmaf(gu, uw[c][e], fmaf(gz, gw[c][e], gxa[c][e]));
+        for (int e = 0; e < E; ++e) gxa[c][e] = fmaf(gu, uw[c][e], fmaf(gz, gw[c][e], gxa[c][e]));
       if (lane == 0) a.co[pos] = f32x4_t{gz, gu, h * u, 0.f};
     }
   }
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int e = 4 * (kWave * c + lane);
-    if (e < a.D) *(f32x4_t*)(a.gx + (size_t)t * a.D + e) = gxa[c];
+    const int e0 = E * (kWave * c + lane);
+    if (e0 < a.D)
+#pragma unroll
+      for (int e = 0; e < E; ++e) Elt<T>::store1(a.gx, (size_t)t * a.D + e0 + e, gxa[c][e]);
   }
 }
 
 // One wave per column: its list's entries (row order) summed into the three
 // weight-gradient rows and gb; every column is written (zero when inactive).
-template <int NCH>
-__global__ __launch_bounds__(256) void f32_cols(F32Args a, const int* col_ptr, const f32x4_t* csc) {
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void gen_cols(GenArgs a, const int* col_ptr, const f32x4_t* csc) {
+  constexpr int E = Elt<T>::kPerChunk;
   const int lane = lane_id();
   const int j = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
   if (j >= a.N) return;
-  f32x4_t ag[NCH], au[NCH], ad[NCH];
+  float ag[NCH][E], au[NCH][E], ad[NCH][E];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) ag[c] = au[c] = ad[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < E; ++e) ag[c][e] = au[c][e] = ad[c][e] = 0.f;
   float gbs = 0.f;
   const int e0 = uniform(col_ptr[j]), e1 = uniform(col_ptr[j + 1]);
-  for (int e = e0; e < e1; ++e) {
-    const f32x4_t v = csc[e];
+  for (int i = e0; i < e1; ++i) {
+    const f32x4_t v = csc[i];
     const int t = min(max(__float_as_int(v[0]), 0), a.T - 1);
-    f32x4_t xc[NCH], gc[NCH];
-    f32_row<NCH>(a.x + (size_t)t * a.D, a.D, xc);
-    f32_row<NCH>(a.gy + (size_t)t * a.D, a.D, gc);
+    float xc[NCH][E], gc[NCH][E];
+    gen_row<T, NCH>(a.x, t, a.D, xc);
+    gen_row<T, NCH>(a.gy, t, a.D, gc);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < E; ++q) {
         ag[c][q] = fmaf(v[1], xc[c][q], ag[c][q]);
         au[c][q] = fmaf(v[2], xc[c][q], au[c][q]);
         ad[c][q] = fmaf(v[3], gc[c][q], ad[c][q]);
@@ -1043,15 +1057,39 @@ __global__ __launch_bounds__(256) void f32_cols(F32Args a, const int* col_ptr, c
   }
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int e = 4 * (kWave * c + lane);
+    const int e = E * (kWave * c + lane);
     if (e < a.D) {
       const size_t o = (size_t)j * a.D + e;
-      *(f32x4_t*)(a.gwg + o) = ag[c];
-      *(f32x4_t*)(a.gwu + o) = au[c];
-      *(f32x4_t*)(a.gwd + o) = ad[c];
+#pragma unroll
+      for (int q = 0; q < E; q += 4) {
+        *(f32x4_t*)(a.gwg + o + q) = f32x4_t{ag[c][q], ag[c][q + 1], ag[c][q + 2], ag[c][q + 3]};
+        *(f32x4_t*)(a.gwu + o + q) = f32x4_t{au[c][q], au[c][q + 1], au[c][q + 2], au[c][q + 3]};
+        *(f32x4_t*)(a.gwd + o + q) = f32x4_t{ad[c][q], ad[c][q + 1], ad[c][q + 2], ad[c][q + 3]};
+      }
     }
   }
   if (a.gb && lane == 0) a.gb[j] = gbs;
+}
+
+template <typename T>
+void launch_gen_kernels(const GenArgs& a, const int* col_ptr, const f32x4_t* csc, bool rows,
+                        hipStream_t stream) {
+  constexpr int E = Elt<T>::kPerChunk;
+  const int nch = (a.D / E + kWave - 1) / kWave;  // 16-byte chunks per lane
+  const dim3 blk(256);
+  if (rows) {
+    const dim3 g((unsigned)((a.T + 3) / 4));
+    if (nch <= 1) hipLaunchKernelGGL((gen_rows<T, 1>), g, blk, 0, stream, a);
+    else if (nch <= 2) hipLaunchKernelGGL((gen_rows<T, 2>), g, blk, 0, stream, a);
+    else if (nch <= 4) hipLaunchKernelGGL((gen_rows<T, 4>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((gen_rows<T, 8>), g, blk, 0, stream, a);
+  } else {
+    const dim3 g((unsigned)((a.N + 3) / 4));
+    if (nch <= 1) hipLaunchKernelGGL((gen_cols<T, 1>), g, blk, 0, stream, a, col_ptr, csc);
+    else if (nch <= 2) hipLaunchKernelGGL((gen_cols<T, 2>), g, blk, 0, stream, a, col_ptr, csc);
+    else if (nch <= 4) hipLaunchKernelGGL((gen_cols<T, 4>), g, blk, 0, stream, a, col_ptr, csc);
+    else hipLaunchKernelGGL((gen_cols<T, 8>), g, blk, 0, stream, a, col_ptr, csc);
+  }
 }
 
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1059,35 +1097,38 @@ size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 bool backward_supported(int dtype, int d_model) {
-  if (dtype == 0) return d_model % 4 == 0 && d_model <= kF32MaxD;
-  return dtype == 1 && d_model % 512 == 0 && d_model <= 4096;
+  return (dtype == 1 && d_model % 512 == 0 && d_model <= 4096) || backward_general(dtype, d_model);
 }
 
-int backward_f32_cap() { return kF32Cap; }
+bool backward_general(int dtype, int d_model) {
+  return (dtype == 0 || d_model % 512 != 0) && d_model % 8 == 0 && d_model <= kGenMaxD;
+}
 
-// Float32: tile-major copies, per-entry gradients, column lists of the
-// complete lists (capacity kF32Cap).
-size_t backward_f32_workspace_bytes(int T, int N) {
-  const size_t nt = (size_t)N / kBTile, cap = kF32Cap;
+int backward_general_cap() { return kGenCap; }
+
+// The general path: tile-major copies, per-entry gradients, column lists of
+// the complete lists (capacity kGenCap).
+size_t backward_general_workspace_bytes(int T, int N) {
+  const size_t nt = (size_t)N / kBTile, cap = kGenCap;
   return al256(nt * T * 2) + al256(nt * T * cap * 2) + al256((size_t)T * nt * cap * 16) +
          al256((size_t)((T + kCscRows - 1) / kCscRows) * N * 4) + al256((size_t)N * 4) +
          al256(((size_t)N + 1) * 4) + al256((size_t)T * nt * cap * 16);
 }
 
-hipError_t launch_backward_f32(const float* x, const float* wg_t, const float* wu_t,
-                               const float* wd, const uint16_t* count, const uint16_t* idx,
-                               const float* val, const float* gy, float* gx, float* gwg_t,
-                               float* gwu_t, float* gwd, float* gb, int T, int D, int N, float l1g,
-                               void* ws, hipStream_t stream) {
-  if (D % 4 != 0 || D > kF32MaxD) return hipErrorInvalidValue;
+hipError_t launch_backward_general(int dtype, const void* x, const void* wg_t, const void* wu_t,
+                                   const void* wd, const uint16_t* count, const uint16_t* idx,
+                                   const void* val, const void* gy, void* gx, float* gwg_t,
+                                   float* gwu_t, float* gwd, float* gb, int T, int D, int N,
+                                   float l1g, void* ws, hipStream_t stream) {
+  if (!backward_general(dtype, D)) return hipErrorInvalidValue;
   const int nt = N / kBTile;
   char* p = (char*)ws;
   uint16_t* count_t = (uint16_t*)p;
   p += al256((size_t)nt * T * 2);
   uint16_t* idx_t = (uint16_t*)p;
-  p += al256((size_t)nt * T * kF32Cap * 2);
+  p += al256((size_t)nt * T * kGenCap * 2);
   f32x4_t* co = (f32x4_t*)p;
-  p += al256((size_t)T * nt * kF32Cap * 16);
+  p += al256((size_t)T * nt * kGenCap * 16);
   const int nblk = (T + kCscRows - 1) / kCscRows;
   int* hist = (int*)p;
   p += al256((size_t)nblk * N * 4);
@@ -1108,26 +1149,20 @@ hipError_t launch_backward_f32(const float* x, const float* wg_t, const float* w
   b.D = D;
   b.N = N;
   b.nt = nt;
-  b.cap = kF32Cap;
-  F32Args a{x, wg_t, wu_t, wd, gy, count, idx, val, co, gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, l1g};
-  const dim3 rows_grid((unsigned)((T + 3) / 4)), blk(256);
-  hipLaunchKernelGGL(bwd_prep, rows_grid, blk, 0, stream, b);
-  const int nch = (D / 4 + kWave - 1) / kWave;  // 4-float chunks per lane
-  if (nch <= 1) hipLaunchKernelGGL(f32_rows<1>, rows_grid, blk, 0, stream, a);
-  else if (nch <= 2) hipLaunchKernelGGL(f32_rows<2>, rows_grid, blk, 0, stream, a);
-  else if (nch <= 4) hipLaunchKernelGGL(f32_rows<4>, rows_grid, blk, 0, stream, a);
-  else hipLaunchKernelGGL(f32_rows<8>, rows_grid, blk, 0, stream, a);
+  b.cap = kGenCap;
+  GenArgs a{x, wg_t, wu_t, wd, gy, count, idx, val, co, gx, gwg_t, gwu_t, gwd, gb, T, D, N, nt, l1g};
+  const dim3 blk(256);
+  hipLaunchKernelGGL(bwd_prep, dim3((unsigned)((T + 3) / 4)), blk, 0, stream, b);
+  if (dtype == 0) launch_gen_kernels<float>(a, nullptr, nullptr, true, stream);
+  else launch_gen_kernels<uint16_t>(a, nullptr, nullptr, true, stream);
   hipLaunchKernelGGL(csc_count, dim3((unsigned)(nblk * nt)), dim3(64), 0, stream, b, hist);
   hipLaunchKernelGGL(csc_colscan, dim3((unsigned)((N + 255) / 256)), blk, 0, stream, b, hist,
                      total, nblk);
   hipLaunchKernelGGL(csc_ptr, dim3(1), dim3(1024), 0, stream, (const int*)total, N, col_ptr);
   hipLaunchKernelGGL(csc_fill, dim3((unsigned)(nblk * nt)), dim3(64), 0, stream, b,
                      (const int*)hist, (const int*)col_ptr, csc, 1);
-  const dim3 cols_grid((unsigned)((N + 3) / 4));
-  if (nch <= 1) hipLaunchKernelGGL(f32_cols<1>, cols_grid, blk, 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc);
-  else if (nch <= 2) hipLaunchKernelGGL(f32_cols<2>, cols_grid, blk, 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc);
-  else if (nch <= 4) hipLaunchKernelGGL(f32_cols<4>, cols_grid, blk, 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc);
-  else hipLaunchKernelGGL(f32_cols<8>, cols_grid, blk, 0, stream, a, (const int*)col_ptr, (const f32x4_t*)csc);
+  if (dtype == 0) launch_gen_kernels<float>(a, col_ptr, csc, false, stream);
+  else launch_gen_kernels<uint16_t>(a, col_ptr, csc, false, stream);
   return hipGetLastError();
 }
 

@@ -61,16 +61,19 @@ hipError_t launch_ell_convert(const float* z, const void* x, const void* wg_t, c
 // routed more, gb and the first row of gx are set to NaN.  xnorm: ||x_t|| of every row; wnorm: ||wg_t[j]||.  ws:
 // backward_workspace_bytes().
 bool backward_supported(int dtype, int d_model);
-// Float32 backward: from complete activity lists of every row (twell_pack at
-// capacity backward_f32_cap()): count [T, N/128], idx and val [T, N/128, cap]
-// (val float32); workspace backward_f32_workspace_bytes(T, N).
-int backward_f32_cap();
-size_t backward_f32_workspace_bytes(int T, int N);
-hipError_t launch_backward_f32(const float* x, const float* wg_t, const float* wu_t,
-                               const float* wd, const uint16_t* count, const uint16_t* idx,
-                               const float* val, const float* gy, float* gx, float* gwg_t,
-                               float* gwu_t, float* gwd, float* gb, int T, int D, int N, float l1g,
-                               void* ws, hipStream_t stream);
+// The general backward (float32, and bf16 widths not a multiple of 512; up
+// to d_model 2048): from complete activity lists of every row (twell_pack at
+// capacity backward_general_cap()): count [T, N/128], idx and val
+// [T, N/128, cap] (val in the element type); workspace
+// backward_general_workspace_bytes(T, N).
+bool backward_general(int dtype, int d_model);
+int backward_general_cap();
+size_t backward_general_workspace_bytes(int T, int N);
+hipError_t launch_backward_general(int dtype, const void* x, const void* wg_t, const void* wu_t,
+                                   const void* wd, const uint16_t* count, const uint16_t* idx,
+                                   const void* val, const void* gy, void* gx, float* gwg_t,
+                                   float* gwu_t, float* gwd, float* gb, int T, int D, int N,
+                                   float l1g, void* ws, hipStream_t stream);
 size_t backward_workspace_bytes(int T, int N, int D, int cap, int R);
 
 // The routed rows' backward on MFMA tiles (backward_routed.hip): launched when

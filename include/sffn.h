@@ -240,12 +240,13 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
  * runs in a fixed order: the result is deterministic.  Every element of the outputs is written
  * (weight-gradient rows of inactive columns are zero); gb may be NULL.
  *
- * bf16 with d_model % 512 == 0 and d_model <= 4096, or float32 with
- * d_model <= 2048 (else SFFN_ERR_UNSUPPORTED), plus twell_pack's size limits.
- * Float32 takes the entries of every row from complete activity lists that it
- * rebuilds with twell_pack's own kernels at the full capacity of 128 per tile
- * (the same exact activity decision; routed rows included, so routed,
- * n_routed and max_routed are not read, and the workspace does not depend on
+ * bf16 with d_model % 512 == 0 and d_model <= 4096, or any other d_model
+ * up to 2048 in bf16 or float32 (else SFFN_ERR_UNSUPPORTED), plus
+ * twell_pack's size limits.  The latter (the general path) takes the entries
+ * of every row from complete activity lists that it rebuilds with
+ * twell_pack's own kernels at the full capacity of 128 per tile (the same
+ * exact activity decision; routed rows included, so routed, n_routed and
+ * max_routed are not read, and the workspace does not depend on
  * max_routed).  gy, gx: [T, d_model]
  * dtype; gwg_t, gwu_t, gwd: float32 [d_ff, d_model]; gb: float32 [d_ff].
  * wg_norms as for twell_pack (or NULL); routed and n_routed of the same
@@ -256,8 +257,8 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
  * gb (when given) and the first row of gx are set to NaN.  workspace: at
  * least sparse_ffn_bwd_workspace_bytes(shape, max_routed) bytes (about
  * 20 max_routed d_ff + 32 max_routed d_model bytes for the routed rows plus
- * about 20 T n_tiles cap bytes for the TwELL entries in bf16; about 40 T d_ff
- * bytes in float32), no initial contents; calls sharing it must be
+ * about 20 T n_tiles cap bytes for the TwELL entries; about 40 T d_ff bytes
+ * on the general path), no initial contents; calls sharing it must be
  * stream-ordered.
  */
 int32_t sparse_ffn_bwd(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,

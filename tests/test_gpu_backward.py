@@ -189,14 +189,28 @@ def test_backward_float32(case):
         assert e["n_routed"] > 10
 
 
+@pytest.mark.parametrize("T,d_model,d_ff,beta,cap,lam", [
+    (300, 264, 384, 1.5, 4, 0.0),    # one masked chunk per lane row, routed rows
+    (64, 768, 512, 1.2, 8, 0.2),     # a common width, many routed rows, the L1 term
+    (257, 1288, 256, 1.9, 2, 0.0),   # three chunks, the last one partly masked
+])
+def test_backward_bf16_general_width(T, d_model, d_ff, beta, cap, lam):
+    """bf16 widths that are not a multiple of 512 take the general path
+    (complete lists of every row, as for float32) within the bf16 tolerance."""
+    inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype="bf16", beta=beta,
+                             seed_base=160 + d_model, cap=cap)
+    e = check(inp, cap, dense=True, lam=lam)
+    assert e["n_routed"] > 0
+
+
 def test_backward_rejects_unsupported_width():
     sffn = _sffn()
-    s = sffn.make_shape(64, 264, 256, 8, sffn.SFFN_BF16)
+    s = sffn.make_shape(64, 2056, 256, 8, sffn.SFFN_BF16)  # not a multiple of 512, over 2048
     ws = torch.empty(max(sffn.workspace_bytes(s, sffn.WS_BACKWARD), 16), dtype=torch.uint8,
                      device="cuda")
-    b = torch.zeros((64, 264), dtype=torch.bfloat16, device="cuda")
-    w = torch.zeros((256, 264), dtype=torch.bfloat16, device="cuda")
-    g = [torch.zeros((256, 264), device="cuda") for _ in range(3)]
+    b = torch.zeros((64, 2056), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((256, 2056), dtype=torch.bfloat16, device="cuda")
+    g = [torch.zeros((256, 2056), device="cuda") for _ in range(3)]
     c = torch.zeros((64, 2), dtype=torch.uint16, device="cuda")
     i = torch.zeros((64, 2, 8), dtype=torch.uint16, device="cuda")
     v = torch.zeros((64, 2, 8), dtype=torch.bfloat16, device="cuda")
