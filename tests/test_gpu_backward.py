@@ -203,6 +203,41 @@ def test_backward_bf16_general_width(T, d_model, d_ff, beta, cap, lam):
     assert e["n_routed"] > 0
 
 
+@pytest.mark.parametrize("T,d_model,d_ff,dtype,beta,cap", [
+    (8200, 1024, 1024, "bf16", 1.0, 2),   # routed rows on MFMA tiles (recomputed gate)
+    (300, 512, 1024, "bf16", 1.9, 4),     # per-entry routed rows
+    (130, 200, 384, "f32", 1.2, 2),       # the general path (complete lists of every row)
+])
+def test_backward_precomputed_weight_norms(T, d_model, d_ff, dtype, beta, cap):
+    """The gate-weight row norms only set the guard band of the recomputed
+    activity decisions, which are exact: passing twell_weight_norms' result
+    gives the same gradients, bit for bit, as letting the call compute them."""
+    sffn = _sffn()
+    inp = wl.generate_custom(T=T, d_model=d_model, d_ff=d_ff, dtype=dtype, beta=beta,
+                             seed_base=170 + d_model, cap=cap)
+    w = inp.workload
+    d = device_inputs(inp)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    ffn = sffn.SparseFFN(T, d_model, d_ff, cap, dt)
+    wn = ffn.weight_norms(d["wg_t"])
+    ffn.forward(d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], wn)
+    s = ffn.shape
+    gy = to_device(wl.upstream_grad(w), dtype)
+    ws = sffn.alloc_workspace(s, sffn.WS_BACKWARD)
+    outs = []
+    for norms in (None, wn):
+        gx = torch.empty((T, d_model), dtype=dt, device="cuda")
+        g = [torch.empty((d_ff, d_model), device="cuda") for _ in range(3)]
+        gb = torch.empty(d_ff, device="cuda")
+        sffn.sparse_ffn_bwd(s, d["x"], d["wg_t"], d["b_g"], d["wu_t"], d["wd"], ffn.count,
+                            ffn.idx, ffn.val, ffn.routed, ffn.n_routed, gy, gx, *g, gb, ws, norms)
+        torch.cuda.synchronize()
+        outs.append([gx.view(torch.int16) if dt == torch.bfloat16 else gx] + g + [gb])
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
+    assert int(ffn.n_routed.item()) > 0
+
+
 def test_backward_rejects_unsupported_width():
     sffn = _sffn()
     s = sffn.make_shape(64, 2056, 256, 8, sffn.SFFN_BF16)  # not a multiple of 512, over 2048
