@@ -927,8 +927,8 @@ __global__ __launch_bounds__(256) void bwd_gx(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The general path: float32 shapes, and bf16 widths that are not a multiple
-// of 512 (d_model up to kGenMaxD).  The entries come from complete activity
+// The general path: float32 shapes (d_model up to 2048), and bf16 widths that
+// are not a multiple of 512 (up to 4096): at most 8 16-byte chunks per lane.  The entries come from complete activity
 // lists for every row: twell_pack's own kernels run again at the full capacity
 // of 128 per tile (the same exact activity decision, so a row within the
 // forward's capacity gets exactly its forward entries and a routed row its
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(256) void bwd_gx(BwdArgs a) {
 // the last chunk masked); the column lists of the bf16 path (bwd_prep, csc_*)
 // are built on these arrays; one wave per column sums the weight gradients.
 constexpr int kGenCap = 128;
-constexpr int kGenMaxD = 2048;
+constexpr int kGenMaxChunks = 8;  // 16-byte chunks per lane and row
 
 struct GenArgs {
   const void* x;
@@ -1101,7 +1101,9 @@ bool backward_supported(int dtype, int d_model) {
 }
 
 bool backward_general(int dtype, int d_model) {
-  return (dtype == 0 || d_model % 512 != 0) && d_model % 8 == 0 && d_model <= kGenMaxD;
+  const int per_chunk = dtype == 0 ? 4 : 8;  // values per 16 bytes
+  return (dtype == 0 || d_model % 512 != 0) && d_model % 8 == 0 &&
+         d_model <= kGenMaxChunks * kWave * per_chunk;
 }
 
 int backward_general_cap() { return kGenCap; }

@@ -340,11 +340,9 @@ def training_memory(w, x, wg, b, wu, wd, wg_norms, gy) -> dict:
 
 
 def backward_ok(w) -> bool:
-    """Shapes sparse_ffn_bwd takes: bf16 with d_model a multiple of 512 up to
-    4096, any other width (a multiple of 8) up to 2048 in bf16 or float32."""
-    if w.dtype == "bf16" and w.d_model % 512 == 0:
-        return w.d_model <= 4096
-    return w.d_model % 8 == 0 and w.d_model <= 2048
+    """Shapes sparse_ffn_bwd takes: bf16 up to d_model 4096 (any multiple of
+    8), float32 up to 2048."""
+    return w.d_model % 8 == 0 and w.d_model <= (4096 if w.dtype == "bf16" else 2048)
 
 
 def d_model_ok(d_model: int) -> bool:

@@ -240,9 +240,9 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t,
  * runs in a fixed order: the result is deterministic.  Every element of the outputs is written
  * (weight-gradient rows of inactive columns are zero); gb may be NULL.
  *
- * bf16 with d_model % 512 == 0 and d_model <= 4096, or any other d_model
- * up to 2048 in bf16 or float32 (else SFFN_ERR_UNSUPPORTED), plus
- * twell_pack's size limits.  The latter (the general path) takes the entries
+ * bf16 with d_model <= 4096 or float32 with d_model <= 2048 (else
+ * SFFN_ERR_UNSUPPORTED), plus twell_pack's size limits.  Float32 and bf16
+ * widths that are not a multiple of 512 take the general path: the entries
  * of every row from complete activity lists that it rebuilds with
  * twell_pack's own kernels at the full capacity of 128 per tile (the same
  * exact activity decision; routed rows included, so routed, n_routed and

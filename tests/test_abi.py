@@ -199,8 +199,8 @@ def test_backward_errors(sffn):
     bad = list(args)
     bad[9] = MISALIGNED  # routed
     assert lib.sparse_ffn_bwd(ctypes.byref(s), *bad, WS, need, None) == -1
-    # bf16 widths not a multiple of 512 are taken up to 2048 (the general path)
-    s264 = _shape(sffn, d_model=2056)
+    # bf16 is taken up to d_model 4096
+    s264 = _shape(sffn, d_model=4104)
     n264 = sffn.workspace_bytes(s264, sffn.WS_BACKWARD)
     assert lib.sparse_ffn_bwd(ctypes.byref(s264), *args, WS, n264, None) == -2
     # float32 is taken up to d_model 2048

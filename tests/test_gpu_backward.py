@@ -193,6 +193,7 @@ def test_backward_float32(case):
     (300, 264, 384, 1.5, 4, 0.0),    # one masked chunk per lane row, routed rows
     (64, 768, 512, 1.2, 8, 0.2),     # a common width, many routed rows, the L1 term
     (257, 1288, 256, 1.9, 2, 0.0),   # three chunks, the last one partly masked
+    (100, 2304, 256, 1.7, 2, 0.0),   # wider than 2048: five chunks per lane
 ])
 def test_backward_bf16_general_width(T, d_model, d_ff, beta, cap, lam):
     """bf16 widths that are not a multiple of 512 take the general path
@@ -240,12 +241,12 @@ def test_backward_precomputed_weight_norms(T, d_model, d_ff, dtype, beta, cap):
 
 def test_backward_rejects_unsupported_width():
     sffn = _sffn()
-    s = sffn.make_shape(64, 2056, 256, 8, sffn.SFFN_BF16)  # not a multiple of 512, over 2048
+    s = sffn.make_shape(64, 4104, 256, 8, sffn.SFFN_BF16)  # wider than 4096
     ws = torch.empty(max(sffn.workspace_bytes(s, sffn.WS_BACKWARD), 16), dtype=torch.uint8,
                      device="cuda")
-    b = torch.zeros((64, 2056), dtype=torch.bfloat16, device="cuda")
-    w = torch.zeros((256, 2056), dtype=torch.bfloat16, device="cuda")
-    g = [torch.zeros((256, 2056), device="cuda") for _ in range(3)]
+    b = torch.zeros((64, 4104), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((256, 4104), dtype=torch.bfloat16, device="cuda")
+    g = [torch.zeros((256, 4104), device="cuda") for _ in range(3)]
     c = torch.zeros((64, 2), dtype=torch.uint16, device="cuda")
     i = torch.zeros((64, 2, 8), dtype=torch.uint16, device="cuda")
     v = torch.zeros((64, 2, 8), dtype=torch.bfloat16, device="cuda")
