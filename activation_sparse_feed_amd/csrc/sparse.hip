@@ -269,6 +269,15 @@ __global__ __launch_bounds__(WAVES * 64) void sparse_updown_win(SparseArgs a) {
       if (n > 0) load_row(ur, row_j(0));
       int i = 0;
       for (; i + 1 < n; i += 2) {
+        // the waves with the most entries left set the window's length (the
+        // others wait at its barrier): they issue first
+        {
+          const int rem = n - i;
+          if (rem >= 8) __builtin_amdgcn_s_setprio(3);
+          else if (rem >= 5) __builtin_amdgcn_s_setprio(2);
+          else if (rem >= 3) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
+        }
         const float h0 = list_h[w][i], h1 = list_h[w][i + 1];
         load_row(dr0, drow_j(i));
         const float p0 = dot_x(ur);
