@@ -278,18 +278,24 @@ int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t, c
   hipStream_t s = (hipStream_t)stream;
   const int T = shape->T, K = shape->d_model, N = shape->d_ff;
   void* h = (char*)workspace + route_workspace_bytes(T);
-  const bool fused_route = routed_fast_path(shape) && T <= kRouteBlock;
   hipError_t e = hipSuccess;
-  if (!fused_route) {
-    e = launch_route(count, T, N / 128, shape->cap, routed, n_routed, workspace, s);
-    if (e != hipSuccess) return SFFN_ERR_HIP;
-  }
   if (routed_fast_path(shape)) {
+    // the MFMA fallback's gate+up kernel compacts the routed rows itself:
+    // from the TwELL counts (few tokens) or from the routed-row mask
+    const bool fused_route = T <= kRouteBlock;
+    uint16_t* mask = (uint16_t*)workspace;
+    if (!fused_route) {
+      e = launch_route_mask(count, T, N / 128, shape->cap, mask, s);
+      if (e != hipSuccess) return SFFN_ERR_HIP;
+    }
     float* partial = (float*)((char*)h + align256((size_t)T * N * elt_bytes(shape->dtype)));
     return hip_status(launch_routed_ffn(x, wg_t, b_g, wu_t, wd, h, y, partial, T, routed,
-                                        n_routed, fused_route ? count : nullptr, N / 128,
-                                        shape->cap, K, N, s));
+                                        n_routed, fused_route ? count : nullptr,
+                                        fused_route ? nullptr : mask, N / 128, shape->cap, K, N,
+                                        s));
   }
+  e = launch_route(count, T, N / 128, shape->cap, routed, n_routed, workspace, s);
+  if (e != hipSuccess) return SFFN_ERR_HIP;
   e = launch_dense_gateup(shape->dtype, x, wg_t, b_g, wu_t, h, T, routed, n_routed, K, N, s);
   if (e != hipSuccess) return SFFN_ERR_HIP;
   e = launch_down(shape->dtype, h, wd, y, T, routed, n_routed, N, K, s);

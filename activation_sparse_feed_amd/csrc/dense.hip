@@ -39,6 +39,12 @@ struct DenseArgs {
   int route_nt = 0, route_cap = 0;
   int32_t* routed_out = nullptr;
   int32_t* n_routed_out = nullptr;
+  // routed gate+up only: when route_mask is set (many tokens), each workgroup
+  // finds its tiles' routed rows in the route_flags mask of route_groups
+  // words and writes its share of routed_out (and workgroup 0 n_routed_out);
+  // the row map and device count are then left to the kernels after it.
+  const uint16_t* route_mask = nullptr;
+  int route_groups = 0;
   // fused route only: per-output-tile split counters of the down GEMM, zeroed
   // by workgroup 0 of the routed gate+up before the down GEMM runs
   int* tile_count = nullptr;
@@ -255,9 +261,14 @@ constexpr int kRoutedMaxSplit = 8;   // K splits of the routed down GEMM
 
 // gate+up of the routed rows for one Gemm2 configuration: tiles
 // blockIdx.x, blockIdx.x + gridDim.x, ... of the mt x nt tiles.
+// ranks (mask mode): each tile's rows are written from the mask into the
+// start of the pipeline LDS, read into the loaders' offsets, and released
+// before the ring is filled.
 template <typename G>
-__device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, uint8_t* lds) {
+__device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, uint8_t* lds,
+                                                    const MaskRanks* ranks = nullptr) {
   constexpr int TW = G::BN / 2;  // columns of each of the two B matrices per tile
+  static_assert(G::LDS_BYTES >= G::BM * 4, "a tile's row list fits the pipeline LDS");
   const int mt = (mv + G::BM - 1) / G::BM, nt = a.N / TW;
   const int lane = lane_id();
   const int w = uniform((int)(threadIdx.x >> 6));
@@ -267,7 +278,16 @@ __device__ __forceinline__ void gateup_routed_tiles(const DenseArgs& a, int mv, 
   G g;
   for (int tile = (int)blockIdx.x; tile < mt * nt; tile += (int)gridDim.x) {
     const int m0 = (tile % mt) * G::BM, n0 = (tile / mt) * TW;
-    g.init((const uint16_t*)a.a, (size_t)a.M, a.rowmap, m0, mv, B, n0, a.N, a.K);
+    if (ranks) {
+      int* rows_s = (int*)lds;
+      __syncthreads();  // the previous tile's ring reads are done
+      ranks->emit(a.route_mask, m0, min(mv, m0 + G::BM), rows_s);
+      __syncthreads();
+      g.init((const uint16_t*)a.a, (size_t)a.M, rows_s, 0, min(G::BM, mv - m0), B, n0, a.N, a.K);
+      __syncthreads();  // every wave holds its row offsets
+    } else {
+      g.init((const uint16_t*)a.a, (size_t)a.M, a.rowmap, m0, mv, B, n0, a.N, a.K);
+    }
     g.run_pipe(lds, a.K);
 #pragma unroll
     for (int fn = 0; fn < G::FN; ++fn) {
@@ -325,6 +345,19 @@ __global__ __launch_bounds__(256, 2) void gateup_routed(DenseArgs a) {
     }
     a.rowmap = rows_s;
     gateup_routed_tiles<RoutedFused>(a, mv, lds);
+  } else if (a.route_mask) {
+    // the routed list from the mask: this workgroup's share of it for the
+    // kernels after this one, and its own tiles' rows (wave totals of the
+    // scan in the pipeline LDS past the largest tile's row list)
+    MaskRanks ranks;
+    ranks.init(a.route_mask, a.route_groups, (int*)lds + 256);
+    const int mv = uniform(ranks.total);
+    const int share = (mv + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int lo = min(mv, (int)blockIdx.x * share);
+    ranks.emit(a.route_mask, lo, min(mv, lo + share), a.routed_out + lo);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.n_routed_out = mv;
+    if (mv <= kRoutedBigRows) gateup_routed_tiles<RoutedSmall>(a, mv, lds, &ranks);
+    else if (!a.routed_wide) gateup_routed_tiles<RoutedBig>(a, mv, lds, &ranks);
   } else {
     const int mv = uniform(rows_valid(a));  // scalar: the tile loop and buffer descriptors stay uniform
     if (mv <= kRoutedBigRows) gateup_routed_tiles<RoutedSmall>(a, mv, lds);
@@ -582,8 +615,8 @@ size_t routed_partial_bytes(int T, int N, int K) {
 hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
                              const void* wd, void* h, void* y, float* partial, int T,
                              int32_t* routed, int32_t* n_routed, const uint16_t* route_count,
-                             int route_nt, int route_cap, int d_model, int d_ff,
-                             hipStream_t stream) {
+                             const uint16_t* route_mask, int route_nt, int route_cap,
+                             int d_model, int d_ff, hipStream_t stream) {
   // h [rows, d_ff] = gate+up of the routed rows of x
   DenseArgs g{x, wg_t, wu_t, b_g, h, routed, n_routed, T, d_model, d_ff};
   // fused route (few tokens): the down GEMM's splits are summed by the last
@@ -599,6 +632,11 @@ hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, 
     tile_count = (int*)((char*)partial + routed_partial_core_bytes(T, d_model, d_ff));
     g.tile_count = tile_count;
     g.tile_count_n = count_n;
+  } else if (route_mask) {
+    g.route_mask = route_mask;
+    g.route_groups = route_mask_words(T);
+    g.routed_out = routed;
+    g.n_routed_out = n_routed;
   }
   // from kRoutedWideTokens tokens on, counts above kRoutedBigRows go to the
   // eight-wave kernels launched after the four-wave ones (which then return

@@ -123,15 +123,16 @@ hipError_t launch_down(int dtype, const void* h, const void* wd, void* y, int M,
 // Dense FFN of the routed rows (hybrid fallback), row count on the device:
 // h [T, d_ff] (first n_routed rows used) and partial (routed_partial_bytes)
 // are workspace; y rows routed[m] are written.  bf16, d_model and d_ff
-// multiples of 32.  With route_count (T <= kRouteBlock), the routed rows are
-// found from the TwELL counts inside the gate+up kernel, which also writes
-// routed and n_routed; otherwise they are read from routed and n_routed.
+// multiples of 32.  The gate+up kernel finds the routed rows and writes
+// routed and n_routed for the kernels after it: with route_count
+// (T <= kRouteBlock) from the TwELL counts, else from route_mask (the
+// route_flags mask, launch_route_mask).
 size_t routed_partial_bytes(int T, int d_model, int d_ff);
 hipError_t launch_routed_ffn(const void* x, const void* wg_t, const float* b_g, const void* wu_t,
                              const void* wd, void* h, void* y, float* partial, int T,
                              int32_t* routed, int32_t* n_routed, const uint16_t* route_count,
-                             int route_nt, int route_cap, int d_model, int d_ff,
-                             hipStream_t stream);
+                             const uint16_t* route_mask, int route_nt, int route_cap,
+                             int d_model, int d_ff, hipStream_t stream);
 
 // Dense gated FFN for few tokens (split-K weight streams): bf16, M <= 32,
 // d_model and d_ff multiples of 128.  h [M, d_ff] and partial
@@ -151,9 +152,14 @@ hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, cons
                                 void* y, void* ws, int T, int K, int n_tiles, int cap,
                                 hipStream_t stream);
 
-// Routing scan: flags, per-block counts, ascending compaction.
+// Routing scan: the routed-row mask (one 16-bit word per 16 rows, at the
+// start of ws), then the ascending compaction into routed and n_routed.
 size_t route_workspace_bytes(int T);
+int route_mask_words(int T);
 hipError_t launch_route(const uint16_t* count, int T, int n_tiles, int cap, int32_t* routed,
                         int32_t* n_routed, void* ws, hipStream_t stream);
+// The mask alone (route_mask_words(T) words), for launch_routed_ffn.
+hipError_t launch_route_mask(const uint16_t* count, int T, int n_tiles, int cap, uint16_t* mask,
+                             hipStream_t stream);
 
 }  // namespace sffn

@@ -51,4 +51,63 @@ __device__ __forceinline__ int route_rows_lds(const uint16_t* __restrict__ count
   return n;
 }
 
+// Routed-row mask: bit i of word g is set when row 16 g + i is routed
+// (route_flags writes it, one word per 16 rows).  MaskRanks turns it into the
+// ascending routed list inside one 256-thread workgroup: init gives each
+// thread a run of words and the number of routed rows before them (one block
+// scan), after which emit writes any range of ranks with no further scan, so
+// the consumers of the list can build the parts they need themselves.
+struct MaskRanks {
+  int g0, g1;   // this thread's words
+  int before;   // routed rows in the words before g0
+  int total;    // routed rows in all (the same in every thread)
+
+  // wave_s: kRouteBlock / kWave ints of LDS; ends with a barrier.
+  __device__ __forceinline__ void init(const uint16_t* __restrict__ mask, int groups,
+                                       int* wave_s) {
+    const int per = (groups + kRouteBlock - 1) / kRouteBlock;
+    const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+    g0 = min(groups, (int)threadIdx.x * per);
+    g1 = min(groups, g0 + per);
+    int c = 0;
+    for (int g = g0; g < g1; ++g) c += __popc((uint32_t)mask[g]);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (lane == kWave - 1) wave_s[w] = incl;
+    __syncthreads();
+    before = incl - c;
+    total = 0;
+    for (int i = 0; i < kRouteBlock / kWave; ++i) {
+      const int t = wave_s[i];
+      before += i < w ? t : 0;
+      total += t;
+    }
+    __syncthreads();
+  }
+
+  // out[r - lo] = the routed row of rank r, for lo <= r < hi.
+  __device__ __forceinline__ void emit(const uint16_t* __restrict__ mask, int lo, int hi,
+                                       int* out) const {
+    int r = before;
+    for (int g = g0; g < g1 && r < hi; ++g) {
+      uint32_t m = mask[g];
+      const int n = __popc(m);
+      if (r + n <= lo) {
+        r += n;
+        continue;
+      }
+      while (m != 0u) {
+        const int i = __ffs(m) - 1;
+        m &= m - 1u;
+        if (r >= lo && r < hi) out[r - lo] = 16 * g + i;
+        ++r;
+      }
+    }
+  }
+};
+
 }  // namespace sffn

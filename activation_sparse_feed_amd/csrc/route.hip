@@ -2,13 +2,15 @@
 // tokens that do not fit the compact format are diverted to a dense path).
 //
 // A row is routed when any of its TwELL tiles holds more active columns than
-// the capacity.  Two small kernels, no atomics, deterministic:
+// the capacity.  Small kernels, no atomics, deterministic:
 //   route_flags    per row (lanes over the tiles): flag = OR_k (count[t, k] > cap),
-//                  and the number of flagged rows of each 16-row group
-//   route_compact  each 256-row block adds the group counts before it, then
-//                  writes its flagged rows in ascending order; the last block
-//                  writes n_routed.
+//                  written as a mask of one 16-bit word per 16 rows
+//   route_compact  each 256-row block counts the routed rows of the words
+//                  before it, then writes its routed rows in ascending order;
+//                  the last block writes n_routed.
 // With at most 256 rows, one workgroup does both (route_small, route.cuh).
+// The MFMA fallback needs only route_flags: its gate+up kernel builds the
+// list from the mask itself (MaskRanks, route.cuh), one launch fewer.
 #include "common.cuh"
 #include "launch.h"
 #include "route.cuh"
@@ -22,8 +24,8 @@ constexpr int kBlock = 256;
 constexpr int kFlagRows = 16;  // rows per workgroup of route_flags (4 per wave)
 
 __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict__ count, int T,
-                                                      int nt, int cap, int* __restrict__ flags,
-                                                      int* __restrict__ group_count) {
+                                                      int nt, int cap,
+                                                      uint16_t* __restrict__ mask) {
   // wave w takes rows w, w + 4, ... of the workgroup's 16; for each row the
   // lanes read the tiles' counts side by side (coalesced), all four rows'
   // loads in flight together
@@ -37,32 +39,28 @@ __global__ __launch_bounds__(kBlock) void route_flags(const uint16_t* __restrict
     if (t < T)
       for (int k = lane; k < nt; k += kWave) over[u] |= (int)count[(size_t)t * nt + k] > cap;
   }
-  __shared__ int wave_n[kBlock / kWave];
-  int n = 0;
+  __shared__ int wave_bits[kBlock / kWave];
+  int bits = 0;
 #pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int t = blockIdx.x * kFlagRows + u * 4 + w;
-    const int f = __ballot(over[u]) != 0ull;
-    if (t < T && lane == 0) flags[t] = f;
-    n += f;
-  }
-  if (lane == 0) wave_n[w] = n;
+  for (int u = 0; u < R; ++u)
+    if (__ballot(over[u]) != 0ull) bits |= 1 << (u * 4 + w);  // row u * 4 + w of the 16
+  if (lane == 0) wave_bits[w] = bits;
   __syncthreads();
   if (threadIdx.x == 0)
-    group_count[blockIdx.x] = (wave_n[0] + wave_n[1]) + (wave_n[2] + wave_n[3]);
+    mask[blockIdx.x] = (uint16_t)((wave_bits[0] | wave_bits[1]) | (wave_bits[2] | wave_bits[3]));
 }
 
-__global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ flags, int T,
-                                                        const int* __restrict__ group_count,
+__global__ __launch_bounds__(kBlock) void route_compact(const uint16_t* __restrict__ mask, int T,
                                                         int32_t* __restrict__ routed,
                                                         int32_t* __restrict__ n_routed) {
   __shared__ int wave_tot[kBlock / kWave];
   __shared__ int prefix_s;
   const int b = blockIdx.x;
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  // flagged rows before this block: the counts of the 16-row groups before it
+  // routed rows before this block: the set bits of the words before it
   int acc = 0;
-  for (int i = threadIdx.x; i < b * (kBlock / kFlagRows); i += kBlock) acc += group_count[i];
+  for (int i = threadIdx.x; i < b * (kBlock / kFlagRows); i += kBlock)
+    acc += __popc((uint32_t)mask[i]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
   if (lane == 0) wave_tot[w] = acc;
@@ -77,7 +75,7 @@ __global__ __launch_bounds__(kBlock) void route_compact(const int* __restrict__ 
   __syncthreads();
   // in-block scan of the flags
   const int t = b * kBlock + threadIdx.x;
-  const int f = (t < T) ? flags[t] : 0;
+  const int f = (t < T) ? ((int)mask[t / kFlagRows] >> (t % kFlagRows)) & 1 : 0;
   const uint64_t m = __ballot(f);
   if (lane == 0) wave_tot[w] = __popcll(m);
   __syncthreads();
@@ -106,8 +104,16 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t route_workspace_bytes(int T) {
-  const int groups = (T + kFlagRows - 1) / kFlagRows;
-  return align256((size_t)T * 4) + align256((size_t)groups * 4);
+  return align256((size_t)route_mask_words(T) * 2);
+}
+
+int route_mask_words(int T) { return (T + kFlagRows - 1) / kFlagRows; }
+
+hipError_t launch_route_mask(const uint16_t* count, int T, int n_tiles, int cap, uint16_t* mask,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(route_flags, dim3((unsigned)route_mask_words(T)), dim3(kBlock), 0, stream,
+                     count, T, n_tiles, cap, mask);
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const uint16_t* count, int T, int n_tiles, int cap, int32_t* routed,
@@ -117,15 +123,11 @@ hipError_t launch_route(const uint16_t* count, int T, int n_tiles, int cap, int3
                        routed, n_routed);
     return hipGetLastError();
   }
-  const int groups = (T + kFlagRows - 1) / kFlagRows;
-  int* flags = (int*)ws;
-  int* group_count = (int*)((char*)ws + align256((size_t)T * 4));
-  hipLaunchKernelGGL(route_flags, dim3((unsigned)groups), dim3(kBlock), 0, stream, count, T,
-                     n_tiles, cap, flags, group_count);
-  hipError_t e = hipGetLastError();
+  uint16_t* mask = (uint16_t*)ws;
+  hipError_t e = launch_route_mask(count, T, n_tiles, cap, mask, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_compact, dim3((unsigned)((T + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                     stream, flags, T, group_count, routed, n_routed);
+                     stream, mask, T, routed, n_routed);
   return hipGetLastError();
 }
 
