@@ -16,7 +16,7 @@ import torch
 
 from activation_sparse_feed_amd import workloads as wl
 from helpers import (check_twell, check_y, device_inputs, oracle_rows, oracle_twell_all_rows,
-                     sample_rows, to_f64)
+                     row_magnitude, sample_rows, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,8 @@ def compare(inp: wl.Inputs, cap: int, rows=None, ffn=None, y=None) -> dict:
         assert n_r == len(ref["routed"])
     mask = np.zeros(len(rows), dtype=bool)
     mask[ref["routed"]] = True
-    errs = check_y(w.dtype, to_f64(y[rows]), ref["y"], mask)
+    mag = row_magnitude(inp, rows) if w.dtype == "f32" else None
+    errs = check_y(w.dtype, to_f64(y[rows]), ref["y"], mask, mag)
     errs["n_routed"] = n_r
     print(f"{w.name}: rows {len(rows)}/{T} routed {n_r} rel_err {errs['all']:.3e} "
           f"max_row {errs['max_row']:.3e}")
@@ -74,11 +75,14 @@ def test_tiny_f32_all_rows():
     assert e["n_routed"] == 0
 
 
-def test_bf16_ragged_tail_with_routing():
-    inp = wl.generate_custom(T=300, d_model=512, d_ff=1024, dtype="bf16", beta=1.9,
+@pytest.mark.parametrize("beta", [1.9, 2.3])  # most rows routed; about one in eight
+def test_bf16_ragged_tail_with_routing(beta):
+    # 300 tokens: the routed-row mask with a ragged last word (300 = 18 x 16 + 12),
+    # compacted inside the fallback's gate+up kernel
+    inp = wl.generate_custom(T=300, d_model=512, d_ff=1024, dtype="bf16", beta=beta,
                              seed_base=11, cap=4)
     e = compare(inp, 4)
-    assert e["n_routed"] > 0
+    assert 0 < e["n_routed"] < 300
 
 
 def test_f32_ragged_tail_with_routing():
@@ -86,6 +90,16 @@ def test_f32_ragged_tail_with_routing():
                              seed_base=12, cap=3)
     e = compare(inp, 3)
     assert e["n_routed"] > 0
+
+
+def test_f32_many_tokens_with_routing():
+    # more than 256 tokens in float32: the routed-row mask, then the separate
+    # compaction kernel (the float32 fallback has no fused scan); a ragged last
+    # mask word (600 = 37 x 16 + 8)
+    inp = wl.generate_custom(T=600, d_model=264, d_ff=384, dtype="f32", beta=2.3,
+                             seed_base=13, cap=3)
+    e = compare(inp, 3)
+    assert 0 < e["n_routed"] < 600
 
 
 def test_prefill_full_size_all_rows():
