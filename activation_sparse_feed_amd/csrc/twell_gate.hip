@@ -325,9 +325,9 @@ __global__ __launch_bounds__(256) void gate_twell_f32(GateArgs a) {
   }
 }
 
-// Few tokens (T <= 64, e.g. decode): the gate GEMM is a stream of wg_t, and
-// a grid of one workgroup per column tile would leave most CUs idle.  Two
-// kernels:
+// Few tokens (T <= 64, e.g. decode, or up to 128 with d_model % 64 == 0): the
+// gate GEMM is a stream of wg_t, and a grid of one workgroup per column tile
+// (or per 256-row tile) would leave most CUs idle.  Two kernels:
 //
 // gate_skinny_partial: workgroup = (column tile kt, K split s) of S splits;
 // its four waves take consecutive quarters of the split's K range (at most
@@ -467,6 +467,10 @@ __global__ __launch_bounds__(256) void gate_skinny_partial(GateArgs a, float* pa
         (redsq[i] + redsq[2 * SK::ROWS + i]) + (redsq[SK::ROWS + i] + redsq[3 * SK::ROWS + i]);
 }
 
+template <int MF>
+constexpr int kStreamBK = 64;     // K depth of a stage of the streaming kernel
+constexpr int kStreamWgs8 = 256;  // workgroups of the streaming kernel above 64 tokens
+
 // gate_skinny_stream (d_model % 64 == 0): the same partials from a workgroup
 // that streams its tile's wg_t rows over its split's K range through an LDS
 // ring (the buffer-load pipeline with an A tile of the 16 MF token rows; every
@@ -475,7 +479,7 @@ __global__ __launch_bounds__(256) void gate_skinny_partial(GateArgs a, float* pa
 // one workgroup per (tile, split) with S chosen so that the grid fits the chip
 // at once (about one workgroup per CU).  Wave 0 also sums the squares of the x values it feeds to the MFMA.
 template <int MF>
-using StreamGemm = Gemm2<1, kTile, false, 64, 4, false, 16 * MF, 4, 4>;
+using StreamGemm = Gemm2<1, kTile, false, kStreamBK<MF>, 4, false, 16 * MF, 4, 4>;
 
 template <int MF>
 __global__ __launch_bounds__(256) void gate_skinny_stream(GateArgs a, float* partial, int S) {
@@ -601,19 +605,26 @@ int skinny_splits(int K, int N) {
   return max(S, 1);
 }
 
-bool use_skinny(int dtype, int T, int K) { return dtype == 1 && T <= 64 && K % 32 == 0; }
 bool use_stream(int K) { return K % 64 == 0; }
+// 65 to 128 tokens: the streaming kernel only (the register-staged partial
+// kernel would need twice its registers for 8 row fragments)
+bool use_skinny(int dtype, int T, int K) {
+  return dtype == 1 && K % 32 == 0 && (T <= 64 || (T <= 128 && use_stream(K)));
+}
 
 // Splits of the streaming kernel: about one workgroup per CU (kStreamWgs
 // in all; fewer, longer streams also leave fewer partials to sum), at most one
 // per 64-wide K chunk.
 constexpr int kStreamWgs = 256;
-int stream_splits(int K, int N) {
+int stream_splits(int K, int N, int T) {
   const int nt = N / kTile;
-  return max(1, min(kStreamWgs / nt, K / 64));
+  const int wgs = T > 64 ? kStreamWgs8 : kStreamWgs;
+  return max(1, min(wgs / nt, K / 64));
 }
 
-int few_token_splits(int K, int N) { return use_stream(K) ? stream_splits(K, N) : skinny_splits(K, N); }
+int few_token_splits(int K, int N, int T) {
+  return use_stream(K) ? stream_splits(K, N, T) : skinny_splits(K, N);
+}
 
 
 }  // namespace
@@ -621,8 +632,8 @@ int few_token_splits(int K, int N) { return use_stream(K) ? stream_splits(K, N) 
 size_t gate_workspace_bytes(int dtype, int T, int K, int N) {
   if (!use_skinny(dtype, T, K)) return 0;
   const int nt = N / kTile;
-  const int S = few_token_splits(K, N);
-  const size_t part = T <= 32 ? Skinny<2>::PART : Skinny<4>::PART;
+  const int S = few_token_splits(K, N, T);
+  const size_t part = T <= 32 ? Skinny<2>::PART : T <= 64 ? Skinny<4>::PART : Skinny<8>::PART;
   return (size_t)nt * S * part * 4;
 }
 
@@ -645,7 +656,7 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
     // rounding per instruction) the total is below u (2 steps + S + 11)
     // ||x|| ||w||, which 4u (steps + S + 2) covers.
     const bool strm = use_stream(K);
-    const int S = few_token_splits(K, N);
+    const int S = few_token_splits(K, N, T);
     const int steps = strm ? 2 * ((K / 64 + S - 1) / S) : kSkinnySteps + 2;
     a.gb.coef_xw = 0x1p-22f * (float)(steps + S + 2);
     float* partial = (float*)gate_ws;
@@ -654,10 +665,13 @@ hipError_t launch_gate_twell(int dtype, const void* x, const void* wg_t, const f
       if (strm) hipLaunchKernelGGL(gate_skinny_stream<2>, gp, blk, 0, stream, a, partial, S);
       else hipLaunchKernelGGL(gate_skinny_partial<2>, gp, blk, 0, stream, a, partial, S);
       hipLaunchKernelGGL(gate_skinny_epilogue<2>, dim3((unsigned)(nt * 2)), blk, 0, stream, a, partial, S);
-    } else {
+    } else if (T <= 64) {
       if (strm) hipLaunchKernelGGL(gate_skinny_stream<4>, gp, blk, 0, stream, a, partial, S);
       else hipLaunchKernelGGL(gate_skinny_partial<4>, gp, blk, 0, stream, a, partial, S);
       hipLaunchKernelGGL(gate_skinny_epilogue<4>, dim3((unsigned)(nt * 4)), blk, 0, stream, a, partial, S);
+    } else {  // use_skinny: d_model % 64 == 0 here
+      hipLaunchKernelGGL(gate_skinny_stream<8>, gp, blk, 0, stream, a, partial, S);
+      hipLaunchKernelGGL(gate_skinny_epilogue<8>, dim3((unsigned)(nt * 8)), blk, 0, stream, a, partial, S);
     }
   } else if (dtype == 1 && K % GateGemm::BK == 0) {
     int wide_nt, narrow_nt;

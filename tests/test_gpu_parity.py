@@ -234,6 +234,9 @@ def test_dense_reference_few_tokens(T, K, N):
     (64, 2048, 2048, 2.0, 8),   # split-K gate, several splits per tile
     (17, 4096, 1408, 2.3, 8),   # ragged row fragment, long K
     (5, 2048, 8192, 2.0, 8),    # one workgroup per column tile, ragged rows
+    (65, 512, 1024, 1.5, 8),    # streaming gate with 8 row fragments, one valid row in the last
+    (96, 1088, 2048, 1.8, 8),   # 8 row fragments, K not a multiple of 128
+    (128, 2048, 5632, 2.3, 8),  # most tokens of the streaming gate
     (100, 264, 640, 1.5, 4),    # two-pass sparse kernels with K % 32 != 0, routing
     (256, 512, 1024, 1.9, 8),   # largest token count of the two-pass kernels
     (256, 512, 1024, 1.2, 8),   # many routed rows, route scan inside the routed gate+up kernel
