@@ -264,6 +264,20 @@ int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t,
                                          (hipStream_t)stream));
 }
 
+int32_t sparse_ffn_fwd_union(const sffn_shape* shape, const void* x, const void* wu_t,
+                             const void* wd, const uint16_t* count, const uint16_t* idx,
+                             const void* val, void* y, void* stream) {
+  int32_t st = check_shape(shape);
+  if (st != SFFN_OK) return st;
+  if (!union_supported(shape->dtype, shape->d_model, shape->cap)) return SFFN_ERR_UNSUPPORTED;
+  if (shape->T == 0) return SFFN_OK;
+  if (!ptrs_ok({x, wu_t, wd, count, y})) return SFFN_ERR_ARG;
+  if (shape->cap > 0 && !ptrs_ok({idx, val})) return SFFN_ERR_ARG;
+  return hip_status(launch_sparse_union(x, wu_t, wd, count, idx, val, y, shape->T,
+                                        shape->d_model, shape->d_ff / 128, shape->cap,
+                                        (hipStream_t)stream));
+}
+
 int32_t hybrid_route(const sffn_shape* shape, const void* x, const void* wg_t, const float* b_g,
                      const void* wu_t, const void* wd, const uint16_t* count, int32_t* routed,
                      int32_t* n_routed, void* workspace, size_t ws_bytes, void* y, void* stream) {

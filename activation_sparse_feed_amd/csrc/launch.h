@@ -152,6 +152,13 @@ hipError_t launch_sparse_updown(int dtype, const void* x, const void* wu_t, cons
                                 void* y, void* ws, int T, int K, int n_tiles, int cap,
                                 hipStream_t stream);
 
+// The column-union variant of the fused kernel (union.hip): bf16, d_model in
+// {512, 1024, 2048, 4096}, cap <= 32.
+bool union_supported(int dtype, int d_model, int cap);
+hipError_t launch_sparse_union(const void* x, const void* wu_t, const void* wd,
+                               const uint16_t* count, const uint16_t* idx, const void* val,
+                               void* y, int T, int K, int n_tiles, int cap, hipStream_t stream);
+
 // Routing scan: the routed-row mask (one 16-bit word per 16 rows, at the
 // start of ws), then the ascending compaction into routed and n_routed.
 size_t route_workspace_bytes(int T);

@@ -23,7 +23,8 @@ WS_HYBRID, WS_DENSE, WS_SPARSE, WS_PACK, WS_CONVERT, WS_PACK_L1, WS_BACKWARD = 0
 TILE = 128
 
 EXPORTED = ("twell_weight_norms", "twell_pack", "twell_pack_noalloc",
-            "twell_pack_noalloc_max_bytes", "twell_pack_l1", "sparse_ffn_fwd", "hybrid_route",
+            "twell_pack_noalloc_max_bytes", "twell_pack_l1", "sparse_ffn_fwd", "sparse_ffn_fwd_union",
+            "hybrid_route",
             "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
             "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
             "sffn_probe_cached", "sffn_probe_gather", "sffn_probe_bf16_round",
@@ -55,6 +56,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.twell_pack_noalloc_max_bytes.restype = sz
     lib.twell_pack_l1.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
     lib.sparse_ffn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sparse_ffn_fwd_union.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hybrid_route.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.dense_ffn_ref.argtypes = [sp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.gate_preact.argtypes = [sp, vp, vp, vp, vp, vp]
@@ -70,7 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.twell_from_preact.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ell_from_preact.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("twell_weight_norms", "twell_pack", "twell_pack_noalloc", "twell_pack_l1",
-               "sparse_ffn_fwd", "hybrid_route", "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
+               "sparse_ffn_fwd", "sparse_ffn_fwd_union", "hybrid_route", "dense_ffn_ref", "sparse_ffn_bwd", "gate_preact", "twell_from_preact",
                "ell_from_preact", "sffn_probe_hbm", "sffn_probe_mfma", "sffn_probe_mfma_step",
                "sffn_probe_cached", "sffn_probe_gather", "sffn_probe_bf16_round"):
         getattr(lib, fn).restype = i32
@@ -190,6 +192,12 @@ def sparse_ffn_fwd(shape: Shape, x, wu_t, wd, count, idx, val, y, workspace=None
     _check("sparse_ffn_fwd", _lib.sparse_ffn_fwd(
         ctypes.byref(shape), _ptr(x), _ptr(wu_t), _ptr(wd), _ptr(count), _ptr(idx), _ptr(val),
         _ptr(y), _ptr(workspace), ws_n, _stream(stream)))
+
+
+def sparse_ffn_fwd_union(shape: Shape, x, wu_t, wd, count, idx, val, y, stream=None) -> None:
+    _check("sparse_ffn_fwd_union", _lib.sparse_ffn_fwd_union(
+        ctypes.byref(shape), _ptr(x), _ptr(wu_t), _ptr(wd), _ptr(count), _ptr(idx), _ptr(val),
+        _ptr(y), _stream(stream)))
 
 
 def hybrid_route(shape: Shape, x, wg_t, b_g, wu_t, wd, count, routed, n_routed, workspace, y,

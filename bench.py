@@ -587,6 +587,37 @@ def main() -> int:
         }
         del z, tw, ell, ws_c
 
+    # ---- the column-union organisation of the fused kernel (the token block's
+    # distinct columns staged once in LDS) on the same TwELL, against the row
+    # walk of sparse_ffn_fwd: K calls each back to back, then y compared
+    union = None
+    if w.dtype == "bf16" and w.d_model in (512, 1024, 2048, 4096) and w.cap <= 32:
+        y_u = torch.empty_like(ffn.y)
+        ffn.forward(x, wg, b, wu, wd, wg_norms)
+        for _ in range(2):
+            sffn.sparse_ffn_fwd_union(s, x, wu, wd, ffn.count, ffn.idx, ffn.val, y_u)
+        u0, u1, u2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
+        torch.cuda.synchronize()
+        u0.record()
+        for _ in range(K):
+            sffn.sparse_ffn_fwd_union(s, x, wu, wd, ffn.count, ffn.idx, ffn.val, y_u)
+        u1.record()
+        for _ in range(K):
+            sffn.sparse_ffn_fwd(s, x, wu, wd, ffn.count, ffn.idx, ffn.val, ffn.y, ffn.ws_sparse)
+        u2.record()
+        torch.cuda.synchronize()
+        t_union, t_walk = u0.elapsed_time(u1) / K, u1.elapsed_time(u2) / K
+        keep = torch.ones(w.T, dtype=torch.bool, device="cuda")
+        keep[ffn.routed[:int(ffn.n_routed.item())].long()] = False
+        yu_, yw_ = y_u[keep].float(), ffn.y[keep].float()
+        cnt_u = ffn.count.to(torch.int64)
+        live_u = nnz_live_of(cnt_u[keep], w.cap)
+        union = {"sparse_ffn_fwd_union_ms": t_union, "sparse_ffn_fwd_ms": t_walk,
+                 "union_over_row_walk": t_union / t_walk,
+                 "union_gflop_per_s": 4.0 * w.d_model * live_u / (t_union * 1e-3) / 1e9,
+                 "y_rel_diff_vs_row_walk": float(((yu_ - yw_).norm() / yw_.norm().clamp_min(1e-30)).item())}
+        del y_u
+
     # ---- the L1 regulariser fused into the gate epilogue: twell_pack_l1 against
     # twell_pack, K calls each back to back
     l1 = None
@@ -777,6 +808,7 @@ def main() -> int:
         "cold": cold,
         "torch_dense_ms": t_torch,
         "separate_conversion": conversion,
+        "union_variant": union,
         "l1_regulariser": l1,
         "backward": backward,
         "dense_tokens_per_s": (T / (t_dense * 1e-3)) if t_dense else None,

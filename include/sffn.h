@@ -192,6 +192,24 @@ int32_t sparse_ffn_fwd(const sffn_shape* shape, const void* x, const void* wu_t,
                        void* stream);
 
 /*
+ * sparse_ffn_fwd_union -- the same sum as sparse_ffn_fwd, computed with the
+ * organisation of the pages' fused kernel (pwwt.cn article, section 02): per
+ * block of consecutive tokens, the active columns the block shares within a
+ * column tile are deduplicated, and the wu_t and wd rows of each distinct
+ * column are read from global memory once per block into LDS, where every
+ * token of the block that uses the column reads them.  A measured alternative
+ * to sparse_ffn_fwd (which walks each token's entries against rows served by
+ * the caches); y agrees with it to float32 rounding of the down projection,
+ * not bit for bit.  Rows with any count above cap are not touched.
+ * Supported: dtype SFFN_BF16, d_model in {512, 1024, 2048, 4096},
+ * cap <= 32 (else SFFN_ERR_UNSUPPORTED, nothing written).  No workspace; no
+ * state between calls.
+ */
+int32_t sparse_ffn_fwd_union(const sffn_shape* shape, const void* x, const void* wu_t,
+                             const void* wd, const uint16_t* count, const uint16_t* idx,
+                             const void* val, void* y, void* stream);
+
+/*
  * hybrid_route -- route overflowing rows to a dense fallback (pwwt.cn article,
  * section 03: rare high-activity tokens go to a dense backup path on the
  * matrix cores).

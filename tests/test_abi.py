@@ -115,6 +115,20 @@ def test_workspace_errors(sffn):
     assert sffn.workspace_bytes(_shape(sffn, T=4096), sffn.WS_SPARSE) == 0
 
 
+def test_union_variant_refuses_unsupported_shapes(sffn):
+    # checked on the host before any launch: d_model outside {512, ..., 4096},
+    # cap above 32, float32
+    lib = sffn._lib
+    for d_model, cap, dt in ((768, 8, sffn.SFFN_BF16), (512, 33, sffn.SFFN_BF16),
+                             (512, 8, sffn.SFFN_F32), (8192, 8, sffn.SFFN_BF16)):
+        s = sffn.make_shape(16, d_model, 1024, cap, dt)
+        assert lib.sparse_ffn_fwd_union(ctypes.byref(s), P, P, P, P, P, P, P, None) == -2
+    s = sffn.make_shape(16, 512, 1000, 8, sffn.SFFN_BF16)  # d_ff not a multiple of 128
+    assert lib.sparse_ffn_fwd_union(ctypes.byref(s), P, P, P, P, P, P, P, None) == -2
+    s = sffn.make_shape(16, 512, 1024, 8, sffn.SFFN_BF16)
+    assert lib.sparse_ffn_fwd_union(ctypes.byref(s), P, None, P, P, P, P, P, None) == -1
+
+
 def test_workspace_query_of_invalid_shape_is_zero(sffn):
     assert sffn.workspace_bytes(_shape(sffn, tile=32), sffn.WS_DENSE) == 0
     assert sffn.workspace_bytes(_shape(sffn), 9) == 0
