@@ -16,7 +16,8 @@
 //                 iters < 8192), which also checks that every MFMA ran.
 //   probe_cached  every workgroup reads the same small window (resident in
 //                 each XCD's L2 after the first pass) many times with 16-byte
-//                 loads, four in flight per lane: the rate at which the
+//                 loads, eight in flight per lane (four reach only about 60%
+//                 of the rate): the rate at which the
 //                 vector-memory path brings cached data into the CUs, the
 //                 ceiling of any kernel that gathers rows it re-reads from L2.
 //   probe_gather  one wave per listed row reads that row of two matrices
@@ -85,15 +86,19 @@ __global__ __launch_bounds__(kProbeBlock) void probe_mfma(float* __restrict__ ou
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+constexpr int kCachedInflight = 8;  // 16-byte loads in flight per lane
+
 __global__ __launch_bounds__(kProbeBlock) void probe_cached(const u32x4_t* __restrict__ src,
                                                             size_t n16, int reps) {
   uint32_t acc = 0;
   for (int r = 0; r < reps; ++r) {
     size_t i = threadIdx.x;
-    for (; i + 3 * kProbeBlock < n16; i += 4 * kProbeBlock) {
-      const u32x4_t v0 = src[i], v1 = src[i + kProbeBlock], v2 = src[i + 2 * kProbeBlock],
-                    v3 = src[i + 3 * kProbeBlock];
-      acc ^= (v0.x ^ v1.y) ^ (v2.z ^ v3.w);
+    for (; i + (kCachedInflight - 1) * kProbeBlock < n16; i += kCachedInflight * kProbeBlock) {
+      u32x4_t v[kCachedInflight];
+#pragma unroll
+      for (int q = 0; q < kCachedInflight; ++q) v[q] = src[i + q * kProbeBlock];
+#pragma unroll
+      for (int q = 0; q < kCachedInflight; ++q) acc ^= v[q].x ^ v[q].w;
     }
     for (; i < n16; i += kProbeBlock) acc ^= src[i].x;
   }

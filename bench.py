@@ -103,7 +103,7 @@ def measured_peaks() -> dict:
             "cached_load_gb_s": float(cwg) * reps * win / t_cached / 1e9,
             "probe": "sffn_probe_hbm over 1 GiB, 65536 workgroups (read-only; copy counts read + write), "
                      "sffn_probe_mfma 4096 workgroups x 4 waves x 16 chains x 1024 MFMAs, "
-                     "sffn_probe_cached 2048 workgroups x 24 passes over one 2 MiB window"}
+                     "sffn_probe_cached 2048 workgroups x 24 passes over one 2 MiB window, 8 loads in flight per lane"}
 
 
 def gather_probe(wu, wd, idx_live, flush) -> dict:

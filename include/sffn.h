@@ -381,7 +381,7 @@ int32_t sffn_probe_mfma(float* out, int32_t workgroups, int32_t iters, void* str
 
 /*
  * sffn_probe_cached -- `workgroups` workgroups of 256 threads each read the
- * same window [src, src + window_bytes) `reps` times with 16-byte loads, four
+ * same window [src, src + window_bytes) `reps` times with 16-byte loads, eight
  * in flight per lane (workgroups * reps * window_bytes bytes in all).  With a
  * window that fits the L2 of an XCD (a few MiB) this is the rate at which the
  * vector-memory path brings cached data into the CUs: the ceiling of a kernel
