@@ -82,6 +82,7 @@ def test_union_decode_d4096():
     (1, 512, 1024, 1.2, 32),     # one token, one partly filled block
     (37, 1024, 2048, 1.6, 16),   # ragged last block, unions larger than one staged chunk
     (300, 512, 1152, 2.0, 4),    # routed rows, ragged tail, 9 tiles
+    (64, 512, 1024, 3.0, 0),     # capacity 0: every row with an active entry routed, the rest 0
 ])
 def test_union_small_shapes(T, d_model, d_ff, beta, cap):
     inp = wl.generate_custom(T, d_model, d_ff, "bf16", beta, seed_base=70 + T, cap=cap)
