@@ -83,6 +83,7 @@ def test_union_decode_d4096():
     (37, 1024, 2048, 1.6, 16),   # ragged last block, unions larger than one staged chunk
     (300, 512, 1152, 2.0, 4),    # routed rows, ragged tail, 9 tiles
     (64, 512, 1024, 3.0, 0),     # capacity 0: every row with an active entry routed, the rest 0
+    (520, 4096, 2048, 2.3, 8),   # d_model 4096 (8 tokens per workgroup, 8 staged columns), 65 blocks
 ])
 def test_union_small_shapes(T, d_model, d_ff, beta, cap):
     inp = wl.generate_custom(T, d_model, d_ff, "bf16", beta, seed_base=70 + T, cap=cap)
