@@ -249,6 +249,16 @@ def test_few_token_paths(T, K, N, beta, cap):
         assert e["n_routed"] > 10
 
 
+@pytest.mark.parametrize("T,K,N,beta,cap", [
+    (300, 1024, 1024, 0.8, 32),  # windowed kernel at its largest capacity: up to 128 listed entries per window
+    (300, 1024, 1024, 0.8, 40),  # capacity above 32: the per-token kernel instead of the windowed one
+])
+def test_many_token_capacity_bounds(T, K, N, beta, cap):
+    inp = wl.generate_custom(T=T, d_model=K, d_ff=N, dtype="bf16", beta=beta, seed_base=43)
+    e = compare(inp, cap)
+    assert 0 < e["n_routed"] < T
+
+
 # ---------------------------------------------------------------- edge cases
 def _small(beta, dtype="bf16", T=64, seed=21):
     return wl.generate_custom(T=T, d_model=256, d_ff=512, dtype=dtype, beta=beta, seed_base=seed)
